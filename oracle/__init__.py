@@ -1,0 +1,8 @@
+"""CPU oracle for the MoE sublayer and the FarSkip stack (test infrastructure only).
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg import this package.
+"""
+from .moe_oracle import *  # noqa: F401,F403
+from .moe_oracle import (router_logits, select_topk, gate_scores, gate_weights, route, permute,
+                         permute_rows, silu, mlp, grouped_mlp, shared_mlp, combine, moe_layer,
+                         farskip_stack, moe_stack, round_to_bf16, topk_gap)

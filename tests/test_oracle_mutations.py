@@ -1,0 +1,139 @@
+"""Planted mistakes in the oracle must make its pins fail.
+
+Each case swaps one oracle function for a plausibly wrong variant (on the CPU, inside this test
+only) and runs the pins that should catch it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as om
+from tests import test_oracle_pins as pins
+
+
+def _mlp_gate_up_swapped(X, W1, W2, W3):
+    X = np.asarray(X, np.float64)
+    return ((X @ np.asarray(W2, np.float64).T) * om.silu(X @ np.asarray(W1, np.float64).T)) @ np.asarray(W3, np.float64).T
+
+
+def _mlp_w3_untransposed(X, W1, W2, W3):
+    X = np.asarray(X, np.float64)
+    H = (X @ np.asarray(W1, np.float64).T) * om.silu(X @ np.asarray(W2, np.float64).T)
+    return H @ np.asarray(W3, np.float64)
+
+
+def _mlp_sigmoid_not_silu(X, W1, W2, W3):
+    X = np.asarray(X, np.float64)
+    G = X @ np.asarray(W2, np.float64).T
+    H = (X @ np.asarray(W1, np.float64).T) * (1 / (1 + np.exp(-G)))
+    return H @ np.asarray(W3, np.float64).T
+
+
+def _scores_softmax_wrong_sign(logits, gate):
+    L = np.asarray(logits, np.float64)
+    if gate == "softmax":
+        e = np.exp(-(L - L.min(1, keepdims=True)))
+        return e / e.sum(1, keepdims=True)
+    return 1 / (1 + np.exp(-L))
+
+
+def _weights_softmax_over_k(logits, idx, gate, renormalize):
+    sel = np.take_along_axis(np.asarray(logits, np.float64), np.asarray(idx, np.int64), 1)
+    p = om.gate_scores(sel, gate)
+    return p / p.sum(1, keepdims=True) if renormalize else p
+
+
+def _topk_ties_to_higher_index(logits, k):
+    L = np.asarray(logits, np.float64)
+    E = L.shape[1]
+    order = np.argsort(-L[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int32)
+
+
+def _topk_unordered(logits, k):
+    return np.sort(ORIG["select_topk"](logits, k), axis=1)
+
+
+def _permute_unstable(topk_idx, E):
+    off, src, dest = ORIG["permute"](topk_idx, E)
+    src = src.copy()
+    for e in range(E):
+        src[off[e]:off[e + 1]] = src[off[e]:off[e + 1]][::-1]
+    dest = np.empty_like(src)
+    dest[src] = np.arange(src.size)
+    return off, src, dest
+
+
+def _permute_offsets_shifted(topk_idx, E):
+    off, src, dest = ORIG["permute"](topk_idx, E)
+    return np.concatenate([[0], off[:-1]]).astype(np.int32), src, dest
+
+
+def _combine_weight_index_reversed(Y, topk_w, dest_row, addend=None, residual=None):
+    return ORIG["combine"](Y, np.asarray(topk_w)[:, ::-1], dest_row, addend, residual)
+
+
+def _combine_dropped_last_slot(Y, topk_w, dest_row, addend=None, residual=None):
+    w = np.array(topk_w, np.float64, copy=True)
+    w[:, -1] = 0
+    return ORIG["combine"](Y, w, dest_row, addend, residual)
+
+
+def _stack_partial_without_residual(o0, layers, mode, mask=None, round_inputs=None, record=None):
+    # partial input taken as S_k alone (o_{k-1} dropped)
+    n = len(layers)
+    mask = [1] * n if mask is None else list(mask)
+    o_prev = np.asarray(o0, np.float64)
+    x = o_prev
+    for j, (sf, rf) in enumerate(layers):
+        S, R = sf(x), rf(x)
+        o = o_prev + S + R
+        x_next = o if (mode == "none" or not mask[j]) else (S if mode == "partial" else o_prev)
+        o_prev, x = o, x_next
+    return o_prev
+
+
+def _stack_outdated_as_current(o0, layers, mode, mask=None, round_inputs=None, record=None):
+    return ORIG["farskip_stack"](o0, layers, "none" if mode == "outdated" else mode, mask, round_inputs, record)
+
+
+def _stack_dropped_o0(o0, layers, mode, mask=None, round_inputs=None, record=None):
+    return ORIG["farskip_stack"](o0, layers, mode, mask, round_inputs, record) - np.asarray(o0, np.float64)
+
+
+ORIG = {name: getattr(om, name) for name in ("select_topk", "permute", "combine", "farskip_stack", "mlp",
+                                            "gate_scores", "gate_weights")}
+
+GOLDEN_ROUTED = [lambda c=c: pins.test_routed_layer_golden(c) for c in range(6)]
+GOLDEN_STACK = [lambda c=c: pins.test_stack_golden_scalar(c) for c in range(5)]
+
+CASES = [
+    ("mlp", _mlp_gate_up_swapped, [pins.test_mlp_golden]),
+    ("mlp", _mlp_w3_untransposed, [pins.test_mlp_golden]),
+    ("mlp", _mlp_sigmoid_not_silu, [pins.test_mlp_golden]),
+    ("gate_scores", _scores_softmax_wrong_sign, [pins.test_softmax_scores_sum_to_one_and_k_equals_E] + GOLDEN_ROUTED),
+    ("gate_weights", _weights_softmax_over_k, GOLDEN_ROUTED),
+    ("select_topk", _topk_ties_to_higher_index, [lambda: pins.test_topk_exhaustive_small(3)]),
+    ("select_topk", _topk_unordered, [lambda: pins.test_topk_exhaustive_small(4)]),
+    ("permute", _permute_unstable, [pins.test_permute_bruteforce_all_maps_T2_k2_E3]),
+    ("permute", _permute_offsets_shifted, [pins.test_permute_bruteforce_all_maps_T2_k2_E3]),
+    ("combine", _combine_weight_index_reversed, GOLDEN_ROUTED + [pins.test_combine_is_linear_in_weights_and_uses_dest_rows]),
+    ("combine", _combine_dropped_last_slot, GOLDEN_ROUTED + [pins.test_topk_equals_E_softmax_is_the_full_weighted_sum]),
+    ("farskip_stack", _stack_partial_without_residual, GOLDEN_STACK),
+    ("farskip_stack", _stack_outdated_as_current, GOLDEN_STACK),
+    ("farskip_stack", _stack_dropped_o0, GOLDEN_STACK),
+]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=[c[1].__name__.lstrip("_") for c in CASES])
+def test_planted_mistake_is_caught(i, monkeypatch):
+    name, bad, pin_fns = CASES[i]
+    monkeypatch.setattr(om, name, bad)
+    monkeypatch.setattr(oracle, name, bad)
+    caught = 0
+    for fn in pin_fns:
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {bad.__name__}"
