@@ -1,0 +1,230 @@
+"""Benchmark: the DeepSeek-V3-shaped 4-layer FarSkip MoE stack on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload dsv3-stack]
+
+One step = one farskip_stack_forward over the whole hot path (router, top-k, permutation, routed
+grouped SwiGLU GEMM, shared expert, combine, FarSkip wiring) for T tokens through L layers, with
+the inputs and weights already resident in HBM.  Layer k's routed work runs on the main HIP stream
+while layer k+1's router and shared expert run on a second stream.
+
+Prints one JSON line.  value = T * L / step time: tokens through one MoE sublayer per second
+(routed tokens/s of the metric).  The roofline object reports the dominant kernel (the grouped
+gate/up GEMM, 2/3 of the routed FLOPs) from HIP-event timings recorded live on its own stream
+during the timed steps.  cpu_baseline times the CPU oracle on a bounded sample of tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s + MFMA util, bf16 MoE layer (DeepSeek-V3 shape), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="dsv3-stack")
+    p.add_argument("--mode", default="partial", choices=["none", "partial", "outdated"])
+    p.add_argument("--single-stream-steps", type=int, default=3,
+                   help="extra steps with both streams merged into one (overlap reference); 0 = skip")
+    p.add_argument("--cpu-sample", type=int, default=4, help="tokens in the CPU-oracle sample; 0 = skip")
+    return p.parse_args()
+
+
+def kernel_report(prof: dict, c, steps: int) -> dict:
+    """Per-kind averages and the algorithmic throughput of each kernel kind."""
+    T, d, E, k, c_, cs = c.T, c.d, c.E, c.k, c.c, c.shared_width
+    N = T * k
+    per_launch = {  # (algorithmic work per launch, unit)
+        "router_gemm": (2.0 * T * d * E, "flop"),
+        "topk": (T * E * 4.0 + T * k * 8.0, "byte"),
+        "permute_index": (N * 4.0 * 4 + (E + 1) * 4.0, "byte"),   # read idx twice, write 2 arrays
+        "permute_rows": (T * d * 2.0 + N * d * 2.0 + N * 4.0, "byte"),
+        "gemm_gate_up": (4.0 * N * d * c_, "flop"),
+        "gemm_down": (2.0 * N * d * c_, "flop"),
+        "dense_gate_up": (4.0 * T * d * cs, "flop"),
+        "dense_down": (2.0 * T * d * cs, "flop"),
+        "combine": (N * d * 2.0 + N * 8.0 + T * d * (2.0 + 4.0 + 4.0), "byte"),
+        "layer_input": (T * d * (4.0 + 2.0 + 2.0), "byte"),
+    }
+    out = {}
+    for kind, (n, ms) in prof.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        row = {"launches": n, "avg_ms": round(avg, 4), "ms_per_step": round(ms / steps, 3)}
+        if kind in per_launch:
+            work, unit = per_launch[kind]
+            if unit == "flop":
+                row["tflops"] = round(work / (avg * 1e-3) / 1e12, 1)
+                row["frac_mfma_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+            else:
+                row["gbs"] = round(work / (avg * 1e-3) / 1e9, 1)
+                row["frac_hbm_peak"] = round(row["gbs"] / PEAK_HBM_GBS, 4)
+        out[kind] = row
+    return out
+
+
+def cpu_baseline(c, layers, o0, n_tokens: int) -> dict:
+    """The CPU oracle as it stands, on n_tokens seeded tokens through all layers of the stack.
+    Expert weights are copied from the device on demand; the copy time is measured and excluded."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import oracle
+
+    fetch = [0.0]
+
+    class Slices:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            t0 = time.perf_counter()
+            host = self.t[int(e)].float().cpu().numpy()
+            fetch[0] += time.perf_counter() - t0
+            return host
+
+    def small(t):
+        if t is None:
+            return None
+        t0 = time.perf_counter()
+        a = t.float().cpu().numpy()
+        fetch[0] += time.perf_counter() - t0
+        return a
+
+    Wo = [{"W_R": small(W["W_R"]), "bias": small(W["bias"]), "W1": Slices(W["W1"]), "W2": Slices(W["W2"]),
+           "W3": Slices(W["W3"]), "Ws1": small(W["Ws1"]), "Ws2": small(W["Ws2"]), "Ws3": small(W["Ws3"])}
+          for W in layers]
+    rows = mi.sample_rows(c.T, n_tokens, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 7))
+    x0 = o0[rows.to(o0.device)].cpu().numpy()
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.moe_stack(x0, Wo, c.k, c.gate, c.renormalize, "partial", None, c.n_shared, c.c_shared)
+    wall = time.perf_counter() - t0
+    compute = max(wall - fetch[0], 1e-9)
+    return {"value": round(n_tokens * c.layers / compute, 3), "unit": "tokens/s", "cores":
+            threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{n_tokens} seeded tokens of the {c.name} workload through all {c.layers} layers "
+                      f"(float64 NumPy oracle; {compute:.1f} s compute, {fetch[0]:.1f} s of device-to-host "
+                      f"weight copies excluded)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU expert-parallel "
+              "path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_inputs as mi
+    from mixture_experts_layer_sum_amd import ops
+
+    c = mi.BY_NAME[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"workload {c.name}: T={c.T} d={c.d} E={c.E} k={c.k} c={c.c} shared={c.shared_width} L={c.layers}")
+    t0 = time.perf_counter()
+    layers = []
+    for j in range(c.layers):
+        layers.append(mi.layer_weights(c, j, dev))
+        torch.cuda.synchronize()
+        log(f"layer {j} weights generated ({time.perf_counter() - t0:.1f} s)")
+    o0 = mi.activations(c, dev).float()
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_workspace_bytes(cfg), dev)
+    oL = torch.empty_like(o0)
+    main_s = torch.cuda.current_stream()
+    side_s = torch.cuda.Stream()
+    log(f"workspace {ws.numel() / 2**30:.1f} GiB, HBM in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def step(ss):
+        ops.farskip_stack_forward(layers, cfg, args.mode, o0, oL, ws, s_main=main_s, s_side=ss)
+
+    for _ in range(args.warmup):
+        step(side_s)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    ops.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(side_s)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ops.profile_enable(False)
+    prof = ops.profile_collect()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step")
+    assert torch.isfinite(oL).all().item(), "non-finite stack output"
+
+    single_ms = None
+    if args.single_stream_steps > 0:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.single_stream_steps):
+            step(main_s)
+        torch.cuda.synchronize()
+        single_ms = (time.perf_counter() - t1) * 1e3 / args.single_stream_steps
+        log(f"one-stream reference: {single_ms:.2f} ms/step")
+
+    kernels = kernel_report(prof, c, args.steps)
+    g = kernels.get("gemm_gate_up", {})
+    flops_launch = 4.0 * c.T * c.k * c.d * c.c
+    roofline = {"kernel": "k_gemm_bf16 (grouped gate/up + SwiGLU, phase 1)", "bound": "mfma",
+                "achieved": g.get("tflops"), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": g.get("frac_mfma_peak"), "traffic": None,
+                "algorithmic_flop_per_launch": flops_launch, "avg_launch_ms": g.get("avg_ms")}
+
+    total_flop = c.layers * c.T * c.flops_per_token()["total"]
+    value = c.T * c.layers / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": c.name, "tokens": c.T, "d_model": c.d, "experts": c.E, "top_k": c.k,
+                   "expert_hidden": c.c, "shared_hidden": c.shared_width, "layers": c.layers,
+                   "gate": c.gate, "renormalize": c.renormalize, "farskip": args.mode, "streams": 2,
+                   "value_is": "tokens x layers / s"},
+        "routed_assignments_per_s": round(c.T * c.k * c.layers / (ms_per_step * 1e-3), 1),
+        "stack_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
+        "stack_frac_mfma_peak": round(total_flop / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "one_stream_ms_per_step": None if single_ms is None else round(single_ms, 3),
+        "two_stream_speedup": None if single_ms is None else round(single_ms / ms_per_step, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if args.cpu_sample > 0:
+        log("timing the CPU oracle on a token sample")
+        result["cpu_baseline"] = cpu_baseline(c, layers, o0, args.cpu_sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * farskip_moe.h -- C ABI of the MI355X (gfx950) MoE sublayer library, libfarskip_moe.so.
+ *
+ * One GPU's forward pass of a Mixture-of-Experts sublayer and of a FarSkip-Collective residual
+ * stack built from such sublayers.  The operations follow the page "FarSkip-Collective:
+ * Unhobbling Blocking Communication in Mixture of Experts Models" (papercache summary):
+ *   section 2.1, modern MLP equation:  MLP(A) = sigma(A W1^T . g(A W2^T)) W3^T,
+ *              W1, W2 in R^{c x d}, W3 in R^{d x c}; here g = SiLU, sigma = identity, '.' is
+ *              the elementwise product;
+ *   section 2.1, MoE equation:         MoE(A) = sum_j G(A)_j MLP^j(A), G(A) = s(A W_R^T);
+ *   section 2.1, Dispatch / Combine:   token rows are permuted into expert-contiguous order, and
+ *              the routed expert outputs are summed back per token;
+ *   section 3, eqs. (8a)/(8b):         the FarSkip inputs o*_k ("outdated" / "partial").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer to memory the caller owns (row-major, densely
+ *     packed, 16-byte aligned), unless the argument says "host".  The library never allocates,
+ *     frees or keeps device memory beyond the call, except that farskip_stack_forward creates
+ *     HIP events that it destroys before returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  All work is
+ *     enqueued asynchronously on it; results are valid once the stream has been synchronised.
+ *   - dtype: MOE_F32 (float32) or MOE_BF16 (bfloat16 storage, float32 accumulation).
+ *   - Return value: MOE_OK (0) or a negative moe_status_t.  Argument checks run on the host
+ *     before anything is enqueued; on an error nothing is enqueued and moe_last_error() returns a
+ *     message (thread-local).  A failed kernel launch returns MOE_ERR_HIP.  Data-dependent
+ *     preconditions (finite inputs, expert ids in [0, E), offsets non-decreasing) are the
+ *     caller's and are not checked on the device.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef FARSKIP_MOE_H
+#define FARSKIP_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, k > E, inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, alignment, E or k too large) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace pointer null or ws_bytes below the queried size */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate_t;
+typedef enum { FARSKIP_NONE = 0, FARSKIP_PARTIAL = 1, FARSKIP_OUTDATED = 2 } farskip_mode_t;
+
+/* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/*
+ * moe_route -- router logits and top-k gating (section 2.1: G(A) = s(A W_R^T), a linear
+ * classifier followed by a sparse selection s()).
+ *
+ *   A       [T, d] dtype      token activations
+ *   W_R     [E, d] dtype      router weight (logits = A W_R^T)
+ *   bias    [E] float32       optional per-expert logit bias (NULL = none)
+ *   logits  [T, E] float32    OUTPUT logits = A W_R^T + bias.  If A and W_R are both NULL,
+ *                             logits is instead an INPUT and only the selection runs (dtype,
+ *                             d and bias are then ignored).
+ *   topk_idx [T, k] int32     OUTPUT: per token the k experts with the largest logits, in
+ *                             descending logit order; equal logits go to the lower expert index.
+ *   topk_w  [T, k] float32    OUTPUT gate weights: gate = MOE_GATE_SOFTMAX -> softmax over all E
+ *                             logits, evaluated at the selected experts; MOE_GATE_SIGMOID ->
+ *                             1/(1+exp(-logit)).  renormalize != 0 divides by their sum over k.
+ * Limits: 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, bf16 needs d % 64 == 0.
+ */
+int moe_route(const void* A, const void* W_R, const float* bias, int dtype, int64_t T, int64_t d,
+              int32_t E, int32_t k, int gate, int renormalize, float* logits, int32_t* topk_idx,
+              float* topk_w, void* stream);
+
+/*
+ * moe_permute -- the Dispatch permutation of section 2.1 on one GPU: every (token t, slot i)
+ * pair becomes one row; rows are grouped by expert, and inside an expert ordered by the flat
+ * slot f = t*k + i (a stable counting sort).
+ *
+ *   topk_idx       [T, k] int32   expert of each slot (values in [0, E))
+ *   expert_offsets [E+1] int32    OUTPUT: rows of expert e are [offsets[e], offsets[e+1])
+ *   sorted_src     [T*k] int32    OUTPUT: flat slot placed at each row
+ *   dest_row       [T*k] int32    OUTPUT: row of each flat slot (inverse of sorted_src)
+ *   A              [T, d] dtype   token activations, may be NULL when A_perm is NULL
+ *   A_perm         [T*k, d] dtype OUTPUT (optional, NULL = skip): A_perm[dest_row[t*k+i]] = A[t]
+ *   ws, ws_bytes   scratch of at least moe_permute_workspace_bytes(T, E, k) bytes
+ * All outputs are deterministic (bit-identical from run to run).
+ */
+int moe_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_src,
+                int32_t* dest_row, void* A_perm, void* ws, size_t ws_bytes, void* stream);
+size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_grouped_swiglu -- the modern MLP of section 2.1 applied per group (expert):
+ * for rows r in [group_offsets[g], group_offsets[g+1]):
+ *     H[r] = (X[r] W1[g]^T) . SiLU(X[r] W2[g]^T)      (H kept in dtype, in the workspace)
+ *     Y[r] = H[r] W3[g]^T
+ *
+ *   X             [N, d] dtype     input rows, grouped (e.g. A_perm from moe_permute)
+ *   group_offsets [G+1] int32      device array, non-decreasing, offsets[0] = 0, offsets[G] = N
+ *   W1, W2        [G, c, d] dtype  up and gate projections (row-major c x d per group)
+ *   W3            [G, d, c] dtype  down projection (row-major d x c per group)
+ *   Y             [N, d] dtype     OUTPUT
+ *   ws, ws_bytes  scratch of at least moe_grouped_swiglu_workspace_bytes(N, G, c, dtype)
+ * A shared expert is the call with G = 1 and offsets {0, T}; several shared experts are one call
+ * with their hidden dimensions concatenated (c = n_shared * c_shared).
+ * Limits: bf16 needs d % 64 == 0 and c % 64 == 0.
+ */
+int moe_grouped_swiglu(const void* X, const int32_t* group_offsets, int32_t G, const void* W1,
+                       const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
+                       void* Y, void* ws, size_t ws_bytes, void* stream);
+size_t moe_grouped_swiglu_workspace_bytes(int64_t N, int32_t G, int64_t c, int dtype);
+
+/*
+ * moe_combine -- the Combine of section 2.1: routed expert outputs summed back per token.
+ *   out[t] = residual[t] + addend[t] + sum_{i<k} topk_w[t,i] * Y[dest_row[t*k+i]]
+ * accumulated in float32, slots in order i = 0..k-1 (deterministic, no atomics).
+ *
+ *   Y        [T*k, d] dtype   expert outputs in permuted row order
+ *   topk_w   [T, k] float32   gate weights
+ *   dest_row [T*k] int32      row of each flat slot (from moe_permute)
+ *   addend   [T, d] dtype     optional (NULL = 0), e.g. the shared-expert output
+ *   residual [T, d] float32   optional (NULL = 0), e.g. the residual stream o_{k-1}
+ *   out      [T, d] float32   OUTPUT; may alias residual (in-place update of the stream)
+ *   out_x    [T, d] dtype     optional OUTPUT: out rounded to dtype (next layer's input)
+ */
+int moe_combine(const void* Y, int dtype, const float* topk_w, const int32_t* dest_row, int64_t T,
+                int64_t d, int32_t k, const void* addend, const float* residual, float* out,
+                void* out_x, void* stream);
+
+/* One MoE sublayer's weights for farskip_stack_forward (device pointers, layouts as above). */
+typedef struct {
+  const void* W_R;   /* [E, d] */
+  const float* bias; /* [E] or NULL */
+  const void* W1;    /* [E, c, d] */
+  const void* W2;    /* [E, c, d] */
+  const void* W3;    /* [E, d, c] */
+  const void* Ws1;   /* [c_shared, d] or NULL when c_shared == 0 */
+  const void* Ws2;   /* [c_shared, d] */
+  const void* Ws3;   /* [d, c_shared] */
+} moe_layer_desc_t;
+
+/* Shapes and gating shared by every layer of a stack. */
+typedef struct {
+  int64_t T, d, c;   /* tokens, model width, routed expert hidden width */
+  int64_t c_shared;  /* total shared hidden width (n_shared * per-expert width), 0 = none */
+  int32_t E, k;      /* routed experts, experts per token */
+  int32_t gate;      /* moe_gate_t */
+  int32_t renormalize;
+  int32_t dtype;     /* moe_dtype_t of activations and weights */
+} moe_stack_cfg_t;
+
+/*
+ * farskip_stack_forward -- L MoE sublayers f_j = S_j + R_j (shared + routed) on the residual
+ * stream, wired as section 3 of the page describes:
+ *     o_j = o_{j-1} + S_j(x_j) + R_j(x_j),  x_1 = o_0, and
+ *     x_{j+1} = o_j                      if mode == FARSKIP_NONE or skip_mask[j] == 0,
+ *     x_{j+1} = o_{j-1} + S_j(x_j)       if mode == FARSKIP_PARTIAL  (eq. 8b, f* = shared expert),
+ *     x_{j+1} = o_{j-1}                  if mode == FARSKIP_OUTDATED (eq. 8a).
+ * The residual o_j is kept in float32; each layer input x_j is rounded to cfg->dtype.
+ * With the skip on, layer j+1's router and shared expert are enqueued on s_side while layer j's
+ * permutation, routed grouped GEMM and combine run on s_main (HIP events order the two).
+ * s_side == s_main gives the same results with everything serialised on one stream.
+ *
+ *   layers    host array [L] of device-pointer descriptors
+ *   cfg       host pointer
+ *   skip_mask host array [L] of 0/1, or NULL = skip on for every layer
+ *   o0        [T, d] float32 input o_0;  oL [T, d] float32 OUTPUT o_L (must not alias o0)
+ *   ws        scratch of at least farskip_stack_workspace_bytes(cfg) bytes
+ */
+int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg,
+                          int mode, const uint8_t* skip_mask, const float* o0, float* oL, void* ws,
+                          size_t ws_bytes, void* s_main, void* s_side);
+size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
+
+/*
+ * Kernel timing for measurement harnesses.  While enabled (process-wide), every kernel the
+ * library launches is bracketed by two timing hipEvents recorded on the stream it is launched on.
+ * moe_profile_collect waits for the recorded events, returns per-kind launch counts and summed
+ * durations (milliseconds), and clears the records.  Kinds are the moe_kernel_kind_t values; out
+ * must hold MOE_KERNEL_KINDS entries.  Disabled by default; enabling costs two event records per
+ * launch.
+ */
+typedef enum {
+  MOE_K_ROUTER_GEMM = 0,  /* logits = A W_R^T */
+  MOE_K_TOPK = 1,         /* top-k selection and gate weights */
+  MOE_K_PERMUTE_INDEX = 2,/* histogram + scan + stable rank (all three kernels) */
+  MOE_K_PERMUTE_ROWS = 3, /* A -> A_perm row copy */
+  MOE_K_TILE_TABLE = 4,   /* grouped GEMM M-tile table */
+  MOE_K_GEMM_GATE_UP = 5, /* grouped GEMM phase 1, G > 1: H = (X W1^T) . SiLU(X W2^T) */
+  MOE_K_GEMM_DOWN = 6,    /* grouped GEMM phase 2, G > 1: Y = H W3^T */
+  MOE_K_COMBINE = 7,      /* combine */
+  MOE_K_LAYER_INPUT = 8,  /* FarSkip layer input x = cast(o [+ S]) */
+  MOE_K_DENSE_GATE_UP = 9,/* phase 1 of a single-group call (e.g. the shared expert) */
+  MOE_K_DENSE_DOWN = 10,  /* phase 2 of a single-group call */
+  MOE_KERNEL_KINDS = 11
+} moe_kernel_kind_t;
+
+typedef struct {
+  int32_t count;   /* launches recorded */
+  double total_ms; /* summed event-to-event durations */
+} moe_kernel_time_t;
+
+int moe_profile_enable(int on);
+int moe_profile_collect(moe_kernel_time_t* out /* [MOE_KERNEL_KINDS] */);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FARSKIP_MOE_H */

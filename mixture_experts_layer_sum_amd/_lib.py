@@ -1,0 +1,90 @@
+"""ctypes loader for libfarskip_moe.so (the C ABI declared in include/farskip_moe.h).
+
+There is no fallback: if the library is missing or cannot be loaded, importing raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfarskip_moe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
+FARSKIP_NONE, FARSKIP_PARTIAL, FARSKIP_OUTDATED = 0, 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOPK = 1024, 32
+
+EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_swiglu",
+           "moe_grouped_swiglu_workspace_bytes", "moe_combine", "farskip_stack_forward",
+           "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect", "moe_last_error",
+           "moe_version")
+KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
+                "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("W_R", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("W1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("Ws1", ctypes.c_void_p),
+                ("Ws2", ctypes.c_void_p), ("Ws3", ctypes.c_void_p)]
+
+
+class StackCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("c", ctypes.c_int64),
+                ("c_shared", ctypes.c_int64), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
+class FarSkipMoEError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+def _declare(lib):
+    vp, i64, i32, i, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
+    lib.moe_route.argtypes = [vp, vp, vp, i, i64, i64, i32, i32, i, i, vp, vp, vp, vp]
+    lib.moe_route.restype = i
+    lib.moe_permute.argtypes = [vp, i, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_permute.restype = i
+    lib.moe_permute_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.moe_permute_workspace_bytes.restype = sz
+    lib.moe_grouped_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i, i64, i64, i64, vp, vp, sz, vp]
+    lib.moe_grouped_swiglu.restype = i
+    lib.moe_grouped_swiglu_workspace_bytes.argtypes = [i64, i32, i64, i]
+    lib.moe_grouped_swiglu_workspace_bytes.restype = sz
+    lib.moe_combine.argtypes = [vp, i, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.moe_combine.restype = i
+    lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,
+                                          ctypes.POINTER(ctypes.c_uint8), vp, vp, vp, sz, vp, vp]
+    lib.farskip_stack_forward.restype = i
+    lib.farskip_stack_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
+    lib.farskip_stack_workspace_bytes.restype = sz
+    lib.moe_profile_enable.argtypes = [i]
+    lib.moe_profile_enable.restype = i
+    lib.moe_profile_collect.argtypes = [ctypes.POINTER(KernelTime)]
+    lib.moe_profile_collect.restype = i
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    return lib
+
+
+def load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_sum_amd.build` "
+                          "(the HIP library is required, there is no fallback)")
+    return _declare(ctypes.CDLL(LIB_PATH))
+
+
+lib = load()
+
+
+def check(fn: str, rc: int) -> None:
+    if rc != MOE_OK:
+        raise FarSkipMoEError(fn, rc, lib.moe_last_error().decode(errors="replace"))

@@ -1,0 +1,389 @@
+// extern "C" entry points of libfarskip_moe: argument checks on the host, then kernel launches.
+// The FarSkip stack scheduler ("FarSkip-Collective" section 3, eqs. (8a)/(8b), and section 4's
+// explicit overlap on a second queue) lives at the end of this file.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace fsm {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+constexpr int64_t kMaxRows = 0x7FFFFFFF;
+
+int check_route(const void* A, const void* W_R, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                int gate, const float* logits, const int32_t* idx, const float* w) {
+  if ((A == nullptr) != (W_R == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: A and W_R must both be set or both be NULL");
+  if (T < 0 || T > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%lld out of range", (long long)T);
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: E=%d must be >= 1", E);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "moe_route: need 1 <= k <= E (k=%d, E=%d)", k, E);
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E=%d > %d", E, MOE_MAX_EXPERTS);
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "moe_route: k=%d > %d", k, MOE_MAX_TOPK);
+  if (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown gate %d", gate);
+  if (A) {
+    if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown dtype %d", dtype);
+    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "moe_route: d=%lld must be >= 1", (long long)d);
+    if (dtype == MOE_BF16 && d % 64 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 needs d %% 64 == 0 (d=%lld)", (long long)d);
+  }
+  if (T > 0 && (!logits || !idx || !w))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: logits, topk_idx and topk_w are required");
+  return MOE_OK;
+}
+
+int check_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k, const int32_t* idx,
+                  const int32_t* off, const int32_t* src, const int32_t* dest, const void* A_perm,
+                  const void* ws, size_t ws_bytes) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_permute: T=%lld < 0", (long long)T);
+  if (E < 1 || k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_permute: need E >= 1 and k >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E=%d > %d", E, MOE_MAX_EXPERTS);
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: k=%d > %d", k, MOE_MAX_TOPK);
+  if (T * int64_t(k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: T*k exceeds 2^31-1");
+  if (!off) return fail(MOE_ERR_INVALID_ARG, "moe_permute: expert_offsets is required");
+  if (T > 0 && (!idx || !src || !dest))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: topk_idx, sorted_src and dest_row are required");
+  if (A_perm) {
+    if (!A) return fail(MOE_ERR_INVALID_ARG, "moe_permute: A_perm given without A");
+    if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_permute: unknown dtype %d", dtype);
+    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "moe_permute: d=%lld must be >= 1", (long long)d);
+    if ((d * int64_t(esize(dtype))) % 16 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_permute: row bytes must be a multiple of 16");
+  }
+  const size_t need = permute_ws_bytes(T, E, k);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu bytes, need %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+int check_swiglu(const void* X, const int32_t* off, int32_t G, const void* W1, const void* W2, const void* W3,
+                 int dtype, int64_t N, int64_t d, int64_t c, const void* Y, const void* ws, size_t ws_bytes,
+                 const char* who) {
+  if (G < 1) return fail(MOE_ERR_INVALID_ARG, "%s: G=%d must be >= 1", who, G);
+  if (G > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d > %d", who, G, MOE_MAX_EXPERTS);
+  if (N < 0 || N > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "%s: N=%lld out of range", who, (long long)N);
+  if (d < 1 || c < 1) return fail(MOE_ERR_INVALID_ARG, "%s: d and c must be >= 1", who);
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (dtype == MOE_BF16 && (d % 64 != 0 || c % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs d %% 64 == 0 and c %% 64 == 0 (d=%lld, c=%lld)", who,
+                (long long)d, (long long)c);
+  if (!off || !W1 || !W2 || !W3) return fail(MOE_ERR_INVALID_ARG, "%s: offsets and weights are required", who);
+  if (N > 0 && (!X || !Y)) return fail(MOE_ERR_INVALID_ARG, "%s: X and Y are required", who);
+  if (c * d > (int64_t(1) << 40)) return fail(MOE_ERR_UNSUPPORTED, "%s: c*d too large", who);
+  const size_t need = swiglu_ws_bytes(N, G, c, dtype);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  return MOE_OK;
+}
+
+int check_combine(const void* Y, int dtype, const float* w, const int32_t* dest, int64_t T, int64_t d,
+                  int32_t k, const float* out) {
+  if (T < 0 || T > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "moe_combine: T=%lld out of range", (long long)T);
+  if (d < 1 || k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine: need d >= 1 and k >= 1");
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_combine: unknown dtype %d", dtype);
+  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: needs d %% 8 == 0 (d=%lld)", (long long)d);
+  if (T * int64_t(k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: T*k exceeds 2^31-1");
+  if (T > 0 && (!Y || !w || !dest || !out))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: Y, topk_w, dest_row and out are required");
+  return MOE_OK;
+}
+
+// ---- FarSkip stack workspace ---------------------------------------------------------------------
+struct StackWs {
+  void* x[2];
+  void* S[2];
+  float* logits[2];
+  int32_t* idx[2];
+  float* w[2];
+  int32_t* offsets;
+  int32_t* sorted_src;
+  int32_t* dest_row;
+  int32_t* shared_off;
+  void* perm_ws;
+  void* A_perm;
+  void* Y;
+  void* gemm_ws;
+  void* shared_ws;
+};
+
+StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total) {
+  const size_t es = esize(c.dtype);
+  const size_t T = size_t(c.T), d = size_t(c.d), E = size_t(c.E), k = size_t(c.k);
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base + off;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  StackWs s{};
+  for (int b = 0; b < 2; ++b) {
+    s.x[b] = take(T * d * es);
+    s.S[b] = c.c_shared ? take(T * d * es) : nullptr;
+    s.logits[b] = static_cast<float*>(take(T * E * 4));
+    s.idx[b] = static_cast<int32_t*>(take(T * k * 4));
+    s.w[b] = static_cast<float*>(take(T * k * 4));
+  }
+  s.offsets = static_cast<int32_t*>(take((E + 1) * 4));
+  s.sorted_src = static_cast<int32_t*>(take(T * k * 4));
+  s.dest_row = static_cast<int32_t*>(take(T * k * 4));
+  s.shared_off = static_cast<int32_t*>(take(2 * 4));
+  s.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
+  s.A_perm = take(T * k * d * es);
+  s.Y = take(T * k * d * es);
+  s.gemm_ws = take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
+  s.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype)) : nullptr;
+  if (total) *total = off;
+  return s;
+}
+
+__global__ void k_set_shared_offsets(int32_t* off, int32_t T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+int check_stack(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                const float* o0, const float* oL, const void* ws, size_t ws_bytes) {
+  if (!layers || !cfg) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layers and cfg are required");
+  if (L < 1) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: L=%d must be >= 1", L);
+  if (mode != FARSKIP_NONE && mode != FARSKIP_PARTIAL && mode != FARSKIP_OUTDATED)
+    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown mode %d", mode);
+  const moe_stack_cfg_t& c = *cfg;
+  if (c.T < 1 || c.d < 1 || c.c < 1 || c.c_shared < 0)
+    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: bad shapes");
+  if (c.E < 1 || c.k < 1 || c.k > c.E)
+    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: need 1 <= k <= E (k=%d, E=%d)", c.k, c.E);
+  if (c.E > MOE_MAX_EXPERTS || c.k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: E or k above the library limits");
+  if (c.gate != MOE_GATE_SOFTMAX && c.gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown gate %d", c.gate);
+  if (!dtype_ok(c.dtype)) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown dtype %d", c.dtype);
+  if (c.dtype == MOE_BF16 && c.d % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: bf16 needs d %% 64 == 0");
+  if (c.dtype == MOE_BF16 && (c.c % 64 != 0 || c.c_shared % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: bf16 needs c and c_shared multiples of 64");
+  if (c.d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: needs d %% 8 == 0");
+  if (c.T * int64_t(c.k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: T*k too large");
+  if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: o0 and oL are required");
+  if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: oL must not alias o0");
+  for (int j = 0; j < L; ++j) {
+    const moe_layer_desc_t& l = layers[j];
+    if (!l.W_R || !l.W1 || !l.W2 || !l.W3)
+      return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layer %d is missing routed weights", j);
+    if (c.c_shared && (!l.Ws1 || !l.Ws2 || !l.Ws3))
+      return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layer %d is missing shared weights", j);
+  }
+  size_t need = 0;
+  carve_stack(nullptr, c, &need);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "farskip_stack_forward: workspace %zu bytes, need %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+struct Events {
+  std::vector<hipEvent_t> ev;
+  ~Events() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+  int make(size_t n) {
+    ev.reserve(n);
+    for (size_t i = 0; i < n; ++i) {
+      hipEvent_t e;
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(r));
+      ev.push_back(e);
+    }
+    return MOE_OK;
+  }
+};
+
+int record(hipEvent_t e, hipStream_t s) {
+  const hipError_t r = hipEventRecord(e, s);
+  return r == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(r));
+}
+int wait(hipStream_t s, hipEvent_t e) {
+  const hipError_t r = hipStreamWaitEvent(s, e, 0);
+  return r == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipStreamWaitEvent: %s", hipGetErrorString(r));
+}
+
+// Layer j (0-based) of the stack; x_j lives in x[j % 2].
+//   side stream: route_j(x_j); S_j = shared_j(x_j); if the skip is on, wait for o_{j-1} and build
+//                x_{j+1} = o_{j-1} (+ S_j when partial)        -> the next layer's router and shared
+//                expert are enqueued right behind it, so they overlap this layer's routed GEMM
+//   main stream: wait route_j; permute_j; routed grouped GEMM_j; wait side_j;
+//                combine_j: o_j = o_{j-1} + S_j + R_j (+ x_{j+1} = o_j when the skip is off)
+int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
+                  const uint8_t* mask, const float* o0, float* oL, void* ws, hipStream_t sm,
+                  hipStream_t ss) {
+  StackWs w = carve_stack(ws, c, nullptr);
+  const bool two = sm != ss;
+  Events E_route, E_side, E_comb;
+  if (two) {
+    if (int rc = E_route.make(L)) return rc;
+    if (int rc = E_side.make(L)) return rc;
+    if (int rc = E_comb.make(L)) return rc;
+  }
+  const int64_t N = c.T * c.k;
+  k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));
+  if (int rc = check_launch("stack setup")) return rc;
+  if (int rc = launch_make_input(o0, nullptr, c.dtype, c.T, c.d, w.x[0], ss)) return rc;
+
+  const float* o_prev = o0;
+  for (int j = 0; j < L; ++j) {
+    const moe_layer_desc_t& l = layers[j];
+    const int cur = j & 1, nxt = cur ^ 1;
+    const bool last = j + 1 == L;
+    const bool skip = mode != FARSKIP_NONE && (mask ? mask[j] != 0 : true);
+    // side: router and shared expert of layer j
+    if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
+    if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
+      return rc;
+    if (two)
+      if (int rc = record(E_route.ev[j], ss)) return rc;
+    if (c.c_shared) {
+      if (int rc = launch_grouped_swiglu(w.x[cur], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, c.dtype, c.T, c.d,
+                                         c.c_shared, w.S[cur], w.shared_ws, ss))
+        return rc;
+    }
+    if (skip && !last) {
+      if (two && j > 0)
+        if (int rc = wait(ss, E_comb.ev[j - 1])) return rc;
+      const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
+      if (int rc = launch_make_input(o_prev, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
+    }
+    if (two)
+      if (int rc = record(E_side.ev[j], ss)) return rc;
+    // main: routed path of layer j
+    if (two)
+      if (int rc = wait(sm, E_route.ev[j])) return rc;
+    if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
+                                w.dest_row, w.A_perm, w.perm_ws, sm))
+      return rc;
+    if (int rc = launch_grouped_swiglu(w.A_perm, w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y,
+                                       w.gemm_ws, sm))
+      return rc;
+    if (two)
+      if (int rc = wait(sm, E_side.ev[j])) return rc;
+    void* out_x = (!skip && !last) ? w.x[nxt] : nullptr;
+    if (int rc = launch_combine(w.Y, c.dtype, w.w[cur], w.dest_row, c.T, c.d, c.k, c.c_shared ? w.S[cur] : nullptr,
+                                o_prev, oL, out_x, sm))
+      return rc;
+    if (two) {
+      if (int rc = record(E_comb.ev[j], sm)) return rc;
+      if (!skip && !last)
+        if (int rc = wait(ss, E_comb.ev[j])) return rc;
+    }
+    o_prev = oL;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace fsm
+
+using namespace fsm;
+
+extern "C" {
+
+int moe_route(const void* A, const void* W_R, const float* bias, int dtype, int64_t T, int64_t d, int32_t E,
+              int32_t k, int gate, int renormalize, float* logits, int32_t* topk_idx, float* topk_w,
+              void* stream) {
+  clear_error();
+  if (int rc = check_route(A, W_R, dtype, T, d, E, k, gate, logits, topk_idx, topk_w)) return rc;
+  if (T == 0) return MOE_OK;
+  const hipStream_t s = as_stream(stream);
+  if (A)
+    if (int rc = launch_router_logits(A, W_R, bias, dtype, T, d, E, logits, s)) return rc;
+  return launch_topk(logits, T, E, k, gate, renormalize, topk_idx, topk_w, s);
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return permute_ws_bytes(T, E, k);
+}
+
+int moe_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k, const int32_t* topk_idx,
+                int32_t* expert_offsets, int32_t* sorted_src, int32_t* dest_row, void* A_perm, void* ws,
+                size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_permute(A, dtype, T, d, E, k, topk_idx, expert_offsets, sorted_src, dest_row, A_perm, ws,
+                             ws_bytes))
+    return rc;
+  return launch_permute(A, dtype, T, d, E, k, topk_idx, expert_offsets, sorted_src, dest_row, A_perm, ws,
+                        as_stream(stream));
+}
+
+size_t moe_grouped_swiglu_workspace_bytes(int64_t N, int32_t G, int64_t c, int dtype) {
+  if (N < 0 || G < 1 || c < 1 || !dtype_ok(dtype)) return 0;
+  return swiglu_ws_bytes(N, G, c, dtype);
+}
+
+int moe_grouped_swiglu(const void* X, const int32_t* group_offsets, int32_t G, const void* W1, const void* W2,
+                       const void* W3, int dtype, int64_t N, int64_t d, int64_t c, void* Y, void* ws,
+                       size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_swiglu(X, group_offsets, G, W1, W2, W3, dtype, N, d, c, Y, ws, ws_bytes,
+                            "moe_grouped_swiglu"))
+    return rc;
+  return launch_grouped_swiglu(X, group_offsets, G, W1, W2, W3, dtype, N, d, c, Y, ws, as_stream(stream));
+}
+
+int moe_combine(const void* Y, int dtype, const float* topk_w, const int32_t* dest_row, int64_t T, int64_t d,
+                int32_t k, const void* addend, const float* residual, float* out, void* out_x, void* stream) {
+  clear_error();
+  if (int rc = check_combine(Y, dtype, topk_w, dest_row, T, d, k, out)) return rc;
+  return launch_combine(Y, dtype, topk_w, dest_row, T, d, k, addend, residual, out, out_x, as_stream(stream));
+}
+
+size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg) {
+  if (!cfg || cfg->T < 1 || cfg->d < 1 || cfg->c < 1 || cfg->E < 1 || cfg->k < 1 || !dtype_ok(cfg->dtype))
+    return 0;
+  size_t total = 0;
+  carve_stack(nullptr, *cfg, &total);
+  return total;
+}
+
+int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                          const uint8_t* skip_mask, const float* o0, float* oL, void* ws, size_t ws_bytes,
+                          void* s_main, void* s_side) {
+  clear_error();
+  if (int rc = check_stack(layers, L, cfg, mode, o0, oL, ws, ws_bytes)) return rc;
+  return stack_forward(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side));
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_version(void) { return "farskip_moe 0.1 (gfx950)"; }
+
+}  // extern "C"

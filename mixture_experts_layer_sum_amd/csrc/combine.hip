@@ -1,0 +1,122 @@
+// Combine and FarSkip layer-input kernels for gfx950.
+//
+// Combine ("FarSkip-Collective" section 2.1: the routed expert activations are aggregated and
+// summed back per token):
+//   out[t] = residual[t] + addend[t] + sum_{i<k} w[t,i] * Y[dest_row[t*k+i]]
+// as a per-token gather in float32, slots in order, so the result is deterministic and needs no
+// float atomics.  Each thread owns 8 consecutive columns of one token (16-byte bf16 / 32-byte fp32
+// vectors); a workgroup of 128 threads covers 1024 columns of one token.  The optional rounded
+// copy out_x is the next layer's input when the skip is off (x_{j+1} = o_j).
+//
+// Layer input (section 3, eqs. (8a)/(8b)): x = cast(o) or x = cast(o + S), the "outdated" and
+// "partial" FarSkip inputs built from the float32 residual stream and the shared-expert output.
+#include "common.h"
+
+namespace fsm {
+
+constexpr int CB_THR = 128;
+constexpr int CB_COLS = CB_THR * 8;
+
+__device__ __forceinline__ void load8(const void* base, int dtype, int64_t off, float* f) {
+  if (dtype == MOE_BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    unpack8(v, f);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void store8(void* base, int dtype, int64_t off, const float* f) {
+  if (dtype == MOE_BF16) {
+    uint4 v;
+    v.x = pack2(f[0], f[1]);
+    v.y = pack2(f[2], f[3]);
+    v.z = pack2(f[4], f[5]);
+    v.w = pack2(f[6], f[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = v;
+  } else {
+    float* p = static_cast<float*>(base) + off;
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+
+__global__ __launch_bounds__(CB_THR) void k_combine(const void* __restrict__ Y, int dtype,
+                                                    const float* __restrict__ w,
+                                                    const int32_t* __restrict__ dest_row, int64_t d, int k,
+                                                    int col_blocks, const void* __restrict__ addend,
+                                                    const float* residual, float* out, void* out_x) {
+  const int64_t t = blockIdx.x / col_blocks;
+  const int64_t col = int64_t(blockIdx.x % col_blocks) * CB_COLS + threadIdx.x * 8;
+  if (col >= d) return;
+  const int64_t o = t * d + col;
+  float acc[8];
+  if (residual) {
+    const float4 a = *reinterpret_cast<const float4*>(residual + o);
+    const float4 b = *reinterpret_cast<const float4*>(residual + o + 4);
+    acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+    acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  }
+  if (addend) {
+    float s[8];
+    load8(addend, dtype, o, s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += s[q];
+  }
+  for (int i = 0; i < k; ++i) {
+    const int64_t r = dest_row[t * k + i];
+    const float wi = w[t * k + i];
+    float y[8];
+    load8(Y, dtype, r * d + col, y);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wi, y[q], acc[q]);
+  }
+  *reinterpret_cast<float4*>(out + o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(out + o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (out_x) store8(out_x, dtype, o, acc);
+}
+
+__global__ __launch_bounds__(256) void k_make_input(const float* __restrict__ o, const void* __restrict__ S,
+                                                    int dtype, int64_t n8, void* __restrict__ x) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t off = i * 8;
+  const float4 a = *reinterpret_cast<const float4*>(o + off);
+  const float4 b = *reinterpret_cast<const float4*>(o + off + 4);
+  float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if (S) {
+    float s[8];
+    load8(S, dtype, off, s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f[q] += s[q];
+  }
+  store8(x, dtype, off, f);
+}
+
+int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
+                   int64_t d, int32_t k, const void* addend, const float* residual, float* out,
+                   void* out_x, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  const int col_blocks = int(cdiv(d, CB_COLS));
+  ProfScope prof(MOE_K_COMBINE, s);
+  k_combine<<<unsigned(T * col_blocks), CB_THR, 0, s>>>(Y, dtype, w, dest_row, d, k, col_blocks, addend,
+                                                         residual, out, out_x);
+  return check_launch("combine");
+}
+
+int launch_make_input(const float* o, const void* S, int dtype, int64_t T, int64_t d, void* x,
+                      hipStream_t s) {
+  const int64_t n8 = T * d / 8;
+  if (n8 == 0) return MOE_OK;
+  ProfScope prof(MOE_K_LAYER_INPUT, s);
+  k_make_input<<<unsigned(cdiv(n8, 256)), 256, 0, s>>>(o, S, dtype, n8, x);
+  return check_launch("layer input");
+}
+
+}  // namespace fsm

@@ -1,0 +1,82 @@
+// Shared device helpers and host-side status plumbing for libfarskip_moe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/farskip_moe.h"
+
+namespace fsm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- host status -----------------------------------------------------------------------------
+int fail(int code, const char* fmt, ...);   // records the message, returns code
+int check_launch(const char* what);          // MOE_OK or MOE_ERR_HIP after a launch
+void clear_error();
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- bf16 <-> f32 (bf16 stored as uint16_t) ----------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// round to nearest even; inputs are finite by precondition (inf stays inf)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// a 16-byte vector of 8 bf16 unpacked to floats
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+}
+
+// ---- opt-in kernel timing (prof.hip): brackets one launch with timing events on its stream ------
+class ProfScope {
+ public:
+  ProfScope(int kind, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t s_;
+  hipEvent_t a_, b_;
+};
+
+// ---- internal launchers (defined in the kernel files) -----------------------------------------
+int launch_router_logits(const void* A, const void* W_R, const float* bias, int dtype, int64_t T,
+                         int64_t d, int32_t E, float* logits, hipStream_t s);
+int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int gate, int renorm,
+                int32_t* topk_idx, float* topk_w, hipStream_t s);
+size_t permute_ws_bytes(int64_t T, int32_t E, int32_t k);
+int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                   const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
+                   void* A_perm, void* ws, hipStream_t s);
+size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype);
+int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
+                          const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
+                          void* Y, void* ws, hipStream_t s);
+int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
+                   int64_t d, int32_t k, const void* addend, const float* residual, float* out,
+                   void* out_x, hipStream_t s);
+// x = cast(o [+ S]) : the FarSkip layer input from the fp32 residual (and the shared output)
+int launch_make_input(const float* o, const void* S, int dtype, int64_t T, int64_t d, void* x,
+                      hipStream_t s);
+
+}  // namespace fsm

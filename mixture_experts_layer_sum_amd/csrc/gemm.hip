@@ -1,0 +1,435 @@
+// Grouped SwiGLU GEMM pair and the router GEMM for gfx950.
+//
+// The expert MLP of "FarSkip-Collective" section 2.1, MLP(A) = sigma(A W1^T . g(A W2^T)) W3^T with
+// g = SiLU and sigma = identity, is run as two contractions per expert group:
+//   phase 1:  H = (X W1^T) . SiLU(X W2^T)    one tile holds matching columns of W1 and W2, so the
+//                                             SwiGLU product is formed in registers (no U/G in HBM)
+//   phase 2:  Y = H W3^T
+// Both are "NT" products (both operands contiguous along K), which is the layout the bf16 MFMA
+// wants.  The router logits A W_R^T (section 2.1, G(A) = s(A W_R^T)) use the same tile kernel with
+// a float32 epilogue.
+//
+// Tile kernel: BM x BN output tile per workgroup, BK = 64, waves laid out WAVES_M x WAVES_N, each
+// wave owning a (BM/WAVES_M) x (BN/WAVES_N) block of v_mfma_f32_16x16x32_bf16 tiles.  Global
+// tiles are staged through registers into two LDS buffers (one barrier per K step); LDS rows are
+// 128 bytes and their eight 16-byte chunks are XOR-swizzled with the row index so that the MFMA
+// fragment reads (16 rows x one chunk per 16 lanes) are bank-conflict free.  The MFMA is issued
+// with the weight fragment as its first operand, which leaves every lane holding four consecutive
+// output columns of one row: the epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
+//
+// Groups (experts) have data-dependent row counts that stay on the device: a one-block kernel
+// turns the group offsets into a prefix sum of M-tiles per group and a map from M-tile to group,
+// which each workgroup reads with one scalar load.  The grid is sized for the worst case
+// (ceil(N/BM) + G M-tiles); the surplus workgroups exit at once.
+#include "common.h"
+
+namespace fsm {
+
+enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
+
+struct GemmArgs {
+  const void* A;              // [rows, K]
+  const void* B1;             // [G, n_b, K] (n_b = n_out, or c for SwiGLU)
+  const void* B2;             // SwiGLU gate weights, same layout as B1
+  void* out;                  // [rows, n_out]
+  const float* bias;          // EPI_F32_BIAS: [n_out] or null
+  const int32_t* offsets;     // [G+1] or null (dense: rows [0, M))
+  const int32_t* tile_start;  // [G+1] M-tile prefix per group, or null
+  const int32_t* tile_group;  // [max M-tiles] group of each M-tile (-1 = surplus), or null
+  int64_t b_group_stride;     // elements between consecutive groups of B1/B2
+  int32_t K, n_out, M, G, n_tiles;
+};
+
+// ------------------------------------------------------------------------------------------------
+// M-tile table: tile_start[g] = sum_{g' < g} ceil(count_g' / BM), and tile_group[t] = the group of
+// M-tile t (-1 for t >= total, up to max_tiles).  One block, G <= 1024.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int G, int BM,
+                                                     int max_tiles, int32_t* __restrict__ tile_start,
+                                                     int32_t* __restrict__ tile_group) {
+  __shared__ int32_t s[1024];
+  const int t = threadIdx.x;
+  int v = 0;
+  if (t < G) {
+    const int cnt = offsets[t + 1] - offsets[t];
+    v = (cnt + BM - 1) / BM;
+  }
+  s[t] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = (t >= off) ? s[t - off] : 0;
+    __syncthreads();
+    s[t] += add;
+    __syncthreads();
+  }
+  const int total = s[1023];
+  if (t < G) {
+    tile_start[t + 1] = s[t];
+    for (int j = s[t] - v; j < s[t] && j < max_tiles; ++j) tile_group[j] = t;
+  }
+  if (t == 0) tile_start[0] = 0;
+  for (int j = total + t; j < max_tiles; j += 1024) tile_group[j] = -1;
+}
+
+// Resolve M-tile mt of a grouped product (or of a dense one with M rows) to (group, first row,
+// row count).  Returns false for a surplus workgroup.
+__device__ __forceinline__ bool resolve_mtile(const GemmArgs& p, int mt, int BM, int& g, int& row0,
+                                              int& rows) {
+  if (p.tile_group) {
+    g = p.tile_group[mt];
+    if (g < 0) return false;
+    row0 = p.offsets[g] + (mt - p.tile_start[g]) * BM;
+    rows = min(BM, p.offsets[g + 1] - row0);
+    return true;
+  }
+  g = 0;
+  row0 = mt * BM;
+  if (row0 >= p.M) return false;
+  rows = min(BM, p.M - row0);
+  return true;
+}
+
+// ------------------------------------------------------------------------------------------------
+// bf16 MFMA tile kernel
+// ------------------------------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int BK = 64;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
+  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile/thread mismatch");
+  static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
+  static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
+
+  int g, row0, rows;
+  if (!resolve_mtile(p, mt, BM, g, row0, rows)) return;
+
+  const int64_t K = p.K;
+  const uint16_t* Ab = static_cast<const uint16_t*>(p.A) + int64_t(row0) * K;
+  const uint16_t* Bu;
+  const uint16_t* Bg;
+  int nvalid;
+  if (EPI == EPI_SWIGLU) {
+    const int n0 = nt * (BN / 2);
+    Bu = static_cast<const uint16_t*>(p.B1) + g * p.b_group_stride + int64_t(n0) * K;
+    Bg = static_cast<const uint16_t*>(p.B2) + g * p.b_group_stride + int64_t(n0) * K;
+    nvalid = min(BN / 2, p.n_out - n0);
+  } else {
+    const int n0 = nt * BN;
+    Bu = static_cast<const uint16_t*>(p.B1) + g * p.b_group_stride + int64_t(n0) * K;
+    Bg = Bu;
+    nvalid = min(BN, p.n_out - n0);
+  }
+
+  uint4 ra[ACH], rb[BCH];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
+      ra[i] = (r < rows) ? *reinterpret_cast<const uint4*>(Ab + int64_t(r) * K + k0 + ch * 8) : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
+      const uint16_t* src;
+      bool ok;
+      if (EPI == EPI_SWIGLU) {
+        if (r < BN / 2) { src = Bu + int64_t(r) * K; ok = r < nvalid; }
+        else { src = Bg + int64_t(r - BN / 2) * K; ok = (r - BN / 2) < nvalid; }
+      } else {
+        src = Bu + int64_t(r) * K;
+        ok = r < nvalid;
+      }
+      rb[i] = ok ? *reinterpret_cast<const uint4*>(src + k0 + ch * 8) : zero4;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
+      *reinterpret_cast<uint4*>(&sA[buf][r * BK + ((ch ^ (r & 7)) << 3)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
+      *reinterpret_cast<uint4*>(&sB[buf][r * BK + ((ch ^ (r & 7)) << 3)]) = rb[i];
+    }
+  };
+  auto brow = [&](int j) -> int {
+    if (EPI == EPI_SWIGLU)
+      return (j < FN / 2) ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 16;
+    return wn * WTN + j * 16;
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int ch = ks * 4 + (lane >> 4);
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = brow(j) + (lane & 15);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int KT = p.K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    compute(cur);
+    if (kt + 1 < KT) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4*(lane >> 4) + {0..3}
+  const int ml = lane & 15, nl = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = wm * WTM + i * 16 + ml;
+    if (m >= rows) continue;
+    const int64_t orow = int64_t(row0 + m);
+    if (EPI == EPI_SWIGLU) {
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const int col = nt * (BN / 2) + wn * (WTN / 2) + j * 16 + nl;
+        if (col >= p.n_out) continue;
+        const f32x4 u = acc[i][j], gt = acc[i][j + FN / 2];
+        uint2 v;
+        v.x = pack2(u[0] * silu_f(gt[0]), u[1] * silu_f(gt[1]));
+        v.y = pack2(u[2] * silu_f(gt[2]), u[3] * silu_f(gt[3]));
+        *reinterpret_cast<uint2*>(out + orow * p.n_out + col) = v;
+      }
+    } else if (EPI == EPI_PLAIN) {
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = nt * BN + wn * WTN + j * 16 + nl;
+        if (col >= p.n_out) continue;
+        const f32x4 a = acc[i][j];
+        uint2 v;
+        v.x = pack2(a[0], a[1]);
+        v.y = pack2(a[2], a[3]);
+        *reinterpret_cast<uint2*>(out + orow * p.n_out + col) = v;
+      }
+    } else {
+      float* out = static_cast<float*>(p.out);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = nt * BN + wn * WTN + j * 16 + nl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (col + r < p.n_out) {
+            const float b = p.bias ? p.bias[col + r] : 0.f;
+            out[orow * p.n_out + col + r] = acc[i][j][r] + b;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// float32 path (the tiny fp32 workload): 16 x 16 output tile per workgroup, plain FMA.
+// ------------------------------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs p) {
+  constexpr int BM = 16, BN = 16, BKF = 16;
+  __shared__ float sA[BM][BKF + 1], sU[BN][BKF + 1], sG[BN][BKF + 1];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
+
+  int g, row0, rows;
+  if (!resolve_mtile(p, mt, BM, g, row0, rows)) return;
+  const int K = p.K;
+  const int n0 = nt * BN;
+  const float* A = static_cast<const float*>(p.A) + int64_t(row0) * K;
+  const float* B1 = static_cast<const float*>(p.B1) + g * p.b_group_stride;
+  const float* B2 = (EPI == EPI_SWIGLU) ? static_cast<const float*>(p.B2) + g * p.b_group_stride : nullptr;
+
+  float accU = 0.f, accG = 0.f;
+  for (int k0 = 0; k0 < K; k0 += BKF) {
+    const int k = k0 + tx;
+    sA[ty][tx] = (ty < rows && k < K) ? A[int64_t(ty) * K + k] : 0.f;
+    const int n = n0 + ty;
+    const bool nok = n < p.n_out && k < K;
+    sU[ty][tx] = nok ? B1[int64_t(n) * K + k] : 0.f;
+    if (EPI == EPI_SWIGLU) sG[ty][tx] = nok ? B2[int64_t(n) * K + k] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BKF; ++kk) {
+      accU = fmaf(sA[ty][kk], sU[tx][kk], accU);
+      if (EPI == EPI_SWIGLU) accG = fmaf(sA[ty][kk], sG[tx][kk], accG);
+    }
+    __syncthreads();
+  }
+  const int n = n0 + tx;
+  if (ty >= rows || n >= p.n_out) return;
+  float* out = static_cast<float*>(p.out);
+  const int64_t o = int64_t(row0 + ty) * p.n_out + n;
+  if (EPI == EPI_SWIGLU) {
+    out[o] = accU * (accG / (1.0f + expf(-accG)));
+  } else if (EPI == EPI_F32_BIAS) {
+    out[o] = accU + (p.bias ? p.bias[n] : 0.f);
+  } else {
+    out[o] = accU;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host launchers
+// ------------------------------------------------------------------------------------------------
+namespace {
+// bf16 tilings (the phase-1 tile holds BN/2 columns of W1 and the same BN/2 columns of W2)
+constexpr int P1_BM = 128, P1_BN = 128, P1_WM = 2, P1_WN = 2;
+constexpr int P2_BM = 128, P2_BN = 128, P2_WM = 2, P2_WN = 2;
+constexpr int R_BM = 128, R_BN = 128, R_WM = 2, R_WN = 2;
+constexpr int F_BM = 16, F_BN = 16;
+
+struct SwigluWs {
+  int32_t* ts1;
+  int32_t* grp1;
+  int32_t* ts2;
+  int32_t* grp2;
+  void* H;
+};
+
+SwigluWs carve(void* ws, int32_t G, int64_t N, int64_t c, int dtype, size_t* total) {
+  const bool bf = dtype == MOE_BF16;
+  const size_t esz = bf ? 2 : 4;
+  const int64_t mt1 = cdiv(N, bf ? P1_BM : F_BM) + G, mt2 = cdiv(N, bf ? P2_BM : F_BM) + G;
+  size_t off = 0;
+  SwigluWs w;
+  char* base = static_cast<char*>(ws);
+  w.ts1 = reinterpret_cast<int32_t*>(base + off);
+  off = align_up(off + size_t(G + 1) * 4, 256);
+  w.grp1 = reinterpret_cast<int32_t*>(base + off);
+  off = align_up(off + size_t(mt1) * 4, 256);
+  w.ts2 = reinterpret_cast<int32_t*>(base + off);
+  off = align_up(off + size_t(G + 1) * 4, 256);
+  w.grp2 = reinterpret_cast<int32_t*>(base + off);
+  off = align_up(off + size_t(mt2) * 4, 256);
+  w.H = base + off;
+  off = align_up(off + size_t(N) * size_t(c) * esz, 256);
+  if (total) *total = off;
+  return w;
+}
+}  // namespace
+
+size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype) {
+  size_t total = 0;
+  carve(nullptr, G, N, c, dtype, &total);
+  return total;
+}
+
+int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
+                          const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
+                          void* Y, void* ws, hipStream_t s) {
+  SwigluWs w = carve(ws, G, N, c, dtype, nullptr);
+  if (N == 0) return MOE_OK;
+  const bool bf = dtype == MOE_BF16;
+  const int bm1 = bf ? P1_BM : F_BM, bm2 = bf ? P2_BM : F_BM;
+  const int64_t mt1 = cdiv(N, bm1) + G, mt2 = cdiv(N, bm2) + G;
+  {
+    ProfScope prof(MOE_K_TILE_TABLE, s);
+    k_tile_table<<<1, 1024, 0, s>>>(offsets, G, bm1, int(mt1), w.ts1, w.grp1);
+    if (int rc = check_launch("tile table")) return rc;
+  }
+  if (bm2 != bm1) {
+    ProfScope prof(MOE_K_TILE_TABLE, s);
+    k_tile_table<<<1, 1024, 0, s>>>(offsets, G, bm2, int(mt2), w.ts2, w.grp2);
+    if (int rc = check_launch("tile table")) return rc;
+  } else {
+    w.ts2 = w.ts1;
+    w.grp2 = w.grp1;
+  }
+
+  GemmArgs a1{};
+  a1.A = X; a1.B1 = W1; a1.B2 = W2; a1.out = w.H; a1.bias = nullptr;
+  a1.offsets = offsets; a1.tile_start = w.ts1; a1.tile_group = w.grp1; a1.b_group_stride = c * d;
+  a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G;
+
+  GemmArgs a2{};
+  a2.A = w.H; a2.B1 = W3; a2.B2 = nullptr; a2.out = Y; a2.bias = nullptr;
+  a2.offsets = offsets; a2.tile_start = w.ts2; a2.tile_group = w.grp2; a2.b_group_stride = d * c;
+  a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G;
+
+  if (bf) {
+    a1.n_tiles = int32_t(cdiv(c, P1_BN / 2));
+    const int64_t grid1 = mt1 * a1.n_tiles;
+    {
+      ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
+      k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
+      if (int rc = check_launch("grouped gemm phase 1")) return rc;
+    }
+    a2.n_tiles = int32_t(cdiv(d, P2_BN));
+    const int64_t grid2 = mt2 * a2.n_tiles;
+    ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
+    k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
+    return check_launch("grouped gemm phase 2");
+  }
+  a1.n_tiles = int32_t(cdiv(c, F_BN));
+  {
+    ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
+    k_gemm_f32<EPI_SWIGLU><<<dim3(unsigned(mt1 * a1.n_tiles)), 256, 0, s>>>(a1);
+    if (int rc = check_launch("grouped gemm phase 1 (f32)")) return rc;
+  }
+  a2.n_tiles = int32_t(cdiv(d, F_BN));
+  ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
+  k_gemm_f32<EPI_PLAIN><<<dim3(unsigned(mt2 * a2.n_tiles)), 256, 0, s>>>(a2);
+  return check_launch("grouped gemm phase 2 (f32)");
+}
+
+int launch_router_logits(const void* A, const void* W_R, const float* bias, int dtype, int64_t T,
+                         int64_t d, int32_t E, float* logits, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  GemmArgs a{};
+  a.A = A; a.B1 = W_R; a.B2 = nullptr; a.out = logits; a.bias = bias;
+  a.offsets = nullptr; a.tile_start = nullptr; a.tile_group = nullptr; a.b_group_stride = 0;
+  a.K = int32_t(d); a.n_out = E; a.M = int32_t(T); a.G = 1;
+  ProfScope prof(MOE_K_ROUTER_GEMM, s);
+  if (dtype == MOE_BF16) {
+    a.n_tiles = int32_t(cdiv(E, R_BN));
+    const int64_t grid = cdiv(T, R_BM) * a.n_tiles;
+    k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);
+    return check_launch("router gemm");
+  }
+  a.n_tiles = int32_t(cdiv(E, F_BN));
+  k_gemm_f32<EPI_F32_BIAS><<<dim3(unsigned(cdiv(T, F_BM) * a.n_tiles)), 256, 0, s>>>(a);
+  return check_launch("router gemm (f32)");
+}
+
+}  // namespace fsm

@@ -1,0 +1,166 @@
+// Dispatch permutation for gfx950 ("FarSkip-Collective" section 2.1: the token rows A[l,:] are
+// grouped by their selected experts by permuting A).
+//
+// Every flat slot f = t*k + i is one row.  Rows are ordered by expert, and inside an expert by f
+// (a stable counting sort), so the result is unique and deterministic:
+//   1. k_perm_hist   per chunk of PCH slots, an LDS histogram of expert ids (integer atomics in
+//                    LDS; the counts do not depend on their order)
+//   2. k_perm_scan   per expert, the exclusive prefix of the chunk counts over chunks, and the
+//                    exclusive prefix of the expert totals over experts (= expert offsets)
+//   3. k_perm_rank   each chunk walks its slots in rounds of 256 in slot order; inside a round a
+//                    slot's rank among equal experts comes from wavefront ballots over the bits
+//                    of the expert id (the lanes of one expert form a bit-mask; the rank is the
+//                    population count below the lane) plus the counts of earlier wavefronts, so
+//                    dest_row[f] = offsets[e] + (earlier slots of e); sorted_src is its inverse
+//   4. k_perm_rows   one wavefront per token reads its row once and writes it to its k
+//                    destination rows (16-byte vectors): the row copy reads A exactly once
+#include "common.h"
+
+namespace fsm {
+
+constexpr int PCH = 4096;  // slots per chunk (workgroup)
+constexpr int PTHR = 256;
+
+__global__ __launch_bounds__(PTHR) void k_perm_hist(const int32_t* __restrict__ idx, int64_t n, int E,
+                                                    int32_t* __restrict__ counts) {
+  __shared__ int32_t h[MOE_MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += PTHR) h[e] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * PCH;
+  for (int s = threadIdx.x; s < PCH; s += PTHR) {
+    const int64_t f = base + s;
+    if (f < n) atomicAdd(&h[idx[f]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PTHR) counts[int64_t(blockIdx.x) * E + e] = h[e];
+}
+
+// One block of 1024 threads; thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ counts, int nblk, int E,
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+  __shared__ int32_t s[1024];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) {
+      const int c = counts[int64_t(b) * E + e];
+      base[int64_t(b) * E + e] = run;
+      run += c;
+    }
+  }
+  s[e] = run;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = (e >= off) ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = s[e] - run;  // exclusive prefix
+  if (e == 0) offsets[E] = s[1023];
+}
+
+__global__ __launch_bounds__(PTHR) void k_perm_rank(const int32_t* __restrict__ idx, int64_t n, int E,
+                                                    int nbits, const int32_t* __restrict__ base,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ sorted_src,
+                                                    int32_t* __restrict__ dest_row) {
+  __shared__ int32_t run[MOE_MAX_EXPERTS];
+  __shared__ int32_t wc[PTHR / 64][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += PTHR) {
+    run[e] = offsets[e] + base[int64_t(blockIdx.x) * E + e];
+#pragma unroll
+    for (int w = 0; w < PTHR / 64; ++w) wc[w][e] = 0;
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  const int64_t chunk0 = int64_t(blockIdx.x) * PCH;
+  for (int r0 = 0; r0 < PCH; r0 += PTHR) {
+    const int64_t f = chunk0 + r0 + tid;
+    const bool valid = f < n;
+    const int e = valid ? idx[f] : E;  // E is a sentinel that matches no real expert
+    uint64_t peers = ~uint64_t(0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank_w = __popcll(peers & lt_mask);
+    const int cnt_w = __popcll(peers);
+    const bool leader = rank_w == 0;
+    if (valid && leader) wc[wave][e] = cnt_w;
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += wc[w][e];
+      const int r = run[e] + pre + rank_w;
+      dest_row[f] = r;
+      sorted_src[r] = int32_t(f);
+    }
+    __syncthreads();
+    if (valid && leader) {
+      atomicAdd(&run[e], cnt_w);
+      wc[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// A_perm[dest_row[t*k+i]] = A[t]; row_vec = row length in 16-byte vectors.
+__global__ __launch_bounds__(256) void k_perm_rows(const uint4* __restrict__ A, int64_t T, int64_t row_vec,
+                                                   int k, const int32_t* __restrict__ dest_row,
+                                                   uint4* __restrict__ A_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int myrow = lane < k ? dest_row[t * k + lane] : 0;
+  const uint4* src = A + t * row_vec;
+  for (int64_t c = lane; c < row_vec; c += 64) {
+    const uint4 v = src[c];
+    for (int i = 0; i < k; ++i) {
+      const int r = __builtin_amdgcn_readlane(myrow, i);
+      A_perm[int64_t(r) * row_vec + c] = v;
+    }
+  }
+}
+
+size_t permute_ws_bytes(int64_t T, int32_t E, int32_t k) {
+  const int64_t nblk = cdiv(T * k, PCH);
+  return 2 * align_up(size_t(nblk) * size_t(E) * 4, 256) + 256;
+}
+
+int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                   const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
+                   void* A_perm, void* ws, hipStream_t s) {
+  const int64_t n = T * k;
+  const int nblk = int(cdiv(n, PCH));
+  int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                             align_up(size_t(nblk) * size_t(E) * 4, 256));
+  {
+    ProfScope prof(MOE_K_PERMUTE_INDEX, s);
+    if (nblk > 0) {
+      k_perm_hist<<<nblk, PTHR, 0, s>>>(topk_idx, n, E, counts);
+      if (int rc = check_launch("permute histogram")) return rc;
+    }
+    k_perm_scan<<<1, 1024, 0, s>>>(counts, nblk, E, base, offsets);
+    if (int rc = check_launch("permute scan")) return rc;
+    if (nblk == 0) return MOE_OK;
+    int nbits = 0;
+    while ((1 << nbits) <= E) ++nbits;  // enough bits for the values 0..E (E = sentinel)
+    k_perm_rank<<<nblk, PTHR, 0, s>>>(topk_idx, n, E, nbits, base, offsets, sorted_src, dest_row);
+    if (int rc = check_launch("permute rank")) return rc;
+  }
+  if (A_perm) {
+    ProfScope prof(MOE_K_PERMUTE_ROWS, s);
+    const int64_t row_bytes = d * (dtype == MOE_BF16 ? 2 : 4);
+    k_perm_rows<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(static_cast<const uint4*>(A), T, row_bytes / 16, k,
+                                                    dest_row, static_cast<uint4*>(A_perm));
+    if (int rc = check_launch("permute rows")) return rc;
+  }
+  return MOE_OK;
+}
+
+}  // namespace fsm

@@ -1,0 +1,80 @@
+// Opt-in kernel timing: timing events recorded on the launch stream around each library kernel.
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace fsm {
+
+namespace {
+struct Rec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::atomic<bool> g_on{false};
+std::mutex g_mu;
+std::vector<Rec> g_recs;
+}  // namespace
+
+bool prof_on() { return g_on.load(std::memory_order_relaxed); }
+
+ProfScope::ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s), a_(nullptr), b_(nullptr) {
+  if (!prof_on()) return;
+  if (hipEventCreate(&a_) != hipSuccess) { a_ = nullptr; return; }
+  if (hipEventCreate(&b_) != hipSuccess) { (void)hipEventDestroy(a_); a_ = nullptr; b_ = nullptr; return; }
+  if (hipEventRecord(a_, s_) != hipSuccess) {
+    (void)hipEventDestroy(a_);
+    (void)hipEventDestroy(b_);
+    a_ = b_ = nullptr;
+  }
+}
+
+ProfScope::~ProfScope() {
+  if (!a_) return;
+  if (hipEventRecord(b_, s_) != hipSuccess) {
+    (void)hipEventDestroy(a_);
+    (void)hipEventDestroy(b_);
+    return;
+  }
+  std::lock_guard<std::mutex> g(g_mu);
+  g_recs.push_back({kind_, a_, b_});
+}
+
+}  // namespace fsm
+
+extern "C" {
+
+int moe_profile_enable(int on) {
+  fsm::g_on.store(on != 0);
+  return MOE_OK;
+}
+
+int moe_profile_collect(moe_kernel_time_t* out) {
+  if (!out) return fsm::fail(MOE_ERR_INVALID_ARG, "moe_profile_collect: out is required");
+  for (int i = 0; i < MOE_KERNEL_KINDS; ++i) out[i] = moe_kernel_time_t{0, 0.0};
+  std::vector<fsm::Rec> recs;
+  {
+    std::lock_guard<std::mutex> g(fsm::g_mu);
+    recs.swap(fsm::g_recs);
+  }
+  int rc = MOE_OK;
+  for (const fsm::Rec& r : recs) {
+    float ms = 0.f;
+    if (rc == MOE_OK) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess) {
+        rc = fsm::fail(MOE_ERR_HIP, "moe_profile_collect: %s", hipGetErrorString(e));
+      } else if (r.kind >= 0 && r.kind < MOE_KERNEL_KINDS) {
+        out[r.kind].count += 1;
+        out[r.kind].total_ms += ms;
+      }
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  return rc;
+}
+
+}  // extern "C"

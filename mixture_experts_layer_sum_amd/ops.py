@@ -1,0 +1,186 @@
+"""Python binding of libfarskip_moe: argument marshalling from torch tensors to the C ABI.
+
+Every function takes device tensors that the caller allocated (outputs included) and enqueues the
+work on a HIP stream (default: torch's current stream).  Nothing here computes; each step runs in
+the library's HIP kernels.  Names and argument order follow include/farskip_moe.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
+                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelTime, LayerDesc, StackCfg, check, lib)
+
+GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
+MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MOE_F32
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _gate(g) -> int:
+    return GATES[g] if isinstance(g, str) else int(g)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------------
+def moe_route(A, W_R, k: int, gate, renormalize: bool, logits, topk_idx, topk_w, bias=None, stream=None):
+    """logits = A W_R^T (+ bias); topk_idx / topk_w = top-k selection and gate weights."""
+    T, d = A.shape
+    E = W_R.shape[0]
+    check("moe_route", lib.moe_route(_p(A), _p(W_R), _p(bias), dtype_code(A.dtype), T, d, E, k, _gate(gate),
+                                     int(bool(renormalize)), _p(logits), _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def moe_route_from_logits(logits, k: int, gate, renormalize: bool, topk_idx, topk_w, stream=None):
+    """Selection and weights only, from given fp32 logits [T, E]."""
+    T, E = logits.shape
+    check("moe_route", lib.moe_route(None, None, None, MOE_F32, T, 0, E, k, _gate(gate), int(bool(renormalize)),
+                                     _p(logits), _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def permute_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(lib.moe_permute_workspace_bytes(T, E, k))
+
+
+def moe_permute(topk_idx, E: int, expert_offsets, sorted_src, dest_row, A=None, A_perm=None, ws=None,
+                stream=None):
+    T, k = topk_idx.shape
+    if ws is None:
+        ws = workspace(permute_workspace_bytes(T, E, k), topk_idx.device)
+    d = A.shape[1] if A is not None else 0
+    dt = dtype_code(A.dtype) if A is not None else MOE_F32
+    check("moe_permute", lib.moe_permute(_p(A), dt, T, d, E, k, _p(topk_idx), _p(expert_offsets), _p(sorted_src),
+                                         _p(dest_row), _p(A_perm), _p(ws), ws.numel(), _s(stream)))
+
+
+def grouped_swiglu_workspace_bytes(N: int, G: int, c: int, dtype) -> int:
+    return int(lib.moe_grouped_swiglu_workspace_bytes(N, G, c, dtype_code(dtype)))
+
+
+def moe_grouped_swiglu(X, group_offsets, W1, W2, W3, Y, ws=None, stream=None):
+    """Y[rows of group g] = ((X W1[g]^T) . SiLU(X W2[g]^T)) W3[g]^T.  W1/W2: [G,c,d] (or [c,d] for
+    one group), W3: [G,d,c] (or [d,c])."""
+    N, d = X.shape
+    G = group_offsets.numel() - 1
+    c = W1.shape[-2]
+    if ws is None:
+        ws = workspace(grouped_swiglu_workspace_bytes(N, G, c, X.dtype), X.device)
+    check("moe_grouped_swiglu",
+          lib.moe_grouped_swiglu(_p(X), _p(group_offsets), G, _p(W1), _p(W2), _p(W3), dtype_code(X.dtype), N, d, c,
+                                 _p(Y), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_combine(Y, topk_w, dest_row, out, addend=None, residual=None, out_x=None, stream=None):
+    """out = residual + addend + sum_i topk_w[:, i] * Y[dest_row[t*k+i]]  (fp32)."""
+    T, k = topk_w.shape
+    d = Y.shape[1]
+    check("moe_combine", lib.moe_combine(_p(Y), dtype_code(Y.dtype), _p(topk_w), _p(dest_row), T, d, k, _p(addend),
+                                         _p(residual), _p(out), _p(out_x), _s(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+def stack_cfg(T, d, c, c_shared, E, k, gate, renormalize, dtype) -> StackCfg:
+    return StackCfg(T=T, d=d, c=c, c_shared=c_shared, E=E, k=k, gate=_gate(gate),
+                    renormalize=int(bool(renormalize)), dtype=dtype_code(dtype) if isinstance(dtype, torch.dtype)
+                    else int(dtype))
+
+
+def stack_workspace_bytes(cfg: StackCfg) -> int:
+    return int(lib.farskip_stack_workspace_bytes(ctypes.byref(cfg)))
+
+
+def layer_desc(W: dict) -> LayerDesc:
+    return LayerDesc(W_R=W["W_R"].data_ptr(), bias=W["bias"].data_ptr() if W.get("bias") is not None else None,
+                     W1=W["W1"].data_ptr(), W2=W["W2"].data_ptr(), W3=W["W3"].data_ptr(),
+                     Ws1=W["Ws1"].data_ptr() if W.get("Ws1") is not None else None,
+                     Ws2=W["Ws2"].data_ptr() if W.get("Ws2") is not None else None,
+                     Ws3=W["Ws3"].data_ptr() if W.get("Ws3") is not None else None)
+
+
+def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws, skip_mask=None,
+                          s_main=None, s_side=None):
+    """o_L of the FarSkip stack (mode "none" | "partial" | "outdated").  s_side defaults to s_main."""
+    L = len(layers)
+    descs = (LayerDesc * L)(*[layer_desc(W) for W in layers])
+    mask = None
+    if skip_mask is not None:
+        mask = (ctypes.c_uint8 * L)(*[1 if m else 0 for m in skip_mask])
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    sm = _s(s_main)
+    ss = _s(s_side) if s_side is not None else sm
+    check("farskip_stack_forward",
+          lib.farskip_stack_forward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(), sm, ss))
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start/stop timing every library kernel launch with HIP events on its own stream."""
+    check("moe_profile_enable", lib.moe_profile_enable(int(bool(on))))
+
+
+def profile_collect() -> dict:
+    """Wait for the recorded events; {kind: (launches, summed ms)} since the last collect."""
+    out = (KernelTime * len(KERNEL_KINDS))()
+    check("moe_profile_collect", lib.moe_profile_collect(out))
+    return {name: (out[i].count, out[i].total_ms) for i, name in enumerate(KERNEL_KINDS)}
+
+
+# ---------------------------------------------------------------------------------------------
+class LayerBuffers:
+    """Preallocated device buffers for one MoE sublayer forward (so a timed loop allocates nothing)."""
+
+    def __init__(self, T, d, E, k, c, c_shared, dtype, device):
+        N = T * k
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+        self.sorted_src = torch.empty((N,), dtype=torch.int32, device=device)
+        self.dest_row = torch.empty((N,), dtype=torch.int32, device=device)
+        self.A_perm = torch.empty((N, d), dtype=dtype, device=device)
+        self.Y = torch.empty((N, d), dtype=dtype, device=device)
+        self.perm_ws = workspace(permute_workspace_bytes(T, E, k), device)
+        self.gemm_ws = workspace(grouped_swiglu_workspace_bytes(N, E, c, dtype), device)
+        self.S = torch.empty((T, d), dtype=dtype, device=device) if c_shared else None
+        self.shared_off = torch.tensor([0, T], dtype=torch.int32, device=device)
+        self.shared_ws = workspace(grouped_swiglu_workspace_bytes(T, 1, c_shared, dtype), device) if c_shared else None
+        self.out = torch.empty((T, d), dtype=torch.float32, device=device)
+
+
+def moe_layer_forward(A, W: dict, k: int, gate, renormalize: bool, buf: LayerBuffers, residual=None,
+                      stream=None):
+    """One MoE sublayer: route, permute, routed grouped SwiGLU, shared expert, combine.
+    Returns buf.out = residual + S(A) + sum_i w_i Y_i (fp32)."""
+    E = W["W_R"].shape[0]
+    moe_route(A, W["W_R"], k, gate, renormalize, buf.logits, buf.topk_idx, buf.topk_w, bias=W.get("bias"),
+              stream=stream)
+    moe_permute(buf.topk_idx, E, buf.offsets, buf.sorted_src, buf.dest_row, A=A, A_perm=buf.A_perm, ws=buf.perm_ws,
+                stream=stream)
+    moe_grouped_swiglu(buf.A_perm, buf.offsets, W["W1"], W["W2"], W["W3"], buf.Y, ws=buf.gemm_ws, stream=stream)
+    if buf.S is not None:
+        moe_grouped_swiglu(A, buf.shared_off, W["Ws1"], W["Ws2"], W["Ws3"], buf.S, ws=buf.shared_ws, stream=stream)
+    moe_combine(buf.Y, buf.topk_w, buf.dest_row, buf.out, addend=buf.S, residual=residual, stream=stream)
+    return buf.out

@@ -11,7 +11,11 @@ Combine (aggregate and sum the routed expert outputs); its section 3 defines the
 and the FarSkip inputs o*_k, "outdated" (8a) and "partial" (8b).
 
 Arithmetic is float64 throughout.  Inputs given as float32 or bfloat16-valued float32 are upcast
-exactly.  Where the pages leave a step open, the reading taken is stated at the function.
+exactly.  Where the pages leave a step open, the reading taken is stated at the function.  An
+optional `store` rounding (off by default) can be applied to the intermediates an implementation
+keeps in a narrower storage type (expert hidden, expert and shared outputs), and `round_inputs` to
+the stack's layer inputs: a routing decision of a deep layer then sees inputs of the same precision
+as the implementation's, so the decision is comparable; it changes no other arithmetic.
 
 Pins (tests that tie this module to something other than itself): brute-force top-k enumeration,
 brute-force stable permutation, hand-derived worked examples under tests/golden/, the closed forms
@@ -135,34 +139,43 @@ def silu(x):
         return x / (1.0 + np.exp(-x))
 
 
-def mlp(X, W1, W2, W3):
+def mlp(X, W1, W2, W3, store=None):
+    """store: optional rounding applied to the values an implementation keeps in its storage
+    dtype (the hidden H and the output); None = exact."""
     X = _f64(X)
     U = X @ _f64(W1).T
     G = X @ _f64(W2).T
     H = U * silu(G)
-    return H @ _f64(W3).T
+    if store is not None:
+        H = _f64(store(H))
+    Y = H @ _f64(W3).T
+    return Y if store is None else _f64(store(Y))
 
 
-def grouped_mlp(X, offsets, W1, W2, W3):
-    """Rows [offsets[e], offsets[e+1]) of X go through expert e's MLP."""
+def grouped_mlp(X, offsets, W1, W2, W3, store=None):
+    """Rows [offsets[e], offsets[e+1]) of X go through expert e's MLP.  W1, W2, W3 only need to
+    support indexing by expert (W1[e] is expert e's c x d matrix)."""
     X = _f64(X)
-    Y = np.zeros((X.shape[0], np.asarray(W3).shape[1]), dtype=F64)
+    Y = np.zeros_like(X)  # the MLP maps width d back to width d
     for e in range(len(offsets) - 1):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
-            Y[a:b] = mlp(X[a:b], W1[e], W2[e], W3[e])
+            Y[a:b] = mlp(X[a:b], W1[e], W2[e], W3[e], store)
     return Y
 
 
-def shared_mlp(A, Ws1, Ws2, Ws3, n_shared, c_shared):
+def shared_mlp(A, Ws1, Ws2, Ws3, n_shared, c_shared, store=None):
     """Sum over the shared experts (each processes every token, section 2.1) with weight 1.  Shared
     expert s owns hidden rows [s*c_shared, (s+1)*c_shared) of Ws1/Ws2 and the same columns of Ws3."""
     A = _f64(A)
-    S = np.zeros((A.shape[0], np.asarray(Ws3).shape[0]), dtype=F64)
+    S = np.zeros_like(A)
     for s in range(n_shared):
         h = slice(s * c_shared, (s + 1) * c_shared)
-        S += mlp(A, Ws1[h], Ws2[h], Ws3[:, h])
-    return S
+        H = (A @ _f64(Ws1[h]).T) * silu(A @ _f64(Ws2[h]).T)
+        if store is not None:
+            H = _f64(store(H))
+        S += H @ _f64(Ws3[:, h]).T
+    return S if store is None else _f64(store(S))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -188,7 +201,7 @@ def combine(Y, topk_w, dest_row, addend=None, residual=None):
 # One MoE sublayer (section 2.1, MoE equation plus the shared expert): f(A) = S(A) + R(A) with
 # R(A) = sum over selected experts of G(A)_j MLP_j(A).
 # ---------------------------------------------------------------------------------------------
-def moe_layer(A, W, k, gate, renormalize, n_shared=0, c_shared=0):
+def moe_layer(A, W, k, gate, renormalize, n_shared=0, c_shared=0, store=None):
     """W: dict with W_R, bias, W1, W2, W3, Ws1, Ws2, Ws3 (numpy or None).  Returns a dict with the
     logits, topk_idx, topk_w, offsets, sorted_src, dest_row, Y, S (shared sum or zeros) and R."""
     A = _f64(A)
@@ -196,10 +209,10 @@ def moe_layer(A, W, k, gate, renormalize, n_shared=0, c_shared=0):
     L, idx, w = route(A, W["W_R"], k, gate, renormalize, W.get("bias"))
     offsets, sorted_src, dest_row = permute(idx, E)
     Xp = permute_rows(A, sorted_src, k)
-    Y = grouped_mlp(Xp, offsets, W["W1"], W["W2"], W["W3"])
+    Y = grouped_mlp(Xp, offsets, W["W1"], W["W2"], W["W3"], store)
     R = combine(Y, w, dest_row)
     if n_shared:
-        S = shared_mlp(A, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared)
+        S = shared_mlp(A, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared, store)
     else:
         S = np.zeros_like(A)
     return dict(logits=L, topk_idx=idx, topk_w=w, offsets=offsets, sorted_src=sorted_src,
@@ -244,17 +257,17 @@ def farskip_stack(o0, layers, mode, mask=None, round_inputs=None, record=None):
 
 
 def moe_stack(o0, layer_weights, k, gate, renormalize, mode, mask=None, n_shared=0, c_shared=0,
-              round_inputs=None, record=None):
-    """The FarSkip stack with MoE sublayers as the blocks f_k = S_k + R_k."""
+              round_inputs=None, record=None, store=None):
+    """The FarSkip stack with MoE sublayers as the blocks f_k = S_k + R_k.  `store` as in mlp()."""
     layers = []
     for W in layer_weights:
         def shared_fn(x, W=W):
             if n_shared:
-                return shared_mlp(x, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared)
+                return shared_mlp(x, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared, store)
             return np.zeros_like(_f64(x))
 
         def routed_fn(x, W=W):
-            return moe_layer(x, W, k, gate, renormalize)["R"]
+            return moe_layer(x, W, k, gate, renormalize, store=store)["R"]
         layers.append((shared_fn, routed_fn))
     return farskip_stack(o0, layers, mode, mask, round_inputs, record)
 

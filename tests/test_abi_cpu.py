@@ -1,0 +1,162 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares, and every
+argument check returns its documented error code before anything is enqueued (no GPU needed:
+these calls never reach a kernel launch)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_sum_amd as pkg
+from mixture_experts_layer_sum_amd import _lib as L
+from tests.helpers import header_exports
+
+lib = pkg.lib
+BAD = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host-side checks
+
+
+def test_header_declares_the_boundary():
+    names = header_exports()
+    for fn in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "farskip_stack_forward"):
+        assert fn in names
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for fn in header_exports():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_version_and_empty_last_error():
+    assert b"gfx950" in lib.moe_version()
+    lib.moe_permute_workspace_bytes(0, 1, 1)
+    assert isinstance(lib.moe_last_error(), bytes)
+
+
+def err(rc, code, needle=None):
+    assert rc == code, (rc, lib.moe_last_error())
+    if needle:
+        assert needle in lib.moe_last_error().decode()
+
+
+def test_route_argument_errors():
+    f = lib.moe_route
+    err(f(BAD, None, None, 0, 4, 64, 8, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "both")
+    err(f(None, None, None, 0, 4, 0, 8, 9, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "k <= E")
+    err(f(None, None, None, 0, 4, 0, 8, 0, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, None, None, 0, 4, 0, 0, 1, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, None, None, 0, -1, 0, 8, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, None, None, 0, 4, 0, 2048, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_UNSUPPORTED)
+    err(f(None, None, None, 0, 4, 0, 64, 33, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_UNSUPPORTED)
+    err(f(None, None, None, 0, 4, 0, 8, 2, 7, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "gate")
+    err(f(BAD, BAD, None, 5, 4, 64, 8, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "dtype")
+    err(f(BAD, BAD, None, 1, 4, 100, 8, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_UNSUPPORTED, "% 64")
+    err(f(BAD, BAD, None, 1, 4, 0, 8, 2, 0, 0, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, None, None, 0, 4, 0, 8, 2, 0, 0, None, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "required")
+    # an empty batch is valid and enqueues nothing
+    assert f(None, None, None, 0, 0, 0, 8, 2, 0, 0, None, None, None, None) == L.MOE_OK
+
+
+def test_permute_argument_errors():
+    f = lib.moe_permute
+    ws_need = lib.moe_permute_workspace_bytes(100, 8, 2)
+    assert ws_need > 0
+    err(f(None, 0, 100, 0, 8, 2, BAD, BAD, BAD, BAD, None, BAD, ws_need - 1, None), L.MOE_ERR_WORKSPACE)
+    err(f(None, 0, 100, 0, 8, 2, BAD, BAD, BAD, BAD, None, None, ws_need, None), L.MOE_ERR_WORKSPACE)
+    err(f(None, 0, 100, 0, 0, 2, BAD, BAD, BAD, BAD, None, BAD, ws_need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 0, -1, 0, 8, 2, BAD, BAD, BAD, BAD, None, BAD, ws_need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 0, 100, 0, 8, 2, BAD, None, BAD, BAD, None, BAD, ws_need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 0, 100, 0, 8, 2, None, BAD, BAD, BAD, None, BAD, ws_need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 1, 100, 64, 8, 2, BAD, BAD, BAD, BAD, BAD, BAD, ws_need, None), L.MOE_ERR_INVALID_ARG, "without A")
+    err(f(BAD, 1, 100, 12, 8, 2, BAD, BAD, BAD, BAD, BAD, BAD, ws_need, None), L.MOE_ERR_UNSUPPORTED, "16")
+    err(f(BAD, 1, 1 << 30, 64, 8, 4, BAD, BAD, BAD, BAD, BAD, BAD, ws_need, None), L.MOE_ERR_UNSUPPORTED)
+    err(f(None, 0, 100, 0, 2000, 2, BAD, BAD, BAD, BAD, None, BAD, ws_need, None), L.MOE_ERR_UNSUPPORTED)
+
+
+def test_grouped_swiglu_argument_errors():
+    f = lib.moe_grouped_swiglu
+    need = lib.moe_grouped_swiglu_workspace_bytes(256, 4, 128, 1)
+    assert need >= 256 * 128 * 2
+    assert lib.moe_grouped_swiglu_workspace_bytes(256, 4, 128, 0) >= 256 * 128 * 4
+    err(f(BAD, BAD, 4, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need - 1, None), L.MOE_ERR_WORKSPACE)
+    err(f(BAD, BAD, 0, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(BAD, BAD, 4, BAD, BAD, BAD, 1, 256, 100, 128, BAD, BAD, need, None), L.MOE_ERR_UNSUPPORTED, "% 64")
+    err(f(BAD, BAD, 4, BAD, BAD, BAD, 1, 256, 128, 96, BAD, BAD, need, None), L.MOE_ERR_UNSUPPORTED)
+    err(f(BAD, None, 4, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(BAD, BAD, 4, BAD, None, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, BAD, 4, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_INVALID_ARG)
+    err(f(BAD, BAD, 4, BAD, BAD, BAD, 9, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_INVALID_ARG, "dtype")
+    err(f(BAD, BAD, 4096, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_UNSUPPORTED)
+
+
+def test_combine_argument_errors():
+    f = lib.moe_combine
+    err(f(BAD, 1, BAD, BAD, 10, 12, 2, None, None, BAD, None, None), L.MOE_ERR_UNSUPPORTED, "% 8")
+    err(f(BAD, 1, BAD, BAD, 10, 16, 0, None, None, BAD, None, None), L.MOE_ERR_INVALID_ARG)
+    err(f(BAD, 1, None, BAD, 10, 16, 2, None, None, BAD, None, None), L.MOE_ERR_INVALID_ARG, "required")
+    err(f(BAD, 1, BAD, BAD, 10, 16, 2, None, None, None, None, None), L.MOE_ERR_INVALID_ARG)
+    err(f(BAD, 3, BAD, BAD, 10, 16, 2, None, None, BAD, None, None), L.MOE_ERR_INVALID_ARG, "dtype")
+    assert f(None, 1, None, None, 0, 16, 2, None, None, None, None, None) == L.MOE_OK
+
+
+def _cfg(**kw):
+    base = dict(T=64, d=128, c=256, c_shared=0, E=8, k=2, gate=0, renormalize=1, dtype=0)
+    base.update(kw)
+    return L.StackCfg(**base)
+
+
+def test_stack_argument_errors():
+    f = lib.farskip_stack_forward
+    cfg = _cfg()
+    need = lib.farskip_stack_workspace_bytes(ctypes.byref(cfg))
+    assert need > 64 * 2 * 128 * 4 * 2
+    desc = (L.LayerDesc * 2)(*[L.LayerDesc(W_R=0x1000, W1=0x1000, W2=0x1000, W3=0x1000) for _ in range(2)])
+    ok_args = (desc, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None)
+    bad = list(ok_args)
+    bad[8] = need - 1
+    err(f(*bad), L.MOE_ERR_WORKSPACE)
+    bad = list(ok_args)
+    bad[3] = 7
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "mode")
+    bad = list(ok_args)
+    bad[1] = 0
+    err(f(*bad), L.MOE_ERR_INVALID_ARG)
+    bad = list(ok_args)
+    bad[6] = BAD
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "alias")
+    c2 = _cfg(k=9)
+    bad = list(ok_args)
+    bad[2] = ctypes.byref(c2)
+    err(f(*bad), L.MOE_ERR_INVALID_ARG)
+    c3 = _cfg(c_shared=256)
+    bad = list(ok_args)
+    bad[2] = ctypes.byref(c3)
+    bad[8] = lib.farskip_stack_workspace_bytes(ctypes.byref(c3))
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "shared")
+    desc_missing = (L.LayerDesc * 2)(L.LayerDesc(W_R=0x1000, W1=0x1000, W2=0x1000, W3=0x1000), L.LayerDesc())
+    bad = list(ok_args)
+    bad[0] = desc_missing
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "layer 1")
+    c4 = _cfg(dtype=1, d=96)
+    bad = list(ok_args)
+    bad[2] = ctypes.byref(c4)
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED)
+
+
+def test_workspace_queries_scale():
+    small = lib.moe_grouped_swiglu_workspace_bytes(1000, 8, 256, 1)
+    big = lib.moe_grouped_swiglu_workspace_bytes(2000, 8, 256, 1)
+    assert big > small
+    assert lib.moe_grouped_swiglu_workspace_bytes(-1, 8, 256, 1) == 0
+    assert lib.moe_permute_workspace_bytes(65536, 256, 8) >= 2 * (65536 * 8 // 4096) * 256 * 4
+    c5 = _cfg(T=65536, d=7168, c=2048, c_shared=2048, E=256, k=8, gate=1, dtype=1)
+    assert lib.farskip_stack_workspace_bytes(ctypes.byref(c5)) > 2 * 65536 * 8 * 7168 * 2
+
+
+def test_python_binding_refuses_unknown_dtype():
+    import torch
+    from mixture_experts_layer_sum_amd import ops
+    with pytest.raises(TypeError):
+        ops.dtype_code(torch.float16)

@@ -1,0 +1,349 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: integer and copy outputs (top-k indices given identical fp32 logits, permutation arrays,
+permuted rows) bit-exact; float outputs max|err| <= 2e-2 * max|ref| (bf16 storage, fp32
+accumulation) or <= 1e-4 * max|ref| (fp32).  Full-size workloads are checked on seeded samples of
+rows: with dropless routing every output row depends only on its own input row, so the oracle
+evaluates exactly those rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tests.helpers import (NEAR_TIE, ExpertSlices, assert_parity, dkey, max_rel_err, oracle_weights, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from mixture_experts_layer_sum_amd import ops as _ops
+    return _ops
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+CFG = {c.name: c for c in mi.CONFIGS}
+ALL = [c.name for c in mi.CONFIGS]
+
+
+# =================================================================================================
+# a2: top-k selection and gate weights, identical fp32 logits on both sides
+# =================================================================================================
+def run_topk(ops, L, k, gate, renorm):
+    T, E = L.shape
+    Ld = L.to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ops.moe_route_from_logits(Ld, k, gate, renorm, idx, w)
+    _sync()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_topk_bitexact_config(ops, name):
+    c = CFG[name]
+    bias = mi.normal((c.E,), 1.0, mi.seed_for(c.cfg_id, 0, mi.T_BIAS)) if c.router_bias else None
+    L = mi.logits(c.T, c.E, mi.seed_for(c.cfg_id, 0, mi.T_LOGITS), bias=bias)
+    idx, w = run_topk(ops, L, c.k, c.gate, c.renormalize)
+    Ln = L.numpy()
+    ref_idx = oracle.select_topk(Ln, c.k)
+    np.testing.assert_array_equal(idx, ref_idx)
+    ref_w = oracle.gate_weights(Ln, ref_idx, c.gate, c.renormalize)
+    np.testing.assert_allclose(w, ref_w, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (3, 3), (8, 2), (64, 6), (65, 7), (128, 8), (200, 5), (256, 8),
+                                 (512, 16), (1024, 32)])
+@pytest.mark.parametrize("gate,renorm", [("softmax", False), ("softmax", True), ("sigmoid", True)])
+def test_topk_ties_and_shapes(ops, E, k, gate, renorm):
+    # logits snapped to multiples of 0.5 so that exact ties are everywhere
+    L = mi.logits(777, E, mi.seed_for(99, E, mi.T_LOGITS, k), quantum=0.5)
+    idx, w = run_topk(ops, L, k, gate, renorm)
+    ref_idx = oracle.select_topk(L.numpy(), k)
+    np.testing.assert_array_equal(idx, ref_idx)
+    np.testing.assert_allclose(w, oracle.gate_weights(L.numpy(), ref_idx, gate, renorm), rtol=2e-6, atol=1e-7)
+
+
+def test_topk_all_equal_and_signed_zero(ops):
+    L = torch.zeros((5, 16), dtype=torch.float32)
+    L[1] = -0.0
+    L[2, ::2] = -0.0
+    L[3] = 1.0
+    L[4] = torch.arange(16, dtype=torch.float32)
+    idx, w = run_topk(ops, L, 4, "softmax", False)
+    np.testing.assert_array_equal(idx, oracle.select_topk(L.numpy(), 4))
+    assert idx[0].tolist() == [0, 1, 2, 3] and idx[4].tolist() == [15, 14, 13, 12]
+
+
+# =================================================================================================
+# a1: router logits (bf16 MFMA / fp32), sampled rows at full size
+# =================================================================================================
+@pytest.mark.parametrize("name", ALL)
+def test_router_logits(ops, name):
+    c = CFG[name]
+    A = mi.activations(c, DEV)
+    W_R = mi.normal((c.E, c.d), c.w_std, mi.seed_for(c.cfg_id, 0, mi.T_WR), DEV, c.torch_dtype)
+    bias = mi.normal((c.E,), 1.0, mi.seed_for(c.cfg_id, 0, mi.T_BIAS), DEV) if c.router_bias else None
+    logits = torch.empty((c.T, c.E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((c.T, c.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((c.T, c.k), dtype=torch.float32, device=DEV)
+    ops.moe_route(A, W_R, c.k, c.gate, c.renormalize, logits, idx, w, bias=bias)
+    _sync()
+    rows = mi.sample_rows(c.T, 1024, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE))
+    ref = oracle.router_logits(to_np(A[rows.to(DEV)]), to_np(W_R), None if bias is None else to_np(bias))
+    got = to_np(logits[rows.to(DEV)])
+    # the products are exact in fp32 and summed in fp32: far inside the bf16 bar
+    assert_parity(got, ref, c.torch_dtype, "logits")
+    assert max_rel_err(got, ref) < 1e-5
+    # the selection made on the GPU's own logits satisfies the top-k rule (property, all T)
+    check_topk_property(to_np(logits), idx.cpu().numpy())
+
+
+def check_topk_property(L, idx):
+    T, E = L.shape
+    k = idx.shape[1]
+    sel = np.take_along_axis(L, idx.astype(np.int64), 1)
+    # slot order: descending logit, ties by ascending index
+    assert np.all((sel[:, :-1] > sel[:, 1:]) | ((sel[:, :-1] == sel[:, 1:]) & (idx[:, :-1] < idx[:, 1:])))
+    mask = np.ones((T, E), bool)
+    np.put_along_axis(mask, idx.astype(np.int64), False, 1)
+    rest = np.where(mask, L, -np.inf)
+    worst_sel = sel[:, -1]
+    best_rest = rest.max(1)
+    assert np.all(worst_sel >= best_rest)
+    # where the boundary ties, the unselected equal logits have larger indices
+    tie_rows = np.nonzero(worst_sel == best_rest)[0]
+    for t in tie_rows:
+        tied = np.nonzero(mask[t] & (L[t] == worst_sel[t]))[0]
+        assert tied.min() > idx[t][sel[t] == worst_sel[t]].max()
+
+
+# =================================================================================================
+# a3: dispatch permutation, bit-exact
+# =================================================================================================
+def run_permute(ops, idx_np, E, A=None):
+    T, k = idx_np.shape
+    idx = torch.from_numpy(np.ascontiguousarray(idx_np)).to(torch.int32).to(DEV)
+    off = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    src = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    dest = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    Ap = torch.empty((T * k, A.shape[1]), dtype=A.dtype, device=DEV) if A is not None else None
+    ops.moe_permute(idx, E, off, src, dest, A=A, A_perm=Ap)
+    _sync()
+    return off.cpu().numpy(), src.cpu().numpy(), dest.cpu().numpy(), Ap
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_permute_bitexact_config(ops, name):
+    c = CFG[name]
+    zipf = 1.1 if c.router_bias else 0.0
+    idx = mi.topk_assignments(c.T, c.E, c.k, mi.seed_for(c.cfg_id, 0, mi.T_TOPK), zipf=zipf).numpy()
+    A = mi.activations(c, DEV)
+    off, src, dest, Ap = run_permute(ops, idx, c.E, A)
+    r_off, r_src, r_dest = oracle.permute(idx, c.E)
+    np.testing.assert_array_equal(off, r_off)
+    np.testing.assert_array_equal(src, r_src)
+    np.testing.assert_array_equal(dest, r_dest)
+    rows = mi.sample_rows(c.T * c.k, 4096, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 1))
+    got = Ap[rows.to(DEV)]
+    ref_tok = torch.from_numpy(r_src[rows.numpy()].astype(np.int64) // c.k).to(DEV)
+    assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                       A[ref_tok].view(torch.int16) if A.dtype == torch.bfloat16 else A[ref_tok].view(torch.int32))
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(1, 1, 1, "uniform"), (1, 8, 8, "uniform"), (3, 4, 2, "uniform"),
+                                        (4097, 5, 3, "uniform"), (5000, 64, 6, "one-hot"),
+                                        (2500, 1024, 4, "zipf"), (333, 7, 5, "repeats"), (1, 1024, 32, "uniform")])
+def test_permute_edges(ops, T, E, k, kind):
+    seed = mi.seed_for(98, T, E, k)
+    if kind == "one-hot":
+        idx = np.zeros((T, k), np.int32)
+        idx[:] = np.arange(k, dtype=np.int32)  # every token picks experts 0..k-1: the rest stay empty
+    elif kind == "repeats":
+        g = np.random.default_rng(seed)
+        idx = g.integers(0, E, size=(T, k)).astype(np.int32)  # ids may repeat inside a token
+    else:
+        idx = mi.topk_assignments(T, E, k, seed, zipf=1.5 if kind == "zipf" else 0.0).numpy()
+    A = mi.normal((T, 64), 1.0, seed, DEV, torch.bfloat16)
+    off, src, dest, Ap = run_permute(ops, idx, E, A)
+    r_off, r_src, r_dest = oracle.permute(idx, E)
+    np.testing.assert_array_equal(off, r_off)
+    np.testing.assert_array_equal(src, r_src)
+    np.testing.assert_array_equal(dest, r_dest)
+    ref = A[torch.from_numpy(r_src.astype(np.int64) // k).to(DEV)]
+    assert torch.equal(Ap.view(torch.int16), ref.view(torch.int16))
+
+
+def test_permute_empty_batch_writes_zero_offsets(ops):
+    idx = np.zeros((0, 2), np.int32)
+    off, _, _, _ = run_permute(ops, idx, 6)
+    np.testing.assert_array_equal(off, np.zeros(7, np.int32))
+
+
+def test_permute_is_deterministic(ops):
+    c = CFG["dsv3-stack"]
+    idx = mi.topk_assignments(c.T, c.E, c.k, mi.seed_for(c.cfg_id, 0, mi.T_TOPK)).numpy()
+    a = run_permute(ops, idx, c.E)
+    b = run_permute(ops, idx, c.E)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+
+
+# =================================================================================================
+# a4: grouped SwiGLU GEMM
+# =================================================================================================
+def run_swiglu(ops, X, sizes, W1, W2, W3):
+    off = torch.zeros(len(sizes) + 1, dtype=torch.int32)
+    off[1:] = torch.cumsum(torch.as_tensor(sizes, dtype=torch.int64), 0).to(torch.int32)
+    offd = off.to(DEV)
+    Y = torch.full((X.shape[0], X.shape[1]), float("nan"), dtype=X.dtype, device=DEV)
+    ops.moe_grouped_swiglu(X, offd, W1, W2, W3, Y)
+    _sync()
+    return off.numpy(), Y
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,G,d,c,sizes", [
+    (1000, 8, 256, 192, None),          # ragged tails in every group
+    (777, 5, 128, 128, [0, 700, 0, 77, 0]),   # empty groups
+    (129, 1, 192, 64, None),            # one group, one row past a tile
+    (1, 3, 64, 64, [0, 1, 0]),          # a single row
+    (0, 4, 64, 64, [0, 0, 0, 0]),       # empty input
+    (3000, 16, 512, 320, "zipf"),       # skewed groups spanning many tiles
+])
+def test_grouped_swiglu_small(ops, dtype, N, G, d, c, sizes):
+    seed = mi.seed_for(97, N, G, d, c)
+    if sizes is None:
+        sizes = mi.group_sizes(N, G, seed).tolist()
+    elif sizes == "zipf":
+        sizes = mi.group_sizes(N, G, seed, zipf=1.5).tolist()
+    std = 1.0 / d ** 0.5
+    X = mi.normal((N, d), 1.0, seed + 1, DEV, dtype)
+    W1 = mi.normal((G, c, d), std, seed + 2, DEV, dtype)
+    W2 = mi.normal((G, c, d), std, seed + 3, DEV, dtype)
+    W3 = mi.normal((G, d, c), 1.0 / c ** 0.5, seed + 4, DEV, dtype)
+    off, Y = run_swiglu(ops, X, sizes, W1, W2, W3)
+    if N == 0:
+        return
+    ref = oracle.grouped_mlp(to_np(X), off, ExpertSlices(W1), ExpertSlices(W2), ExpertSlices(W3))
+    assert_parity(to_np(Y), ref, dtype, "grouped swiglu")
+
+
+@pytest.mark.parametrize("name", ["dsv2-lite", "qwen3-30b-a3b", "llama4-scout", "dsv3-stack"])
+def test_grouped_swiglu_config_dims(ops, name):
+    """The workloads' (d, c) with a few experts and ragged row counts."""
+    c = CFG[name]
+    G = 3
+    sizes = [130, 0, 301] if c.d <= 5120 else [70, 0, 200]
+    N = sum(sizes)
+    seed = mi.seed_for(c.cfg_id, 5, mi.T_MISC)
+    X = mi.normal((N, c.d), 1.0, seed, DEV, c.torch_dtype)
+    W1 = mi.normal((G, c.c, c.d), c.w_std, seed + 1, DEV, c.torch_dtype)
+    W2 = mi.normal((G, c.c, c.d), c.w_std, seed + 2, DEV, c.torch_dtype)
+    W3 = mi.normal((G, c.d, c.c), c.w3_std, seed + 3, DEV, c.torch_dtype)
+    off, Y = run_swiglu(ops, X, sizes, W1, W2, W3)
+    ref = oracle.grouped_mlp(to_np(X), off, ExpertSlices(W1), ExpertSlices(W2), ExpertSlices(W3))
+    assert_parity(to_np(Y), ref, c.torch_dtype, name)
+
+
+def test_grouped_swiglu_dsv3_full_size_sampled(ops):
+    """All 524288 routed rows of the DeepSeek-V3-shaped layer in the bench launch configuration;
+    rows of four experts are checked against the oracle."""
+    c = CFG["dsv3-stack"]
+    N = c.T * c.k
+    W = mi.layer_weights(c, 0, DEV)
+    sizes = mi.group_sizes(N, c.E, mi.seed_for(c.cfg_id, 0, mi.T_GROUPS)).tolist()
+    X = mi.normal((N, c.d), 1.0, mi.seed_for(c.cfg_id, 0, mi.T_ACT, 9), DEV, c.torch_dtype)
+    off, Y = run_swiglu(ops, X, sizes, W["W1"], W["W2"], W["W3"])
+    W1, W2, W3 = ExpertSlices(W["W1"]), ExpertSlices(W["W2"]), ExpertSlices(W["W3"])
+    for e in (0, 17, 128, 255):
+        a, b = int(off[e]), int(off[e + 1])
+        rows = list(range(a, min(a + 8, b))) + list(range(max(a, b - 8), b))
+        ref = oracle.mlp(to_np(X[rows]), W1[e], W2[e], W3[e])
+        assert_parity(to_np(Y[rows]), ref, c.torch_dtype, f"expert {e}")
+    assert not torch.isnan(Y.float()).any().item()
+
+
+# =================================================================================================
+# a5: combine
+# =================================================================================================
+@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("with_add", [False, True])
+def test_combine(ops, name, with_add):
+    c = CFG[name]
+    N = c.T * c.k
+    seed = mi.seed_for(c.cfg_id, 0, mi.T_Y, int(with_add))
+    Y = mi.normal((N, c.d), 1.0, seed, DEV, c.torch_dtype)
+    w = mi.uniform((c.T, c.k), 0.0, 1.0, seed + 1, DEV)
+    dest = mi.randperm(N, seed + 2, DEV)
+    addend = mi.normal((c.T, c.d), 1.0, seed + 3, DEV, c.torch_dtype) if with_add else None
+    resid = mi.normal((c.T, c.d), 2.0, seed + 4, DEV) if with_add else None
+    out = torch.empty((c.T, c.d), dtype=torch.float32, device=DEV)
+    out_x = torch.empty((c.T, c.d), dtype=c.torch_dtype, device=DEV)
+    ops.moe_combine(Y, w, dest, out, addend=addend, residual=resid, out_x=out_x)
+    _sync()
+    rows = mi.sample_rows(c.T, 512, seed + 5)
+    rd = rows.to(DEV)
+    Yn = to_np(Y)
+    ref = oracle.combine(Yn, to_np(w)[rows.numpy()], dest.cpu().numpy().reshape(c.T, c.k)[rows.numpy()].reshape(-1),
+                         None if addend is None else to_np(addend[rd]), None if resid is None else to_np(resid[rd]))
+    got = to_np(out[rd])
+    # every product is exact in fp32: only fp32 summation rounding remains
+    assert_parity(got, ref, torch.float32, "combine")
+    # out_x is out rounded to the workload dtype (round to nearest even)
+    if c.torch_dtype == torch.bfloat16:
+        np.testing.assert_array_equal(to_np(out_x[rd]), oracle.round_to_bf16(got))
+    else:
+        np.testing.assert_array_equal(to_np(out_x[rd]), got)
+
+
+def test_combine_in_place_residual(ops):
+    T, k, d = 300, 3, 256
+    Y = mi.normal((T * k, d), 1.0, 5, DEV, torch.bfloat16)
+    w = mi.uniform((T, k), 0.0, 1.0, 6, DEV)
+    dest = mi.randperm(T * k, 7, DEV)
+    o = mi.normal((T, d), 1.0, 8, DEV)
+    o_ref = to_np(o)
+    ops.moe_combine(Y, w, dest, o, residual=o)
+    _sync()
+    ref = oracle.combine(to_np(Y), to_np(w), dest.cpu().numpy(), residual=o_ref)
+    assert_parity(to_np(o), ref, torch.float32, "in-place combine")
+
+
+# =================================================================================================
+# One MoE sublayer end to end (a1..a5), full size, sampled tokens, near-tie tokens excluded
+# =================================================================================================
+def layer_check(ops, c, n_sample):
+    from mixture_experts_layer_sum_amd.ops import LayerBuffers, moe_layer_forward
+    W = mi.layer_weights(c, 0, DEV)
+    A = mi.activations(c, DEV)
+    buf = LayerBuffers(c.T, c.d, c.E, c.k, c.c, c.shared_width, c.torch_dtype, DEV)
+    out = moe_layer_forward(A, W, c.k, c.gate, c.renormalize, buf)
+    _sync()
+    rows = mi.sample_rows(c.T, n_sample, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 2))
+    Wo = oracle_weights(W)
+    res = oracle.moe_layer(to_np(A[rows.to(DEV)]), Wo, c.k, c.gate, c.renormalize, c.n_shared, c.c_shared)
+    keep = oracle.topk_gap(res["logits"], c.k) >= NEAR_TIE
+    assert keep.mean() > 0.9
+    got = to_np(out[rows.to(DEV)])
+    r = assert_parity(got[keep], res["out"][keep], c.torch_dtype, c.name)
+    # routing of the kept tokens matches exactly
+    np.testing.assert_array_equal(buf.topk_idx[rows.to(DEV)].cpu().numpy()[keep], res["topk_idx"][keep])
+    return r
+
+
+@pytest.mark.parametrize("name,n_sample", [("tiny-fp32", 64), ("dsv2-lite", 256), ("qwen3-30b-a3b", 256),
+                                           ("llama4-scout", 128)])
+def test_layer_end_to_end(ops, name, n_sample):
+    layer_check(ops, CFG[name], n_sample)
+
+
+def test_layer_dsv3_full_size_sampled(ops):
+    layer_check(ops, CFG["dsv3-stack"].scaled(layers=1), 8)

@@ -1,0 +1,180 @@
+"""GPU parity of farskip_stack_forward (the FarSkip residual stack of MoE sublayers).
+
+- fp32 (tiny dims plus a shared expert, 4 layers): free-running against the oracle, 1e-4 bar, for
+  every mode and a mixed skip mask.
+- bf16: against the oracle with the implementation's storage precision mirrored (expert hidden,
+  expert/shared outputs and layer inputs rounded to bf16), so that the routing decisions of layers
+  2..L see inputs of the same precision.  Tokens whose k-th/(k+1)-th logit gap falls below the
+  margin at any layer are excluded: 1e-4 at layer 1 (identical inputs), 1e-2 at deeper layers,
+  where the two sides' inputs may still differ by one bf16 unit in a few elements (estimated
+  logit shift ~2e-3 at d = 7168, so the margin is about 5 sigma).
+- properties: two streams == one stream (bitwise), the stack == the same ABI calls composed by
+  hand on one stream (bitwise), runs are bitwise repeatable.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tests.helpers import NEAR_TIE, ExpertSlices, assert_parity, oracle_weights, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DEEP_MARGIN_BF16 = 1e-2
+
+TINY_STACK = mi.BY_NAME["tiny-fp32"].scaled(cfg_id=10, name="tiny-fp32-stack", n_shared=1, c_shared=256, layers=4)
+MID_STACK = mi.MoEConfig(11, "mid-bf16-stack", T=2048, d=512, E=16, k=4, c=256, n_shared=1, c_shared=256,
+                         gate="sigmoid", renormalize=True, dtype="bf16", layers=4)
+MID_SOFTMAX_2SH = mi.MoEConfig(12, "mid-bf16-softmax-2shared", T=1536, d=256, E=12, k=3, c=192, n_shared=2,
+                               c_shared=128, gate="softmax", renormalize=False, dtype="bf16", layers=3,
+                               router_bias=True)
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from mixture_experts_layer_sum_amd import ops as _ops
+    return _ops
+
+
+def make_stack(c):
+    layers = [mi.layer_weights(c, j, DEV) for j in range(c.layers)]
+    o0 = mi.activations(c, DEV).float()  # values representable in the workload dtype
+    return layers, o0
+
+
+def run_stack(ops, c, layers, o0, mode, mask=None, two_streams=True):
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
+    oL = torch.full_like(o0, float("nan"))
+    sm = torch.cuda.current_stream()
+    ss = torch.cuda.Stream() if two_streams else sm
+    ops.farskip_stack_forward(layers, cfg, mode, o0, oL, ws, skip_mask=mask, s_main=sm, s_side=ss)
+    torch.cuda.synchronize()
+    return oL
+
+
+def oracle_stack(c, layers, o0_rows, mode, mask=None):
+    bf = c.dtype == "bf16"
+    rnd = oracle.round_to_bf16 if bf else None
+    rec = []
+    Wo = [oracle_weights(W) for W in layers]
+    oL = oracle.moe_stack(o0_rows, Wo, c.k, c.gate, c.renormalize, mode, mask, c.n_shared, c.c_shared,
+                          round_inputs=rnd, record=rec, store=rnd)
+    keep = np.ones(o0_rows.shape[0], bool)
+    for j, (x, _, _, _) in enumerate(rec):
+        gap = oracle.topk_gap(oracle.router_logits(x, Wo[j]["W_R"], Wo[j]["bias"]), c.k)
+        keep &= gap >= (NEAR_TIE if (j == 0 or not bf) else DEEP_MARGIN_BF16)
+    return oL, keep
+
+
+MODES = [("none", None), ("partial", None), ("outdated", None), ("partial", [1, 0, 1, 1]),
+         ("outdated", [0, 1, 1, 0])]
+
+
+@pytest.mark.parametrize("mode,mask", MODES)
+def test_stack_fp32_free_running(ops, mode, mask):
+    c = TINY_STACK
+    layers, o0 = make_stack(c)
+    oL = run_stack(ops, c, layers, o0, mode, mask)
+    ref, keep = oracle_stack(c, layers, to_np(o0), mode, mask)
+    assert keep.mean() > 0.8
+    assert_parity(to_np(oL)[keep], ref[keep], torch.float32, f"fp32 stack {mode} {mask}")
+
+
+@pytest.mark.parametrize("c", [MID_STACK, MID_SOFTMAX_2SH], ids=lambda c: c.name)
+@pytest.mark.parametrize("mode,mask", MODES[:4])
+def test_stack_bf16_vs_oracle(ops, c, mode, mask):
+    if mask is not None:
+        mask = mask[:c.layers]
+    layers, o0 = make_stack(c)
+    oL = run_stack(ops, c, layers, o0, mode, mask)
+    rows = mi.sample_rows(c.T, 384, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE))
+    ref, keep = oracle_stack(c, layers, to_np(o0[rows.to(DEV)]), mode, mask)
+    assert keep.mean() > 0.5
+    assert_parity(to_np(oL[rows.to(DEV)])[keep], ref[keep], torch.bfloat16, f"bf16 stack {mode}")
+
+
+def test_stack_modes_differ(ops):
+    """The three wirings are really different functions (guards against a mode being ignored)."""
+    c = MID_STACK
+    layers, o0 = make_stack(c)
+    outs = [run_stack(ops, c, layers, o0, m) for m in ("none", "partial", "outdated")]
+    for a in range(3):
+        for b in range(a + 1, 3):
+            assert not torch.equal(outs[a], outs[b])
+
+
+@pytest.mark.parametrize("mode,mask", MODES)
+def test_stack_two_streams_equals_one_stream(ops, mode, mask):
+    c = MID_STACK
+    layers, o0 = make_stack(c)
+    a = run_stack(ops, c, layers, o0, mode, mask, two_streams=True)
+    b = run_stack(ops, c, layers, o0, mode, mask, two_streams=False)
+    assert torch.equal(a, b)
+    c2 = run_stack(ops, c, layers, o0, mode, mask, two_streams=True)
+    assert torch.equal(a, c2)  # bitwise repeatable
+
+
+def composed(ops, c, layers, o0, mode, mask):
+    """The stack recursion written with the single ABI calls on one stream."""
+    from mixture_experts_layer_sum_amd.ops import LayerBuffers
+    dt = c.torch_dtype
+    buf = LayerBuffers(c.T, c.d, c.E, c.k, c.c, c.shared_width, dt, DEV)
+    o_prev = o0.clone()
+    x = o0.to(dt)
+    L = len(layers)
+    for j, W in enumerate(layers):
+        ops.moe_route(x, W["W_R"], c.k, c.gate, c.renormalize, buf.logits, buf.topk_idx, buf.topk_w, bias=W["bias"])
+        ops.moe_permute(buf.topk_idx, c.E, buf.offsets, buf.sorted_src, buf.dest_row, A=x, A_perm=buf.A_perm,
+                        ws=buf.perm_ws)
+        ops.moe_grouped_swiglu(buf.A_perm, buf.offsets, W["W1"], W["W2"], W["W3"], buf.Y, ws=buf.gemm_ws)
+        S = None
+        if c.shared_width:
+            ops.moe_grouped_swiglu(x, buf.shared_off, W["Ws1"], W["Ws2"], W["Ws3"], buf.S, ws=buf.shared_ws)
+            S = buf.S
+        skip = mode != "none" and (mask is None or mask[j])
+        x_next = None
+        if skip and j + 1 < L:
+            x_next = ((o_prev + S.float()) if (mode == "partial" and S is not None) else o_prev).to(dt)
+        o_new = torch.empty_like(o_prev)
+        ops.moe_combine(buf.Y, buf.topk_w, buf.dest_row, o_new, addend=S, residual=o_prev)
+        if not skip and j + 1 < L:
+            x_next = o_new.to(dt)
+        o_prev, x = o_new, x_next
+    torch.cuda.synchronize()
+    return o_prev
+
+
+@pytest.mark.parametrize("c", [MID_STACK, MID_SOFTMAX_2SH, TINY_STACK], ids=lambda c: c.name)
+@pytest.mark.parametrize("mode,mask", MODES[:4])
+def test_stack_equals_composed_ops(ops, c, mode, mask):
+    if mask is not None:
+        mask = mask[:c.layers]
+    layers, o0 = make_stack(c)
+    a = run_stack(ops, c, layers, o0, mode, mask)
+    b = composed(ops, c, layers, o0, mode, mask)
+    assert torch.equal(a, b)
+
+
+def test_stack_dsv3_full_size_sampled(ops):
+    """The DeepSeek-V3-shaped 4-layer partial stack in the bench launch configuration (T = 65536,
+    two streams); 16 seeded tokens are followed through all four layers by the oracle."""
+    c = mi.BY_NAME["dsv3-stack"]
+    layers, o0 = make_stack(c)
+    oL = run_stack(ops, c, layers, o0, "partial")
+    assert not torch.isnan(oL).any().item()
+    rows = mi.sample_rows(c.T, 16, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 3))
+    # fetch expert weights on demand, one layer at a time, without caching (4 x 22.5 GB on device)
+    Wo = [oracle_weights(W, cache=False) for W in layers]
+    rnd = oracle.round_to_bf16
+    rec = []
+    ref = oracle.moe_stack(to_np(o0[rows.to(DEV)]), Wo, c.k, c.gate, c.renormalize, "partial", None, c.n_shared,
+                           c.c_shared, round_inputs=rnd, record=rec, store=rnd)
+    keep = np.ones(len(rows), bool)
+    for j, (x, _, _, _) in enumerate(rec):
+        gap = oracle.topk_gap(oracle.router_logits(x, Wo[j]["W_R"]), c.k)
+        keep &= gap >= (NEAR_TIE if j == 0 else DEEP_MARGIN_BF16)
+    assert keep.sum() >= 4
+    assert_parity(to_np(oL[rows.to(DEV)])[keep], ref[keep], torch.bfloat16, "dsv3 stack")
+

@@ -11,18 +11,18 @@ import oracle.moe_oracle as om
 from tests import test_oracle_pins as pins
 
 
-def _mlp_gate_up_swapped(X, W1, W2, W3):
+def _mlp_gate_up_swapped(X, W1, W2, W3, store=None):
     X = np.asarray(X, np.float64)
     return ((X @ np.asarray(W2, np.float64).T) * om.silu(X @ np.asarray(W1, np.float64).T)) @ np.asarray(W3, np.float64).T
 
 
-def _mlp_w3_untransposed(X, W1, W2, W3):
+def _mlp_w3_untransposed(X, W1, W2, W3, store=None):
     X = np.asarray(X, np.float64)
     H = (X @ np.asarray(W1, np.float64).T) * om.silu(X @ np.asarray(W2, np.float64).T)
     return H @ np.asarray(W3, np.float64)
 
 
-def _mlp_sigmoid_not_silu(X, W1, W2, W3):
+def _mlp_sigmoid_not_silu(X, W1, W2, W3, store=None):
     X = np.asarray(X, np.float64)
     G = X @ np.asarray(W2, np.float64).T
     H = (X @ np.asarray(W1, np.float64).T) * (1 / (1 + np.exp(-G)))

@@ -340,3 +340,16 @@ def test_topk_gap():
     L = np.array([[3.0, 1.0, 2.0, 2.0], [0.0, 5.0, 1.0, -1.0]])
     np.testing.assert_array_equal(oracle.topk_gap(L, 2), [0.0, 1.0])
     np.testing.assert_array_equal(oracle.topk_gap(L, 4), [np.inf, np.inf])
+
+
+def test_store_hook_identity_and_rounding_bound():
+    o0, Ws, kw = moe_stack_setup(L=2)
+    exact = oracle.moe_stack(o0, Ws, mode="partial", **kw)
+    ident = oracle.moe_stack(o0, Ws, mode="partial", store=lambda v: v, **kw)
+    np.testing.assert_array_equal(exact, ident)
+    A = o0
+    W = Ws[0]
+    Y = oracle.mlp(A, W["W1"][0], W["W2"][0], W["W3"][0])
+    Yr = oracle.mlp(A, W["W1"][0], W["W2"][0], W["W3"][0], store=oracle.round_to_bf16)
+    np.testing.assert_array_equal(Yr, oracle.round_to_bf16(Yr))  # stored values are bf16 values
+    assert np.max(np.abs(Yr - Y)) <= 2 ** -7 * np.max(np.abs(Y))
