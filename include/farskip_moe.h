@@ -163,7 +163,9 @@ typedef struct {
  * The residual o_j is kept in float32; each layer input x_j is rounded to cfg->dtype.
  * With the skip on, layer j+1's router and shared expert are enqueued on s_side while layer j's
  * permutation, routed grouped GEMM and combine run on s_main (HIP events order the two).
- * s_side == s_main gives the same results with everything serialised on one stream.
+ * s_side == s_main gives the same results with everything serialised on one stream.  Inputs
+ * are taken as ordered on s_main: s_side first waits for all work enqueued on s_main before the
+ * call, and the call's last kernel runs on s_main, so the result is ready when s_main is.
  *
  *   layers    host array [L] of device-pointer descriptors
  *   cfg       host pointer

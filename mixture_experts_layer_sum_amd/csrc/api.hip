@@ -248,11 +248,15 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
                   hipStream_t ss) {
   StackWs w = carve_stack(ws, c, nullptr);
   const bool two = sm != ss;
-  Events E_route, E_side, E_comb;
+  Events E_route, E_side, E_comb, E_entry;
   if (two) {
     if (int rc = E_route.make(L)) return rc;
     if (int rc = E_side.make(L)) return rc;
     if (int rc = E_comb.make(L)) return rc;
+    if (int rc = E_entry.make(1)) return rc;
+    // The inputs (o0, weights) may still be in flight on s_main: s_side starts behind them.
+    if (int rc = record(E_entry.ev[0], sm)) return rc;
+    if (int rc = wait(ss, E_entry.ev[0])) return rc;
   }
   const int64_t N = c.T * c.k;
   k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));

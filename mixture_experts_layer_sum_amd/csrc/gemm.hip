@@ -38,6 +38,7 @@ struct GemmArgs {
   const int32_t* tile_group;  // [max M-tiles] group of each M-tile (-1 = surplus), or null
   int64_t b_group_stride;     // elements between consecutive groups of B1/B2
   int32_t K, n_out, M, G, n_tiles;
+  int32_t group_m;            // M-tiles per scheduling group (tiles of a group share weights)
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -89,6 +90,28 @@ __device__ __forceinline__ bool resolve_mtile(const GemmArgs& p, int mt, int BM,
   return true;
 }
 
+// Workgroup -> (M-tile, N-tile).  Only the first (real M-tiles x n_tiles) workgroups get work, so
+// the surplus of the worst-case grid exits at once.  Workgroups are dealt round-robin to the 8
+// XCDs; each XCD is given one contiguous range of the logical tile order, and inside that order
+// group_m M-tiles sweep the N-tiles together, so the tiles resident on one XCD at a time share
+// their weight panel and their activation rows in that XCD's L2.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int& nt) {
+  const int total_mt = p.tile_group ? p.tile_start[p.G] : (p.M + BM - 1) / BM;
+  const int total = total_mt * p.n_tiles;
+  const int b = blockIdx.x;
+  if (b >= total) return false;
+  const int q = total / kXcds, r = total % kXcds, x = b % kXcds, i = b / kXcds;
+  const int L = x * q + min(x, r) + i;
+  const int gsz = p.group_m * p.n_tiles;
+  const int grp = L / gsz, within = L - grp * gsz;
+  const int m_in = min(p.group_m, total_mt - grp * p.group_m);
+  mt = grp * p.group_m + within % m_in;
+  nt = within / m_in;
+  return true;
+}
+
 // ------------------------------------------------------------------------------------------------
 // bf16 MFMA tile kernel
 // ------------------------------------------------------------------------------------------------
@@ -108,7 +131,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
+  int mt, nt;
+  if (!map_tile(p, BM, mt, nt)) return;
 
   int g, row0, rows;
   if (!resolve_mtile(p, mt, BM, g, row0, rows)) return;
@@ -314,9 +338,20 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs p) {
 // ------------------------------------------------------------------------------------------------
 namespace {
 // bf16 tilings (the phase-1 tile holds BN/2 columns of W1 and the same BN/2 columns of W2)
-constexpr int P1_BM = 128, P1_BN = 128, P1_WM = 2, P1_WN = 2;
-constexpr int P2_BM = 128, P2_BN = 128, P2_WM = 2, P2_WN = 2;
-constexpr int R_BM = 128, R_BN = 128, R_WM = 2, R_WN = 2;
+#ifndef FSM_P1
+#define FSM_P1 256, 256, 2, 4, 4   /* BM, BN, waves along M, waves along N, M-tiles per group */
+#endif
+#ifndef FSM_P2
+#define FSM_P2 256, 256, 2, 4, 4
+#endif
+#ifndef FSM_R
+#define FSM_R 256, 256, 2, 4, 1
+#endif
+struct TileCfg { int bm, bn, wm, wn, gm; };
+constexpr TileCfg kP1{FSM_P1}, kP2{FSM_P2}, kR{FSM_R};
+constexpr int P1_BM = kP1.bm, P1_BN = kP1.bn, P1_WM = kP1.wm, P1_WN = kP1.wn;
+constexpr int P2_BM = kP2.bm, P2_BN = kP2.bn, P2_WM = kP2.wm, P2_WN = kP2.wn;
+constexpr int R_BM = kR.bm, R_BN = kR.bn, R_WM = kR.wm, R_WN = kR.wn;
 constexpr int F_BM = 16, F_BN = 16;
 
 struct SwigluWs {
@@ -380,12 +415,12 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   GemmArgs a1{};
   a1.A = X; a1.B1 = W1; a1.B2 = W2; a1.out = w.H; a1.bias = nullptr;
   a1.offsets = offsets; a1.tile_start = w.ts1; a1.tile_group = w.grp1; a1.b_group_stride = c * d;
-  a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G;
+  a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G; a1.group_m = bf ? kP1.gm : 1;
 
   GemmArgs a2{};
   a2.A = w.H; a2.B1 = W3; a2.B2 = nullptr; a2.out = Y; a2.bias = nullptr;
   a2.offsets = offsets; a2.tile_start = w.ts2; a2.tile_group = w.grp2; a2.b_group_stride = d * c;
-  a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G;
+  a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G; a2.group_m = bf ? kP2.gm : 1;
 
   if (bf) {
     a1.n_tiles = int32_t(cdiv(c, P1_BN / 2));
@@ -419,7 +454,7 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
   GemmArgs a{};
   a.A = A; a.B1 = W_R; a.B2 = nullptr; a.out = logits; a.bias = bias;
   a.offsets = nullptr; a.tile_start = nullptr; a.tile_group = nullptr; a.b_group_stride = 0;
-  a.K = int32_t(d); a.n_out = E; a.M = int32_t(T); a.G = 1;
+  a.K = int32_t(d); a.n_out = E; a.M = int32_t(T); a.G = 1; a.group_m = kR.gm;
   ProfScope prof(MOE_K_ROUTER_GEMM, s);
   if (dtype == MOE_BF16) {
     a.n_tiles = int32_t(cdiv(E, R_BN));
