@@ -115,6 +115,19 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int
 // ------------------------------------------------------------------------------------------------
 // bf16 MFMA tile kernel
 // ------------------------------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
+
+// 16-byte load through a buffer resource: offsets at or beyond the resource size read as zero.
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -122,8 +135,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
+  constexpr int ROWS_PER_PASS = NT / 8;  // tile rows covered by one 16-byte load per thread
   static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile/thread mismatch");
   static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
+  static_assert(EPI != EPI_SWIGLU || (BN / 2) % ROWS_PER_PASS == 0, "B halves must align with load passes");
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
@@ -153,90 +168,86 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     Bg = Bu;
     nvalid = min(BN, p.n_out - n0);
   }
+  // Rows past `rows` (A) or `nvalid` (B) lie beyond the resource size and load as zeros.
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, int64_t(rows) * K * 2);
+  const __amdgpu_buffer_rsrc_t rU = make_rsrc(Bu, int64_t(nvalid) * K * 2);
+  const __amdgpu_buffer_rsrc_t rG = make_rsrc(Bg, int64_t(nvalid) * K * 2);
+
+  // Loads: thread tid owns 16-byte chunk ch = tid % 8 of tile rows r_l + i * ROWS_PER_PASS.  The
+  // pass stride is a multiple of 8 rows, so the row swizzle (r & 7) is the same for all of a
+  // thread's chunks: one LDS base plus constant offsets, one buffer offset plus a uniform stride.
+  const int r_l = tid >> 3, ch = tid & 7;
+  const uint32_t rowB = uint32_t(K) * 2u;  // bytes per row of A and B
+  const uint32_t offA0 = uint32_t(r_l) * rowB + uint32_t(ch) * 16u;
+  const int lds0 = r_l * BK + ((ch ^ (r_l & 7)) << 3);
+  // Fragment reads: rows (base + 16 i + lane % 16); base is a multiple of 16, so the swizzle
+  // term depends on the lane only.
+  const int fa0 = (wm * WTM + (lane & 15)) * BK;
+  const int fb0 = (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
+  const int sw = lane & 7;
 
   uint4 ra[ACH], rb[BCH];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
-      ra[i] = (r < rows) ? *reinterpret_cast<const uint4*>(Ab + int64_t(r) * K + k0 + ch * 8) : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
-      const uint16_t* src;
-      bool ok;
-      if (EPI == EPI_SWIGLU) {
-        if (r < BN / 2) { src = Bu + int64_t(r) * K; ok = r < nvalid; }
-        else { src = Bg + int64_t(r - BN / 2) * K; ok = (r - BN / 2) < nvalid; }
-      } else {
-        src = Bu + int64_t(r) * K;
-        ok = r < nvalid;
-      }
-      rb[i] = ok ? *reinterpret_cast<const uint4*>(src + k0 + ch * 8) : zero4;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][r * BK + ((ch ^ (r & 7)) << 3)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int id = tid + i * NT, r = id >> 3, ch = id & 7;
-      *reinterpret_cast<uint4*>(&sB[buf][r * BK + ((ch ^ (r & 7)) << 3)]) = rb[i];
-    }
-  };
-  auto brow = [&](int j) -> int {
-    if (EPI == EPI_SWIGLU)
-      return (j < FN / 2) ? wn * (WTN / 2) + j * 16 : BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 16;
-    return wn * WTN + j * 16;
-  };
-
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int ch = ks * 4 + (lane >> 4);
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = brow(j) + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  };
+#define FSM_GLOAD(KT)                                                                          \
+  {                                                                                            \
+    const uint32_t kb = uint32_t(KT) * BK * 2u;                                                \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
+      ra[i] = buf_load16(rA, offA0 + kb + uint32_t(i * ROWS_PER_PASS) * rowB);                 \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                          \
+      const int r = i * ROWS_PER_PASS;                                                         \
+      const bool gate = EPI == EPI_SWIGLU && r >= BN / 2;                                      \
+      const int rr = gate ? r - BN / 2 : r;                                                    \
+      rb[i] = buf_load16(gate ? rG : rU, offA0 + kb + uint32_t(rr) * rowB);                    \
+    }                                                                                          \
+  }
+#define FSM_SSTORE(BUF)                                                                        \
+  {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
+      *reinterpret_cast<uint4*>(&sA[BUF][lds0 + i * ROWS_PER_PASS * BK]) = ra[i];              \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                            \
+      *reinterpret_cast<uint4*>(&sB[BUF][lds0 + i * ROWS_PER_PASS * BK]) = rb[i];              \
+  }
+#define FSM_BROW(J) \
+  ((EPI == EPI_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
+#define FSM_COMPUTE(BUF)                                                                       \
+  {                                                                                            \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                                   \
+      const int cs = ((ks * 4 + (lane >> 4)) ^ sw) << 3;                                       \
+      bf16x8 bfr[FN];                                                                          \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) bfr[j] =                                  \
+          *reinterpret_cast<const bf16x8*>(&sB[BUF][fb0 + FSM_BROW(j) * BK + cs]);             \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA[BUF][fa0 + i * 16 * BK + cs]);  \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                         \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0); \
+      }                                                                                        \
+    }                                                                                          \
+  }
 
   const int KT = p.K / BK;
-  gload(0);
-  sstore(0);
+  FSM_GLOAD(0);
+  FSM_SSTORE(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    compute(cur);
-    if (kt + 1 < KT) sstore(cur ^ 1);
+  int cur = 0;
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    FSM_GLOAD(kt + 1);                    // next stage in flight during this stage's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    FSM_COMPUTE(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    FSM_SSTORE(cur ^ 1);
     __syncthreads();
+    cur ^= 1;
   }
+  FSM_COMPUTE(cur);
+#undef FSM_GLOAD
+#undef FSM_SSTORE
+#undef FSM_BROW
+#undef FSM_COMPUTE
 
   // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4*(lane >> 4) + {0..3}
   const int ml = lane & 15, nl = (lane >> 4) * 4;
