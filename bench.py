@@ -43,7 +43,30 @@ def parse():
     p.add_argument("--single-stream-steps", type=int, default=3,
                    help="extra steps with both streams merged into one (overlap reference); 0 = skip")
     p.add_argument("--cpu-sample", type=int, default=4, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                   help="before the steps, one plain device copy of this many GiB (a known-size kernel whose "
+                        "FETCH_SIZE / WRITE_SIZE calibrate the HBM counters); 0 = skip")
     return p.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_gate_up_dsv3_stack_hbm_traffic.txt")
+
+
+def measured_traffic():
+    """Calibrated HBM bytes per launch of the routed gate/up GEMM from the committed rocprofv3
+    counter summary, or None when that summary was taken with other library sources."""
+    from mixture_experts_layer_sum_amd.profiling import source_digest
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    lines = open(TRAFFIC_PROFILE).read().splitlines()
+    digest = next((l.split()[-1] for l in lines if l.startswith("# library source digest")), None)
+    if digest != source_digest():
+        return None
+    for l in lines:
+        f = l.split("|")
+        if l.startswith("traffic|") and "k_gemm_bf16<" in f[1] and f[1].rstrip(")").endswith(", 1, 0>(fsm::GemmArgs"):
+            return {"fetch_GB": float(f[3]), "write_GB": float(f[4]), "total_GB": float(f[5])}
+    return None
 
 
 def kernel_report(prof: dict, c, steps: int) -> dict:
@@ -161,6 +184,16 @@ def main():
     side_s = torch.cuda.Stream()
     log(f"workspace {ws.numel() / 2**30:.1f} GiB, HBM in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n * 4 / 2**30:.2f} GiB done")
+        del src, dst
+
     def step(ss):
         ops.farskip_stack_forward(layers, cfg, args.mode, o0, oL, ws, s_main=main_s, s_side=ss)
 
@@ -195,10 +228,17 @@ def main():
     kernels = kernel_report(prof, c, args.steps)
     g = kernels.get("gemm_gate_up", {})
     flops_launch = 4.0 * c.T * c.k * c.d * c.c
+    traffic = measured_traffic()
     roofline = {"kernel": "k_gemm_bf16 (grouped gate/up + SwiGLU, phase 1)", "bound": "mfma",
                 "achieved": g.get("tflops"), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": g.get("frac_mfma_peak"), "traffic": None,
                 "algorithmic_flop_per_launch": flops_launch, "avg_launch_ms": g.get("avg_ms")}
+    if traffic is not None:
+        # HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE); the algorithmic minimum is one
+        # read of the permuted rows and of W1/W2 plus one write of H
+        roofline["traffic"] = round(traffic["total_GB"] * 1e9)
+        roofline["traffic_detail"] = traffic
+        roofline["algorithmic_bytes_per_launch"] = 2 * (c.T * c.k * c.d + 2 * c.E * c.c * c.d + c.T * c.k * c.c)
 
     total_flop = c.layers * c.T * c.flops_per_token()["total"]
     value = c.T * c.layers / (ms_per_step * 1e-3)

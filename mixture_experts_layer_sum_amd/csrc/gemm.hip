@@ -128,7 +128,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+// SINGLE = 1 for single-group calls (a shared expert): the same code under its own symbol, so
+// profilers report routed and shared launches separately.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int SINGLE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int BK = 64;
@@ -438,13 +440,19 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
     const int64_t grid1 = mt1 * a1.n_tiles;
     {
       ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
-      k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
+      if (G > 1)
+        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, 0><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
+      else
+        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, 1><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
       if (int rc = check_launch("grouped gemm phase 1")) return rc;
     }
     a2.n_tiles = int32_t(cdiv(d, P2_BN));
     const int64_t grid2 = mt2 * a2.n_tiles;
     ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
-    k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
+    if (G > 1)
+      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, 0><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
+    else
+      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, 1><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
     return check_launch("grouped gemm phase 2");
   }
   a1.n_tiles = int32_t(cdiv(c, F_BN));
@@ -470,7 +478,7 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
   if (dtype == MOE_BF16) {
     a.n_tiles = int32_t(cdiv(E, R_BN));
     const int64_t grid = cdiv(T, R_BM) * a.n_tiles;
-    k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);
+    k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS, 1><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);
     return check_launch("router gemm");
   }
   a.n_tiles = int32_t(cdiv(E, F_BN));
