@@ -142,6 +142,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
   static_assert(EPI != EPI_SWIGLU || (BN / 2) % ROWS_PER_PASS == 0, "B halves must align with load passes");
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
+  static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
@@ -216,19 +217,43 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   }
 #define FSM_BROW(J) \
   ((EPI == EPI_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
+#define FSM_LDA(BUF, KS, I) \
+  (*reinterpret_cast<const bf16x8*>(&sA[BUF][fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define FSM_LDB(BUF, KS, J) \
+  (*reinterpret_cast<const bf16x8*>(&sB[BUF][fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+  // One K step (BK = 64 = two MFMA K slices) with the fragment reads software-pipelined: the A
+  // fragment for row block i+1 (and, in the first slice, the B fragments of the second slice) are
+  // read before the MFMAs of row block i, and scheduling groups pin that order, so an LDS read is
+  // always in flight under FN MFMAs instead of being waited for right before its first use.
+#define FSM_STEP0(BUF, I, WITH_B)                                                              \
+  {                                                                                            \
+    a_nxt = ((I) + 1 < FM) ? FSM_LDA(BUF, 0, (I) + 1) : FSM_LDA(BUF, 1, 0);                     \
+    if (WITH_B) b1[I] = FSM_LDB(BUF, 1, I);                                                    \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      acc[I][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[I][j], 0, 0, 0);   \
+    __builtin_amdgcn_sched_group_barrier(0x100, (WITH_B) ? 2 : 1, 0);                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
+    a_cur = a_nxt;                                                                             \
+  }
 #define FSM_COMPUTE(BUF)                                                                       \
   {                                                                                            \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                                   \
-      const int cs = ((ks * 4 + (lane >> 4)) ^ sw) << 3;                                       \
-      bf16x8 bfr[FN];                                                                          \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) bfr[j] =                                  \
-          *reinterpret_cast<const bf16x8*>(&sB[BUF][fb0 + FSM_BROW(j) * BK + cs]);             \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sA[BUF][fa0 + i * 16 * BK + cs]);  \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                         \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0); \
-      }                                                                                        \
+    bf16x8 b0[FN], b1[FN], a_cur, a_nxt;                                                       \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) b0[j] = FSM_LDB(BUF, 0, j);                 \
+    a_cur = FSM_LDA(BUF, 0, 0);                                                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                    \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) FSM_STEP0(BUF, i, true);                    \
+    _Pragma("unroll") for (int i = FN; i < FM; ++i) FSM_STEP0(BUF, i, false);                  \
+    _Pragma("unroll") for (int i = 0; i < FM - 1; ++i) {                                       \
+      a_nxt = FSM_LDA(BUF, 1, i + 1);                                                          \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[i][j], 0, 0, 0); \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                      \
+      a_cur = a_nxt;                                                                           \
     }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+      acc[FM - 1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[FM - 1][j], 0, 0, 0); \
+    __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
   }
 
   const int KT = p.K / BK;
@@ -249,6 +274,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 #undef FSM_GLOAD
 #undef FSM_SSTORE
 #undef FSM_BROW
+#undef FSM_LDA
+#undef FSM_LDB
+#undef FSM_STEP0
 #undef FSM_COMPUTE
 
   // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4*(lane >> 4) + {0..3}
