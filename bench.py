@@ -64,7 +64,7 @@ def measured_traffic():
         return None
     for l in lines:
         f = l.split("|")
-        if l.startswith("traffic|") and "k_gemm_bf16<" in f[1] and f[1].rstrip(")").endswith(", 1, 0>(fsm::GemmArgs"):
+        if l.startswith("traffic|") and "k_gemm_bf16<" in f[1] and (", 1, 2>" in f[1] or ", 1, 0>" in f[1]):
             return {"fetch_GB": float(f[3]), "write_GB": float(f[4]), "total_GB": float(f[5])}
     return None
 
@@ -77,7 +77,7 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
         "router_gemm": (2.0 * T * d * E, "flop"),
         "topk": (T * E * 4.0 + T * k * 8.0, "byte"),
         "permute_index": (N * 4.0 * 4 + (E + 1) * 4.0, "byte"),   # read idx twice, write 2 arrays
-        "permute_rows": (T * d * 2.0 + N * d * 2.0 + N * 4.0, "byte"),
+        "permute_rows": (T * d * 2.0 + N * d * 2.0 + N * 4.0, "byte"),  # not launched by the stack
         "gemm_gate_up": (4.0 * N * d * c_, "flop"),
         "gemm_down": (2.0 * N * d * c_, "flop"),
         "dense_gate_up": (4.0 * T * d * cs, "flop"),
@@ -229,7 +229,7 @@ def main():
     g = kernels.get("gemm_gate_up", {})
     flops_launch = 4.0 * c.T * c.k * c.d * c.c
     traffic = measured_traffic()
-    roofline = {"kernel": "k_gemm_bf16 (grouped gate/up + SwiGLU, phase 1)", "bound": "mfma",
+    roofline = {"kernel": "k_gemm_bf16 (grouped gate/up + SwiGLU, rows gathered)", "bound": "mfma",
                 "achieved": g.get("tflops"), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": g.get("frac_mfma_peak"), "traffic": None,
                 "algorithmic_flop_per_launch": flops_launch, "avg_launch_ms": g.get("avg_ms")}
@@ -238,7 +238,8 @@ def main():
         # read of the permuted rows and of W1/W2 plus one write of H
         roofline["traffic"] = round(traffic["total_GB"] * 1e9)
         roofline["traffic_detail"] = traffic
-        roofline["algorithmic_bytes_per_launch"] = 2 * (c.T * c.k * c.d + 2 * c.E * c.c * c.d + c.T * c.k * c.c)
+        # rows are gathered from x (read once: T*d), W1/W2 read once, H written once
+        roofline["algorithmic_bytes_per_launch"] = 2 * (c.T * c.d + 2 * c.E * c.c * c.d + c.T * c.k * c.c)
 
     total_flop = c.layers * c.T * c.flops_per_token()["total"]
     value = c.T * c.layers / (ms_per_step * 1e-3)

@@ -115,6 +115,23 @@ int moe_grouped_swiglu(const void* X, const int32_t* group_offsets, int32_t G, c
 size_t moe_grouped_swiglu_workspace_bytes(int64_t N, int32_t G, int64_t c, int dtype);
 
 /*
+ * moe_grouped_swiglu_gathered -- moe_grouped_swiglu with the Dispatch permutation of section 2.1
+ * folded into its loads: grouped row r is token row X[sorted_src[r] / k], so the permuted copy
+ * of the activations (A_perm) is never written.  Same result, bit for bit, as moe_permute with
+ * A_perm followed by moe_grouped_swiglu on A_perm.
+ *
+ *   X             [T, d] dtype    token activations
+ *   sorted_src    [N] int32       flat slot of each grouped row (moe_permute output); values in [0, T*k)
+ *   k             slots per token (sorted_src[r] / k is the token)
+ *   other arguments as moe_grouped_swiglu (N rows, G groups, workspace of the same size)
+ * Limits: as moe_grouped_swiglu; bf16 also needs T * d * 2 < 2^31 bytes.
+ */
+int moe_grouped_swiglu_gathered(const void* X, int64_t T, const int32_t* sorted_src, int32_t k,
+                                const int32_t* group_offsets, int32_t G, const void* W1, const void* W2,
+                                const void* W3, int dtype, int64_t N, int64_t d, int64_t c, void* Y,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_combine -- the Combine of section 2.1: routed expert outputs summed back per token.
  *   out[t] = residual[t] + addend[t] + sum_{i<k} topk_w[t,i] * Y[dest_row[t*k+i]]
  * accumulated in float32, slots in order i = 0..k-1 (deterministic, no atomics).
@@ -162,7 +179,8 @@ typedef struct {
  *     x_{j+1} = o_{j-1}                  if mode == FARSKIP_OUTDATED (eq. 8a).
  * The residual o_j is kept in float32; each layer input x_j is rounded to cfg->dtype.
  * With the skip on, layer j+1's router and shared expert are enqueued on s_side while layer j's
- * permutation, routed grouped GEMM and combine run on s_main (HIP events order the two).
+ * permutation, routed grouped GEMM (rows gathered through the permutation) and combine run on
+ * s_main (HIP events order the two).
  * s_side == s_main gives the same results with everything serialised on one stream.  Inputs
  * are taken as ordered on s_main: s_side first waits for all work enqueued on s_main before the
  * call, and the call's last kernel runs on s_main, so the result is ready when s_main is.

@@ -129,7 +129,6 @@ struct StackWs {
   int32_t* dest_row;
   int32_t* shared_off;
   void* perm_ws;
-  void* A_perm;
   void* Y;
   void* gemm_ws;
   void* shared_ws;
@@ -158,7 +157,6 @@ StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   s.dest_row = static_cast<int32_t*>(take(T * k * 4));
   s.shared_off = static_cast<int32_t*>(take(2 * 4));
   s.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
-  s.A_perm = take(T * k * d * es);
   s.Y = take(T * k * d * es);
   s.gemm_ws = take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
   s.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype)) : nullptr;
@@ -195,6 +193,8 @@ int check_stack(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t
     return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: bf16 needs c and c_shared multiples of 64");
   if (c.d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: needs d %% 8 == 0");
   if (c.T * int64_t(c.k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: T*k too large");
+  if (c.T * c.d * int64_t(esize(c.dtype)) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: a layer input above 2^31 bytes");
   if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: o0 and oL are required");
   if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: oL must not alias o0");
   for (int j = 0; j < L; ++j) {
@@ -292,10 +292,10 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
     if (two)
       if (int rc = wait(sm, E_route.ev[j])) return rc;
     if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
-                                w.dest_row, w.A_perm, w.perm_ws, sm))
+                                w.dest_row, nullptr, w.perm_ws, sm))
       return rc;
-    if (int rc = launch_grouped_swiglu(w.A_perm, w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y,
-                                       w.gemm_ws, sm))
+    if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y,
+                                       w.gemm_ws, sm, w.sorted_src, c.k, c.T))
       return rc;
     if (two)
       if (int rc = wait(sm, E_side.ev[j])) return rc;
@@ -361,6 +361,23 @@ int moe_grouped_swiglu(const void* X, const int32_t* group_offsets, int32_t G, c
                             "moe_grouped_swiglu"))
     return rc;
   return launch_grouped_swiglu(X, group_offsets, G, W1, W2, W3, dtype, N, d, c, Y, ws, as_stream(stream));
+}
+
+int moe_grouped_swiglu_gathered(const void* X, int64_t T, const int32_t* sorted_src, int32_t k,
+                                const int32_t* group_offsets, int32_t G, const void* W1, const void* W2,
+                                const void* W3, int dtype, int64_t N, int64_t d, int64_t c, void* Y, void* ws,
+                                size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_swiglu(X, group_offsets, G, W1, W2, W3, dtype, N, d, c, Y, ws, ws_bytes,
+                            "moe_grouped_swiglu_gathered"))
+    return rc;
+  if (T < 0 || k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu_gathered: need T >= 0 and k >= 1");
+  if (N > 0 && (!sorted_src || T == 0))
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu_gathered: sorted_src and T > 0 are required");
+  if (T * d * int64_t(esize(dtype)) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu_gathered: X larger than 2^31 bytes");
+  return launch_grouped_swiglu(X, group_offsets, G, W1, W2, W3, dtype, N, d, c, Y, ws, as_stream(stream),
+                               sorted_src, k, T);
 }
 
 int moe_combine(const void* Y, int dtype, const float* topk_w, const int32_t* dest_row, int64_t T, int64_t d,

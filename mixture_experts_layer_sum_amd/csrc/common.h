@@ -69,9 +69,11 @@ int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, in
                    const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
                    void* A_perm, void* ws, hipStream_t s);
 size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype);
+// gather != null: row r of the grouped input is X[gather[r] / gather_k], X having x_rows rows
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
-                          void* Y, void* ws, hipStream_t s);
+                          void* Y, void* ws, hipStream_t s, const int32_t* gather = nullptr,
+                          int32_t gather_k = 1, int64_t x_rows = 0);
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
                    void* out_x, hipStream_t s);

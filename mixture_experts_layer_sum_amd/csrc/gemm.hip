@@ -39,7 +39,15 @@ struct GemmArgs {
   int64_t b_group_stride;     // elements between consecutive groups of B1/B2
   int32_t K, n_out, M, G, n_tiles;
   int32_t group_m;            // M-tiles per scheduling group (tiles of a group share weights)
+  const int32_t* gather;      // ROWS_GATHER: grouped row r reads A row gather[r] / gather_k
+  int32_t gather_k;
+  int64_t a_rows;             // ROWS_GATHER: rows of A (its buffer-resource extent)
 };
+
+// How a workgroup finds its A rows: contiguous rows of a grouped input, a single group, or rows
+// gathered from the token matrix through the dispatch permutation (the permuted copy of the
+// activations is then never written).
+enum { ROWS_GROUPED = 0, ROWS_SINGLE = 1, ROWS_GATHER = 2 };
 
 // ------------------------------------------------------------------------------------------------
 // M-tile table: tile_start[g] = sum_{g' < g} ceil(count_g' / BM), and tile_group[t] = the group of
@@ -128,9 +136,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
 }
 
-// SINGLE = 1 for single-group calls (a shared expert): the same code under its own symbol, so
-// profilers report routed and shared launches separately.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int SINGLE>
+// ROWS (ROWS_GROUPED / ROWS_SINGLE / ROWS_GATHER) also gives routed and shared launches their own
+// symbols, so profilers report them separately.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int BK = 64;
@@ -172,7 +180,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     nvalid = min(BN, p.n_out - n0);
   }
   // Rows past `rows` (A) or `nvalid` (B) lie beyond the resource size and load as zeros.
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, int64_t(rows) * K * 2);
+  const __amdgpu_buffer_rsrc_t rA =
+      ROWS == ROWS_GATHER ? make_rsrc(p.A, p.a_rows * K * 2) : make_rsrc(Ab, int64_t(rows) * K * 2);
   const __amdgpu_buffer_rsrc_t rU = make_rsrc(Bu, int64_t(nvalid) * K * 2);
   const __amdgpu_buffer_rsrc_t rG = make_rsrc(Bg, int64_t(nvalid) * K * 2);
 
@@ -182,6 +191,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   const int r_l = tid >> 3, ch = tid & 7;
   const uint32_t rowB = uint32_t(K) * 2u;  // bytes per row of A and B
   const uint32_t offA0 = uint32_t(r_l) * rowB + uint32_t(ch) * 16u;
+  // gathered rows: one offset per row this thread loads; rows past the tile point beyond the
+  // resource (0x80000000 > its extent) and read as zeros
+  uint32_t offG[ROWS == ROWS_GATHER ? ACH : 1];
+  if (ROWS == ROWS_GATHER) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int r = r_l + i * ROWS_PER_PASS;
+      offG[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(ch) * 16u : 0x80000000u;
+    }
+  }
   const int lds0 = r_l * BK + ((ch ^ (r_l & 7)) << 3);
   // Fragment reads: rows (base + 16 i + lane % 16); base is a multiple of 16, so the swizzle
   // term depends on the lane only.
@@ -200,7 +219,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   {                                                                                            \
     const uint32_t kb = uint32_t(KT) * BK * 2u;                                                \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
-      ra[i] = buf_load16(rA, offA0 + kb + uint32_t(i * ROWS_PER_PASS) * rowB);                 \
+      ra[i] = buf_load16(rA, (ROWS == ROWS_GATHER ? offG[i] : offA0 + uint32_t(i * ROWS_PER_PASS) * rowB) + kb); \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                          \
       const int r = i * ROWS_PER_PASS;                                                         \
       const bool gate = EPI == EPI_SWIGLU && r >= BN / 2;                                      \
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 // ------------------------------------------------------------------------------------------------
 // float32 path (the tiny fp32 workload): 16 x 16 output tile per workgroup, plain FMA.
 // ------------------------------------------------------------------------------------------------
-template <int EPI>
+template <int EPI, int ROWS>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs p) {
   constexpr int BM = 16, BN = 16, BKF = 16;
   __shared__ float sA[BM][BKF + 1], sU[BN][BKF + 1], sG[BN][BKF + 1];
@@ -348,7 +367,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs p) {
   float accU = 0.f, accG = 0.f;
   for (int k0 = 0; k0 < K; k0 += BKF) {
     const int k = k0 + tx;
-    sA[ty][tx] = (ty < rows && k < K) ? A[int64_t(ty) * K + k] : 0.f;
+    if (ROWS == ROWS_GATHER)
+      sA[ty][tx] = (ty < rows && k < K)
+                       ? static_cast<const float*>(p.A)[int64_t(p.gather[row0 + ty] / p.gather_k) * K + k]
+                       : 0.f;
+    else
+      sA[ty][tx] = (ty < rows && k < K) ? A[int64_t(ty) * K + k] : 0.f;
     const int n = n0 + ty;
     const bool nok = n < p.n_out && k < K;
     sU[ty][tx] = nok ? B1[int64_t(n) * K + k] : 0.f;
@@ -433,7 +457,8 @@ size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype) {
 
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
-                          void* Y, void* ws, hipStream_t s) {
+                          void* Y, void* ws, hipStream_t s, const int32_t* gather, int32_t gather_k,
+                          int64_t x_rows) {
   SwigluWs w = carve(ws, G, N, c, dtype, nullptr);
   if (N == 0) return MOE_OK;
   const bool bf = dtype == MOE_BF16;
@@ -457,41 +482,51 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   a1.A = X; a1.B1 = W1; a1.B2 = W2; a1.out = w.H; a1.bias = nullptr;
   a1.offsets = offsets; a1.tile_start = w.ts1; a1.tile_group = w.grp1; a1.b_group_stride = c * d;
   a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G; a1.group_m = bf ? kP1.gm : 1;
+  a1.gather = gather; a1.gather_k = gather_k; a1.a_rows = x_rows;
 
   GemmArgs a2{};
   a2.A = w.H; a2.B1 = W3; a2.B2 = nullptr; a2.out = Y; a2.bias = nullptr;
   a2.offsets = offsets; a2.tile_start = w.ts2; a2.tile_group = w.grp2; a2.b_group_stride = d * c;
   a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G; a2.group_m = bf ? kP2.gm : 1;
 
+  const int rows1 = gather ? ROWS_GATHER : (G > 1 ? ROWS_GROUPED : ROWS_SINGLE);
+  const int rows2 = G > 1 ? ROWS_GROUPED : ROWS_SINGLE;
   if (bf) {
     a1.n_tiles = int32_t(cdiv(c, P1_BN / 2));
-    const int64_t grid1 = mt1 * a1.n_tiles;
+    const dim3 grid1(unsigned(mt1 * a1.n_tiles));
+    constexpr int nt1 = 64 * P1_WM * P1_WN;
     {
       ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
-      if (G > 1)
-        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, 0><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
+      if (rows1 == ROWS_GATHER)
+        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_GATHER><<<grid1, nt1, 0, s>>>(a1);
+      else if (rows1 == ROWS_GROUPED)
+        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_GROUPED><<<grid1, nt1, 0, s>>>(a1);
       else
-        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, 1><<<dim3(unsigned(grid1)), 64 * P1_WM * P1_WN, 0, s>>>(a1);
+        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_SINGLE><<<grid1, nt1, 0, s>>>(a1);
       if (int rc = check_launch("grouped gemm phase 1")) return rc;
     }
     a2.n_tiles = int32_t(cdiv(d, P2_BN));
-    const int64_t grid2 = mt2 * a2.n_tiles;
+    const dim3 grid2(unsigned(mt2 * a2.n_tiles));
+    constexpr int nt2 = 64 * P2_WM * P2_WN;
     ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
-    if (G > 1)
-      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, 0><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
+    if (rows2 == ROWS_GROUPED)
+      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, ROWS_GROUPED><<<grid2, nt2, 0, s>>>(a2);
     else
-      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, 1><<<dim3(unsigned(grid2)), 64 * P2_WM * P2_WN, 0, s>>>(a2);
+      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, ROWS_SINGLE><<<grid2, nt2, 0, s>>>(a2);
     return check_launch("grouped gemm phase 2");
   }
   a1.n_tiles = int32_t(cdiv(c, F_BN));
   {
     ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
-    k_gemm_f32<EPI_SWIGLU><<<dim3(unsigned(mt1 * a1.n_tiles)), 256, 0, s>>>(a1);
+    if (rows1 == ROWS_GATHER)
+      k_gemm_f32<EPI_SWIGLU, ROWS_GATHER><<<dim3(unsigned(mt1 * a1.n_tiles)), 256, 0, s>>>(a1);
+    else
+      k_gemm_f32<EPI_SWIGLU, ROWS_GROUPED><<<dim3(unsigned(mt1 * a1.n_tiles)), 256, 0, s>>>(a1);
     if (int rc = check_launch("grouped gemm phase 1 (f32)")) return rc;
   }
   a2.n_tiles = int32_t(cdiv(d, F_BN));
   ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
-  k_gemm_f32<EPI_PLAIN><<<dim3(unsigned(mt2 * a2.n_tiles)), 256, 0, s>>>(a2);
+  k_gemm_f32<EPI_PLAIN, ROWS_GROUPED><<<dim3(unsigned(mt2 * a2.n_tiles)), 256, 0, s>>>(a2);
   return check_launch("grouped gemm phase 2 (f32)");
 }
 
@@ -506,11 +541,11 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
   if (dtype == MOE_BF16) {
     a.n_tiles = int32_t(cdiv(E, R_BN));
     const int64_t grid = cdiv(T, R_BM) * a.n_tiles;
-    k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS, 1><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);
+    k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS, ROWS_SINGLE><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);
     return check_launch("router gemm");
   }
   a.n_tiles = int32_t(cdiv(E, F_BN));
-  k_gemm_f32<EPI_F32_BIAS><<<dim3(unsigned(cdiv(T, F_BM) * a.n_tiles)), 256, 0, s>>>(a);
+  k_gemm_f32<EPI_F32_BIAS, ROWS_GROUPED><<<dim3(unsigned(cdiv(T, F_BM) * a.n_tiles)), 256, 0, s>>>(a);
   return check_launch("router gemm (f32)");
 }
 

@@ -94,6 +94,19 @@ def moe_grouped_swiglu(X, group_offsets, W1, W2, W3, Y, ws=None, stream=None):
                                  _p(Y), _p(ws), ws.numel(), _s(stream)))
 
 
+def moe_grouped_swiglu_gathered(X, sorted_src, k: int, group_offsets, W1, W2, W3, Y, ws=None, stream=None):
+    """moe_grouped_swiglu on the rows X[sorted_src[r] // k] without materialising them."""
+    T, d = X.shape
+    N = sorted_src.numel()
+    G = group_offsets.numel() - 1
+    c = W1.shape[-2]
+    if ws is None:
+        ws = workspace(grouped_swiglu_workspace_bytes(N, G, c, X.dtype), X.device)
+    check("moe_grouped_swiglu_gathered",
+          lib.moe_grouped_swiglu_gathered(_p(X), T, _p(sorted_src), k, _p(group_offsets), G, _p(W1), _p(W2), _p(W3),
+                                          dtype_code(X.dtype), N, d, c, _p(Y), _p(ws), ws.numel(), _s(stream)))
+
+
 def moe_combine(Y, topk_w, dest_row, out, addend=None, residual=None, out_x=None, stream=None):
     """out = residual + addend + sum_i topk_w[:, i] * Y[dest_row[t*k+i]]  (fp32)."""
     T, k = topk_w.shape

@@ -119,7 +119,7 @@ def cmd_trace(path, skip_first=0):
         disp.append((t0, t1, q, name))
     disp.sort()
     lib = [d for d in disp if LIB_PREFIX in d[3]]
-    gemm = [d for d in lib if "k_gemm_bf16" in d[3] and ", 1, 0>" in d[3]]  # routed gate/up
+    gemm = [d for d in lib if "k_gemm_bf16" in d[3] and (", 1, 0>" in d[3] or ", 1, 2>" in d[3])]  # routed gate/up
     if skip_first and len(gemm) > skip_first:
         t_begin = gemm[skip_first][0]
         lib = [d for d in lib if d[0] >= t_begin - 50_000_000]  # keep the rest of that step's head
@@ -131,7 +131,8 @@ def cmd_trace(path, skip_first=0):
     print(f"{'kernel':<70} {'queue':>6} {'calls':>6} {'avg_us':>10} {'total_ms':>10}")
     for (name, q), ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         print(f"{short(name, 70):<70} {q:>6} {len(ds):>6} {sum(ds) / len(ds) / 1e3:>10.1f} {sum(ds) / 1e6:>10.2f}")
-    main_q = {d[2] for d in lib if "k_gemm_bf16" in d[3] and ", 0>" in d[3]}
+    # routed GEMMs (row modes 0 = grouped, 2 = gathered) run on the main queue
+    main_q = {d[2] for d in lib if "k_gemm_bf16" in d[3] and (", 0>" in d[3] or ", 2>" in d[3])}
     if len(main_q) != 1:
         print("# overlap: could not identify a single main queue")
         return

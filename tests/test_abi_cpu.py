@@ -91,6 +91,23 @@ def test_grouped_swiglu_argument_errors():
     err(f(BAD, BAD, 4096, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None), L.MOE_ERR_UNSUPPORTED)
 
 
+def test_grouped_swiglu_gathered_argument_errors():
+    f = lib.moe_grouped_swiglu_gathered
+    need = lib.moe_grouped_swiglu_workspace_bytes(256, 4, 128, 1)
+    args = [BAD, 128, BAD, 2, BAD, 4, BAD, BAD, BAD, 1, 256, 128, 128, BAD, BAD, need, None]
+    bad = list(args); bad[15] = need - 1
+    err(f(*bad), L.MOE_ERR_WORKSPACE)
+    bad = list(args); bad[2] = None
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "sorted_src")
+    bad = list(args); bad[3] = 0
+    err(f(*bad), L.MOE_ERR_INVALID_ARG)
+    bad = list(args); bad[1] = 1 << 20; bad[11] = 1024
+    bad[15] = lib.moe_grouped_swiglu_workspace_bytes(256, 4, 128, 1)
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "2^31")
+    bad = list(args); bad[11] = 100
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "% 64")
+
+
 def test_combine_argument_errors():
     f = lib.moe_combine
     err(f(BAD, 1, BAD, BAD, 10, 12, 2, None, None, BAD, None, None), L.MOE_ERR_UNSUPPORTED, "% 8")
@@ -152,7 +169,9 @@ def test_workspace_queries_scale():
     assert lib.moe_grouped_swiglu_workspace_bytes(-1, 8, 256, 1) == 0
     assert lib.moe_permute_workspace_bytes(65536, 256, 8) >= 2 * (65536 * 8 // 4096) * 256 * 4
     c5 = _cfg(T=65536, d=7168, c=2048, c_shared=2048, E=256, k=8, gate=1, dtype=1)
-    assert lib.farskip_stack_workspace_bytes(ctypes.byref(c5)) > 2 * 65536 * 8 * 7168 * 2
+    # Y [T*k, d] is the largest buffer; the permuted copy of the activations is not kept
+    ws5 = lib.farskip_stack_workspace_bytes(ctypes.byref(c5))
+    assert 65536 * 8 * 7168 * 2 < ws5 < 2 * 65536 * 8 * 7168 * 2
 
 
 def test_python_binding_refuses_unknown_dtype():

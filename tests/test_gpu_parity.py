@@ -272,6 +272,36 @@ def test_grouped_swiglu_dsv3_full_size_sampled(ops):
 
 
 # =================================================================================================
+# a3 + a4 fused: rows gathered through the permutation (the stack's launch configuration)
+# =================================================================================================
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,E,k,d,c,kind", [(333, 6, 2, 128, 192, "uniform"), (1000, 16, 4, 256, 128, "zipf"),
+                                            (5, 8, 8, 64, 64, "uniform"), (700, 4, 3, 192, 320, "repeats")])
+def test_grouped_swiglu_gathered(ops, dtype, T, E, k, d, c, kind):
+    seed = mi.seed_for(96, T, E, k)
+    if kind == "repeats":
+        idx = np.random.default_rng(seed).integers(0, E, size=(T, k)).astype(np.int32)
+    else:
+        idx = mi.topk_assignments(T, E, k, seed, zipf=1.5 if kind == "zipf" else 0.0).numpy()
+    A = mi.normal((T, d), 1.0, seed + 1, DEV, dtype)
+    off, src, dest, Ap = run_permute(ops, idx, E, A)
+    std = 1.0 / d ** 0.5
+    W1 = mi.normal((E, c, d), std, seed + 2, DEV, dtype)
+    W2 = mi.normal((E, c, d), std, seed + 3, DEV, dtype)
+    W3 = mi.normal((E, d, c), 1.0 / c ** 0.5, seed + 4, DEV, dtype)
+    offd = torch.from_numpy(off).to(DEV)
+    Yg = torch.full((T * k, d), float("nan"), dtype=dtype, device=DEV)
+    ops.moe_grouped_swiglu_gathered(A, torch.from_numpy(src).to(DEV), k, offd, W1, W2, W3, Yg)
+    Yp = torch.full_like(Yg, float("nan"))
+    ops.moe_grouped_swiglu(Ap, offd, W1, W2, W3, Yp)
+    _sync()
+    assert torch.equal(Yg, Yp)  # same rows, same order: bit-identical
+    ref = oracle.grouped_mlp(oracle.permute_rows(to_np(A), src, k), off, ExpertSlices(W1), ExpertSlices(W2),
+                             ExpertSlices(W3))
+    assert_parity(to_np(Yg), ref, dtype, "gathered grouped swiglu")
+
+
+# =================================================================================================
 # a5: combine
 # =================================================================================================
 @pytest.mark.parametrize("name", ALL)
