@@ -79,6 +79,11 @@ def _declare(lib):
 
 
 def load():
+    # The library must run on the same HIP runtime as the framework that owns the device memory and
+    # streams it is handed.  torch bundles its own libamdhip64; importing torch first makes the
+    # library's libamdhip64.so.7 dependency resolve to that already-loaded copy instead of loading a
+    # second runtime into the process.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_sum_amd.build` "
                           "(the HIP library is required, there is no fallback)")

@@ -124,6 +124,16 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int
 // bf16 MFMA tile kernel
 // ------------------------------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#ifndef FSM_DMA
+#define FSM_DMA 1  // 1: stage tiles with direct-to-LDS buffer loads; 0: through registers
+#endif
+// The direct-to-LDS body uses device-only builtins; the host pass (which only needs the kernels'
+// launch stubs) parses the register-staging body.
+#if FSM_DMA && defined(__HIP_DEVICE_COMPILE__)
+#define FSM_DMA_ON 1
+#else
+#define FSM_DMA_ON 0
+#endif
 constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
 
 // 16-byte load through a buffer resource: offsets at or beyond the resource size read as zero.
@@ -152,10 +162,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
   static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
 
+#if FSM_DMA_ON
+  // one named array per stage, so the compiler can tell the stage being filled from the one read
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[BM * BK], sA1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[BN * BK], sB1[BN * BK];
+#else
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+#endif
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave: readfirstlane lets the compiler keep it (and every
+  // address derived from it) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   int mt, nt;
   if (!map_tile(p, BM, mt, nt)) return;
@@ -230,16 +248,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 #define FSM_SSTORE(BUF)                                                                        \
   {                                                                                            \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
-      *reinterpret_cast<uint4*>(&sA[BUF][lds0 + i * ROWS_PER_PASS * BK]) = ra[i];              \
+      *reinterpret_cast<uint4*>(&FSM_SA(BUF)[lds0 + i * ROWS_PER_PASS * BK]) = ra[i];          \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                            \
-      *reinterpret_cast<uint4*>(&sB[BUF][lds0 + i * ROWS_PER_PASS * BK]) = rb[i];              \
+      *reinterpret_cast<uint4*>(&FSM_SB(BUF)[lds0 + i * ROWS_PER_PASS * BK]) = rb[i];          \
   }
 #define FSM_BROW(J) \
   ((EPI == EPI_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
+#if FSM_DMA_ON
+#define FSM_SA(BUF) ((BUF) ? sA1 : sA0)
+#define FSM_SB(BUF) ((BUF) ? sB1 : sB0)
+#else
+#define FSM_SA(BUF) (sA[BUF])
+#define FSM_SB(BUF) (sB[BUF])
+#endif
 #define FSM_LDA(BUF, KS, I) \
-  (*reinterpret_cast<const bf16x8*>(&sA[BUF][fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+  (*reinterpret_cast<const bf16x8*>(&FSM_SA(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
 #define FSM_LDB(BUF, KS, J) \
-  (*reinterpret_cast<const bf16x8*>(&sB[BUF][fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+  (*reinterpret_cast<const bf16x8*>(&FSM_SB(BUF)[fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
   // One K step (BK = 64 = two MFMA K slices) with the fragment reads software-pipelined: the A
   // fragment for row block i+1 (and, in the first slice, the B fragments of the second slice) are
   // read before the MFMAs of row block i, and scheduling groups pin that order, so an LDS read is
@@ -276,6 +301,65 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   }
 
   const int KT = p.K / BK;
+#if FSM_DMA_ON
+  // Direct-to-LDS staging: each wave fills whole 1 KB runs (8 tile rows) of a stage with
+  // buffer_load ... lds; lane l writes physical chunk l % 8 of row l / 8 of its run, so it loads
+  // logical chunk (l % 8) ^ (l / 8), which reproduces the swizzled layout the fragment reads use.
+  constexpr int NW = NT / 64;
+  constexpr int A_RUNS = BM / 8 / NW, B_RUNS = BN / 8 / NW;  // 1 KB runs per wave per stage
+  static_assert(A_RUNS * 8 * NW == BM && B_RUNS * 8 * NW == BN, "runs must tile the stage");
+  static_assert(EPI != EPI_SWIGLU || (BN / 2) % (B_RUNS * 8) == 0, "a wave's B rows must lie in one half");
+  const int d_row = lane >> 3, d_ch = (lane & 7) ^ (lane >> 3);
+  uint32_t dA[A_RUNS], dB[B_RUNS];
+#pragma unroll
+  for (int i = 0; i < A_RUNS; ++i) {
+    const int r = (wave * A_RUNS + i) * 8 + d_row;
+    if (ROWS == ROWS_GATHER)
+      dA[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(d_ch) * 16u : 0x80000000u;
+    else
+      dA[i] = uint32_t(r) * rowB + uint32_t(d_ch) * 16u;
+  }
+  const int wb_row0 = wave * B_RUNS * 8;  // first B tile row of this wave
+  const bool b_gate = EPI == EPI_SWIGLU && wb_row0 >= BN / 2;
+  const __amdgpu_buffer_rsrc_t rBw = b_gate ? rG : rU;
+#pragma unroll
+  for (int i = 0; i < B_RUNS; ++i) {
+    const int r = wb_row0 + i * 8 + d_row;
+    dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
+  }
+#define FSM_DMA_STAGE(KT, BUF)                                                                        \
+  {                                                                                                   \
+    const uint32_t kb = uint32_t(KT) * BK * 2u;                                                       \
+    _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rA, (__attribute__((address_space(3))) void*)&FSM_SA(BUF)[(wave * A_RUNS + i) * 8 * BK], 16,  \
+        dA[i] + kb, 0, 0, 0);                                                                         \
+    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rBw, (__attribute__((address_space(3))) void*)&FSM_SB(BUF)[(wb_row0 + i * 8) * BK], 16,       \
+        dB[i] + kb, 0, 0, 0);                                                                         \
+  }
+  (void)ra; (void)rb;
+  FSM_DMA_STAGE(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage-0 runs are in LDS
+  __syncthreads();
+  // unrolled by two so that each half names its stage buffers as constants
+  for (int kt = 0;;) {
+    if (kt + 1 < KT) FSM_DMA_STAGE(kt + 1, 1);  // buffer 1 was last read before the previous barrier
+    __builtin_amdgcn_sched_barrier(0);
+    FSM_COMPUTE(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++kt >= KT) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (kt + 1 < KT) FSM_DMA_STAGE(kt + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    FSM_COMPUTE(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++kt >= KT) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+#undef FSM_DMA_STAGE
+#else
   FSM_GLOAD(0);
   FSM_SSTORE(0);
   __syncthreads();
@@ -290,11 +374,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     cur ^= 1;
   }
   FSM_COMPUTE(cur);
+#endif
 #undef FSM_GLOAD
 #undef FSM_SSTORE
 #undef FSM_BROW
 #undef FSM_LDA
 #undef FSM_LDB
+#undef FSM_SA
+#undef FSM_SB
 #undef FSM_STEP0
 #undef FSM_COMPUTE
 

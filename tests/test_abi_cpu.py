@@ -2,7 +2,9 @@
 argument check returns its documented error code before anything is enqueued (no GPU needed:
 these calls never reach a kernel launch)."""
 import ctypes
+import os
 import subprocess
+import sys
 
 import pytest
 
@@ -11,6 +13,7 @@ from mixture_experts_layer_sum_amd import _lib as L
 from tests.helpers import header_exports
 
 lib = pkg.lib
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BAD = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host-side checks
 
 
@@ -27,6 +30,17 @@ def test_library_exports_every_declared_symbol():
     for fn in header_exports():
         assert fn in exported, fn
         assert hasattr(lib, fn)
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library (whatever was imported first) leaves a single HIP runtime mapped: the
+    framework's.  Run in a fresh interpreter so that the import order is the library's own."""
+    code = ("import mixture_experts_layer_sum_amd as m; m.lib; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         cwd=ROOT).stdout.strip()
+    libs = eval(out)
+    assert len(libs) == 1, libs
 
 
 def test_version_and_empty_last_error():
