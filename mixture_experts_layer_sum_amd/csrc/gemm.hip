@@ -11,9 +11,10 @@
 //
 // Tile kernel: BM x BN output tile per workgroup, BK = 64, waves laid out WAVES_M x WAVES_N, each
 // wave owning a (BM/WAVES_M) x (BN/WAVES_N) block of v_mfma_f32_16x16x32_bf16 tiles.  Global
-// tiles are staged through registers into two LDS buffers (one barrier per K step); LDS rows are
-// 128 bytes and their eight 16-byte chunks are XOR-swizzled with the row index so that the MFMA
-// fragment reads (16 rows x one chunk per 16 lanes) are bank-conflict free.  The MFMA is issued
+// tiles go straight from HBM into a ring of LDS stages with direct-to-LDS buffer loads (no
+// register staging, one barrier per K step); LDS rows are 128 bytes and their eight 16-byte
+// chunks are XOR-swizzled with the row index so that the MFMA fragment reads (16 rows x one
+// chunk per 16 lanes) are bank-conflict free.  The MFMA is issued
 // with the weight fragment as its first operand, which leaves every lane holding four consecutive
 // output columns of one row: the epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
 //
@@ -42,6 +43,7 @@ struct GemmArgs {
   const int32_t* gather;      // ROWS_GATHER: grouped row r reads A row gather[r] / gather_k
   int32_t gather_k;
   int64_t a_rows;             // ROWS_GATHER: rows of A (its buffer-resource extent)
+  int32_t quad_nb;            // > 0: the 2 x 2 XCD-block order below, with quad_nb N-tiles per block
 };
 
 // How a workgroup finds its A rows: contiguous rows of a grouped input, a single group, or rows
@@ -98,17 +100,43 @@ __device__ __forceinline__ bool resolve_mtile(const GemmArgs& p, int mt, int BM,
   return true;
 }
 
-// Workgroup -> (M-tile, N-tile).  Only the first (real M-tiles x n_tiles) workgroups get work, so
-// the surplus of the worst-case grid exits at once.  Workgroups are dealt round-robin to the 8
-// XCDs; each XCD is given one contiguous range of the logical tile order, and inside that order
-// group_m M-tiles sweep the N-tiles together, so the tiles resident on one XCD at a time share
-// their weight panel and their activation rows in that XCD's L2.
+// Workgroup -> (M-tile, N-tile).  Workgroups are dealt round-robin to the 8 XCDs, so workgroup b
+// runs on XCD b % 8 as that XCD's (b / 8)-th workgroup.  Two orders are used; in both, the
+// workgroups without a tile (the worst-case grid's surplus) exit at once.
+//  - quad_nb > 0 (grouped and shared-expert products): each XCD works through blocks of
+//    group_m x quad_nb tiles, about one tile per CU, so the tiles resident on an XCD share
+//    activation rows and weight panels in its L2; see quad_grid for the block order.
+//  - quad_nb == 0 (router): each XCD is given one contiguous range of the logical tile order, in
+//    which group_m M-tiles sweep the N-tiles together.
 constexpr int kXcds = 8;
+
+// XCD blocks of group_m x quad_nb tiles (one block per XCD at a time), ordered in 2 x 2 quads:
+// the four XCDs that run one quad at the same time pair up on M-groups (same activation rows)
+// and on N-blocks (same weight panels), so each line they share is fetched from HBM once and
+// found in the memory-side cache by the other XCD.  Returns the number of workgroups to launch
+// for at most max_mt M-tiles.
+inline int64_t quad_grid(int64_t max_mt, int n_tiles, int group_m, int quad_nb) {
+  const int64_t n_mg = (max_mt + group_m - 1) / group_m, n_nb = (n_tiles + quad_nb - 1) / quad_nb;
+  const int64_t quads = ((n_mg + 1) / 2) * ((n_nb + 1) / 2);
+  const int64_t rounds = (4 * quads + kXcds - 1) / kXcds;
+  return rounds * kXcds * int64_t(group_m) * quad_nb;
+}
 
 __device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int& nt) {
   const int total_mt = p.tile_group ? p.tile_start[p.G] : (p.M + BM - 1) / BM;
-  const int total = total_mt * p.n_tiles;
   const int b = blockIdx.x;
+  if (p.quad_nb > 0) {
+    const int blk_tiles = p.group_m * p.quad_nb;
+    const int x = b % kXcds, i = b / kXcds;
+    const int blk = (i / blk_tiles) * kXcds + x, pos = i % blk_tiles;
+    const int n_nb = (p.n_tiles + p.quad_nb - 1) / p.quad_nb, nq = (n_nb + 1) / 2;
+    const int quad = blk >> 2;
+    const int mg = 2 * (quad / nq) + (blk & 1), nb = 2 * (quad % nq) + ((blk >> 1) & 1);
+    mt = mg * p.group_m + pos % p.group_m;
+    nt = nb * p.quad_nb + pos / p.group_m;
+    return mt < total_mt && nt < p.n_tiles && nt < (nb + 1) * p.quad_nb;
+  }
+  const int total = total_mt * p.n_tiles;
   if (b >= total) return false;
   const int q = total / kXcds, r = total % kXcds, x = b % kXcds, i = b / kXcds;
   const int L = x * q + min(x, r) + i;
@@ -124,52 +152,92 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int
 // bf16 MFMA tile kernel
 // ------------------------------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-#ifndef FSM_DMA
-#define FSM_DMA 1  // 1: stage tiles with direct-to-LDS buffer loads; 0: through registers
-#endif
-// The direct-to-LDS body uses device-only builtins; the host pass (which only needs the kernels'
-// launch stubs) parses the register-staging body.
-#if FSM_DMA && defined(__HIP_DEVICE_COMPILE__)
-#define FSM_DMA_ON 1
-#else
-#define FSM_DMA_ON 0
-#endif
 constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
 
-// 16-byte load through a buffer resource: offsets at or beyond the resource size read as zero.
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// K depth of one LDS stage and the number of stages in the ring.  A stage holds BM + BN rows of
+// BK bf16 values; two stages of BK = 64 or four of BK = 32 fill 128 KB of the 160 KB LDS.
+#ifndef FSM_BK
+#define FSM_BK 64
+#endif
+#ifndef FSM_STAGES
+#define FSM_STAGES 2
+#endif
+// L2 warm-up distance: with FSM_PF = P > 0 each thread also touches one 128-byte line of the
+// stage P steps beyond the one being loaded into LDS (a 4-byte direct-to-LDS load into a scratch
+// row), so that line is already on its way to L2 when its real load is issued.
+#ifndef FSM_PF
+#define FSM_PF 0
+#endif
+constexpr int kBK = FSM_BK, kStages = FSM_STAGES, kPf = FSM_PF;
+static_assert(kBK == 32 || kBK == 64, "BK must be 32 or 64");
+static_assert(kStages >= 2 && kStages <= 5, "2 to 5 LDS stages");
+static_assert(kPf >= 0 && (kPf == 0 || (kStages == 2 && kBK == 64)), "L2 warm-up needs 2 stages of 128-byte rows");
+
+// 16-byte direct-to-LDS buffer load (device pass only; the host pass needs just the launch stubs
+// and never sees the builtin).
+//
+// The LDS address goes through an empty asm statement, so the compiler cannot tie the load to the
+// stage array it fills.  Its own wait-count pass then leaves LDS reads of the other stages alone
+// (it otherwise waits for every stage in flight before reading any one); the kernel waits for the
+// stage it reads itself, with an explicit s_waitcnt and a barrier.
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)uintptr_t(a), 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)uintptr_t(a), 4, voff, 0, 0, 0);
+}
+#define FSM_LDS_DMA16(RSRC, LDS, VOFF) lds_dma16((RSRC), (LDS), (VOFF))
+#define FSM_LDS_DMA4(RSRC, LDS, VOFF) lds_dma4((RSRC), (LDS), (VOFF))
+#else
+#define FSM_LDS_DMA16(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
+#define FSM_LDS_DMA4(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
+#endif
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
 }
 
+// Physical 16-byte chunk of logical chunk c in LDS tile row r.  Rows are BK * 2 bytes; the XOR
+// makes the eight rows that one ds_read_b128 group of 8 lanes touches cover all 32 banks.
+__device__ __forceinline__ int lds_swz(int r) { return kBK == 64 ? (r & 7) : ((r >> 1) & 3); }
+
 // ROWS (ROWS_GROUPED / ROWS_SINGLE / ROWS_GATHER) also gives routed and shared launches their own
 // symbols, so profilers report them separately.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int BK = 64;
+  constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
+  constexpr int BK = kBK, S = kStages, PF = kPf;
+  constexpr int KSL = BK / 32;                 // MFMA K slices per stage
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
+  constexpr int RUN_ROWS = 64 / CPR;           // rows in one wave's 1 KB direct-to-LDS run
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
-  constexpr int ROWS_PER_PASS = NT / 8;  // tile rows covered by one 16-byte load per thread
-  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "tile/thread mismatch");
+  constexpr int A_RUNS = BM / RUN_ROWS / NW, B_RUNS = BN / RUN_ROWS / NW;  // runs per wave per stage
+  constexpr int LOADS = A_RUNS + B_RUNS;       // vector-memory operations per wave per stage
+  constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage (A rows, then B rows)
+  static_assert(A_RUNS * RUN_ROWS * NW == BM && B_RUNS * RUN_ROWS * NW == BN, "runs must tile the stage");
   static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
-  static_assert(EPI != EPI_SWIGLU || (BN / 2) % ROWS_PER_PASS == 0, "B halves must align with load passes");
+  static_assert(EPI != EPI_SWIGLU || (BN / 2) % (B_RUNS * RUN_ROWS) == 0, "a wave's B rows must lie in one half");
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
   static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
+  static_assert(LOADS * (S - 2) + PF + S < 64, "vmcnt range");
+  static_assert(PF == 0 || (NT == BM + BN && BM % 64 == 0 && (BN / 2) % 64 == 0),
+                "one warmed line per thread, whole waves per operand");
 
-#if FSM_DMA_ON
   // one named array per stage, so the compiler can tell the stage being filled from the one read
-  __shared__ __attribute__((aligned(16))) uint16_t sA0[BM * BK], sA1[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB0[BN * BK], sB1[BN * BK];
-#else
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
-#endif
+  __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE], s1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s2[S > 2 ? STAGE : 8], s3[S > 3 ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s4[S > 4 ? STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint32_t s_pf[PF ? NT : 4];  // never read
 
   // the wave index is uniform across the wave: readfirstlane lets the compiler keep it (and every
   // address derived from it) in scalar registers
@@ -202,76 +270,85 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
       ROWS == ROWS_GATHER ? make_rsrc(p.A, p.a_rows * K * 2) : make_rsrc(Ab, int64_t(rows) * K * 2);
   const __amdgpu_buffer_rsrc_t rU = make_rsrc(Bu, int64_t(nvalid) * K * 2);
   const __amdgpu_buffer_rsrc_t rG = make_rsrc(Bg, int64_t(nvalid) * K * 2);
-
-  // Loads: thread tid owns 16-byte chunk ch = tid % 8 of tile rows r_l + i * ROWS_PER_PASS.  The
-  // pass stride is a multiple of 8 rows, so the row swizzle (r & 7) is the same for all of a
-  // thread's chunks: one LDS base plus constant offsets, one buffer offset plus a uniform stride.
-  const int r_l = tid >> 3, ch = tid & 7;
   const uint32_t rowB = uint32_t(K) * 2u;  // bytes per row of A and B
-  const uint32_t offA0 = uint32_t(r_l) * rowB + uint32_t(ch) * 16u;
-  // gathered rows: one offset per row this thread loads; rows past the tile point beyond the
-  // resource (0x80000000 > its extent) and read as zeros
-  uint32_t offG[ROWS == ROWS_GATHER ? ACH : 1];
-  if (ROWS == ROWS_GATHER) {
+
+  // Direct-to-LDS staging: each wave fills whole 1 KB runs (RUN_ROWS tile rows) of a stage with
+  // buffer_load ... lds; lane l writes physical chunk l % CPR of row l / CPR of its run, so it
+  // loads logical chunk (l % CPR) ^ swz(row), which reproduces the swizzled layout the fragment
+  // reads use (runs start on multiples of 8 or 16 rows, so the swizzle of a run row is that of
+  // l / CPR).
+  const int d_row = lane / CPR, d_ch = (lane % CPR) ^ lds_swz(d_row);
+  uint32_t dA[A_RUNS], dB[B_RUNS];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int r = r_l + i * ROWS_PER_PASS;
-      offG[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(ch) * 16u : 0x80000000u;
+  for (int i = 0; i < A_RUNS; ++i) {
+    const int r = (wave * A_RUNS + i) * RUN_ROWS + d_row;
+    if (ROWS == ROWS_GATHER)  // rows past the tile point beyond the resource and read as zeros
+      dA[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(d_ch) * 16u : 0x80000000u;
+    else
+      dA[i] = uint32_t(r) * rowB + uint32_t(d_ch) * 16u;
+  }
+  const int wb_row0 = wave * B_RUNS * RUN_ROWS;  // first B tile row of this wave
+  const bool b_gate = EPI == EPI_SWIGLU && wb_row0 >= BN / 2;
+  const __amdgpu_buffer_rsrc_t rBw = b_gate ? rG : rU;
+#pragma unroll
+  for (int i = 0; i < B_RUNS; ++i) {
+    const int r = wb_row0 + i * RUN_ROWS + d_row;
+    dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
+  }
+
+  // L2 warm-up: thread tid touches the first 128 bytes (this stage's K slice) of A row tid or of
+  // B row tid - BM; waves are whole operands, so the buffer resource stays uniform.
+  uint32_t pfo = 0;
+  __amdgpu_buffer_rsrc_t rPf = rA;
+  if (PF) {
+    if (wave * 64 < BM) {
+      if (ROWS == ROWS_GATHER)
+        pfo = tid < rows ? uint32_t(p.gather[row0 + tid] / p.gather_k) * rowB : 0x80000000u;
+      else
+        pfo = uint32_t(tid) * rowB;
+    } else {
+      const int rb = tid - BM;
+      const bool gate = EPI == EPI_SWIGLU && wave * 64 - BM >= BN / 2;  // uniform: BN / 2 % 64 == 0
+      rPf = gate ? rG : rU;
+      pfo = uint32_t(gate ? rb - BN / 2 : rb) * rowB;
     }
   }
-  const int lds0 = r_l * BK + ((ch ^ (r_l & 7)) << 3);
+#define FSM_PF_STAGE(KT) FSM_LDS_DMA4(rPf, &s_pf[wave * 64], pfo + uint32_t(KT) * BK * 2u)
+
   // Fragment reads: rows (base + 16 i + lane % 16); base is a multiple of 16, so the swizzle
   // term depends on the lane only.
   const int fa0 = (wm * WTM + (lane & 15)) * BK;
-  const int fb0 = (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
-  const int sw = lane & 7;
+  const int fb0 = BM * BK + (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
+  const int sw = lds_swz(lane & 15);
 
-  uint4 ra[ACH], rb[BCH];
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#define FSM_GLOAD(KT)                                                                          \
-  {                                                                                            \
-    const uint32_t kb = uint32_t(KT) * BK * 2u;                                                \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
-      ra[i] = buf_load16(rA, (ROWS == ROWS_GATHER ? offG[i] : offA0 + uint32_t(i * ROWS_PER_PASS) * rowB) + kb); \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                          \
-      const int r = i * ROWS_PER_PASS;                                                         \
-      const bool gate = EPI == EPI_SWIGLU && r >= BN / 2;                                      \
-      const int rr = gate ? r - BN / 2 : r;                                                    \
-      rb[i] = buf_load16(gate ? rG : rU, offA0 + kb + uint32_t(rr) * rowB);                    \
-    }                                                                                          \
-  }
-#define FSM_SSTORE(BUF)                                                                        \
-  {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                            \
-      *reinterpret_cast<uint4*>(&FSM_SA(BUF)[lds0 + i * ROWS_PER_PASS * BK]) = ra[i];          \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                            \
-      *reinterpret_cast<uint4*>(&FSM_SB(BUF)[lds0 + i * ROWS_PER_PASS * BK]) = rb[i];          \
+#define FSM_SM(BUF) ((BUF) == 0 ? s0 : (BUF) == 1 ? s1 : (BUF) == 2 ? s2 : (BUF) == 3 ? s3 : s4)
+#define FSM_DMA_STAGE(KT, BUF)                                                                     \
+  {                                                                                                \
+    const uint32_t kb = uint32_t(KT) * BK * 2u;                                                    \
+    _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                             \
+      FSM_LDS_DMA16(rA, &FSM_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * BK], dA[i] + kb);             \
+    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                             \
+      FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);        \
   }
 #define FSM_BROW(J) \
   ((EPI == EPI_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
-#if FSM_DMA_ON
-#define FSM_SA(BUF) ((BUF) ? sA1 : sA0)
-#define FSM_SB(BUF) ((BUF) ? sB1 : sB0)
-#else
-#define FSM_SA(BUF) (sA[BUF])
-#define FSM_SB(BUF) (sB[BUF])
-#endif
 #define FSM_LDA(BUF, KS, I) \
-  (*reinterpret_cast<const bf16x8*>(&FSM_SA(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+  (*reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
 #define FSM_LDB(BUF, KS, J) \
-  (*reinterpret_cast<const bf16x8*>(&FSM_SB(BUF)[fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
-  // One K step (BK = 64 = two MFMA K slices) with the fragment reads software-pipelined: the A
-  // fragment for row block i+1 (and, in the first slice, the B fragments of the second slice) are
-  // read before the MFMAs of row block i, and scheduling groups pin that order, so an LDS read is
-  // always in flight under FN MFMAs instead of being waited for right before its first use.
+  (*reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+  // One stage's MFMAs with the fragment reads software-pipelined: the A fragment for row block
+  // i+1 (and, when the stage has a second K slice, that slice's B fragments) are read before the
+  // MFMAs of row block i, and scheduling groups pin that order, so an LDS read is always in flight
+  // under FN MFMAs instead of being waited for right before its first use.
 #define FSM_STEP0(BUF, I, WITH_B)                                                              \
   {                                                                                            \
-    a_nxt = ((I) + 1 < FM) ? FSM_LDA(BUF, 0, (I) + 1) : FSM_LDA(BUF, 1, 0);                     \
+    a_nxt = ((I) + 1 < FM) ? FSM_LDA(BUF, 0, (I) + 1) : FSM_LDA(BUF, KSL - 1, 0);               \
     if (WITH_B) b1[I] = FSM_LDB(BUF, 1, I);                                                    \
     _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
       acc[I][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[I][j], 0, 0, 0);   \
@@ -285,103 +362,92 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     _Pragma("unroll") for (int j = 0; j < FN; ++j) b0[j] = FSM_LDB(BUF, 0, j);                 \
     a_cur = FSM_LDA(BUF, 0, 0);                                                                \
     __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                    \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i) FSM_STEP0(BUF, i, true);                    \
-    _Pragma("unroll") for (int i = FN; i < FM; ++i) FSM_STEP0(BUF, i, false);                  \
-    _Pragma("unroll") for (int i = 0; i < FM - 1; ++i) {                                       \
-      a_nxt = FSM_LDA(BUF, 1, i + 1);                                                          \
+    if (KSL == 2) {                                                                            \
+      _Pragma("unroll") for (int i = 0; i < FN; ++i) FSM_STEP0(BUF, i, true);                  \
+      _Pragma("unroll") for (int i = FN; i < FM; ++i) FSM_STEP0(BUF, i, false);                \
+      _Pragma("unroll") for (int i = 0; i < FM - 1; ++i) {                                     \
+        a_nxt = FSM_LDA(BUF, 1, i + 1);                                                        \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                         \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                    \
+        a_cur = a_nxt;                                                                         \
+      }                                                                                        \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[i][j], 0, 0, 0); \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+        acc[FM - 1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[FM - 1][j], 0, 0, 0); \
       __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                      \
-      a_cur = a_nxt;                                                                           \
+    } else {                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < FM - 1; ++i) FSM_STEP0(BUF, i, false);             \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
+        acc[FM - 1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[FM - 1][j], 0, 0, 0); \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                      \
+      (void)b1;                                                                                \
     }                                                                                          \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
-      acc[FM - 1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[FM - 1][j], 0, 0, 0); \
-    __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
+  }
+  // Workgroup barrier without a memory fence: __syncthreads() would also wait for every
+  // outstanding direct-to-LDS load (vmcnt(0)), including the stages still meant to be in flight.
+  // The explicit s_waitcnt before it covers this wave's loads of the next stage; every LDS read
+  // of the current stage has been consumed by an MFMA before the barrier, so the buffer refilled
+  // after it is free.  The empty asm statements keep the compiler from moving memory accesses
+  // across the barrier.
+#define FSM_BARRIER()                   \
+  {                                     \
+    asm volatile("" ::: "memory");      \
+    __builtin_amdgcn_s_barrier();       \
+    asm volatile("" ::: "memory");      \
+  }
+  // One ring step on stage buffer J: refill the buffer read one step earlier with stage kt+S-1
+  // (and warm the lines of stage kt+S-1+PF), run this stage's MFMAs, then wait until the next
+  // stage is in LDS for every wave.  Each step issues the stage load before its warm-up load, so
+  // S-1 warm-up loads are younger than the next stage's; when some later load was not issued
+  // (the tail), the wait falls back to vmcnt(0).
+#define FSM_RING_STEP(J)                                                                       \
+  {                                                                                            \
+    if (kt + S - 1 < KT) FSM_DMA_STAGE(kt + S - 1, ((J) + S - 1) % S);                         \
+    if (PF && kt + S - 1 + PF < KT) FSM_PF_STAGE(kt + S - 1 + PF);                             \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    FSM_COMPUTE(J);                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    if (++kt >= KT) break;                                                                     \
+    if (kt + S - 2 + PF < KT)                                                                  \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2) + (PF ? S - 1 : 0)));              \
+    else                                                                                       \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                               \
+    FSM_BARRIER();                                                                             \
   }
 
   const int KT = p.K / BK;
-#if FSM_DMA_ON
-  // Direct-to-LDS staging: each wave fills whole 1 KB runs (8 tile rows) of a stage with
-  // buffer_load ... lds; lane l writes physical chunk l % 8 of row l / 8 of its run, so it loads
-  // logical chunk (l % 8) ^ (l / 8), which reproduces the swizzled layout the fragment reads use.
-  constexpr int NW = NT / 64;
-  constexpr int A_RUNS = BM / 8 / NW, B_RUNS = BN / 8 / NW;  // 1 KB runs per wave per stage
-  static_assert(A_RUNS * 8 * NW == BM && B_RUNS * 8 * NW == BN, "runs must tile the stage");
-  static_assert(EPI != EPI_SWIGLU || (BN / 2) % (B_RUNS * 8) == 0, "a wave's B rows must lie in one half");
-  const int d_row = lane >> 3, d_ch = (lane & 7) ^ (lane >> 3);
-  uint32_t dA[A_RUNS], dB[B_RUNS];
+  // prologue: stages 0 .. S-2 in flight, then wait for stage 0.  Each branch is straight-line
+  // code, so the compiler's own wait-count tracking sees exactly which stages are still pending.
+  if (KT >= S - 1 + PF) {
 #pragma unroll
-  for (int i = 0; i < A_RUNS; ++i) {
-    const int r = (wave * A_RUNS + i) * 8 + d_row;
-    if (ROWS == ROWS_GATHER)
-      dA[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(d_ch) * 16u : 0x80000000u;
-    else
-      dA[i] = uint32_t(r) * rowB + uint32_t(d_ch) * 16u;
-  }
-  const int wb_row0 = wave * B_RUNS * 8;  // first B tile row of this wave
-  const bool b_gate = EPI == EPI_SWIGLU && wb_row0 >= BN / 2;
-  const __amdgpu_buffer_rsrc_t rBw = b_gate ? rG : rU;
+    for (int st = 0; st < S - 1; ++st) FSM_DMA_STAGE(st, st);
 #pragma unroll
-  for (int i = 0; i < B_RUNS; ++i) {
-    const int r = wb_row0 + i * 8 + d_row;
-    dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
+    for (int st = 0; st < PF; ++st) FSM_PF_STAGE(S - 1 + st);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2) + PF));
+  } else {
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (st < KT) FSM_DMA_STAGE(st, st);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
-#define FSM_DMA_STAGE(KT, BUF)                                                                        \
-  {                                                                                                   \
-    const uint32_t kb = uint32_t(KT) * BK * 2u;                                                       \
-    _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-        rA, (__attribute__((address_space(3))) void*)&FSM_SA(BUF)[(wave * A_RUNS + i) * 8 * BK], 16,  \
-        dA[i] + kb, 0, 0, 0);                                                                         \
-    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-        rBw, (__attribute__((address_space(3))) void*)&FSM_SB(BUF)[(wb_row0 + i * 8) * BK], 16,       \
-        dB[i] + kb, 0, 0, 0);                                                                         \
-  }
-  (void)ra; (void)rb;
-  FSM_DMA_STAGE(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage-0 runs are in LDS
-  __syncthreads();
-  // unrolled by two so that each half names its stage buffers as constants
+  FSM_BARRIER();
+  // unrolled S times so that every step names its stage buffers as constants
   for (int kt = 0;;) {
-    if (kt + 1 < KT) FSM_DMA_STAGE(kt + 1, 1);  // buffer 1 was last read before the previous barrier
-    __builtin_amdgcn_sched_barrier(0);
-    FSM_COMPUTE(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (++kt >= KT) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (kt + 1 < KT) FSM_DMA_STAGE(kt + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    FSM_COMPUTE(1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (++kt >= KT) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    FSM_RING_STEP(0);
+    FSM_RING_STEP(1);
+    if (S > 2) FSM_RING_STEP(2 % S);
+    if (S > 3) FSM_RING_STEP(3 % S);
+    if (S > 4) FSM_RING_STEP(4 % S);
   }
+#undef FSM_RING_STEP
+#undef FSM_PF_STAGE
+#undef FSM_BARRIER
 #undef FSM_DMA_STAGE
-#else
-  FSM_GLOAD(0);
-  FSM_SSTORE(0);
-  __syncthreads();
-  int cur = 0;
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    FSM_GLOAD(kt + 1);                    // next stage in flight during this stage's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    FSM_COMPUTE(cur);
-    __builtin_amdgcn_sched_barrier(0);
-    FSM_SSTORE(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-  }
-  FSM_COMPUTE(cur);
-#endif
-#undef FSM_GLOAD
-#undef FSM_SSTORE
 #undef FSM_BROW
 #undef FSM_LDA
 #undef FSM_LDB
-#undef FSM_SA
-#undef FSM_SB
+#undef FSM_SM
 #undef FSM_STEP0
 #undef FSM_COMPUTE
 
@@ -499,6 +565,15 @@ namespace {
 #ifndef FSM_R
 #define FSM_R 256, 256, 2, 4, 1
 #endif
+// N-tiles per XCD block of the quad order: one XCD runs 32 tiles at a time (one per CU), so a
+// block is group_m x (32 / group_m) tiles, narrowed to a divisor of n_tiles where one is close
+// (7 for the 28 N-tiles of a 7168-wide down product) so that no block is ragged.
+int quad_width(int n_tiles, int group_m) {
+  const int target = 32 / group_m;
+  for (int q = target; q * 2 > target; --q)
+    if (n_tiles % q == 0) return q;
+  return target;
+}
 struct TileCfg { int bm, bn, wm, wn, gm; };
 constexpr TileCfg kP1{FSM_P1}, kP2{FSM_P2}, kR{FSM_R};
 constexpr int P1_BM = kP1.bm, P1_BN = kP1.bn, P1_WM = kP1.wm, P1_WN = kP1.wn;
@@ -580,7 +655,8 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   const int rows2 = G > 1 ? ROWS_GROUPED : ROWS_SINGLE;
   if (bf) {
     a1.n_tiles = int32_t(cdiv(c, P1_BN / 2));
-    const dim3 grid1(unsigned(mt1 * a1.n_tiles));
+    a1.quad_nb = quad_width(a1.n_tiles, a1.group_m);
+    const dim3 grid1(unsigned(quad_grid(mt1, a1.n_tiles, a1.group_m, a1.quad_nb)));
     constexpr int nt1 = 64 * P1_WM * P1_WN;
     {
       ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
@@ -593,7 +669,8 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
       if (int rc = check_launch("grouped gemm phase 1")) return rc;
     }
     a2.n_tiles = int32_t(cdiv(d, P2_BN));
-    const dim3 grid2(unsigned(mt2 * a2.n_tiles));
+    a2.quad_nb = quad_width(a2.n_tiles, a2.group_m);
+    const dim3 grid2(unsigned(quad_grid(mt2, a2.n_tiles, a2.group_m, a2.quad_nb)));
     constexpr int nt2 = 64 * P2_WM * P2_WN;
     ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
     if (rows2 == ROWS_GROUPED)
