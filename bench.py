@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--mode", default="partial", choices=["none", "partial", "outdated"])
     p.add_argument("--single-stream-steps", type=int, default=3,
                    help="extra steps with both streams merged into one (overlap reference); 0 = skip")
-    p.add_argument("--cpu-sample", type=int, default=4, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--standalone", type=int, default=1,
+                   help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                    help="before the steps, one plain device copy of this many GiB (a known-size kernel whose "
                         "FETCH_SIZE / WRITE_SIZE calibrate the HBM counters); 0 = skip")
@@ -100,6 +102,73 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
                 row["gbs"] = round(work / (avg * 1e-3) / 1e9, 1)
                 row["frac_hbm_peak"] = round(row["gbs"] / PEAK_HBM_GBS, 4)
         out[kind] = row
+    return out
+
+
+def standalone(c, layers, o0, reps: int = 3) -> dict:
+    """After the timed steps: the layer-0 calls one at a time on the whole GPU (the stack shares it
+    between two streams), including the explicit dispatch row copy that the stack folds into the
+    gate/up GEMM, and two measured ceilings of the box (a device copy and a large hipBLASLt
+    product through torch)."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    T, d, E, k, cc = c.T, c.d, c.E, c.k, c.c
+    N = T * k
+    W = layers[0]
+    x = o0.to(c.torch_dtype)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    src = torch.empty((N,), dtype=torch.int32, device=dev)
+    dest = torch.empty((N,), dtype=torch.int32, device=dev)
+    A_perm = torch.empty((N, d), dtype=c.torch_dtype, device=dev)
+    Y = torch.empty((N, d), dtype=c.torch_dtype, device=dev)
+    pws = ops.workspace(ops.permute_workspace_bytes(T, E, k), dev)
+    gws = ops.workspace(ops.grouped_swiglu_workspace_bytes(N, E, cc, c.torch_dtype), dev)
+    ops.moe_route(x, W["W_R"], k, c.gate, c.renormalize, logits, idx, w, bias=W.get("bias"))
+    ops.moe_permute(idx, E, off, src, dest, A=x, A_perm=A_perm, ws=pws)
+    ops.moe_grouped_swiglu_gathered(x, src, k, off, W["W1"], W["W2"], W["W3"], Y, ws=gws)
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    for _ in range(reps):
+        ops.moe_permute(idx, E, off, src, dest, A=x, A_perm=A_perm, ws=pws)
+        ops.moe_grouped_swiglu_gathered(x, src, k, off, W["W1"], W["W2"], W["W3"], Y, ws=gws)
+        o = o0.clone()
+        ops.moe_combine(Y, w, dest, o, addend=x, residual=o)   # in place on o, as in the stack
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    prof = ops.profile_collect()
+    rep_ = kernel_report(prof, c, reps)
+    out = {k_: rep_[k_] for k_ in ("permute_rows", "gemm_gate_up", "gemm_down", "combine") if k_ in rep_}
+    del A_perm, Y, gws, pws, logits
+    # ceilings: plain device-to-device copy and a large bf16 product (hipBLASLt through torch)
+    a = torch.empty(2**30 // 4 * 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    m = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    n = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+
+    def timed(fn, it):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(it):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / it
+
+    ms_copy = timed(lambda: b.copy_(a), 5)
+    ms_mm = timed(lambda: torch.matmul(m, n), 5)
+    out["ceilings"] = {
+        "device_copy_GBps": round(2 * a.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
+        "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
+    }
+    del a, b, m, n
     return out
 
 
@@ -259,6 +328,9 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if args.standalone:
+        log("timing the single calls alone and the ceilings")
+        result["standalone"] = standalone(c, layers, o0)
     if args.cpu_sample > 0:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(c, layers, o0, args.cpu_sample)

@@ -82,15 +82,81 @@ __global__ __launch_bounds__(CB_THR) void k_combine(const void* __restrict__ Y, 
   if (out_x) store8(out_x, dtype, o, acc);
 }
 
+// bf16 combine with k fixed at compile time: every Y row of the token is requested before the
+// first is used (KK + 3 independent 16-byte loads in flight per thread), then the slots are
+// summed in order, as in k_combine.  Y, residual and out are touched once, so they are loaded and
+// stored with the nontemporal hint.
+typedef unsigned int cb_u32x4 __attribute__((ext_vector_type(4)));
+typedef float cb_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int KK>
+__global__ __launch_bounds__(CB_THR) void k_combine_bf16(const uint16_t* __restrict__ Y,
+                                                         const float* __restrict__ w,
+                                                         const int32_t* __restrict__ dest_row, int64_t d,
+                                                         int col_blocks, const uint16_t* __restrict__ addend,
+                                                         const float* residual, float* out,
+                                                         uint16_t* __restrict__ out_x) {
+  const int64_t t = blockIdx.x / col_blocks;
+  const int64_t col = int64_t(blockIdx.x % col_blocks) * CB_COLS + threadIdx.x * 8;
+  if (col >= d) return;
+  const int64_t o = t * d + col;
+  cb_u32x4 yv[KK];
+  float wi[KK];
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    const int64_t r = dest_row[t * KK + i];
+    wi[i] = w[t * KK + i];
+    yv[i] = __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(Y + r * d + col));
+  }
+  cb_f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rb = {0.f, 0.f, 0.f, 0.f};
+  if (residual) {
+    ra = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(residual + o));
+    rb = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(residual + o + 4));
+  }
+  cb_u32x4 av = {0u, 0u, 0u, 0u};
+  if (addend) av = __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(addend + o));
+  float acc[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+  if (addend) {
+    float s[8];
+    unpack8(make_uint4(av[0], av[1], av[2], av[3]), s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += s[q];
+  }
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    float y[8];
+    unpack8(make_uint4(yv[i][0], yv[i][1], yv[i][2], yv[i][3]), y);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wi[i], y[q], acc[q]);
+  }
+  __builtin_nontemporal_store(cb_f32x4{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<cb_f32x4*>(out + o));
+  __builtin_nontemporal_store(cb_f32x4{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<cb_f32x4*>(out + o + 4));
+  if (out_x) {
+    uint4 v;
+    v.x = pack2(acc[0], acc[1]);
+    v.y = pack2(acc[2], acc[3]);
+    v.z = pack2(acc[4], acc[5]);
+    v.w = pack2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(out_x + o) = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_make_input(const float* __restrict__ o, const void* __restrict__ S,
                                                     int dtype, int64_t n8, void* __restrict__ x) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n8) return;
   const int64_t off = i * 8;
-  const float4 a = *reinterpret_cast<const float4*>(o + off);
-  const float4 b = *reinterpret_cast<const float4*>(o + off + 4);
-  float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  if (S) {
+  // o and S are not read again by this layer's kernels: nontemporal loads
+  const cb_f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(o + off));
+  const cb_f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(o + off + 4));
+  float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  if (S && dtype == MOE_BF16) {
+    const cb_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(static_cast<const uint16_t*>(S) + off));
+    float s[8];
+    unpack8(make_uint4(v[0], v[1], v[2], v[3]), s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f[q] += s[q];
+  } else if (S) {
     float s[8];
     load8(S, dtype, off, s);
 #pragma unroll
@@ -105,6 +171,19 @@ int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest
   if (T == 0) return MOE_OK;
   const int col_blocks = int(cdiv(d, CB_COLS));
   ProfScope prof(MOE_K_COMBINE, s);
+  if (dtype == MOE_BF16 && (k == 8 || k == 6 || k == 1)) {
+    const auto* Yb = static_cast<const uint16_t*>(Y);
+    const auto* Ab = static_cast<const uint16_t*>(addend);
+    auto* Xb = static_cast<uint16_t*>(out_x);
+    const unsigned grid = unsigned(T * col_blocks);
+    if (k == 8)
+      k_combine_bf16<8><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+    else if (k == 6)
+      k_combine_bf16<6><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+    else
+      k_combine_bf16<1><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+    return check_launch("combine");
+  }
   k_combine<<<unsigned(T * col_blocks), CB_THR, 0, s>>>(Y, dtype, w, dest_row, d, k, col_blocks, addend,
                                                          residual, out, out_x);
   return check_launch("combine");

@@ -109,19 +109,28 @@ __global__ __launch_bounds__(PTHR) void k_perm_rank(const int32_t* __restrict__ 
 }
 
 // A_perm[dest_row[t*k+i]] = A[t]; row_vec = row length in 16-byte vectors.
-__global__ __launch_bounds__(256) void k_perm_rows(const uint4* __restrict__ A, int64_t T, int64_t row_vec,
+typedef unsigned int pr_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int PR_UNROLL = 4;  // 16-byte vectors per lane in flight before the k stores
+
+__global__ __launch_bounds__(256) void k_perm_rows(const pr_u32x4* __restrict__ A, int64_t T, int64_t row_vec,
                                                    int k, const int32_t* __restrict__ dest_row,
-                                                   uint4* __restrict__ A_perm) {
+                                                   pr_u32x4* __restrict__ A_perm) {
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int myrow = lane < k ? dest_row[t * k + lane] : 0;
-  const uint4* src = A + t * row_vec;
-  for (int64_t c = lane; c < row_vec; c += 64) {
-    const uint4 v = src[c];
+  const pr_u32x4* src = A + t * row_vec;
+  // A is read once and A_perm written once here: both go with the nontemporal hint
+  for (int64_t c0 = lane; c0 < row_vec; c0 += 64 * PR_UNROLL) {
+    pr_u32x4 v[PR_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PR_UNROLL; ++u)
+      if (c0 + 64 * u < row_vec) v[u] = __builtin_nontemporal_load(src + c0 + 64 * u);
     for (int i = 0; i < k; ++i) {
-      const int r = __builtin_amdgcn_readlane(myrow, i);
-      A_perm[int64_t(r) * row_vec + c] = v;
+      pr_u32x4* dst = A_perm + int64_t(__builtin_amdgcn_readlane(myrow, i)) * row_vec + c0;
+#pragma unroll
+      for (int u = 0; u < PR_UNROLL; ++u)
+        if (c0 + 64 * u < row_vec) __builtin_nontemporal_store(v[u], dst + 64 * u);
     }
   }
 }
@@ -156,8 +165,8 @@ int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, in
   if (A_perm) {
     ProfScope prof(MOE_K_PERMUTE_ROWS, s);
     const int64_t row_bytes = d * (dtype == MOE_BF16 ? 2 : 4);
-    k_perm_rows<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(static_cast<const uint4*>(A), T, row_bytes / 16, k,
-                                                    dest_row, static_cast<uint4*>(A_perm));
+    k_perm_rows<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(static_cast<const pr_u32x4*>(A), T, row_bytes / 16, k,
+                                                    dest_row, static_cast<pr_u32x4*>(A_perm));
     if (int rc = check_launch("permute rows")) return rc;
   }
   return MOE_OK;
