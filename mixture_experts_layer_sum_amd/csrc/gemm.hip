@@ -162,16 +162,9 @@ constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor wor
 #ifndef FSM_STAGES
 #define FSM_STAGES 2
 #endif
-// L2 warm-up distance: with FSM_PF = P > 0 each thread also touches one 128-byte line of the
-// stage P steps beyond the one being loaded into LDS (a 4-byte direct-to-LDS load into a scratch
-// row), so that line is already on its way to L2 when its real load is issued.
-#ifndef FSM_PF
-#define FSM_PF 0
-#endif
-constexpr int kBK = FSM_BK, kStages = FSM_STAGES, kPf = FSM_PF;
+constexpr int kBK = FSM_BK, kStages = FSM_STAGES;
 static_assert(kBK == 32 || kBK == 64, "BK must be 32 or 64");
 static_assert(kStages >= 2 && kStages <= 5, "2 to 5 LDS stages");
-static_assert(kPf >= 0 && (kPf == 0 || (kStages == 2 && kBK == 64)), "L2 warm-up needs 2 stages of 128-byte rows");
 
 // 16-byte direct-to-LDS buffer load (device pass only; the host pass needs just the launch stubs
 // and never sees the builtin).
@@ -186,16 +179,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const voi
   asm volatile("" : "+s"(a));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)uintptr_t(a), 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
-  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
-  asm volatile("" : "+s"(a));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)uintptr_t(a), 4, voff, 0, 0, 0);
-}
 #define FSM_LDS_DMA16(RSRC, LDS, VOFF) lds_dma16((RSRC), (LDS), (VOFF))
-#define FSM_LDS_DMA4(RSRC, LDS, VOFF) lds_dma4((RSRC), (LDS), (VOFF))
 #else
 #define FSM_LDS_DMA16(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
-#define FSM_LDS_DMA4(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
 #endif
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
@@ -215,7 +201,7 @@ __device__ __forceinline__ int lds_swz(int r) { return kBK == 64 ? (r & 7) : ((r
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
-  constexpr int BK = kBK, S = kStages, PF = kPf;
+  constexpr int BK = kBK, S = kStages;
   constexpr int KSL = BK / 32;                 // MFMA K slices per stage
   constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
   constexpr int RUN_ROWS = 64 / CPR;           // rows in one wave's 1 KB direct-to-LDS run
@@ -229,15 +215,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   static_assert(EPI != EPI_SWIGLU || (BN / 2) % (B_RUNS * RUN_ROWS) == 0, "a wave's B rows must lie in one half");
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
   static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
-  static_assert(LOADS * (S - 2) + PF + S < 64, "vmcnt range");
-  static_assert(PF == 0 || (NT == BM + BN && BM % 64 == 0 && (BN / 2) % 64 == 0),
-                "one warmed line per thread, whole waves per operand");
+  static_assert(LOADS * (S - 2) < 64, "vmcnt range");
 
   // one named array per stage, so the compiler can tell the stage being filled from the one read
   __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE], s1[STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t s2[S > 2 ? STAGE : 8], s3[S > 3 ? STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t s4[S > 4 ? STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint32_t s_pf[PF ? NT : 4];  // never read
 
   // the wave index is uniform across the wave: readfirstlane lets the compiler keep it (and every
   // address derived from it) in scalar registers
@@ -279,13 +262,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   // l / CPR).
   const int d_row = lane / CPR, d_ch = (lane % CPR) ^ lds_swz(d_row);
   uint32_t dA[A_RUNS], dB[B_RUNS];
+  if (ROWS == ROWS_GATHER) {
+    // all gather indices are requested before the first is used; rows past the tile read a valid
+    // index and are then pointed beyond the resource, so they load zeros
+    int src[A_RUNS];
 #pragma unroll
-  for (int i = 0; i < A_RUNS; ++i) {
-    const int r = (wave * A_RUNS + i) * RUN_ROWS + d_row;
-    if (ROWS == ROWS_GATHER)  // rows past the tile point beyond the resource and read as zeros
-      dA[i] = r < rows ? uint32_t(p.gather[row0 + r] / p.gather_k) * rowB + uint32_t(d_ch) * 16u : 0x80000000u;
-    else
-      dA[i] = uint32_t(r) * rowB + uint32_t(d_ch) * 16u;
+    for (int i = 0; i < A_RUNS; ++i) src[i] = p.gather[row0 + min((wave * A_RUNS + i) * RUN_ROWS + d_row, rows - 1)];
+#pragma unroll
+    for (int i = 0; i < A_RUNS; ++i) {
+      const int r = (wave * A_RUNS + i) * RUN_ROWS + d_row;
+      dA[i] = r < rows ? uint32_t(src[i] / p.gather_k) * rowB + uint32_t(d_ch) * 16u : 0x80000000u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < A_RUNS; ++i) dA[i] = uint32_t((wave * A_RUNS + i) * RUN_ROWS + d_row) * rowB + uint32_t(d_ch) * 16u;
   }
   const int wb_row0 = wave * B_RUNS * RUN_ROWS;  // first B tile row of this wave
   const bool b_gate = EPI == EPI_SWIGLU && wb_row0 >= BN / 2;
@@ -296,24 +286,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
   }
 
-  // L2 warm-up: thread tid touches the first 128 bytes (this stage's K slice) of A row tid or of
-  // B row tid - BM; waves are whole operands, so the buffer resource stays uniform.
-  uint32_t pfo = 0;
-  __amdgpu_buffer_rsrc_t rPf = rA;
-  if (PF) {
-    if (wave * 64 < BM) {
-      if (ROWS == ROWS_GATHER)
-        pfo = tid < rows ? uint32_t(p.gather[row0 + tid] / p.gather_k) * rowB : 0x80000000u;
-      else
-        pfo = uint32_t(tid) * rowB;
-    } else {
-      const int rb = tid - BM;
-      const bool gate = EPI == EPI_SWIGLU && wave * 64 - BM >= BN / 2;  // uniform: BN / 2 % 64 == 0
-      rPf = gate ? rG : rU;
-      pfo = uint32_t(gate ? rb - BN / 2 : rb) * rowB;
-    }
-  }
-#define FSM_PF_STAGE(KT) FSM_LDS_DMA4(rPf, &s_pf[wave * 64], pfo + uint32_t(KT) * BK * 2u)
 
   // Fragment reads: rows (base + 16 i + lane % 16); base is a multiple of 16, so the swizzle
   // term depends on the lane only.
@@ -396,35 +368,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     __builtin_amdgcn_s_barrier();       \
     asm volatile("" ::: "memory");      \
   }
-  // One ring step on stage buffer J: refill the buffer read one step earlier with stage kt+S-1
-  // (and warm the lines of stage kt+S-1+PF), run this stage's MFMAs, then wait until the next
-  // stage is in LDS for every wave.  Each step issues the stage load before its warm-up load, so
-  // S-1 warm-up loads are younger than the next stage's; when some later load was not issued
-  // (the tail), the wait falls back to vmcnt(0).
+  // One ring step on stage buffer J: refill the buffer read one step earlier with stage kt+S-1,
+  // run this stage's MFMAs, then wait until the next stage is in LDS for every wave.  When fewer
+  // than S-2 later stages were issued (the tail), the wait falls back to vmcnt(0).
 #define FSM_RING_STEP(J)                                                                       \
   {                                                                                            \
     if (kt + S - 1 < KT) FSM_DMA_STAGE(kt + S - 1, ((J) + S - 1) % S);                         \
-    if (PF && kt + S - 1 + PF < KT) FSM_PF_STAGE(kt + S - 1 + PF);                             \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     FSM_COMPUTE(J);                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     if (++kt >= KT) break;                                                                     \
-    if (kt + S - 2 + PF < KT)                                                                  \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2) + (PF ? S - 1 : 0)));              \
-    else                                                                                       \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                               \
+    if (kt + S - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2)));              \
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                            \
     FSM_BARRIER();                                                                             \
   }
 
   const int KT = p.K / BK;
   // prologue: stages 0 .. S-2 in flight, then wait for stage 0.  Each branch is straight-line
   // code, so the compiler's own wait-count tracking sees exactly which stages are still pending.
-  if (KT >= S - 1 + PF) {
+  if (KT >= S - 1) {
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) FSM_DMA_STAGE(st, st);
-#pragma unroll
-    for (int st = 0; st < PF; ++st) FSM_PF_STAGE(S - 1 + st);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2) + PF));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2)));
   } else {
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
@@ -441,7 +406,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     if (S > 4) FSM_RING_STEP(4 % S);
   }
 #undef FSM_RING_STEP
-#undef FSM_PF_STAGE
 #undef FSM_BARRIER
 #undef FSM_DMA_STAGE
 #undef FSM_BROW
