@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--single-stream-steps", type=int, default=3,
                    help="extra steps with both streams merged into one (overlap reference); 0 = skip")
     p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--decode", type=int, default=1,
+                   help="after the steps, time a 1024-token decode step through the same layers; 0 = skip")
     p.add_argument("--standalone", type=int, default=1,
                    help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -57,7 +59,7 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_gate_up_dsv3_stack_hbm_tr
 def measured_traffic():
     """Calibrated HBM bytes per launch of the routed gate/up GEMM from the committed rocprofv3
     counter summary, or None when that summary was taken with other library sources."""
-    from mixture_experts_layer_sum_amd.profiling import source_digest
+    from mixture_experts_layer_sum_amd.profiling import is_routed_gate_up, source_digest
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     lines = open(TRAFFIC_PROFILE).read().splitlines()
@@ -66,7 +68,7 @@ def measured_traffic():
         return None
     for l in lines:
         f = l.split("|")
-        if l.startswith("traffic|") and "k_gemm_bf16<" in f[1] and (", 1, 2>" in f[1] or ", 1, 0>" in f[1]):
+        if l.startswith("traffic|") and is_routed_gate_up(f[1]):
             return {"fetch_GB": float(f[3]), "write_GB": float(f[4]), "total_GB": float(f[5])}
     return None
 
@@ -169,6 +171,50 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
     }
     del a, b, m, n
+    return out
+
+
+def decode(layers, steps: int = 10) -> dict:
+    """One decode step of a 1024-sequence batch through the same 4 layers and weights (the
+    dsv3-decode workload): the FarSkip stack with T = 1024.  About 32 rows per expert, so a layer
+    streams all of its weights for few tokens and the step is bound by HBM.  The roofline reports
+    the weight stream: every routed, shared and router weight byte read once per layer."""
+    import torch
+
+    import moe_inputs as mi
+    from mixture_experts_layer_sum_amd import ops
+    c = mi.BY_NAME["dsv3-decode"]
+    dev = layers[0]["W1"].device
+    o0 = mi.activations(c, dev).float()
+    oL = torch.empty_like(o0)
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_workspace_bytes(cfg), dev)
+    main_s, side_s = torch.cuda.current_stream(), torch.cuda.Stream()
+    out = {"workload": c.name, "tokens": c.T, "layers": c.layers}
+    for label, ss in (("two_streams", side_s), ("one_stream", main_s)):
+        for _ in range(2):
+            ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=ss)
+        torch.cuda.synchronize()
+        if label == "two_streams":
+            ops.profile_collect()
+            ops.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=ss)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        if label == "two_streams":
+            ops.profile_enable(False)
+            out["kernels"] = kernel_report(ops.profile_collect(), c, steps)
+        out[label] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1)}
+    assert torch.isfinite(oL).all().item(), "non-finite decode output"
+    esz = 2
+    weight_bytes = c.layers * esz * (3 * c.E * c.c * c.d + 3 * c.shared_width * c.d + c.E * c.d)
+    ms = out["two_streams"]["ms_per_step"]
+    gbs = weight_bytes / (ms * 1e-3) / 1e9
+    out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": weight_bytes,
+                       "what": "expert, shared and router weights read once per layer / step time"}
     return out
 
 
@@ -328,6 +374,9 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if args.decode and c.name == "dsv3-stack":
+        log("timing the decode-shaped stack")
+        result["decode"] = decode(layers)
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = standalone(c, layers, o0)

@@ -194,14 +194,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // Physical 16-byte chunk of logical chunk c in LDS tile row r.  Rows are BK * 2 bytes; the XOR
 // makes the eight rows that one ds_read_b128 group of 8 lanes touches cover all 32 banks.
-__device__ __forceinline__ int lds_swz(int r) { return kBK == 64 ? (r & 7) : ((r >> 1) & 3); }
+template <int BK>
+__device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 
 // ROWS (ROWS_GROUPED / ROWS_SINGLE / ROWS_GATHER) also gives routed and shared launches their own
 // symbols, so profilers report them separately.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS, int BK_ = kBK, int S_ = kStages>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
-  constexpr int BK = kBK, S = kStages;
+  constexpr int BK = BK_, S = S_;
+  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+  static_assert(S >= 2 && S <= 5, "2 to 5 LDS stages");
   constexpr int KSL = BK / 32;                 // MFMA K slices per stage
   constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
   constexpr int RUN_ROWS = 64 / CPR;           // rows in one wave's 1 KB direct-to-LDS run
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   // loads logical chunk (l % CPR) ^ swz(row), which reproduces the swizzled layout the fragment
   // reads use (runs start on multiples of 8 or 16 rows, so the swizzle of a run row is that of
   // l / CPR).
-  const int d_row = lane / CPR, d_ch = (lane % CPR) ^ lds_swz(d_row);
+  const int d_row = lane / CPR, d_ch = (lane % CPR) ^ lds_swz<BK>(d_row);
   uint32_t dA[A_RUNS], dB[B_RUNS];
   if (ROWS == ROWS_GATHER) {
     // all gather indices are requested before the first is used; rows past the tile read a valid
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   // term depends on the lane only.
   const int fa0 = (wm * WTM + (lane & 15)) * BK;
   const int fb0 = BM * BK + (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
-  const int sw = lds_swz(lane & 15);
+  const int sw = lds_swz<BK>(lane & 15);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -538,12 +541,76 @@ int quad_width(int n_tiles, int group_m) {
     if (n_tiles % q == 0) return q;
   return target;
 }
-struct TileCfg { int bm, bn, wm, wn, gm; };
+struct TileCfg { int bm, bn, wm, wn, gm; int bk = kBK; int st = kStages; };
 constexpr TileCfg kP1{FSM_P1}, kP2{FSM_P2}, kR{FSM_R};
-constexpr int P1_BM = kP1.bm, P1_BN = kP1.bn, P1_WM = kP1.wm, P1_WN = kP1.wn;
-constexpr int P2_BM = kP2.bm, P2_BN = kP2.bn, P2_WM = kP2.wm, P2_WN = kP2.wn;
+// Groups of a few dozen rows (a decode batch spread over all experts: 32 rows per expert for 1024
+// tokens, k = 8, E = 256) would leave most of a 256-row tile empty; there the product is bound by
+// the weight stream, not by the MFMA, and 64-row tiles (4 waves of 64 x 64) keep the padding
+// small.  They are used when the groups average at most kSmallRows rows, or when 256-row tiles
+// would not give every CU a workgroup (the shared expert of a decode batch: 1024 rows, one
+// group).  Three 40 KB stages (one workgroup per CU, two stages in flight) stream the weights
+// 1.5% faster in the decode stack than two.
+#ifndef FSM_SMALL_STAGE
+#define FSM_SMALL_STAGE 64, 3
+#endif
+constexpr TileCfg kS1{64, 256, 1, 4, 4, FSM_SMALL_STAGE}, kS2{64, 256, 1, 4, 4, FSM_SMALL_STAGE};
+constexpr int kSmallRows = 96, kCus = 256;
 constexpr int R_BM = kR.bm, R_BN = kR.bn, R_WM = kR.wm, R_WN = kR.wn;
+// Router of a small batch (a decode step): 256 x 256 tiles would give a 1024-token batch four
+// workgroups; 64 x 64 tiles (4 waves of 64 x 16) give it 64.
+constexpr TileCfg kRS{64, 64, 1, 4, 1};
 constexpr int F_BM = 16, F_BN = 16;
+
+bool small_tiles(int64_t N, int32_t G, int64_t c, int dtype) {
+  if (dtype != MOE_BF16) return false;
+  const int64_t big_grid = (cdiv(N, kP1.bm) + G) * cdiv(c, kP1.bn / 2);
+  return N <= int64_t(kSmallRows) * G || big_grid < kCus;
+}
+
+// M-tile rows of the two phases for this problem
+void tile_rows(int64_t N, int32_t G, int64_t c, int dtype, int& bm1, int& bm2) {
+  if (dtype != MOE_BF16) {
+    bm1 = bm2 = F_BM;
+  } else if (small_tiles(N, G, c, dtype)) {
+    bm1 = kS1.bm;
+    bm2 = kS2.bm;
+  } else {
+    bm1 = kP1.bm;
+    bm2 = kP2.bm;
+  }
+}
+
+// Both phases of the bf16 grouped product with tile configurations C1 (gate/up) and C2 (down).
+template <const TileCfg& C1, const TileCfg& C2>
+int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t mt1, int64_t mt2, int64_t c,
+                     int64_t d, int32_t G, hipStream_t s) {
+  a1.group_m = C1.gm;
+  a1.n_tiles = int32_t(cdiv(c, C1.bn / 2));
+  a1.quad_nb = quad_width(a1.n_tiles, a1.group_m);
+  const dim3 grid1(unsigned(quad_grid(mt1, a1.n_tiles, a1.group_m, a1.quad_nb)));
+  constexpr int nt1 = 64 * C1.wm * C1.wn;
+  {
+    ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
+    if (rows1 == ROWS_GATHER)
+      k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GATHER, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
+    else if (rows1 == ROWS_GROUPED)
+      k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GROUPED, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
+    else
+      k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_SINGLE, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
+    if (int rc = check_launch("grouped gemm phase 1")) return rc;
+  }
+  a2.group_m = C2.gm;
+  a2.n_tiles = int32_t(cdiv(d, C2.bn));
+  a2.quad_nb = quad_width(a2.n_tiles, a2.group_m);
+  const dim3 grid2(unsigned(quad_grid(mt2, a2.n_tiles, a2.group_m, a2.quad_nb)));
+  constexpr int nt2 = 64 * C2.wm * C2.wn;
+  ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
+  if (rows2 == ROWS_GROUPED)
+    k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_GROUPED, C2.bk, C2.st><<<grid2, nt2, 0, s>>>(a2);
+  else
+    k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_SINGLE, C2.bk, C2.st><<<grid2, nt2, 0, s>>>(a2);
+  return check_launch("grouped gemm phase 2");
+}
 
 struct SwigluWs {
   int32_t* ts1;
@@ -554,9 +621,10 @@ struct SwigluWs {
 };
 
 SwigluWs carve(void* ws, int32_t G, int64_t N, int64_t c, int dtype, size_t* total) {
-  const bool bf = dtype == MOE_BF16;
-  const size_t esz = bf ? 2 : 4;
-  const int64_t mt1 = cdiv(N, bf ? P1_BM : F_BM) + G, mt2 = cdiv(N, bf ? P2_BM : F_BM) + G;
+  const size_t esz = dtype == MOE_BF16 ? 2 : 4;
+  int bm1, bm2;
+  tile_rows(N, G, c, dtype, bm1, bm2);
+  const int64_t mt1 = cdiv(N, bm1) + G, mt2 = cdiv(N, bm2) + G;
   size_t off = 0;
   SwigluWs w;
   char* base = static_cast<char*>(ws);
@@ -588,7 +656,8 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   SwigluWs w = carve(ws, G, N, c, dtype, nullptr);
   if (N == 0) return MOE_OK;
   const bool bf = dtype == MOE_BF16;
-  const int bm1 = bf ? P1_BM : F_BM, bm2 = bf ? P2_BM : F_BM;
+  int bm1, bm2;
+  tile_rows(N, G, c, dtype, bm1, bm2);
   const int64_t mt1 = cdiv(N, bm1) + G, mt2 = cdiv(N, bm2) + G;
   {
     ProfScope prof(MOE_K_TILE_TABLE, s);
@@ -607,42 +676,19 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   GemmArgs a1{};
   a1.A = X; a1.B1 = W1; a1.B2 = W2; a1.out = w.H; a1.bias = nullptr;
   a1.offsets = offsets; a1.tile_start = w.ts1; a1.tile_group = w.grp1; a1.b_group_stride = c * d;
-  a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G; a1.group_m = bf ? kP1.gm : 1;
+  a1.K = int32_t(d); a1.n_out = int32_t(c); a1.M = int32_t(N); a1.G = G; a1.group_m = 1;
   a1.gather = gather; a1.gather_k = gather_k; a1.a_rows = x_rows;
 
   GemmArgs a2{};
   a2.A = w.H; a2.B1 = W3; a2.B2 = nullptr; a2.out = Y; a2.bias = nullptr;
   a2.offsets = offsets; a2.tile_start = w.ts2; a2.tile_group = w.grp2; a2.b_group_stride = d * c;
-  a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G; a2.group_m = bf ? kP2.gm : 1;
+  a2.K = int32_t(c); a2.n_out = int32_t(d); a2.M = int32_t(N); a2.G = G; a2.group_m = 1;
 
   const int rows1 = gather ? ROWS_GATHER : (G > 1 ? ROWS_GROUPED : ROWS_SINGLE);
   const int rows2 = G > 1 ? ROWS_GROUPED : ROWS_SINGLE;
-  if (bf) {
-    a1.n_tiles = int32_t(cdiv(c, P1_BN / 2));
-    a1.quad_nb = quad_width(a1.n_tiles, a1.group_m);
-    const dim3 grid1(unsigned(quad_grid(mt1, a1.n_tiles, a1.group_m, a1.quad_nb)));
-    constexpr int nt1 = 64 * P1_WM * P1_WN;
-    {
-      ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
-      if (rows1 == ROWS_GATHER)
-        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_GATHER><<<grid1, nt1, 0, s>>>(a1);
-      else if (rows1 == ROWS_GROUPED)
-        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_GROUPED><<<grid1, nt1, 0, s>>>(a1);
-      else
-        k_gemm_bf16<P1_BM, P1_BN, P1_WM, P1_WN, EPI_SWIGLU, ROWS_SINGLE><<<grid1, nt1, 0, s>>>(a1);
-      if (int rc = check_launch("grouped gemm phase 1")) return rc;
-    }
-    a2.n_tiles = int32_t(cdiv(d, P2_BN));
-    a2.quad_nb = quad_width(a2.n_tiles, a2.group_m);
-    const dim3 grid2(unsigned(quad_grid(mt2, a2.n_tiles, a2.group_m, a2.quad_nb)));
-    constexpr int nt2 = 64 * P2_WM * P2_WN;
-    ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
-    if (rows2 == ROWS_GROUPED)
-      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, ROWS_GROUPED><<<grid2, nt2, 0, s>>>(a2);
-    else
-      k_gemm_bf16<P2_BM, P2_BN, P2_WM, P2_WN, EPI_PLAIN, ROWS_SINGLE><<<grid2, nt2, 0, s>>>(a2);
-    return check_launch("grouped gemm phase 2");
-  }
+  if (bf && small_tiles(N, G, c, dtype))
+    return launch_bf16_pair<kS1, kS2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s);
+  if (bf) return launch_bf16_pair<kP1, kP2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s);
   a1.n_tiles = int32_t(cdiv(c, F_BN));
   {
     ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
@@ -667,6 +713,13 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
   a.K = int32_t(d); a.n_out = E; a.M = int32_t(T); a.G = 1; a.group_m = kR.gm;
   ProfScope prof(MOE_K_ROUTER_GEMM, s);
   if (dtype == MOE_BF16) {
+    if (cdiv(T, R_BM) * cdiv(E, R_BN) < kCus) {
+      a.n_tiles = int32_t(cdiv(E, kRS.bn));
+      const int64_t grid = cdiv(T, kRS.bm) * a.n_tiles;
+      k_gemm_bf16<kRS.bm, kRS.bn, kRS.wm, kRS.wn, EPI_F32_BIAS, ROWS_SINGLE>
+          <<<dim3(unsigned(grid)), 64 * kRS.wm * kRS.wn, 0, s>>>(a);
+      return check_launch("router gemm");
+    }
     a.n_tiles = int32_t(cdiv(E, R_BN));
     const int64_t grid = cdiv(T, R_BM) * a.n_tiles;
     k_gemm_bf16<R_BM, R_BN, R_WM, R_WN, EPI_F32_BIAS, ROWS_SINGLE><<<dim3(unsigned(grid)), 64 * R_WM * R_WN, 0, s>>>(a);

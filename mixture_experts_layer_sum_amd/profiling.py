@@ -58,6 +58,31 @@ def _col(row, *names):
     raise KeyError(names)
 
 
+def gemm_args(name: str):
+    """Template arguments of a k_gemm_bf16 symbol as ints (BM, BN, waves_m, waves_n, epilogue, rows,
+    ...), or None for other kernels."""
+    i = name.find("k_gemm_bf16<")
+    if i < 0:
+        return None
+    j = name.find(">", i)
+    try:
+        return tuple(int(a) for a in name[i + len("k_gemm_bf16<"):j].split(","))
+    except ValueError:
+        return None
+
+
+def is_routed_gate_up(name: str) -> bool:
+    """The routed (grouped or gathered rows) gate/up + SwiGLU product."""
+    a = gemm_args(name)
+    return a is not None and len(a) >= 6 and a[4] == 1 and a[5] in (0, 2)
+
+
+def is_routed(name: str) -> bool:
+    """Either routed product (grouped or gathered rows), as opposed to the shared expert / router."""
+    a = gemm_args(name)
+    return a is not None and len(a) >= 6 and a[5] in (0, 2)
+
+
 def short(name: str, width: int = 90) -> str:
     name = name.replace("void ", "")
     return name if len(name) <= width else name[:width - 3] + "..."
@@ -119,7 +144,7 @@ def cmd_trace(path, skip_first=0):
         disp.append((t0, t1, q, name))
     disp.sort()
     lib = [d for d in disp if LIB_PREFIX in d[3]]
-    gemm = [d for d in lib if "k_gemm_bf16" in d[3] and (", 1, 0>" in d[3] or ", 1, 2>" in d[3])]  # routed gate/up
+    gemm = [d for d in lib if is_routed_gate_up(d[3])]
     if skip_first and len(gemm) > skip_first:
         t_begin = gemm[skip_first][0]
         lib = [d for d in lib if d[0] >= t_begin - 50_000_000]  # keep the rest of that step's head
@@ -132,7 +157,7 @@ def cmd_trace(path, skip_first=0):
     for (name, q), ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         print(f"{short(name, 70):<70} {q:>6} {len(ds):>6} {sum(ds) / len(ds) / 1e3:>10.1f} {sum(ds) / 1e6:>10.2f}")
     # routed GEMMs (row modes 0 = grouped, 2 = gathered) run on the main queue
-    main_q = {d[2] for d in lib if "k_gemm_bf16" in d[3] and (", 0>" in d[3] or ", 2>" in d[3])}
+    main_q = {d[2] for d in lib if is_routed(d[3])}
     if len(main_q) != 1:
         print("# overlap: could not identify a single main queue")
         return

@@ -55,6 +55,7 @@ class MoEConfig:
     router_bias: bool = False
     w_std: float = 0.02  # W_R, W1, W2 (and shared W1, W2)
     w3_std: float = 0.02  # W3 (and shared W3)
+    weight_cfg_id: Optional[int] = None  # draw the weights of that workload (same shapes) instead
 
     @property
     def torch_dtype(self):
@@ -88,6 +89,10 @@ CONFIGS = [
               gate="sigmoid", renormalize=False, dtype="bf16"),
     MoEConfig(4, "dsv3-stack", T=65536, d=7168, E=256, k=8, c=2048, n_shared=1, c_shared=2048,
               gate="sigmoid", renormalize=True, dtype="bf16", layers=4),
+    # one decode step of a 1024-sequence batch through the same 4 layers (same weights): every
+    # expert gets about T*k/E = 32 rows, so the layer streams all of its weights for few tokens
+    MoEConfig(5, "dsv3-decode", T=1024, d=7168, E=256, k=8, c=2048, n_shared=1, c_shared=2048,
+              gate="sigmoid", renormalize=True, dtype="bf16", layers=4, weight_cfg_id=4),
 ]
 BY_NAME = {c.name: c for c in CONFIGS}
 
@@ -119,10 +124,15 @@ def activations(cfg: MoEConfig, device="cpu", T: Optional[int] = None, layer: in
                   cfg.torch_dtype if dtype is None else dtype)
 
 
+def weights_id(cfg: MoEConfig) -> int:
+    """The workload id the weights are drawn for (a decode batch shares its prefill's weights)."""
+    return cfg.cfg_id if cfg.weight_cfg_id is None else cfg.weight_cfg_id
+
+
 def _stacked(cfg, layer, tensor, E, rows, cols, std, device, dtype):
     out = torch.empty((E, rows, cols), device=device, dtype=dtype)
     for e in range(E):
-        out[e].copy_(normal((rows, cols), std, seed_for(cfg.cfg_id, layer, tensor, e), device))
+        out[e].copy_(normal((rows, cols), std, seed_for(weights_id(cfg), layer, tensor, e), device))
     return out
 
 
@@ -134,7 +144,7 @@ def layer_weights(cfg: MoEConfig, layer: int = 0, device="cpu") -> dict:
     dimension; shared expert s owns hidden rows/columns [s*cs, (s+1)*cs)), or None without shared.
     """
     dt = cfg.torch_dtype
-    cid = cfg.cfg_id
+    cid = weights_id(cfg)
     w = {}
     w["W_R"] = normal((cfg.E, cfg.d), cfg.w_std, seed_for(cid, layer, T_WR), device, dt)
     w["bias"] = (normal((cfg.E,), 1.0, seed_for(cid, layer, T_BIAS), device)

@@ -271,6 +271,46 @@ def test_grouped_swiglu_dsv3_full_size_sampled(ops):
     assert not torch.isnan(Y.float()).any().item()
 
 
+def test_grouped_swiglu_small_tiles_bitwise_equal_large(ops):
+    """Groups averaging at most 96 rows (or grids too small to give every CU a workgroup) run on
+    64-row tiles, the rest on 256-row tiles.  The same rows and weights with empty groups appended
+    (which moves the average below the switch) must give bit-identical outputs: both tilings sum
+    every output over K in the same order."""
+    d, c = 128, 2048
+    sizes = [2500, 0, 3100, 2592]                   # 2048 rows per group, 576 big tiles: 256-row tiles
+    extra = [0] * 100                               # 8192 rows over 104 groups: 64-row tiles
+    N = sum(sizes)
+    seed = mi.seed_for(95, N, d, c)
+    X = mi.normal((N, d), 1.0, seed, DEV, torch.bfloat16)
+    G = len(sizes) + len(extra)
+    W1 = mi.normal((G, c, d), d ** -0.5, seed + 1, DEV, torch.bfloat16)
+    W2 = mi.normal((G, c, d), d ** -0.5, seed + 2, DEV, torch.bfloat16)
+    W3 = mi.normal((G, d, c), c ** -0.5, seed + 3, DEV, torch.bfloat16)
+    g = len(sizes)
+    _, Y_large = run_swiglu(ops, X, sizes, W1[:g].contiguous(), W2[:g].contiguous(), W3[:g].contiguous())
+    off, Y_small = run_swiglu(ops, X, sizes + extra, W1, W2, W3)
+    assert torch.equal(Y_large, Y_small)
+    ref = oracle.grouped_mlp(to_np(X), off, ExpertSlices(W1), ExpertSlices(W2), ExpertSlices(W3))
+    assert_parity(to_np(Y_small), ref, torch.bfloat16, "64-row tiles")
+
+
+def test_grouped_swiglu_decode_shape_sampled(ops):
+    """One decode step of the DeepSeek-V3-shaped layer: 1024 tokens x 8 slots over 256 experts
+    (about 32 rows each, the 64-row tiling), real layer weights; rows of four experts checked."""
+    c = CFG["dsv3-decode"]
+    N = c.T * c.k
+    W = mi.layer_weights(c, 0, DEV)
+    sizes = mi.group_sizes(N, c.E, mi.seed_for(c.cfg_id, 0, mi.T_GROUPS)).tolist()
+    X = mi.normal((N, c.d), 1.0, mi.seed_for(c.cfg_id, 0, mi.T_ACT, 9), DEV, c.torch_dtype)
+    off, Y = run_swiglu(ops, X, sizes, W["W1"], W["W2"], W["W3"])
+    W1, W2, W3 = ExpertSlices(W["W1"]), ExpertSlices(W["W2"]), ExpertSlices(W["W3"])
+    for e in (0, 31, 200, 255):
+        a, b = int(off[e]), int(off[e + 1])
+        ref = oracle.mlp(to_np(X[a:b]), W1[e], W2[e], W3[e])
+        assert_parity(to_np(Y[a:b]), ref, c.torch_dtype, f"expert {e}")
+    assert not torch.isnan(Y.float()).any().item()
+
+
 # =================================================================================================
 # a3 + a4 fused: rows gathered through the permutation (the stack's launch configuration)
 # =================================================================================================
@@ -370,7 +410,7 @@ def layer_check(ops, c, n_sample):
 
 
 @pytest.mark.parametrize("name,n_sample", [("tiny-fp32", 64), ("dsv2-lite", 256), ("qwen3-30b-a3b", 256),
-                                           ("llama4-scout", 128)])
+                                           ("llama4-scout", 128), ("dsv3-decode", 8)])
 def test_layer_end_to_end(ops, name, n_sample):
     layer_check(ops, CFG[name], n_sample)
 

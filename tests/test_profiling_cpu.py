@@ -63,3 +63,13 @@ def test_traffic_join_picks_copy_closest_to_size(tmp_path, capsys):
     line = [l for l in out.splitlines() if l.startswith("traffic|") and "k_gemm_bf16" in l][0]
     fields = line.split("|")
     assert abs(float(fields[3]) - 2 * 2**30 / 1e9) < 1e-3 and abs(float(fields[4]) - 2**30 / 1e9) < 1e-3
+
+
+def test_gemm_symbol_classification():
+    gu8 = "void fsm::k_gemm_bf16<256, 256, 2, 4, 1, 2, 64, 2>(fsm::GemmArgs)"
+    assert profiling.gemm_args(gu8) == (256, 256, 2, 4, 1, 2, 64, 2)
+    assert profiling.is_routed_gate_up(gu8) and profiling.is_routed_gate_up(G1)
+    assert profiling.is_routed("void fsm::k_gemm_bf16<64, 256, 1, 4, 0, 0, 32, 4>(fsm::GemmArgs)")
+    shared = "void fsm::k_gemm_bf16<256, 256, 2, 4, 1, 1, 64, 2>(fsm::GemmArgs)"
+    assert not profiling.is_routed_gate_up(shared) and not profiling.is_routed(shared)
+    assert not profiling.is_routed(R) and profiling.gemm_args("fsm::k_combine(int)") is None
