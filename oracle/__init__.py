@@ -6,3 +6,4 @@ from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import (router_logits, select_topk, gate_scores, gate_weights, route, permute,
                          permute_rows, silu, mlp, grouped_mlp, shared_mlp, combine, moe_layer,
                          farskip_stack, moe_stack, round_to_bf16, topk_gap)
+from . import mxfp8  # noqa: F401  (MXFP8 numbers of the FP8 expert products)

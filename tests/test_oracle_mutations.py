@@ -125,6 +125,77 @@ CASES = [
 ]
 
 
+# ---- MXFP8 oracle (oracle/mxfp8.py) ----------------------------------------------------------
+from tests import test_oracle_mxfp8_pins as mxpins  # noqa: E402
+
+mx = oracle.mxfp8
+MX_ORIG = {name: getattr(mx, name) for name in ("block_exponent", "e4m3_encode", "mx_quantize", "mlp_mxfp8")}
+
+
+def _scale_floor_rule(amax):          # the clipping rule floor(log2(amax)) - 8
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(amax)
+    return np.clip(np.where(amax > 0, e - 9, 0), -127, 127).astype(np.int64)
+
+
+def _scale_one_too_large(amax):
+    return MX_ORIG["block_exponent"](amax) + 1
+
+
+def _encode_truncating(x):
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    code = np.maximum(np.searchsorted(mx._POS_VALS, a, side="right") - 1, 0)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def _encode_ties_away(x):
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.minimum(np.searchsorted(mx._POS_VALS, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where((mx._POS_VALS[hi] - a) <= (a - mx._POS_VALS[lo]), hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def _quantize_blocks_of_16(X, block=32):
+    return MX_ORIG["mx_quantize"](X, 16)
+
+
+def _mlp_hidden_not_quantised(X, W1q, W2q, W3q, hidden_store=None):
+    Xd = mx.mx_dequantize(*mx.mx_quantize(X))
+    H = (Xd @ mx.mx_dequantize(*W1q).T) * mx.silu(Xd @ mx.mx_dequantize(*W2q).T)
+    return H @ mx.mx_dequantize(*W3q).T
+
+
+def _mlp_gate_up_swapped_fp8(X, W1q, W2q, W3q, hidden_store=None):
+    return MX_ORIG["mlp_mxfp8"](X, W2q, W1q, W3q, hidden_store)
+
+
+MX_CASES = [
+    ("block_exponent", _scale_floor_rule, [mxpins.test_mx_block_scale_rule]),
+    ("block_exponent", _scale_one_too_large, [mxpins.test_mx_representable_blocks_quantize_exactly]),
+    ("e4m3_encode", _encode_truncating, [mxpins.test_e4m3_ties_to_even_and_saturation]),
+    ("e4m3_encode", _encode_ties_away, [mxpins.test_e4m3_ties_to_even_and_saturation]),
+    ("mx_quantize", _quantize_blocks_of_16, [mxpins.test_mx_block_scale_rule]),
+    ("mlp_mxfp8", _mlp_hidden_not_quantised, [mxpins.test_mlp_mxfp8_hand_example_quantises_the_hidden]),
+    ("mlp_mxfp8", _mlp_gate_up_swapped_fp8, [mxpins.test_mlp_mxfp8_equals_the_mlp_on_representable_operands]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MX_CASES)), ids=[c[1].__name__.lstrip("_") for c in MX_CASES])
+def test_planted_mxfp8_mistake_is_caught(i, monkeypatch):
+    name, bad, pin_fns = MX_CASES[i]
+    monkeypatch.setattr(mx, name, bad)
+    caught = 0
+    for fn in pin_fns:
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {bad.__name__}"
+
+
 @pytest.mark.parametrize("i", range(len(CASES)), ids=[c[1].__name__.lstrip("_") for c in CASES])
 def test_planted_mistake_is_caught(i, monkeypatch):
     name, bad, pin_fns = CASES[i]
