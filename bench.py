@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "routed tokens/s + MFMA util, bf16 MoE layer (DeepSeek-V3 shape), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -47,6 +48,8 @@ def parse():
                    help="after the steps, time a 1024-token decode step through the same layers; 0 = skip")
     p.add_argument("--standalone", type=int, default=1,
                    help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
+    p.add_argument("--mxfp8", type=int, default=1,
+                   help="after the steps, time the layer-0 routed experts with MXFP8 operands; 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                    help="before the steps, one plain device copy of this many GiB (a known-size kernel whose "
                         "FETCH_SIZE / WRITE_SIZE calibrate the HBM counters); 0 = skip")
@@ -88,6 +91,9 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
         "dense_down": (2.0 * T * d * cs, "flop"),
         "combine": (N * d * 2.0 + N * 8.0 + T * d * (2.0 + 4.0 + 4.0), "byte"),
         "layer_input": (T * d * (4.0 + 2.0 + 2.0), "byte"),
+        "mx_quantize": (T * d * (2.0 + 1.0 + 1.0 / 32), "byte"),   # the token rows, once per layer
+        "mx_gate_up": (4.0 * N * d * c_, "flop_fp8"),
+        "mx_down": (2.0 * N * d * c_, "flop_fp8"),
     }
     out = {}
     for kind, (n, ms) in prof.items():
@@ -97,9 +103,10 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
         row = {"launches": n, "avg_ms": round(avg, 4), "ms_per_step": round(ms / steps, 3)}
         if kind in per_launch:
             work, unit = per_launch[kind]
-            if unit == "flop":
+            if unit in ("flop", "flop_fp8"):
                 row["tflops"] = round(work / (avg * 1e-3) / 1e12, 1)
-                row["frac_mfma_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+                peak = PEAK_FP8_TFLOPS if unit == "flop_fp8" else PEAK_BF16_TFLOPS
+                row["frac_mfma_peak"] = round(row["tflops"] / peak, 4)
             else:
                 row["gbs"] = round(work / (avg * 1e-3) / 1e9, 1)
                 row["frac_hbm_peak"] = round(row["gbs"] / PEAK_HBM_GBS, 4)
@@ -171,6 +178,53 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
     }
     del a, b, m, n
+    return out
+
+
+def mxfp8(c, layers, o0, reps: int = 3) -> dict:
+    """The layer-0 routed experts with MXFP8 operands: the weights quantised once (as at load
+    time, untimed), then per repetition the token rows quantised and the gathered grouped product
+    on them (fp8 MFMA against the 5 PFLOP/s dense fp8 peak)."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    T, d, E, k, cc = c.T, c.d, c.E, c.k, c.c
+    N = T * k
+    W = layers[0]
+    x = o0.to(torch.bfloat16)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    src = torch.empty((N,), dtype=torch.int32, device=dev)
+    dest = torch.empty((N,), dtype=torch.int32, device=dev)
+    ops.moe_route(x, W["W_R"], k, c.gate, c.renormalize, logits, idx, w, bias=W.get("bias"))
+    ops.moe_permute(idx, E, off, src, dest)
+    W1q, W2q, W3q = ops.mx_quantized(W["W1"]), ops.mx_quantized(W["W2"]), ops.mx_quantized(W["W3"])
+    xq = (torch.empty((T, d), dtype=torch.uint8, device=dev), torch.empty((T, d // 32), dtype=torch.uint8, device=dev))
+    Y = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    ws = ops.workspace(ops.grouped_swiglu_mxfp8_workspace_bytes(N, E, cc), dev)
+
+    def rep():
+        ops.moe_mx_quantize(x, xq[0], xq[1])
+        ops.moe_grouped_swiglu_mxfp8(xq, off, W1q, W2q, W3q, Y, sorted_src=src, k=k, ws=ws)
+
+    rep()
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    for _ in range(reps):
+        rep()
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    rep_ = kernel_report(ops.profile_collect(), c, reps)
+    assert torch.isfinite(Y.float()).all().item(), "non-finite MXFP8 output"
+    out = {k_: rep_[k_] for k_ in ("mx_quantize", "tile_table", "mx_gate_up", "mx_down") if k_ in rep_}
+    ms = sum(v["avg_ms"] for k_, v in out.items())
+    out["routed_experts_ms"] = round(ms, 3)
+    out["routed_experts_tflops"] = round(6.0 * N * d * cc / (ms * 1e-3) / 1e12, 1)
+    del W1q, W2q, W3q, ws, Y
     return out
 
 
@@ -377,6 +431,9 @@ def main():
     if args.decode and c.name == "dsv3-stack":
         log("timing the decode-shaped stack")
         result["decode"] = decode(layers)
+    if args.mxfp8 and c.name == "dsv3-stack":
+        log("timing the MXFP8 routed experts")
+        result["mxfp8"] = mxfp8(c, layers, o0)
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = standalone(c, layers, o0)

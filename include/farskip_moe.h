@@ -132,6 +132,73 @@ int moe_grouped_swiglu_gathered(const void* X, int64_t T, const int32_t* sorted_
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * MXFP8 expert products.  FarSkip-Collective's inference measurements run the MoE forward with FP8
+ * quantisation (the page's experimental setup: software configuration and inference parameters);
+ * the pages name no format.  Format taken: OCP MXFP8 -- FP8 E4M3 elements (largest magnitude 448,
+ * subnormals kept, nearest value with ties to the even code) and one E8M0 power-of-two scale per
+ * 32 consecutive elements along the reduction dimension.  Block scale: the smallest 2^s with
+ * max|x| / 2^s <= 448 (0 for an all-zero block), stored as the byte s + 127.
+ *
+ * moe_mx_quantize -- rows of bf16 X to MXFP8.
+ *   X       [rows, K] bf16      input (device)
+ *   codes   [rows, K] uint8     OUTPUT E4M3 codes, row-major
+ *   scales  [rows, K/32] uint8  OUTPUT E8M0 scales; byte j of a row covers its elements 32j .. 32j+31
+ * Weights are quantised by the same call (W1 / W2 as [G*c, d] along d, W3 as [G*d, c] along c).
+ * Limits: K % 32 == 0; non-finite inputs are not supported.
+ */
+int moe_mx_quantize(const void* X, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_grouped_swiglu_mxfp8 -- moe_grouped_swiglu with MXFP8 operands (all pointers device):
+ *     H[r] = (X[r] W1[g]^T) . SiLU(X[r] W2[g]^T)   fp32 accumulation of the dequantised products,
+ *                                                   H formed in fp32 and quantised to MXFP8 along c
+ *     Y[r] = H[r] W3[g]^T                           fp32 accumulation, Y stored as bf16
+ *
+ *   Xq, Xs        [x_rows, d] / [x_rows, d/32] uint8   activation codes and scales (moe_mx_quantize)
+ *   x_rows        rows of Xq (N when sorted_src is NULL; the token count T when gathering)
+ *   sorted_src    NULL: grouped row r is Xq row r.  Else [N] int32 (moe_permute output, values in
+ *                 [0, x_rows * k)): grouped row r is Xq row sorted_src[r] / k -- the Dispatch
+ *                 permutation of section 2.1 folded into the loads; the result is bit-identical
+ *   k             slots per token (used only with sorted_src)
+ *   group_offsets [G+1] int32      as moe_grouped_swiglu
+ *   W1q, W1s      [G, c, d] / [G, c, d/32] uint8   up projection, quantised along d
+ *   W2q, W2s      [G, c, d] / [G, c, d/32] uint8   gate projection, quantised along d
+ *   W3q, W3s      [G, d, c] / [G, d, c/32] uint8   down projection, quantised along c
+ *   Y             [N, d] bf16      OUTPUT, grouped row order
+ *   ws, ws_bytes  scratch of at least moe_grouped_swiglu_mxfp8_workspace_bytes(N, G, c); after the
+ *                 call it holds H's codes and scales (not part of the interface)
+ * Limits: d % 128 == 0, c % 128 == 0, x_rows * d < 2^31.
+ */
+int moe_grouped_swiglu_mxfp8(const uint8_t* Xq, const uint8_t* Xs, int64_t x_rows, const int32_t* sorted_src,
+                             int32_t k, const int32_t* group_offsets, int32_t G, const uint8_t* W1q,
+                             const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, const uint8_t* W3q,
+                             const uint8_t* W3s, int64_t N, int64_t d, int64_t c, void* Y, void* ws,
+                             size_t ws_bytes, void* stream);
+size_t moe_grouped_swiglu_mxfp8_workspace_bytes(int64_t N, int32_t G, int64_t c);
+
+/*
+ * The two products of moe_grouped_swiglu_mxfp8 as calls of their own (H in the caller's buffers);
+ * gate_up followed by down gives the fused call's Y bit for bit.
+ *
+ * moe_grouped_mxfp8_gate_up -- H = (X W1^T) . SiLU(X W2^T), formed in fp32, quantised along c.
+ *   Xq .. W2s, N, d, c     as moe_grouped_swiglu_mxfp8
+ *   Hq, Hs                 [N, c] / [N, c/32] uint8   OUTPUT H codes and scales, grouped row order
+ * moe_grouped_mxfp8_down -- Y = H W3^T per group, fp32 accumulation, Y stored as bf16.
+ *   Hq, Hs                 [N, c] / [N, c/32] uint8   (e.g. moe_grouped_mxfp8_gate_up output)
+ *   W3q, W3s, Y, N, c, d   as moe_grouped_swiglu_mxfp8 (note the argument order c, d)
+ * Both: ws of at least moe_grouped_mxfp8_phase_workspace_bytes(N, G) bytes (the group tile
+ * table); same limits as moe_grouped_swiglu_mxfp8.
+ */
+int moe_grouped_mxfp8_gate_up(const uint8_t* Xq, const uint8_t* Xs, int64_t x_rows, const int32_t* sorted_src,
+                              int32_t k, const int32_t* group_offsets, int32_t G, const uint8_t* W1q,
+                              const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, int64_t N, int64_t d,
+                              int64_t c, uint8_t* Hq, uint8_t* Hs, void* ws, size_t ws_bytes, void* stream);
+int moe_grouped_mxfp8_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* group_offsets, int32_t G,
+                           const uint8_t* W3q, const uint8_t* W3s, int64_t N, int64_t c, int64_t d, void* Y,
+                           void* ws, size_t ws_bytes, void* stream);
+size_t moe_grouped_mxfp8_phase_workspace_bytes(int64_t N, int32_t G);
+
+/*
  * moe_combine -- the Combine of section 2.1: routed expert outputs summed back per token.
  *   out[t] = residual[t] + addend[t] + sum_{i<k} topk_w[t,i] * Y[dest_row[t*k+i]]
  * accumulated in float32, slots in order i = 0..k-1 (deterministic, no atomics).
@@ -216,7 +283,10 @@ typedef enum {
   MOE_K_LAYER_INPUT = 8,  /* FarSkip layer input x = cast(o [+ S]) */
   MOE_K_DENSE_GATE_UP = 9,/* phase 1 of a single-group call (e.g. the shared expert) */
   MOE_K_DENSE_DOWN = 10,  /* phase 2 of a single-group call */
-  MOE_KERNEL_KINDS = 11
+  MOE_K_MX_QUANTIZE = 11, /* MXFP8 quantisation of rows */
+  MOE_K_MX_GATE_UP = 12,  /* MXFP8 grouped product, phase 1 (with H quantised in its epilogue) */
+  MOE_K_MX_DOWN = 13,     /* MXFP8 grouped product, phase 2 */
+  MOE_KERNEL_KINDS = 14
 } moe_kernel_kind_t;
 
 typedef struct {

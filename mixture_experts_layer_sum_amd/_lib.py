@@ -16,11 +16,14 @@ FARSKIP_NONE, FARSKIP_PARTIAL, FARSKIP_OUTDATED = 0, 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 1024, 32
 
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_swiglu",
-           "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu_gathered", "moe_combine", "farskip_stack_forward",
+           "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu_gathered", "moe_mx_quantize",
+           "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
+           "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_combine", "farskip_stack_forward",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect", "moe_last_error",
            "moe_version")
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
-                "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down")
+                "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
+                "mx_down")
 
 
 class LayerDesc(ctypes.Structure):
@@ -60,6 +63,20 @@ def _declare(lib):
     lib.moe_grouped_swiglu_gathered.argtypes = [vp, i64, vp, i32, vp, i32, vp, vp, vp, i, i64, i64, i64, vp, vp,
                                                  sz, vp]
     lib.moe_grouped_swiglu_gathered.restype = i
+    lib.moe_mx_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.moe_mx_quantize.restype = i
+    lib.moe_grouped_swiglu_mxfp8.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                             vp, vp, sz, vp]
+    lib.moe_grouped_swiglu_mxfp8.restype = i
+    lib.moe_grouped_swiglu_mxfp8_workspace_bytes.argtypes = [i64, i32, i64]
+    lib.moe_grouped_swiglu_mxfp8_workspace_bytes.restype = sz
+    lib.moe_grouped_mxfp8_gate_up.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp,
+                                              vp, sz, vp]
+    lib.moe_grouped_mxfp8_gate_up.restype = i
+    lib.moe_grouped_mxfp8_down.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    lib.moe_grouped_mxfp8_down.restype = i
+    lib.moe_grouped_mxfp8_phase_workspace_bytes.argtypes = [i64, i32]
+    lib.moe_grouped_mxfp8_phase_workspace_bytes.restype = sz
     lib.moe_combine.argtypes = [vp, i, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.moe_combine.restype = i
     lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,

@@ -380,6 +380,105 @@ int moe_grouped_swiglu_gathered(const void* X, int64_t T, const int32_t* sorted_
                                sorted_src, k, T);
 }
 
+int moe_mx_quantize(const void* X, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+  clear_error();
+  if (rows < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize: rows and K must be >= 0");
+  if (K % 32 != 0) return fail(MOE_ERR_UNSUPPORTED, "moe_mx_quantize: K=%lld is not a multiple of 32", (long long)K);
+  if (rows * K > (int64_t(1) << 40)) return fail(MOE_ERR_UNSUPPORTED, "moe_mx_quantize: rows*K too large");
+  if (rows * K > 0 && (!X || !codes || !scales))
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize: X, codes and scales are required");
+  return launch_mx_quantize(X, rows, K, codes, scales, as_stream(stream));
+}
+
+size_t moe_grouped_swiglu_mxfp8_workspace_bytes(int64_t N, int32_t G, int64_t c) {
+  if (N < 0 || G < 1 || c < 1) return 0;
+  return mx_swiglu_ws_bytes(N, G, c);
+}
+
+size_t moe_grouped_mxfp8_phase_workspace_bytes(int64_t N, int32_t G) {
+  if (N < 0 || G < 1) return 0;
+  return mx_swiglu_ws_bytes(N, G, 0);
+}
+
+namespace {
+// shared argument checks of the MXFP8 grouped calls; phases as launch_grouped_swiglu_mx
+int check_mx(const char* who, int phases, const uint8_t* Xq, const uint8_t* Xs, int64_t x_rows,
+             const int32_t* sorted_src, int32_t k, const int32_t* group_offsets, int32_t G, const uint8_t* W1q,
+             const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, const uint8_t* W3q, const uint8_t* W3s,
+             int64_t N, int64_t d, int64_t c, const void* Y, const uint8_t* Hq, const uint8_t* Hs, const void* ws,
+             size_t ws_bytes) {
+  if (G < 1) return fail(MOE_ERR_INVALID_ARG, "%s: G=%d must be >= 1", who, G);
+  if (G > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d > %d", who, G, MOE_MAX_EXPERTS);
+  if (N < 0 || N > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "%s: N=%lld out of range", who, (long long)N);
+  if (d < 1 || c < 1) return fail(MOE_ERR_INVALID_ARG, "%s: d and c must be >= 1", who);
+  if (d % 128 != 0 || c % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: needs d %% 128 == 0 and c %% 128 == 0 (d=%lld, c=%lld)", who,
+                (long long)d, (long long)c);
+  if (c * d > (int64_t(1) << 40)) return fail(MOE_ERR_UNSUPPORTED, "%s: c*d too large", who);
+  if (N * c >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: N * c must be below 2^31", who);
+  if (!group_offsets) return fail(MOE_ERR_INVALID_ARG, "%s: group_offsets is required", who);
+  if ((phases & 1) && (!W1q || !W1s || !W2q || !W2s))
+    return fail(MOE_ERR_INVALID_ARG, "%s: W1 and W2 codes and scales are required", who);
+  if ((phases & 2) && (!W3q || !W3s))
+    return fail(MOE_ERR_INVALID_ARG, "%s: W3 codes and scales are required", who);
+  if (N > 0 && (phases & 1) && (!Xq || !Xs)) return fail(MOE_ERR_INVALID_ARG, "%s: Xq and Xs are required", who);
+  if (N > 0 && (phases & 2) && !Y) return fail(MOE_ERR_INVALID_ARG, "%s: Y is required", who);
+  if (N > 0 && phases != 3 && (!Hq || !Hs)) return fail(MOE_ERR_INVALID_ARG, "%s: Hq and Hs are required", who);
+  if (phases & 1) {
+    if (sorted_src) {
+      if (k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: k=%d must be >= 1 with sorted_src", who, k);
+      if (N > 0 && x_rows < 1) return fail(MOE_ERR_INVALID_ARG, "%s: x_rows must be >= 1 with sorted_src", who);
+    } else if (x_rows != N) {
+      return fail(MOE_ERR_INVALID_ARG, "%s: without sorted_src x_rows (%lld) must equal N (%lld)", who,
+                  (long long)x_rows, (long long)N);
+    }
+    if (x_rows < 0 || x_rows * d >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: x_rows * d must be below 2^31", who);
+  }
+  const size_t need = mx_swiglu_ws_bytes(N, G, phases == 3 ? c : 0);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_grouped_swiglu_mxfp8(const uint8_t* Xq, const uint8_t* Xs, int64_t x_rows, const int32_t* sorted_src,
+                             int32_t k, const int32_t* group_offsets, int32_t G, const uint8_t* W1q,
+                             const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, const uint8_t* W3q,
+                             const uint8_t* W3s, int64_t N, int64_t d, int64_t c, void* Y, void* ws,
+                             size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_mx("moe_grouped_swiglu_mxfp8", 3, Xq, Xs, x_rows, sorted_src, k, group_offsets, G, W1q, W1s,
+                        W2q, W2s, W3q, W3s, N, d, c, Y, nullptr, nullptr, ws, ws_bytes))
+    return rc;
+  return launch_grouped_swiglu_mx(Xq, Xs, group_offsets, G, W1q, W1s, W2q, W2s, W3q, W3s, N, d, c, Y, ws,
+                                  as_stream(stream), sorted_src, sorted_src ? k : 1, x_rows, 3, nullptr, nullptr);
+}
+
+int moe_grouped_mxfp8_gate_up(const uint8_t* Xq, const uint8_t* Xs, int64_t x_rows, const int32_t* sorted_src,
+                              int32_t k, const int32_t* group_offsets, int32_t G, const uint8_t* W1q,
+                              const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, int64_t N, int64_t d,
+                              int64_t c, uint8_t* Hq, uint8_t* Hs, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_mx("moe_grouped_mxfp8_gate_up", 1, Xq, Xs, x_rows, sorted_src, k, group_offsets, G, W1q, W1s,
+                        W2q, W2s, nullptr, nullptr, N, d, c, nullptr, Hq, Hs, ws, ws_bytes))
+    return rc;
+  return launch_grouped_swiglu_mx(Xq, Xs, group_offsets, G, W1q, W1s, W2q, W2s, nullptr, nullptr, N, d, c, nullptr,
+                                  ws, as_stream(stream), sorted_src, sorted_src ? k : 1, x_rows, 1, Hq, Hs);
+}
+
+int moe_grouped_mxfp8_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* group_offsets, int32_t G,
+                           const uint8_t* W3q, const uint8_t* W3s, int64_t N, int64_t c, int64_t d, void* Y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_mx("moe_grouped_mxfp8_down", 2, nullptr, nullptr, N, nullptr, 1, group_offsets, G, nullptr,
+                        nullptr, nullptr, nullptr, W3q, W3s, N, d, c, Y, Hq, Hs, ws, ws_bytes))
+    return rc;
+  return launch_grouped_swiglu_mx(nullptr, nullptr, group_offsets, G, nullptr, nullptr, nullptr, nullptr, W3q, W3s, N,
+                                  d, c, Y, ws, as_stream(stream), nullptr, 1, N, 2, const_cast<uint8_t*>(Hq),
+                                  const_cast<uint8_t*>(Hs));
+}
+
 int moe_combine(const void* Y, int dtype, const float* topk_w, const int32_t* dest_row, int64_t T, int64_t d,
                 int32_t k, const void* addend, const float* residual, float* out, void* out_x, void* stream) {
   clear_error();

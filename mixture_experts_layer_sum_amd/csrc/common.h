@@ -68,6 +68,9 @@ size_t permute_ws_bytes(int64_t T, int32_t E, int32_t k);
 int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
                    const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
                    void* A_perm, void* ws, hipStream_t s);
+// grouped-product M-tile table (tile_start [G+1], tile_group [max_tiles]) for BM-row tiles
+int launch_tile_table(const int32_t* offsets, int G, int BM, int max_tiles, int32_t* tile_start,
+                      int32_t* tile_group, hipStream_t s);
 size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype);
 // gather != null: row r of the grouped input is X[gather[r] / gather_k], X having x_rows rows
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
@@ -77,6 +80,15 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
                    void* out_x, hipStream_t s);
+// MXFP8 (mx.hip): rows of a bf16 matrix -> E4M3 codes + one E8M0 scale per 32 elements
+int launch_mx_quantize(const void* X, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t s);
+size_t mx_swiglu_ws_bytes(int64_t N, int32_t G, int64_t c);
+// the grouped SwiGLU MLP on MXFP8 operands (gather as in launch_grouped_swiglu); Y in bf16
+int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int32_t G,
+                             const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s,
+                             const uint8_t* W3q, const uint8_t* W3s, int64_t N, int64_t d, int64_t c, void* Y,
+                             void* ws, hipStream_t s, const int32_t* gather, int32_t gather_k, int64_t x_rows,
+                             int phases, uint8_t* Hq, uint8_t* Hs);
 // x = cast(o [+ S]) : the FarSkip layer input from the fp32 residual (and the shared output)
 int launch_make_input(const float* o, const void* S, int dtype, int64_t T, int64_t d, void* x,
                       hipStream_t s);

@@ -23,6 +23,7 @@
 // which each workgroup reads with one scalar load.  The grid is sized for the worst case
 // (ceil(N/BM) + G M-tiles); the surplus workgroups exit at once.
 #include "common.h"
+#include "tile_kit.h"
 
 namespace fsm {
 
@@ -82,78 +83,17 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
   for (int j = total + t; j < max_tiles; j += 1024) tile_group[j] = -1;
 }
 
-// Resolve M-tile mt of a grouped product (or of a dense one with M rows) to (group, first row,
-// row count).  Returns false for a surplus workgroup.
-__device__ __forceinline__ bool resolve_mtile(const GemmArgs& p, int mt, int BM, int& g, int& row0,
-                                              int& rows) {
-  if (p.tile_group) {
-    g = p.tile_group[mt];
-    if (g < 0) return false;
-    row0 = p.offsets[g] + (mt - p.tile_start[g]) * BM;
-    rows = min(BM, p.offsets[g + 1] - row0);
-    return true;
-  }
-  g = 0;
-  row0 = mt * BM;
-  if (row0 >= p.M) return false;
-  rows = min(BM, p.M - row0);
-  return true;
-}
-
-// Workgroup -> (M-tile, N-tile).  Workgroups are dealt round-robin to the 8 XCDs, so workgroup b
-// runs on XCD b % 8 as that XCD's (b / 8)-th workgroup.  Two orders are used; in both, the
-// workgroups without a tile (the worst-case grid's surplus) exit at once.
-//  - quad_nb > 0 (grouped and shared-expert products): each XCD works through blocks of
-//    group_m x quad_nb tiles, about one tile per CU, so the tiles resident on an XCD share
-//    activation rows and weight panels in its L2; see quad_grid for the block order.
-//  - quad_nb == 0 (router): each XCD is given one contiguous range of the logical tile order, in
-//    which group_m M-tiles sweep the N-tiles together.
-constexpr int kXcds = 8;
-
-// XCD blocks of group_m x quad_nb tiles (one block per XCD at a time), ordered in 2 x 2 quads:
-// the four XCDs that run one quad at the same time pair up on M-groups (same activation rows)
-// and on N-blocks (same weight panels), so each line they share is fetched from HBM once and
-// found in the memory-side cache by the other XCD.  Returns the number of workgroups to launch
-// for at most max_mt M-tiles.
-inline int64_t quad_grid(int64_t max_mt, int n_tiles, int group_m, int quad_nb) {
-  const int64_t n_mg = (max_mt + group_m - 1) / group_m, n_nb = (n_tiles + quad_nb - 1) / quad_nb;
-  const int64_t quads = ((n_mg + 1) / 2) * ((n_nb + 1) / 2);
-  const int64_t rounds = (4 * quads + kXcds - 1) / kXcds;
-  return rounds * kXcds * int64_t(group_m) * quad_nb;
-}
-
-__device__ __forceinline__ bool map_tile(const GemmArgs& p, int BM, int& mt, int& nt) {
-  const int total_mt = p.tile_group ? p.tile_start[p.G] : (p.M + BM - 1) / BM;
-  const int b = blockIdx.x;
-  if (p.quad_nb > 0) {
-    const int blk_tiles = p.group_m * p.quad_nb;
-    const int x = b % kXcds, i = b / kXcds;
-    const int blk = (i / blk_tiles) * kXcds + x, pos = i % blk_tiles;
-    const int n_nb = (p.n_tiles + p.quad_nb - 1) / p.quad_nb, nq = (n_nb + 1) / 2;
-    const int quad = blk >> 2;
-    const int mg = 2 * (quad / nq) + (blk & 1), nb = 2 * (quad % nq) + ((blk >> 1) & 1);
-    mt = mg * p.group_m + pos % p.group_m;
-    nt = nb * p.quad_nb + pos / p.group_m;
-    return mt < total_mt && nt < p.n_tiles && nt < (nb + 1) * p.quad_nb;
-  }
-  const int total = total_mt * p.n_tiles;
-  if (b >= total) return false;
-  const int q = total / kXcds, r = total % kXcds, x = b % kXcds, i = b / kXcds;
-  const int L = x * q + min(x, r) + i;
-  const int gsz = p.group_m * p.n_tiles;
-  const int grp = L / gsz, within = L - grp * gsz;
-  const int m_in = min(p.group_m, total_mt - grp * p.group_m);
-  mt = grp * p.group_m + within % m_in;
-  nt = within / m_in;
-  return true;
+int launch_tile_table(const int32_t* offsets, int G, int BM, int max_tiles, int32_t* tile_start,
+                      int32_t* tile_group, hipStream_t s) {
+  ProfScope prof(MOE_K_TILE_TABLE, s);
+  k_tile_table<<<1, 1024, 0, s>>>(offsets, G, BM, max_tiles, tile_start, tile_group);
+  return check_launch("tile table");
 }
 
 // ------------------------------------------------------------------------------------------------
 // bf16 MFMA tile kernel
 // ------------------------------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
-
 // K depth of one LDS stage and the number of stages in the ring.  A stage holds BM + BN rows of
 // BK bf16 values; two stages of BK = 64 or four of BK = 32 fill 128 KB of the 160 KB LDS.
 #ifndef FSM_BK
@@ -165,32 +105,6 @@ constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer descriptor wor
 constexpr int kBK = FSM_BK, kStages = FSM_STAGES;
 static_assert(kBK == 32 || kBK == 64, "BK must be 32 or 64");
 static_assert(kStages >= 2 && kStages <= 5, "2 to 5 LDS stages");
-
-// 16-byte direct-to-LDS buffer load (device pass only; the host pass needs just the launch stubs
-// and never sees the builtin).
-//
-// The LDS address goes through an empty asm statement, so the compiler cannot tie the load to the
-// stage array it fills.  Its own wait-count pass then leaves LDS reads of the other stages alone
-// (it otherwise waits for every stage in flight before reading any one); the kernel waits for the
-// stage it reads itself, with an explicit s_waitcnt and a barrier.
-#if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
-  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
-  asm volatile("" : "+s"(a));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)uintptr_t(a), 16, voff, 0, 0, 0);
-}
-#define FSM_LDS_DMA16(RSRC, LDS, VOFF) lds_dma16((RSRC), (LDS), (VOFF))
-#else
-#define FSM_LDS_DMA16(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
-#endif
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
-// outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
-}
 
 // Physical 16-byte chunk of logical chunk c in LDS tile row r.  Rows are BK * 2 bytes; the XOR
 // makes the eight rows that one ds_read_b128 group of 8 lanes touches cover all 32 banks.
@@ -532,15 +446,6 @@ namespace {
 #ifndef FSM_R
 #define FSM_R 256, 256, 2, 4, 1
 #endif
-// N-tiles per XCD block of the quad order: one XCD runs 32 tiles at a time (one per CU), so a
-// block is group_m x (32 / group_m) tiles, narrowed to a divisor of n_tiles where one is close
-// (7 for the 28 N-tiles of a 7168-wide down product) so that no block is ragged.
-int quad_width(int n_tiles, int group_m) {
-  const int target = 32 / group_m;
-  for (int q = target; q * 2 > target; --q)
-    if (n_tiles % q == 0) return q;
-  return target;
-}
 struct TileCfg { int bm, bn, wm, wn, gm; int bk = kBK; int st = kStages; };
 constexpr TileCfg kP1{FSM_P1}, kP2{FSM_P2}, kR{FSM_R};
 // Groups of a few dozen rows (a decode batch spread over all experts: 32 rows per expert for 1024

@@ -107,6 +107,73 @@ def moe_grouped_swiglu_gathered(X, sorted_src, k: int, group_offsets, W1, W2, W3
                                           dtype_code(X.dtype), N, d, c, _p(Y), _p(ws), ws.numel(), _s(stream)))
 
 
+def moe_mx_quantize(X, codes, scales, stream=None):
+    """MXFP8 of the rows of bf16 X [R, K]: codes [R, K] uint8 (E4M3), scales [R, K/32] uint8 (E8M0)."""
+    if X.dtype != torch.bfloat16:
+        raise TypeError("moe_mx_quantize takes bf16 input")
+    K = X.shape[-1]
+    R = X.numel() // K if K else 0
+    check("moe_mx_quantize", lib.moe_mx_quantize(_p(X), R, K, _p(codes), _p(scales), _s(stream)))
+
+
+def mx_quantized(X, stream=None):
+    """(codes, scales) of bf16 X [..., K], allocated here (quantised along the last dimension)."""
+    codes = torch.empty(X.shape, dtype=torch.uint8, device=X.device)
+    scales = torch.empty(X.shape[:-1] + (X.shape[-1] // 32,), dtype=torch.uint8, device=X.device)
+    moe_mx_quantize(X, codes, scales, stream)
+    return codes, scales
+
+
+def grouped_swiglu_mxfp8_workspace_bytes(N: int, G: int, c: int) -> int:
+    return int(lib.moe_grouped_swiglu_mxfp8_workspace_bytes(N, G, c))
+
+
+def moe_grouped_swiglu_mxfp8(Xq, group_offsets, W1q, W2q, W3q, Y, sorted_src=None, k: int = 1, ws=None,
+                             stream=None):
+    """moe_grouped_swiglu on MXFP8 operands.  Xq and W*q are (codes, scales) pairs; W1/W2 codes
+    [G, c, d], W3 codes [G, d, c]; Y [N, d] bf16.  With sorted_src, grouped row r is Xq row
+    sorted_src[r] // k."""
+    x_rows, d = Xq[0].shape
+    N = Y.shape[0]
+    G = group_offsets.numel() - 1
+    c = W1q[0].shape[-2]
+    if ws is None:
+        ws = workspace(grouped_swiglu_mxfp8_workspace_bytes(N, G, c), Y.device)
+    check("moe_grouped_swiglu_mxfp8",
+          lib.moe_grouped_swiglu_mxfp8(_p(Xq[0]), _p(Xq[1]), x_rows, _p(sorted_src), k, _p(group_offsets), G,
+                                       _p(W1q[0]), _p(W1q[1]), _p(W2q[0]), _p(W2q[1]), _p(W3q[0]), _p(W3q[1]), N,
+                                       d, c, _p(Y), _p(ws), ws.numel(), _s(stream)))
+
+
+def grouped_mxfp8_phase_workspace_bytes(N: int, G: int) -> int:
+    return int(lib.moe_grouped_mxfp8_phase_workspace_bytes(N, G))
+
+
+def moe_grouped_mxfp8_gate_up(Xq, group_offsets, W1q, W2q, H, sorted_src=None, k: int = 1, ws=None, stream=None):
+    """Phase 1 alone: H = (codes [N, c], scales [N, c/32]) of (X W1^T) . SiLU(X W2^T) per group."""
+    x_rows, d = Xq[0].shape
+    N, c = H[0].shape
+    G = group_offsets.numel() - 1
+    if ws is None:
+        ws = workspace(grouped_mxfp8_phase_workspace_bytes(N, G), H[0].device)
+    check("moe_grouped_mxfp8_gate_up",
+          lib.moe_grouped_mxfp8_gate_up(_p(Xq[0]), _p(Xq[1]), x_rows, _p(sorted_src), k, _p(group_offsets), G,
+                                        _p(W1q[0]), _p(W1q[1]), _p(W2q[0]), _p(W2q[1]), N, d, c, _p(H[0]), _p(H[1]),
+                                        _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_grouped_mxfp8_down(H, group_offsets, W3q, Y, ws=None, stream=None):
+    """Phase 2 alone: Y [N, d] bf16 = H W3[g]^T per group, H = (codes, scales)."""
+    N, c = H[0].shape
+    d = Y.shape[1]
+    G = group_offsets.numel() - 1
+    if ws is None:
+        ws = workspace(grouped_mxfp8_phase_workspace_bytes(N, G), Y.device)
+    check("moe_grouped_mxfp8_down",
+          lib.moe_grouped_mxfp8_down(_p(H[0]), _p(H[1]), _p(group_offsets), G, _p(W3q[0]), _p(W3q[1]), N, c, d,
+                                     _p(Y), _p(ws), ws.numel(), _s(stream)))
+
+
 def moe_combine(Y, topk_w, dest_row, out, addend=None, residual=None, out_x=None, stream=None):
     """out = residual + addend + sum_i topk_w[:, i] * Y[dest_row[t*k+i]]  (fp32)."""
     T, k = topk_w.shape

@@ -116,6 +116,31 @@ def normal(shape, std: float, seed: int, device="cpu", dtype=torch.float32) -> t
     return x if dtype == torch.float32 else x.to(dtype)
 
 
+def block_scaled_normal(shape, std: float, seed: int, device="cpu", dtype=torch.bfloat16, spread: int = 4,
+                        block: int = 32) -> torch.Tensor:
+    """normal(shape, std) with each run of `block` consecutive elements along the last dimension
+    multiplied by its own power of two 2^j, j uniform in [-spread, spread] (blocks whose magnitudes
+    differ, as the rows of a block-scaled format see them)."""
+    x = normal(shape, std, seed, device, torch.float32)
+    nb = shape[-1] // block
+    j = torch.randint(-spread, spread + 1, tuple(shape[:-1]) + (nb, 1), generator=_gen(seed + 1, device),
+                      device=device)
+    x = (x.view(*shape[:-1], nb, block) * torch.exp2(j.to(torch.float32))).view(shape)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def mx_random_codes(rows: int, cols: int, seed: int, device="cpu", scale_lo: int = 120, scale_hi: int = 134):
+    """A random MXFP8 tensor: E4M3 codes uniform over the 254 finite codes [rows, cols] uint8 and
+    E8M0 scale bytes uniform in [scale_lo, scale_hi] [rows, cols / 32] (inputs for a product whose
+    operands are already quantised)."""
+    g = _gen(seed, device)
+    r = torch.randint(0, 254, (rows, cols), generator=g, device=device, dtype=torch.int32)
+    codes = (r + (r >= 0x7F).to(torch.int32)).to(torch.uint8)      # skips the NaN codes 0x7F and 0xFF
+    scales = torch.randint(scale_lo, scale_hi + 1, (rows, cols // 32), generator=g, device=device,
+                           dtype=torch.int32).to(torch.uint8)
+    return codes, scales
+
+
 def activations(cfg: MoEConfig, device="cpu", T: Optional[int] = None, layer: int = 0,
                 dtype=None) -> torch.Tensor:
     """Token activations A (or the stack input o_0) [T, d] ~ N(0,1), in the workload dtype."""

@@ -97,20 +97,32 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def mlp_mxfp8(X, W1q, W2q, W3q, hidden_store=None):
-    """The expert MLP of section 2.1 (H = (X W1^T) . SiLU(X W2^T), Y = H W3^T) with MXFP8 operands:
-    X is quantised along d, the weights are given quantised ((codes, scales) pairs, W1/W2 along d,
-    W3 along c), and H is quantised along c before the second product.  The products and SiLU are
-    exact float64 on the dequantised values.  hidden_store (optional) rounds H to the precision an
-    implementation forms it in before H is quantised (the decision of each H code is then taken in
-    that precision)."""
+def swiglu_hidden_mxfp8(X, W1q, W2q, hidden_store=None):
+    """The first half of the expert MLP of section 2.1 with MXFP8 operands: H = (X W1^T) . SiLU(X W2^T)
+    with X quantised along d and W1 / W2 given quantised ((codes, scales) pairs along d), the
+    products and SiLU exact in float64; returns H quantised along c as (codes, scales).
+    hidden_store (optional) rounds H to the precision an implementation forms it in before H is
+    quantised (each H code is then decided in that precision)."""
     Xd = mx_dequantize(*mx_quantize(X))
     U = Xd @ mx_dequantize(*W1q).T
     G = Xd @ mx_dequantize(*W2q).T
     H = U * silu(G)
     if hidden_store is not None:
         H = hidden_store(H)
-    return mx_dequantize(*mx_quantize(H)) @ mx_dequantize(*W3q).T
+    return mx_quantize(H)
+
+
+def mx_matmul(Aq, Bq):
+    """A B^T exact in float64 for MXFP8 operands given as (codes, scales) pairs, both quantised
+    along the shared dimension."""
+    return mx_dequantize(*Aq) @ mx_dequantize(*Bq).T
+
+
+def mlp_mxfp8(X, W1q, W2q, W3q, hidden_store=None):
+    """The expert MLP of section 2.1 (H = (X W1^T) . SiLU(X W2^T), Y = H W3^T) with MXFP8 operands:
+    H from swiglu_hidden_mxfp8 (quantised along c), then Y = mx_matmul(H, W3) (W3 given quantised
+    along c)."""
+    return mx_matmul(swiglu_hidden_mxfp8(X, W1q, W2q, hidden_store), W3q)
 
 
 def grouped_mlp_mxfp8(X, offsets, W1q, W2q, W3q, hidden_store=None):
