@@ -124,8 +124,11 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   static_assert(EPI != MX_SWIGLU || (WTN / 2) == 32, "a wave's H columns of a row must be one MX block");
   static_assert(BM + BN == 64 * NW, "one scale row per lane");
 
-  __shared__ __attribute__((aligned(16))) uint8_t d0[DATA], d1[DATA];
-  __shared__ __attribute__((aligned(16))) uint8_t c0[SCL], c1[SCL];
+  // one LDS array per stage (data rows, then their scale bytes): separate objects let the compiler
+  // see that the loads filling one stage never alias the reads of the other
+  constexpr int STAGE = DATA + SCL;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE], st1[STAGE];
+#define MX_SM(BUF) ((BUF) ? st1 : st0)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -187,11 +190,15 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   }
 
   // fragment reads: A rows (wm * WTM + 16 i + lane % 16), B rows likewise; lane group q = lane / 16
-  // takes the 16-byte chunks q and q + 4 of its row (K 16q .. and 64 + 16q ..), swizzled by row & 7
+  // takes the 16-byte chunks q and q + 4 of its row (K 16q .. and 64 + 16q ..), swizzled by row & 7,
+  // and the scale byte of K block q.  Per-lane bases; the row-block terms are constants that fold
+  // into the reads' immediate offsets.
   const int q = lane >> 4, sw = lane & 7;
   const int ch_lo = (q ^ sw) << 4, ch_hi = ((q + 4) ^ sw) << 4;
   const int fa0 = wm * WTM + (lane & 15);
   const int fb0 = BM + (EPI == MX_SWIGLU ? wn * (WTN / 2) : wn * WTN) + (lane & 15);
+  const int a_lo = fa0 * RB + ch_lo, a_hi = fa0 * RB + ch_hi, a_sc = DATA + fa0 * 4 + q;
+  const int b_lo = fb0 * RB + ch_lo, b_hi = fb0 * RB + ch_hi, b_sc = DATA + fb0 * 4 + q;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -201,47 +208,51 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
 
   uint32_t kb_zero;   // opaque zero: every load's voffset is a fresh register (see the bf16 kernel)
   asm volatile("s_mov_b32 %0, 0" : "=s"(kb_zero));
-#define MX_DATA(BUF) ((BUF) ? d1 : d0)
-#define MX_SCL(BUF) ((BUF) ? c1 : c0)
 #define MX_STAGE(KT, BUF)                                                                       \
   {                                                                                             \
     const uint32_t kb = uint32_t(KT) * RB + kb_zero;                                            \
     _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                          \
-      FSM_LDS_DMA16(rA, &MX_DATA(BUF)[(wave * A_RUNS + i) * RUN_ROWS * RB], dA[i] + kb);         \
+      FSM_LDS_DMA16(rA, &MX_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * RB], dA[i] + kb); \
     _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                          \
-      FSM_LDS_DMA16(rB, &MX_DATA(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb);          \
-    FSM_LDS_DMA4(rS, &MX_SCL(BUF)[wave * 64 * 4], dS + uint32_t(KT) * 4u + kb_zero);             \
+      FSM_LDS_DMA16(rB, &MX_SM(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb);  \
+    FSM_LDS_DMA4(rS, &MX_SM(BUF)[DATA + wave * 64 * 4], dS + uint32_t(KT) * 4u + kb_zero); \
   }
 #define MX_BROW(J) \
   ((EPI == MX_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
-#define MX_FRAG(BUF, ROW, OUT)                                                                  \
+#define MX_LD16(BUF, OFF) (*reinterpret_cast<const uint4*>(&MX_SM(BUF)[(OFF)]))
+#define MX_FRAG(BUF, LO, HI, OUT)                                                               \
   {                                                                                             \
-    const uint4 lo = *reinterpret_cast<const uint4*>(&MX_DATA(BUF)[(ROW) * RB + ch_lo]);         \
-    const uint4 hi = *reinterpret_cast<const uint4*>(&MX_DATA(BUF)[(ROW) * RB + ch_hi]);         \
-    OUT = mx_v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)}; \
+    const uint4 lo_ = MX_LD16(BUF, LO), hi_ = MX_LD16(BUF, HI);                                 \
+    OUT = mx_v8i{int(lo_.x), int(lo_.y), int(lo_.z), int(lo_.w), int(hi_.x), int(hi_.y), int(hi_.z), int(hi_.w)}; \
   }
-#define MX_SCALE(BUF, ROW) \
-  int((*reinterpret_cast<const uint32_t*>(&MX_SCL(BUF)[(ROW) * 4]) >> (8 * q)) & 0xFFu)
-  // one stage: B fragments and scales first, then per A row block the next block's fragment is
-  // read under the current block's FN MFMAs
+#define MX_FRAG_A(BUF, I, OUT) MX_FRAG(BUF, a_lo + (I) * 16 * RB, a_hi + (I) * 16 * RB, OUT)
+#define MX_FRAG_B(BUF, J, OUT) MX_FRAG(BUF, b_lo + MX_BROW(J) * RB, b_hi + MX_BROW(J) * RB, OUT)
+#define MX_SC_A(BUF, I) int(MX_SM(BUF)[a_sc + (I) * 64])
+#define MX_SC_B(BUF, J) int(MX_SM(BUF)[b_sc + MX_BROW(J) * 4])
+  // one stage: the B fragments and their scales, then per A row block the next block's fragment
+  // and scale are read before the current block's FN MFMAs; scheduling groups pin that order so
+  // an LDS read is always in flight under FN MFMAs
 #define MX_COMPUTE(BUF)                                                                         \
   {                                                                                             \
     mx_v8i bf[FN], a_cur, a_nxt;                                                                \
     int bsc[FN], as_cur, as_nxt;                                                                \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                            \
-      MX_FRAG(BUF, fb0 + MX_BROW(j), bf[j]);                                                    \
-      bsc[j] = MX_SCALE(BUF, fb0 + MX_BROW(j));                                                 \
+      MX_FRAG_B(BUF, j, bf[j]);                                                                 \
+      bsc[j] = MX_SC_B(BUF, j);                                                                 \
     }                                                                                           \
-    MX_FRAG(BUF, fa0, a_cur);                                                                   \
-    as_cur = MX_SCALE(BUF, fa0);                                                                \
+    MX_FRAG_A(BUF, 0, a_cur);                                                                   \
+    as_cur = MX_SC_A(BUF, 0);                                                                   \
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * FN + 3, 0);                                 \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                            \
       if (i + 1 < FM) {                                                                         \
-        MX_FRAG(BUF, fa0 + (i + 1) * 16, a_nxt);                                                \
-        as_nxt = MX_SCALE(BUF, fa0 + (i + 1) * 16);                                             \
+        MX_FRAG_A(BUF, i + 1, a_nxt);                                                           \
+        as_nxt = MX_SC_A(BUF, i + 1);                                                           \
       }                                                                                         \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                            \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], a_cur, acc[i][j], 0, 0, 0, \
                                                                      bsc[j], 0, as_cur);        \
+      if (i + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                       \
       a_cur = a_nxt;                                                                            \
       as_cur = as_nxt;                                                                          \
     }                                                                                           \
@@ -257,7 +268,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   MX_STAGE(0, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   MX_BARRIER();
-  for (int kt = 0;;) {   // two stages, unrolled by two so each half names its buffers
+  for (int kt = 0;;) {   // two stages, unrolled by two so each half names its buffer
     if (kt + 1 < KT) MX_STAGE(kt + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     MX_COMPUTE(0);
@@ -274,12 +285,15 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
     MX_BARRIER();
   }
   (void)LOADS;
-#undef MX_DATA
-#undef MX_SCL
+#undef MX_SM
 #undef MX_STAGE
 #undef MX_BROW
+#undef MX_LD16
 #undef MX_FRAG
-#undef MX_SCALE
+#undef MX_FRAG_A
+#undef MX_FRAG_B
+#undef MX_SC_A
+#undef MX_SC_B
 #undef MX_COMPUTE
 #undef MX_BARRIER
 
