@@ -208,3 +208,63 @@ def test_planted_mistake_is_caught(i, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught > 0, f"no pin caught the planted mistake {bad.__name__}"
+
+
+# ---- backward oracle --------------------------------------------------------------------------
+import oracle.moe_backward as ob  # noqa: E402
+from tests import test_oracle_backward_pins as bpins  # noqa: E402
+
+BWD_ORIG = {n: getattr(ob, n) for n in ("silu_grad", "gate_backward", "mlp_backward", "unpermute_sum",
+                                        "router_backward", "combine_backward")}
+
+
+def _silu_grad_sigmoid_only(g):
+    return 1.0 / (1.0 + np.exp(-np.asarray(g, np.float64)))
+
+
+def _gate_backward_no_renorm_term(logits, topk_idx, dw, gate, renormalize):
+    return BWD_ORIG["gate_backward"](logits, topk_idx, dw, gate, False)
+
+
+def _mlp_backward_dw3_from_u(X, W1, W2, W3, dY, store=None):
+    dX, dW1, dW2, dW3 = BWD_ORIG["mlp_backward"](X, W1, W2, W3, dY, store)
+    U = np.asarray(X, np.float64) @ np.asarray(W1, np.float64).T
+    return dX, dW1, dW2, np.asarray(dY, np.float64).T @ U
+
+
+def _unpermute_by_sorted_src(dXp, dest_row, k):
+    inv = np.empty_like(np.asarray(dest_row))
+    inv[np.asarray(dest_row)] = np.arange(len(dest_row))
+    return BWD_ORIG["unpermute_sum"](dXp, inv, k)
+
+
+def _router_backward_no_input_gradient(A, W_R, dlogits, store=None):
+    dA, dW_R, db = BWD_ORIG["router_backward"](A, W_R, dlogits, store)
+    return np.zeros_like(dA), dW_R, db
+
+
+def _combine_backward_unweighted(dOut, Y, topk_w, dest_row):
+    return BWD_ORIG["combine_backward"](dOut, Y, np.ones_like(np.asarray(topk_w, np.float64)), dest_row)
+
+
+def _fd_cases():
+    bpins.test_gradients_match_finite_differences("softmax", True, 2)
+    bpins.test_gradients_match_finite_differences("sigmoid", True, 2)
+
+
+BWD_CASES = [
+    ("silu_grad", _silu_grad_sigmoid_only),
+    ("gate_backward", _gate_backward_no_renorm_term),
+    ("mlp_backward", _mlp_backward_dw3_from_u),
+    ("unpermute_sum", _unpermute_by_sorted_src),
+    ("router_backward", _router_backward_no_input_gradient),
+    ("combine_backward", _combine_backward_unweighted),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BWD_CASES)), ids=[c[1].__name__.lstrip("_") for c in BWD_CASES])
+def test_planted_backward_mistake_is_caught(i, monkeypatch):
+    name, bad = BWD_CASES[i]
+    monkeypatch.setattr(ob, name, bad)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _fd_cases()
