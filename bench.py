@@ -50,6 +50,8 @@ def parse():
                    help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
     p.add_argument("--mxfp8", type=int, default=1,
                    help="after the steps, time the layer-0 routed experts with MXFP8 operands; 0 = skip")
+    p.add_argument("--backward", type=int, default=1,
+                   help="after the steps, time the backward pass of layer 0 (one MoE sublayer); 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                    help="before the steps, one plain device copy of this many GiB (a known-size kernel whose "
                         "FETCH_SIZE / WRITE_SIZE calibrate the HBM counters); 0 = skip")
@@ -225,6 +227,78 @@ def mxfp8(c, layers, o0, reps: int = 3) -> dict:
     out["routed_experts_ms"] = round(ms, 3)
     out["routed_experts_tflops"] = round(6.0 * N * d * cc / (ms * 1e-3) / 1e12, 1)
     del W1q, W2q, W3q, ws, Y
+    return out
+
+
+def backward(c, layers, o0, reps: int = 2) -> dict:
+    """Layer 0's backward pass (moe_layer_backward) for a random output gradient, after its forward
+    (router, permutation, gathered grouped product) on the same input.  Per kind of kernel: the
+    summed time per call and, for the products, the algorithmic FLOP of that kind per call over it
+    (bf16 MFMA peak).  Kinds: U and G recomputed; the activation-gradient products (dH = dY W3,
+    dX = [dU | dG] [W1; W2], the router's dlogits W_R); the weight-gradient products (reductions
+    over each expert's rows); transposes; pointwise kernels."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    T, d, E, k, cc, cs = c.T, c.d, c.E, c.k, c.c, c.shared_width
+    N = T * k
+    W = layers[0]
+    x = o0.to(torch.bfloat16)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    src = torch.empty((N,), dtype=torch.int32, device=dev)
+    dest = torch.empty((N,), dtype=torch.int32, device=dev)
+    Y = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    ops.moe_route(x, W["W_R"], k, c.gate, c.renormalize, logits, idx, w, bias=W.get("bias"))
+    ops.moe_permute(idx, E, off, src, dest)
+    ops.moe_grouped_swiglu_gathered(x, src, k, off, W["W1"], W["W2"], W["W3"], Y)
+    dOut = torch.randn((T, d), device=dev) * 0.01
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    grads = {"dA": f32(T, d), "dW_R": f32(E, d), "dW1": f32(E, cc, d), "dW2": f32(E, cc, d), "dW3": f32(E, d, cc)}
+    if cs:
+        grads.update(dWs1=f32(cs, d), dWs2=f32(cs, d), dWs3=f32(d, cs))
+    cfg = ops.stack_cfg(T, d, cc, cs, E, k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.layer_backward_workspace_bytes(cfg), dev)
+    log(f"backward workspace {ws.numel() / 2**30:.1f} GiB, HBM in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def call():
+        ops.moe_layer_backward(W, cfg, x, logits, idx, w, off, src, dest, Y, dOut, grads, ws=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    ops.profile_enable(False)
+    prof = ops.profile_collect()
+    assert all(torch.isfinite(g).all().item() for g in grads.values()), "non-finite gradients"
+    Ep = -(-E // 64) * 64
+    flop = {"bwd_recompute": 4.0 * N * d * cc + 4.0 * T * d * cs,
+            "bwd_dgrad": 6.0 * N * d * cc + 2.0 * T * Ep * d + 6.0 * T * d * cs,
+            "bwd_wgrad": 6.0 * N * d * cc + 2.0 * E * d * T + 6.0 * T * d * cs}
+    out = {"ms_per_layer": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    total_flop = sum(flop.values())
+    out["tflops_overall"] = round(total_flop / (ms * 1e-3) / 1e12, 1)
+    kinds = {}
+    for kind in ("bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise", "tile_table", "combine"):
+        n, t = prof.get(kind, (0, 0.0))
+        if n == 0:
+            continue
+        row = {"launches_per_call": n // reps, "ms_per_call": round(t / reps, 3)}
+        if kind in flop:
+            row["tflops"] = round(flop[kind] / (t / reps * 1e-3) / 1e12, 1)
+            row["frac_mfma_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+        kinds[kind] = row
+    out["kernels"] = kinds
+    del grads, ws, Y
+    torch.cuda.empty_cache()
     return out
 
 
@@ -434,6 +508,11 @@ def main():
     if args.mxfp8 and c.name == "dsv3-stack":
         log("timing the MXFP8 routed experts")
         result["mxfp8"] = mxfp8(c, layers, o0)
+    if args.backward and c.name == "dsv3-stack":
+        del ws
+        torch.cuda.empty_cache()
+        log("timing the backward pass of one layer")
+        result["backward"] = backward(c, layers, o0)
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = standalone(c, layers, o0)

@@ -264,6 +264,49 @@ int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_s
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
 
 /*
+ * moe_layer_backward -- the backward pass of one MoE sublayer: the gradients of its output
+ * out = S(A) + R(A) (section 2.1: router G(A) = s(A W_R^T) + b, the modern MLP per expert,
+ * Dispatch, Combine with the gate weights, and the shared experts S) with respect to the input A
+ * and every weight, given dOut = dLoss/dout.  The chain rule of the forward, in reverse; the top-k
+ * choice itself passes no gradient (only the selected experts' weights do).  The page's training
+ * schedule (section 4.1) runs this pass for every MoE layer; this call is one GPU's share.
+ *
+ *   W            host pointer: the layer's weights (as for farskip_stack_forward)
+ *   cfg          host pointer: T, d, c, c_shared, E, k, gate, renormalize; dtype must be MOE_BF16
+ *   A            [T, d] bf16        the layer input of the forward
+ *   logits       [T, E] float32     the forward's router logits (bias included)
+ *   topk_idx, topk_w                the forward's selection and gate weights ([T, k])
+ *   expert_offsets, sorted_src, dest_row   the forward's permutation (moe_permute)
+ *   Y            [T*k, d] bf16      the forward's routed expert outputs (grouped row order)
+ *   dOut         [T, d] float32     gradient of the loss with respect to out
+ *   grads        host pointer to OUTPUT device pointers, all float32, overwritten:
+ *                  dA [T, d] (the residual's own pass-through is not included), dW_R [E, d],
+ *                  dbias [E] (or NULL: not computed), dW1, dW2 [E, c, d], dW3 [E, d, c], and
+ *                  with c_shared > 0 dWs1, dWs2 [c_shared, d], dWs3 [d, c_shared]
+ *   ws, ws_bytes scratch of at least moe_layer_backward_workspace_bytes(cfg) bytes
+ * Intermediates (dY, the recomputed U and G, H, dH, dU, dG, dX and the router's dlogits) are kept
+ * in bf16 and every product accumulates in fp32.
+ * Limits: bf16 only; d, c and c_shared multiples of 64; E a multiple of 8; T * d * 2 < 2^31.
+ */
+typedef struct {
+  float* dA;
+  float* dW_R;
+  float* dbias;
+  float* dW1;
+  float* dW2;
+  float* dW3;
+  float* dWs1;
+  float* dWs2;
+  float* dWs3;
+} moe_layer_grads_t;
+
+int moe_layer_backward(const moe_layer_desc_t* W, const moe_stack_cfg_t* cfg, const void* A, const float* logits,
+                       const int32_t* topk_idx, const float* topk_w, const int32_t* expert_offsets,
+                       const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
+                       const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream);
+size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg);
+
+/*
  * Kernel timing for measurement harnesses.  While enabled (process-wide), every kernel the
  * library launches is bracketed by two timing hipEvents recorded on the stream it is launched on.
  * moe_profile_collect waits for the recorded events, returns per-kind launch counts and summed
@@ -286,7 +329,12 @@ typedef enum {
   MOE_K_MX_QUANTIZE = 11, /* MXFP8 quantisation of rows */
   MOE_K_MX_GATE_UP = 12,  /* MXFP8 grouped product, phase 1 (with H quantised in its epilogue) */
   MOE_K_MX_DOWN = 13,     /* MXFP8 grouped product, phase 2 */
-  MOE_KERNEL_KINDS = 14
+  MOE_K_BWD_RECOMPUTE = 14, /* backward: U and G recomputed (routed and shared) */
+  MOE_K_BWD_DGRAD = 15,   /* backward: products giving activation gradients (dH, dX, router dA) */
+  MOE_K_BWD_WGRAD = 16,   /* backward: weight-gradient products (reduction over rows) */
+  MOE_K_TRANSPOSE = 17,   /* backward: weight and activation transposes */
+  MOE_K_BWD_POINTWISE = 18, /* backward: combine, gate, SwiGLU and bias-sum kernels */
+  MOE_KERNEL_KINDS = 19
 } moe_kernel_kind_t;
 
 typedef struct {

@@ -18,12 +18,13 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK = 1024, 32
 EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_swiglu",
            "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu_gathered", "moe_mx_quantize",
            "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
-           "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_combine", "farskip_stack_forward",
+           "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
+           "moe_layer_backward_workspace_bytes", "moe_combine", "farskip_stack_forward",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect", "moe_last_error",
            "moe_version")
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
                 "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
-                "mx_down")
+                "mx_down", "bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise")
 
 
 class LayerDesc(ctypes.Structure):
@@ -36,6 +37,10 @@ class StackCfg(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("c", ctypes.c_int64),
                 ("c_shared", ctypes.c_int64), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dA", "dW_R", "dbias", "dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3")]
 
 
 class KernelTime(ctypes.Structure):
@@ -77,6 +82,11 @@ def _declare(lib):
     lib.moe_grouped_mxfp8_down.restype = i
     lib.moe_grouped_mxfp8_phase_workspace_bytes.argtypes = [i64, i32]
     lib.moe_grouped_mxfp8_phase_workspace_bytes.restype = sz
+    lib.moe_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(StackCfg), vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, ctypes.POINTER(LayerGrads), vp, sz, vp]
+    lib.moe_layer_backward.restype = i
+    lib.moe_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
+    lib.moe_layer_backward_workspace_bytes.restype = sz
     lib.moe_combine.argtypes = [vp, i, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.moe_combine.restype = i
     lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,

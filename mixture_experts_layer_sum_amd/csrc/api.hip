@@ -502,6 +502,46 @@ int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_s
   return stack_forward(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side));
 }
 
+size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg) {
+  if (!cfg || cfg->T < 1 || cfg->d < 1 || cfg->c < 1 || cfg->E < 1 || cfg->k < 1 || cfg->c_shared < 0) return 0;
+  return layer_bwd_ws_bytes(*cfg);
+}
+
+int moe_layer_backward(const moe_layer_desc_t* W, const moe_stack_cfg_t* cfg, const void* A, const float* logits,
+                       const int32_t* topk_idx, const float* topk_w, const int32_t* expert_offsets,
+                       const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
+                       const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  const char* who = "moe_layer_backward";
+  if (!W || !cfg || !grads) return fail(MOE_ERR_INVALID_ARG, "%s: W, cfg and grads are required", who);
+  const moe_stack_cfg_t& c = *cfg;
+  if (c.T < 1 || c.T > kMaxRows || c.d < 1 || c.c < 1 || c.E < 1 || c.k < 1 || c.c_shared < 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: sizes must be positive", who);
+  if (c.k > c.E) return fail(MOE_ERR_INVALID_ARG, "%s: k=%d > E=%d", who, c.k, c.E);
+  if (c.E > MOE_MAX_EXPERTS || c.k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E or k beyond the limits", who);
+  if (c.gate != MOE_GATE_SOFTMAX && c.gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown gate %d", who, c.gate);
+  if (c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: only bf16 is implemented", who);
+  if (c.d % 64 || c.c % 64 || c.c_shared % 64 || c.E % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: needs d, c, c_shared multiples of 64 and E a multiple of 8", who);
+  if (c.T * c.k > kMaxRows || c.T * c.d * 2 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k or T*d too large", who);
+  if (!A || !logits || !topk_idx || !topk_w || !expert_offsets || !sorted_src || !dest_row || !Y || !dOut)
+    return fail(MOE_ERR_INVALID_ARG, "%s: forward tensors and dOut are required", who);
+  if (!W->W_R || !W->W1 || !W->W2 || !W->W3) return fail(MOE_ERR_INVALID_ARG, "%s: routed weights are required", who);
+  if (c.c_shared > 0 && (!W->Ws1 || !W->Ws2 || !W->Ws3))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shared weights are required with c_shared > 0", who);
+  if (!grads->dA || !grads->dW_R || !grads->dW1 || !grads->dW2 || !grads->dW3)
+    return fail(MOE_ERR_INVALID_ARG, "%s: dA, dW_R, dW1, dW2 and dW3 are required", who);
+  if (c.c_shared > 0 && (!grads->dWs1 || !grads->dWs2 || !grads->dWs3))
+    return fail(MOE_ERR_INVALID_ARG, "%s: dWs1, dWs2 and dWs3 are required with c_shared > 0", who);
+  const size_t need = layer_bwd_ws_bytes(c);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  return launch_layer_backward(*W, c, A, logits, topk_idx, topk_w, expert_offsets, sorted_src, dest_row, Y, dOut,
+                               *grads, ws, as_stream(stream));
+}
+
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 const char* moe_version(void) { return "farskip_moe 0.1 (gfx950)"; }

@@ -1,0 +1,612 @@
+// Backward pass of one MoE sublayer (bf16 storage, fp32 accumulation).
+//
+// The gradients of out = S(A) + R(A) ("FarSkip-Collective" section 2.1: the router, the modern MLP,
+// Dispatch and Combine, the shared expert) with respect to A and every weight: the chain rule of
+// the forward, in reverse.  The three products that give activation gradients (dH = dY W3,
+// dX = [dU | dG] [W1; W2], and the router's dlogits W_R) run on the forward's grouped bf16 kernel
+// against weights transposed once per call; U and G are recomputed by that kernel's gate/up loads
+// (nothing of the forward beyond its outputs is kept).  The weight gradients are products whose
+// reduction runs over each expert's rows: the operands are transposed into K-contiguous rows,
+// each expert's rows padded to a multiple of 64 with zeros, and k_gemm_kgroup sums one expert's
+// segment per output tile.
+//
+//   k_combine_bwd    dY[dest_row[t,i]] = w[t,i] dOut[t] (bf16), dw[t,i] = <dOut[t], Y[dest_row[t,i]]>
+//   k_gate_bwd       dlogits from dw through the softmax / sigmoid (and renormalisation) Jacobian
+//   k_col_partial    per-expert sums of dlogits (the bias gradient), in two deterministic passes
+//   k_swiglu_bwd     dU = dH SiLU(G), dG = dH U SiLU'(G), and H = U SiLU(G) for dW3
+//   k_transpose      64 x 64 tiles through LDS, optionally gathering rows and padding segments
+//   k_gemm_kgroup    C_g = A[:, seg_g] B[:, seg_g]^T in fp32, per group g of K segments
+#include "common.h"
+#include "tile_kit.h"
+
+namespace fsm {
+
+namespace {
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+}  // namespace
+
+// ---- Combine backward: one workgroup per token ---------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine_bwd(const float* __restrict__ dOut, const uint16_t* __restrict__ Y,
+                                                     const float* __restrict__ w, const int32_t* __restrict__ dest,
+                                                     int32_t d, int32_t k, uint16_t* __restrict__ dY,
+                                                     float* __restrict__ dw, uint16_t* __restrict__ dOut_b) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const float* g = dOut + t * d;
+  for (int i = 0; i < k; ++i) {
+    const int64_t r = dest[t * k + i];
+    const float wi = w[t * k + i];
+    float part = 0.f;
+    for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
+      const float4 g0 = *reinterpret_cast<const float4*>(g + col), g1 = *reinterpret_cast<const float4*>(g + col + 4);
+      float y[8];
+      unpack8(*reinterpret_cast<const uint4*>(Y + r * d + col), y);
+      part += g0.x * y[0] + g0.y * y[1] + g0.z * y[2] + g0.w * y[3] + g1.x * y[4] + g1.y * y[5] + g1.z * y[6] +
+              g1.w * y[7];
+      uint4 o;
+      o.x = pack2(wi * g0.x, wi * g0.y);
+      o.y = pack2(wi * g0.z, wi * g0.w);
+      o.z = pack2(wi * g1.x, wi * g1.y);
+      o.w = pack2(wi * g1.z, wi * g1.w);
+      *reinterpret_cast<uint4*>(dY + r * d + col) = o;
+    }
+    const float s = block_sum_256(part, red);
+    if (threadIdx.x == 0) dw[t * k + i] = s;
+  }
+  if (dOut_b) {
+    for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
+      const float4 g0 = *reinterpret_cast<const float4*>(g + col), g1 = *reinterpret_cast<const float4*>(g + col + 4);
+      *reinterpret_cast<uint4*>(dOut_b + t * d + col) =
+          make_uint4(pack2(g0.x, g0.y), pack2(g0.z, g0.w), pack2(g1.x, g1.y), pack2(g1.z, g1.w));
+    }
+  }
+}
+
+// ---- gate backward: one wave per token ----------------------------------------------------------
+// p = softmax(L) over all E (or sigmoid(L)); w_i = p[e_i] (/ P, P = sum of the selected p, when
+// renormalising).  dp at the selected experts: dw_i, or (dw_i - sum_m dw_m w_m) / P; then
+// softmax: dL_j = p_j (dp_j - sum_a dp_a p_a); sigmoid: dL_j = dp_j p_j (1 - p_j).
+__global__ __launch_bounds__(256) void k_gate_bwd(const float* __restrict__ logits, const int32_t* __restrict__ idx,
+                                                  const float* __restrict__ dw, int64_t T, int32_t E, int32_t k,
+                                                  int gate, int renorm, float* __restrict__ dL,
+                                                  uint16_t* __restrict__ dL_b, int32_t ld_b) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* L = logits + t * E;
+  float m = -INFINITY, s = 0.f;
+  if (gate == MOE_GATE_SOFTMAX) {
+    for (int j = lane; j < E; j += 64) m = fmaxf(m, L[j]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    for (int j = lane; j < E; j += 64) s += expf(L[j] - m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  }
+  auto score = [&](float l) { return gate == MOE_GATE_SOFTMAX ? expf(l - m) / s : 1.f / (1.f + expf(-l)); };
+  // per-token scalars over the k selected experts (every lane computes them)
+  float P = 0.f, S = 0.f;
+  for (int i = 0; i < k; ++i) P += score(L[idx[t * k + i]]);
+  for (int i = 0; i < k; ++i) S += dw[t * k + i] * (score(L[idx[t * k + i]]) / P);
+  float D = 0.f;   // sum_a dp_a p_a (softmax)
+  for (int i = 0; i < k; ++i) {
+    const float ps = score(L[idx[t * k + i]]);
+    const float dps = renorm ? (dw[t * k + i] - S) / P : dw[t * k + i];
+    D += dps * ps;
+  }
+  for (int j = lane; j < E; j += 64) {
+    float dp = 0.f;
+    for (int i = 0; i < k; ++i)
+      if (idx[t * k + i] == j) dp = renorm ? (dw[t * k + i] - S) / P : dw[t * k + i];
+    const float p = score(L[j]);
+    const float g = gate == MOE_GATE_SOFTMAX ? p * (dp - D) : dp * p * (1.f - p);
+    dL[t * E + j] = g;
+    dL_b[t * ld_b + j] = f2bf(g);
+  }
+  for (int j = E + lane; j < ld_b; j += 64) dL_b[t * ld_b + j] = 0;
+}
+
+// ---- column sums of dlogits (bias gradient): partial sums over row chunks, then their sum --------
+__global__ __launch_bounds__(256) void k_col_partial(const float* __restrict__ X, int64_t R, int32_t C,
+                                                     int64_t rows_per_chunk, float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
+  const int64_t r0 = int64_t(blockIdx.y) * rows_per_chunk, r1 = min(R, r0 + rows_per_chunk);
+  float acc = 0.f;
+  if (col < C)
+    for (int64_t r = r0 + rg; r < r1; r += 4) acc += X[r * C + col];
+  red[rg][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (rg == 0 && col < C)
+    part[int64_t(blockIdx.y) * C + col] = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void k_col_final(const float* __restrict__ part, int32_t chunks, int32_t C,
+                                                   float* __restrict__ out) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  float acc = 0.f;
+  for (int c = 0; c < chunks; ++c) acc += part[int64_t(c) * C + col];
+  out[col] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ x, int64_t n, float v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
+// ---- SwiGLU backward: 8 columns per thread ---------------------------------------------------------
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t* __restrict__ dH, const uint16_t* __restrict__ UG,
+                                                    int64_t rows, int32_t c, uint16_t* __restrict__ DUG,
+                                                    uint16_t* __restrict__ H) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;   // chunk of 8 columns
+  const int64_t cpr = c / 8;
+  if (i >= rows * cpr) return;
+  const int64_t r = i / cpr, col = (i - r * cpr) * 8;
+  float dh[8], u[8], g[8];
+  unpack8(*reinterpret_cast<const uint4*>(dH + r * c + col), dh);
+  unpack8(*reinterpret_cast<const uint4*>(UG + r * 2 * c + col), u);
+  unpack8(*reinterpret_cast<const uint4*>(UG + r * 2 * c + c + col), g);
+  float du[8], dg[8], h[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float sg = 1.f / (1.f + expf(-g[q]));
+    const float sl = g[q] * sg;
+    du[q] = dh[q] * sl;
+    dg[q] = dh[q] * u[q] * (sg * (1.f + g[q] * (1.f - sg)));
+    h[q] = u[q] * sl;
+  }
+  *reinterpret_cast<uint4*>(DUG + r * 2 * c + col) =
+      make_uint4(pack2(du[0], du[1]), pack2(du[2], du[3]), pack2(du[4], du[5]), pack2(du[6], du[7]));
+  *reinterpret_cast<uint4*>(DUG + r * 2 * c + c + col) =
+      make_uint4(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]), pack2(dg[4], dg[5]), pack2(dg[6], dg[7]));
+  *reinterpret_cast<uint4*>(H + r * c + col) =
+      make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+}
+
+// ---- padded segment offsets: poff[g] = sum_{g' < g} ceil(count_g' / 64) * 64 (one block) --------
+__global__ __launch_bounds__(1024) void k_pad_offsets(const int32_t* __restrict__ offsets, int32_t G,
+                                                      int32_t* __restrict__ poff) {
+  __shared__ int32_t sc[1024];
+  const int g = threadIdx.x;
+  sc[g] = g < G ? (offsets[g + 1] - offsets[g] + 63) / 64 * 64 : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+    const int32_t v = g >= o ? sc[g - o] : 0;
+    __syncthreads();
+    sc[g] += v;
+    __syncthreads();
+  }
+  if (g < G) poff[g + 1] = sc[g];
+  if (g == 0) poff[0] = 0;
+}
+
+// ---- transpose -----------------------------------------------------------------------------------
+// out[c][col0 + j] = X[src(j)][c] for c < C and padded columns j, with src(j) the source row of
+// output column j: segmented (offsets / poff given): j in [poff[g], poff[g+1]) maps to row
+// offsets[g] + j - poff[g] while that is below offsets[g+1] (zero beyond); plain: row j while
+// j < R (zero beyond).  A gathered source reads X row gather[src] / gk.  Batches (blockIdx.z)
+// step the input by batch_in and the output by batch_out elements.  C % 8 == 0.
+struct TrArgs {
+  const uint16_t* X;
+  int64_t ldx;
+  const int32_t* gather;
+  int32_t gk;
+  const int32_t* offsets;
+  const int32_t* poff;
+  int32_t G;
+  int64_t R;        // source rows (plain)
+  int32_t C;        // source columns = output rows
+  uint16_t* out;
+  int64_t ldo;
+  int64_t col0;
+  int64_t batch_in, batch_out;
+};
+
+__global__ __launch_bounds__(256) void k_transpose(TrArgs p) {
+  __shared__ uint16_t tile[64][72];
+  const int tid = threadIdx.x;
+  const int64_t j0 = int64_t(blockIdx.x) * 64;
+  const int c0 = blockIdx.y * 64;
+  const uint16_t* X = p.X + int64_t(blockIdx.z) * p.batch_in;
+  uint16_t* out = p.out + int64_t(blockIdx.z) * p.batch_out;
+  int64_t rbase = j0, rend = p.R;
+  if (p.poff) {
+    int lo = 0, hi = p.G;   // the segment g with poff[g] <= j0 < poff[g+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (p.poff[mid] <= j0) lo = mid; else hi = mid;
+    }
+    rbase = p.offsets[lo] + (j0 - p.poff[lo]);
+    rend = p.offsets[lo + 1];
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int q = tid + s * 256, row = q >> 3, ch = q & 7;
+    const int64_t r = rbase + row;
+    const int col = c0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rend && col < p.C) {
+      const int64_t src = p.gather ? int64_t(p.gather[r] / p.gk) : r;
+      v = *reinterpret_cast<const uint4*>(X + src * p.ldx + col);
+    }
+    uint16_t* dst = &tile[row][ch * 8];
+    dst[0] = uint16_t(v.x); dst[1] = uint16_t(v.x >> 16); dst[2] = uint16_t(v.y); dst[3] = uint16_t(v.y >> 16);
+    dst[4] = uint16_t(v.z); dst[5] = uint16_t(v.z >> 16); dst[6] = uint16_t(v.w); dst[7] = uint16_t(v.w >> 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int q = tid + s * 256, cc = q >> 3, jch = q & 7;
+    if (c0 + cc >= p.C) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[jch * 8 + e][cc];
+    const uint4 o = make_uint4(uint32_t(v[0]) | (uint32_t(v[1]) << 16), uint32_t(v[2]) | (uint32_t(v[3]) << 16),
+                               uint32_t(v[4]) | (uint32_t(v[5]) << 16), uint32_t(v[6]) | (uint32_t(v[7]) << 16));
+    *reinterpret_cast<uint4*>(out + int64_t(c0 + cc) * p.ldo + p.col0 + j0 + jch * 8) = o;
+  }
+}
+
+// ---- K-grouped product -----------------------------------------------------------------------------
+// C_g[m][n] = sum over K segment g of A[m][k] B[n][k] (fp32 out), A [M, ldk] and B [N, ldk] bf16
+// with K contiguous; segment g is [koff[g], koff[g+1]) (multiples of 64; koff null: one segment
+// [0, K)).  Output rows m < split go to out1 + g * split * N, the rest to out2 + g * (M - split) * N
+// (row m - split).  256 x 256 tiles, 8 waves (2 x 4), v_mfma_f32_16x16x32_bf16 with the B fragment
+// first so a lane holds four consecutive output columns; two direct-to-LDS stages of 64 K values.
+struct KgArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* out1;
+  float* out2;
+  const int32_t* koff;
+  int64_t ldk;
+  int32_t K, M, N, G, split, tm, tn;
+};
+
+__global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
+  constexpr int BM = 256, BN = 256, WAVES_N = 4, BK = 64, RB = BK * 2;   // RB: bytes per LDS row
+  constexpr int WTM = 128, WTN = 64, FM = 8, FN = 4, NW = 8, RUN_ROWS = 8;
+  constexpr int A_RUNS = BM / RUN_ROWS / NW, B_RUNS = BN / RUN_ROWS / NW;
+  constexpr int STAGE = (BM + BN) * BK;   // bf16 elements
+  __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE], s1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // workgroup -> tile: each XCD (workgroups b with b % 8 == x) takes one contiguous range of the
+  // logical order (group-major, then M-tile, then N-tile), so tiles resident together share panels
+  const int total = p.G * p.tm * p.tn, b = blockIdx.x;
+  const int q8 = total / kXcds, r8 = total % kXcds, x = b % kXcds, i8 = b / kXcds;
+  if (i8 >= q8 + (x < r8 ? 1 : 0)) return;
+  const int L = x * q8 + min(x, r8) + i8;
+  const int g = L / (p.tm * p.tn), rem = L - g * (p.tm * p.tn), mt = rem / p.tn, nt = rem - mt * p.tn;
+  const int64_t k0 = p.koff ? p.koff[g] : 0;
+  const int K = p.koff ? int(p.koff[g + 1] - k0) : p.K;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int mrows = min(BM, p.M - m0), nrows = min(BN, p.N - n0);
+  const uint32_t ldb = uint32_t(p.ldk) * 2u;   // bytes per operand row
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + int64_t(m0) * p.ldk + k0, int64_t(mrows) * p.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + int64_t(n0) * p.ldk + k0, int64_t(nrows) * p.ldk * 2);
+  const int d_row = lane >> 3, d_ch = (lane & 7) ^ d_row;
+  uint32_t dA[A_RUNS], dB[B_RUNS];
+#pragma unroll
+  for (int i = 0; i < A_RUNS; ++i) dA[i] = uint32_t((wave * A_RUNS + i) * RUN_ROWS + d_row) * ldb + uint32_t(d_ch) * 16u;
+#pragma unroll
+  for (int i = 0; i < B_RUNS; ++i) dB[i] = uint32_t((wave * B_RUNS + i) * RUN_ROWS + d_row) * ldb + uint32_t(d_ch) * 16u;
+
+  // fragment reads: row (base + 16 i + lane % 16), K slice ks: chunk ((4 ks + lane / 16) ^ (lane & 7))
+  const int sw = lane & 7, fa0 = (wm * WTM + (lane & 15)) * BK, fb0 = BM * BK + (wn * WTN + (lane & 15)) * BK;
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint32_t kb_zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(kb_zero));
+#define KG_SM(BUF) ((BUF) ? s1 : s0)
+#define KG_STAGE(KT, BUF)                                                                        \
+  {                                                                                              \
+    const uint32_t kb = uint32_t(KT) * RB + kb_zero;                                             \
+    _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                           \
+      FSM_LDS_DMA16(rA, &KG_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * BK], dA[i] + kb);            \
+    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
+      FSM_LDS_DMA16(rB, &KG_SM(BUF)[BM * BK + (wave * B_RUNS + i) * RUN_ROWS * BK], dB[i] + kb);  \
+  }
+#define KG_LDA(BUF, KS, I) \
+  (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define KG_LDB(BUF, KS, J) \
+  (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fb0 + (J) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define KG_COMPUTE(BUF)                                                                          \
+  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                             \
+    bf16x8 bf[FN], a_cur, a_nxt;                                                                 \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] = KG_LDB(BUF, ks, j);                   \
+    a_cur = KG_LDA(BUF, ks, 0);                                                                  \
+    __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                      \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                             \
+      if (i + 1 < FM) a_nxt = KG_LDA(BUF, ks, i + 1);                                            \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], a_cur, acc[i][j], 0, 0, 0);   \
+      if (i + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
+      a_cur = a_nxt;                                                                             \
+    }                                                                                            \
+  }
+#define KG_BARRIER()                    \
+  {                                     \
+    asm volatile("" ::: "memory");      \
+    __builtin_amdgcn_s_barrier();       \
+    asm volatile("" ::: "memory");      \
+  }
+
+  const int KT = K / BK;
+  if (KT == 0) {   // an empty segment: the gradient block is zero (uniform across the workgroup)
+    for (int e = tid; e < BM * BN; e += 512) {
+      const int m = m0 + e / BN, n = n0 + e % BN;
+      if (m < p.M && n < p.N) {
+        float* orow = m < p.split ? p.out1 + (int64_t(g) * p.split + m) * p.N
+                                  : p.out2 + (int64_t(g) * (p.M - p.split) + (m - p.split)) * p.N;
+        orow[n] = 0.f;
+      }
+    }
+    return;
+  }
+  KG_STAGE(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  KG_BARRIER();
+  for (int kt = 0;;) {
+    if (kt + 1 < KT) KG_STAGE(kt + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    KG_COMPUTE(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++kt >= KT) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    KG_BARRIER();
+    if (kt + 1 < KT) KG_STAGE(kt + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    KG_COMPUTE(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++kt >= KT) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    KG_BARRIER();
+  }
+#undef KG_SM
+#undef KG_STAGE
+#undef KG_LDA
+#undef KG_LDB
+#undef KG_COMPUTE
+#undef KG_BARRIER
+
+  // epilogue: lane holds rows m0 + .. + (lane & 15), columns n0 + .. + 4 (lane >> 4) + {0..3}
+  const int ml = lane & 15, nl = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 16 + ml;
+    if (m >= p.M) continue;
+    float* orow = m < p.split ? p.out1 + (int64_t(g) * p.split + m) * p.N
+                              : p.out2 + (int64_t(g) * (p.M - p.split) + (m - p.split)) * p.N;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WTN + j * 16 + nl;
+      if (n + 3 < p.N) {
+        *reinterpret_cast<float4*>(orow + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < p.N) orow[n + r] = acc[i][j][r];
+      }
+    }
+  }
+}
+
+// ---- host --------------------------------------------------------------------------------------------
+namespace {
+int64_t r64(int64_t x) { return (x + 63) / 64 * 64; }
+
+struct BwdWs {
+  uint16_t *dY, *dOut_b, *dL_b, *dLT, *W_RT, *UG, *dH, *DUG, *H, *dX, *W3T, *W12T, *dYT, *HT, *DUGT, *XT, *AT;
+  uint16_t *UGs, *dHs, *DUGs, *Hs, *dXs, *Ws3T, *Ws12T, *dOutT, *HsT, *DUGsT;
+  float *dw, *ones, *dLf, *bias_part, *dA_r;
+  int32_t *poff, *ts, *grp;
+};
+
+constexpr int kBiasChunks = 64;
+
+BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
+  const int64_t T = c.T, d = c.d, cc = c.c, cs = c.c_shared, E = c.E, k = c.k, N = T * k;
+  const int64_t Tp = r64(T), Ep = r64(E), Np = r64(N) + 64 * E;
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* q = base + off;
+    off = align_up(off + bytes, 256);
+    return q;
+  };
+  auto b16 = [&](int64_t n) { return static_cast<uint16_t*>(take(size_t(n) * 2)); };
+  auto f32 = [&](int64_t n) { return static_cast<float*>(take(size_t(n) * 4)); };
+  BwdWs w{};
+  w.dY = b16(N * d);
+  w.dOut_b = b16(T * d);
+  w.dw = f32(T * k);
+  w.ones = f32(T * k);
+  w.dLf = f32(T * E);
+  w.dL_b = b16(T * Ep);
+  w.dLT = b16(E * Tp);
+  w.bias_part = f32(kBiasChunks * E);
+  w.W_RT = b16(d * Ep);
+  w.poff = static_cast<int32_t*>(take(size_t(E + 1) * 4));
+  w.ts = static_cast<int32_t*>(take(size_t(E + 1) * 4));
+  w.grp = static_cast<int32_t*>(take(size_t(cdiv(N, 256) + E) * 4));
+  w.UG = b16(N * 2 * cc);
+  w.dH = b16(N * cc);
+  w.DUG = b16(N * 2 * cc);
+  w.H = b16(N * cc);
+  w.dX = b16(N * d);
+  w.W3T = b16(E * cc * d);
+  w.W12T = b16(E * d * 2 * cc);
+  w.dYT = b16(d * Np);
+  w.HT = b16(cc * Np);
+  w.DUGT = b16(2 * cc * Np);
+  w.XT = b16(d * Np);
+  w.AT = b16(d * Tp);
+  w.dA_r = f32(T * d);
+  if (cs > 0) {
+    w.UGs = b16(T * 2 * cs);
+    w.dHs = b16(T * cs);
+    w.DUGs = b16(T * 2 * cs);
+    w.Hs = b16(T * cs);
+    w.dXs = b16(T * d);
+    w.Ws3T = b16(cs * d);
+    w.Ws12T = b16(d * 2 * cs);
+    w.dOutT = b16(d * Tp);
+    w.HsT = b16(cs * Tp);
+    w.DUGsT = b16(2 * cs * Tp);
+  }
+  if (total) *total = off;
+  return w;
+}
+
+// transpose of rows [0, R) (or segments) of X [*, ldx] into out [C, ldo] at column col0
+int transpose(const uint16_t* X, int64_t ldx, int64_t R, int32_t C, uint16_t* out, int64_t ldo, int64_t col0,
+              int64_t out_cols, hipStream_t s, const int32_t* gather = nullptr, int32_t gk = 1,
+              const int32_t* offsets = nullptr, const int32_t* poff = nullptr, int32_t G = 0, int batches = 1,
+              int64_t batch_in = 0, int64_t batch_out = 0) {
+  TrArgs a{X, ldx, gather, gk, offsets, poff, G, R, C, out, ldo, col0, batch_in, batch_out};
+  const dim3 grid(unsigned(out_cols / 64), unsigned(cdiv(C, 64)), unsigned(batches));
+  ProfScope prof(MOE_K_TRANSPOSE, s);
+  k_transpose<<<grid, 256, 0, s>>>(a);
+  return check_launch("transpose");
+}
+
+int kgroup(const uint16_t* A, const uint16_t* B, int64_t ldk, const int32_t* koff, int32_t G, int64_t K, int64_t M,
+           int64_t N, float* out1, float* out2, int64_t split, hipStream_t s) {
+  KgArgs a{};
+  a.A = A; a.B = B; a.out1 = out1; a.out2 = out2 ? out2 : out1; a.koff = koff; a.ldk = ldk;
+  a.K = int32_t(K); a.M = int32_t(M); a.N = int32_t(N); a.G = G; a.split = int32_t(split);
+  a.tm = int32_t(cdiv(M, 256)); a.tn = int32_t(cdiv(N, 256));
+  const int64_t total = int64_t(G) * a.tm * a.tn;
+  ProfScope prof(MOE_K_BWD_WGRAD, s);
+  k_gemm_kgroup<<<dim3(unsigned(total)), 512, 0, s>>>(a);
+  return check_launch("weight-gradient product");
+}
+}  // namespace
+
+size_t layer_bwd_ws_bytes(const moe_stack_cfg_t& c) {
+  size_t total = 0;
+  carve_bwd(nullptr, c, &total);
+  return total;
+}
+
+#define FSM_TRY(x)       \
+  {                      \
+    if (int rc_ = (x)) return rc_; \
+  }
+
+int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, const void* A, const float* logits,
+                          const int32_t* idx, const float* topk_w, const int32_t* offsets,
+                          const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
+                          const moe_layer_grads_t& gr, void* ws, hipStream_t s) {
+  const int64_t T = c.T, d = c.d, cc = c.c, cs = c.c_shared, k = c.k, N = T * k;
+  const int32_t E = c.E;
+  const int64_t Tp = r64(T), Ep = r64(E), Np = r64(N) + 64 * int64_t(E);
+  BwdWs w = carve_bwd(ws, c, nullptr);
+  const uint16_t* Ab = static_cast<const uint16_t*>(A);
+
+  {  // Combine and gate backward, the bias gradient, unit weights for the final sum
+    ProfScope prof(MOE_K_BWD_POINTWISE, s);
+    k_combine_bwd<<<unsigned(T), 256, 0, s>>>(dOut, static_cast<const uint16_t*>(Y), topk_w, dest_row, int32_t(d),
+                                              int32_t(k), w.dY, w.dw, cs > 0 ? w.dOut_b : nullptr);
+    FSM_TRY(check_launch("combine backward"));
+    k_gate_bwd<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(logits, idx, w.dw, T, E, int32_t(k), c.gate, c.renormalize,
+                                                     w.dLf, w.dL_b, int32_t(Ep));
+    FSM_TRY(check_launch("gate backward"));
+    if (gr.dbias) {
+      const int64_t rpc = cdiv(T, kBiasChunks);
+      k_col_partial<<<dim3(unsigned(cdiv(E, 64)), kBiasChunks), 256, 0, s>>>(w.dLf, T, E, rpc, w.bias_part);
+      FSM_TRY(check_launch("bias partial sums"));
+      k_col_final<<<unsigned(cdiv(E, 256)), 256, 0, s>>>(w.bias_part, kBiasChunks, E, gr.dbias);
+      FSM_TRY(check_launch("bias sums"));
+    }
+    k_fill_f32<<<unsigned(cdiv(T * k, 256)), 256, 0, s>>>(w.ones, T * k, 1.f);
+    FSM_TRY(check_launch("fill"));
+    k_pad_offsets<<<1, 1024, 0, s>>>(offsets, E, w.poff);
+    FSM_TRY(check_launch("padded offsets"));
+  }
+  FSM_TRY(launch_tile_table(offsets, E, 256, int(cdiv(N, 256) + E), w.ts, w.grp, s));
+
+  // routed experts: recompute U, G; dH = dY W3; dU, dG, H; dX = [dU | dG] [W1; W2]
+  FSM_TRY(launch_bf16_product(PRODUCT_UG, A, offsets, w.ts, w.grp, E, W.W1, W.W2, cc * d, N, d, cc, w.UG, s,
+                              sorted_src, int32_t(k), T, MOE_K_BWD_RECOMPUTE));
+  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W3), cc, d, int32_t(cc), w.W3T, d, 0, r64(d), s, nullptr, 1,
+                    nullptr, nullptr, 0, E, d * cc, cc * d));
+  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dY, offsets, w.ts, w.grp, E, w.W3T, nullptr, cc * d, N, d, cc, w.dH,
+                              s, nullptr, 1, N, MOE_K_BWD_DGRAD));
+  {
+    ProfScope prof(MOE_K_BWD_POINTWISE, s);
+    k_swiglu_bwd<<<unsigned(cdiv(N * (cc / 8), 256)), 256, 0, s>>>(w.dH, w.UG, N, int32_t(cc), w.DUG, w.H);
+    FSM_TRY(check_launch("swiglu backward"));
+  }
+  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W1), d, cc, int32_t(d), w.W12T, 2 * cc, 0, r64(cc), s, nullptr, 1,
+                    nullptr, nullptr, 0, E, cc * d, d * 2 * cc));
+  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W2), d, cc, int32_t(d), w.W12T, 2 * cc, cc, r64(cc), s, nullptr,
+                    1, nullptr, nullptr, 0, E, cc * d, d * 2 * cc));
+  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUG, offsets, w.ts, w.grp, E, w.W12T, nullptr, d * 2 * cc, N, 2 * cc,
+                              d, w.dX, s, nullptr, 1, N, MOE_K_BWD_DGRAD));
+
+  // routed weight gradients over each expert's rows (segments padded to 64)
+  FSM_TRY(transpose(w.dY, d, N, int32_t(d), w.dYT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
+  FSM_TRY(transpose(w.H, cc, N, int32_t(cc), w.HT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
+  FSM_TRY(transpose(w.DUG, 2 * cc, N, int32_t(2 * cc), w.DUGT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
+  FSM_TRY(transpose(Ab, d, N, int32_t(d), w.XT, Np, 0, Np, s, sorted_src, int32_t(k), offsets, w.poff, E));
+  FSM_TRY(kgroup(w.dYT, w.HT, Np, w.poff, E, 0, d, cc, gr.dW3, nullptr, d, s));
+  FSM_TRY(kgroup(w.DUGT, w.XT, Np, w.poff, E, 0, 2 * cc, d, gr.dW1, gr.dW2, cc, s));
+
+  // router: dA_r = dlogits W_R, dW_R = dlogits^T A
+  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W_R), d, E, int32_t(d), w.W_RT, Ep, 0, Ep, s));
+  FSM_TRY(launch_bf16_product(PRODUCT_F32, w.dL_b, nullptr, nullptr, nullptr, 1, w.W_RT, nullptr, 0, T, Ep, d, w.dA_r,
+                              s, nullptr, 1, T, MOE_K_BWD_DGRAD));
+  FSM_TRY(transpose(w.dL_b, Ep, T, E, w.dLT, Tp, 0, Tp, s));
+  FSM_TRY(transpose(Ab, d, T, int32_t(d), w.AT, Tp, 0, Tp, s));
+  FSM_TRY(kgroup(w.dLT, w.AT, Tp, nullptr, 1, Tp, E, d, gr.dW_R, nullptr, E, s));
+
+  // shared expert (its output gradient is dOut itself)
+  if (cs > 0) {
+    FSM_TRY(launch_bf16_product(PRODUCT_UG, A, nullptr, nullptr, nullptr, 1, W.Ws1, W.Ws2, 0, T, d, cs, w.UGs, s,
+                                nullptr, 1, T, MOE_K_BWD_RECOMPUTE));
+    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws3), cs, d, int32_t(cs), w.Ws3T, d, 0, r64(d), s));
+    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dOut_b, nullptr, nullptr, nullptr, 1, w.Ws3T, nullptr, 0, T, d, cs,
+                                w.dHs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
+    {
+      ProfScope prof(MOE_K_BWD_POINTWISE, s);
+      k_swiglu_bwd<<<unsigned(cdiv(T * (cs / 8), 256)), 256, 0, s>>>(w.dHs, w.UGs, T, int32_t(cs), w.DUGs, w.Hs);
+      FSM_TRY(check_launch("swiglu backward"));
+    }
+    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws1), d, cs, int32_t(d), w.Ws12T, 2 * cs, 0, r64(cs), s));
+    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws2), d, cs, int32_t(d), w.Ws12T, 2 * cs, cs, r64(cs), s));
+    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUGs, nullptr, nullptr, nullptr, 1, w.Ws12T, nullptr, 0, T, 2 * cs,
+                                d, w.dXs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
+    FSM_TRY(transpose(w.dOut_b, d, T, int32_t(d), w.dOutT, Tp, 0, Tp, s));
+    FSM_TRY(transpose(w.Hs, cs, T, int32_t(cs), w.HsT, Tp, 0, Tp, s));
+    FSM_TRY(transpose(w.DUGs, 2 * cs, T, int32_t(2 * cs), w.DUGsT, Tp, 0, Tp, s));
+    FSM_TRY(kgroup(w.dOutT, w.HsT, Tp, nullptr, 1, Tp, d, cs, gr.dWs3, nullptr, d, s));
+    FSM_TRY(kgroup(w.DUGsT, w.AT, Tp, nullptr, 1, Tp, 2 * cs, d, gr.dWs1, gr.dWs2, cs, s));
+  }
+
+  // dA[t] = sum over t's slots of dX[dest_row] + the router's and the shared expert's parts
+  return launch_combine(w.dX, MOE_BF16, w.ones, dest_row, T, d, int32_t(k), cs > 0 ? w.dXs : nullptr, w.dA_r,
+                        gr.dA, nullptr, s);
+}
+#undef FSM_TRY
+
+}  // namespace fsm

@@ -81,6 +81,18 @@ int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
                    void* out_x, hipStream_t s);
 // MXFP8 (mx.hip): rows of a bf16 matrix -> E4M3 codes + one E8M0 scale per 32 elements
+// backward-pass building blocks (gemm.hip); epi codes of the bf16 product
+enum { PRODUCT_PLAIN = 0, PRODUCT_F32 = 2, PRODUCT_UG = 3 };
+int launch_bf16_product(int epi, const void* X, const int32_t* offsets, const int32_t* ts, const int32_t* grp,
+                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t N, int64_t K,
+                        int64_t n_out, void* out, hipStream_t s, const int32_t* gather, int32_t gather_k,
+                        int64_t x_rows, int prof_kind);
+// backward pass of one MoE sublayer (bwd.hip)
+size_t layer_bwd_ws_bytes(const moe_stack_cfg_t& c);
+int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, const void* A, const float* logits,
+                          const int32_t* idx, const float* topk_w, const int32_t* offsets,
+                          const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
+                          const moe_layer_grads_t& gr, void* ws, hipStream_t s);
 int launch_mx_quantize(const void* X, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 size_t mx_swiglu_ws_bytes(int64_t N, int32_t G, int64_t c);
 // the grouped SwiGLU MLP on MXFP8 operands (gather as in launch_grouped_swiglu); Y in bf16

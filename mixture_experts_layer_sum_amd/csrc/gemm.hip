@@ -27,7 +27,9 @@
 
 namespace fsm {
 
-enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
+// EPI_UG: the SwiGLU tile's loads (W1 and W2 columns side by side), storing U and G themselves
+// into [rows, 2 n_out] (U in columns [0, n_out), G in [n_out, 2 n_out)) for a backward pass.
+enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_UG = 3 };
 
 struct GemmArgs {
   const void* A;              // [rows, K]
@@ -117,6 +119,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS, int BK_ =
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
   constexpr int BK = BK_, S = S_;
+  constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_UG;   // tile holds W1 and W2 columns
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(S >= 2 && S <= 5, "2 to 5 LDS stages");
   constexpr int KSL = BK / 32;                 // MFMA K slices per stage
@@ -128,8 +131,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   constexpr int LOADS = A_RUNS + B_RUNS;       // vector-memory operations per wave per stage
   constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage (A rows, then B rows)
   static_assert(A_RUNS * RUN_ROWS * NW == BM && B_RUNS * RUN_ROWS * NW == BN, "runs must tile the stage");
-  static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
-  static_assert(EPI != EPI_SWIGLU || (BN / 2) % (B_RUNS * RUN_ROWS) == 0, "a wave's B rows must lie in one half");
+  static_assert(!PAIRED || (FN % 2) == 0, "SwiGLU needs paired fragments");
+  static_assert(!PAIRED || (BN / 2) % (B_RUNS * RUN_ROWS) == 0, "a wave's B rows must lie in one half");
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
   static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
   static_assert(LOADS * (S - 2) < 64, "vmcnt range");
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   const uint16_t* Bu;
   const uint16_t* Bg;
   int nvalid;
-  if (EPI == EPI_SWIGLU) {
+  if (PAIRED) {
     const int n0 = nt * (BN / 2);
     Bu = static_cast<const uint16_t*>(p.B1) + g * p.b_group_stride + int64_t(n0) * K;
     Bg = static_cast<const uint16_t*>(p.B2) + g * p.b_group_stride + int64_t(n0) * K;
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     for (int i = 0; i < A_RUNS; ++i) dA[i] = uint32_t((wave * A_RUNS + i) * RUN_ROWS + d_row) * rowB + uint32_t(d_ch) * 16u;
   }
   const int wb_row0 = wave * B_RUNS * RUN_ROWS;  // first B tile row of this wave
-  const bool b_gate = EPI == EPI_SWIGLU && wb_row0 >= BN / 2;
+  const bool b_gate = PAIRED && wb_row0 >= BN / 2;
   const __amdgpu_buffer_rsrc_t rBw = b_gate ? rG : rU;
 #pragma unroll
   for (int i = 0; i < B_RUNS; ++i) {
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   // Fragment reads: rows (base + 16 i + lane % 16); base is a multiple of 16, so the swizzle
   // term depends on the lane only.
   const int fa0 = (wm * WTM + (lane & 15)) * BK;
-  const int fb0 = BM * BK + (EPI == EPI_SWIGLU ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
+  const int fb0 = BM * BK + (PAIRED ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
   const int sw = lds_swz<BK>(lane & 15);
 
   f32x4 acc[FM][FN];
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
       FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);        \
   }
 #define FSM_BROW(J) \
-  ((EPI == EPI_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
+  ((PAIRED) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
 #define FSM_LDA(BUF, KS, I) \
   (*reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
 #define FSM_LDB(BUF, KS, J) \
@@ -350,6 +353,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
         v.x = pack2(u[0] * silu_f(gt[0]), u[1] * silu_f(gt[1]));
         v.y = pack2(u[2] * silu_f(gt[2]), u[3] * silu_f(gt[3]));
         *reinterpret_cast<uint2*>(out + orow * p.n_out + col) = v;
+      }
+    } else if (EPI == EPI_UG) {
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+      const int64_t ld = 2 * int64_t(p.n_out);
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const int col = nt * (BN / 2) + wn * (WTN / 2) + j * 16 + nl;
+        if (col >= p.n_out) continue;
+        const f32x4 u = acc[i][j], gt = acc[i][j + FN / 2];
+        *reinterpret_cast<uint2*>(out + orow * ld + col) = make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
+        *reinterpret_cast<uint2*>(out + orow * ld + p.n_out + col) = make_uint2(pack2(gt[0], gt[1]), pack2(gt[2], gt[3]));
       }
     } else if (EPI == EPI_PLAIN) {
       uint16_t* out = static_cast<uint16_t*>(p.out);
@@ -633,6 +647,40 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
   a.n_tiles = int32_t(cdiv(E, F_BN));
   k_gemm_f32<EPI_F32_BIAS, ROWS_GROUPED><<<dim3(unsigned(cdiv(T, F_BM) * a.n_tiles)), 256, 0, s>>>(a);
   return check_launch("router gemm (f32)");
+}
+
+// One bf16 product on 256 x 256 tiles for the backward pass: out = X B^T per group (B = B1 + g *
+// b_stride, [n_out, K]).  epi EPI_UG: B1 and B2 side by side, out [N, 2 n_out] = (X B1^T | X B2^T);
+// EPI_PLAIN: bf16 out [N, n_out]; EPI_F32_BIAS (one group, no bias): fp32 out [N, n_out].  ts / grp:
+// the group tile table for 256-row tiles (null with one group).
+int launch_bf16_product(int epi, const void* X, const int32_t* offsets, const int32_t* ts, const int32_t* grp,
+                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t N, int64_t K,
+                        int64_t n_out, void* out, hipStream_t s, const int32_t* gather, int32_t gather_k,
+                        int64_t x_rows, int prof_kind) {
+  if (N == 0) return MOE_OK;
+  constexpr TileCfg C = kP1;
+  GemmArgs a{};
+  a.A = X; a.B1 = B1; a.B2 = B2; a.out = out; a.bias = nullptr;
+  a.offsets = offsets; a.tile_start = ts; a.tile_group = grp; a.b_group_stride = b_stride;
+  a.K = int32_t(K); a.n_out = int32_t(n_out); a.M = int32_t(N); a.G = G; a.group_m = C.gm;
+  a.gather = gather; a.gather_k = gather_k; a.a_rows = x_rows;
+  a.n_tiles = int32_t(cdiv(n_out, epi == EPI_UG ? C.bn / 2 : C.bn));
+  a.quad_nb = quad_width(a.n_tiles, a.group_m);
+  const int64_t mt = grp ? cdiv(N, C.bm) + G : cdiv(N, C.bm);
+  const dim3 grid(unsigned(quad_grid(mt, a.n_tiles, a.group_m, a.quad_nb)));
+  constexpr int nt = 64 * C.wm * C.wn;
+  ProfScope prof(prof_kind, s);
+  if (epi == EPI_UG && gather)
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_UG, ROWS_GATHER, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+  else if (epi == EPI_UG)
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_UG, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+  else if (epi == EPI_PLAIN && grp)
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_GROUPED, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+  else if (epi == EPI_PLAIN)
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+  else
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_F32_BIAS, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+  return check_launch("backward product");
 }
 
 }  // namespace fsm

@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
-                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelTime, LayerDesc, StackCfg, check, lib)
+                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelTime, LayerDesc, LayerGrads, StackCfg, check, lib)
 
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
 MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
@@ -214,6 +214,26 @@ def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, w
     ss = _s(s_side) if s_side is not None else sm
     check("farskip_stack_forward",
           lib.farskip_stack_forward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(), sm, ss))
+
+
+def layer_backward_workspace_bytes(cfg: StackCfg) -> int:
+    return int(lib.moe_layer_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+GRAD_NAMES = ("dA", "dW_R", "dbias", "dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3")
+
+
+def moe_layer_backward(W: dict, cfg: StackCfg, A, logits, topk_idx, topk_w, expert_offsets, sorted_src, dest_row, Y,
+                       dOut, grads: dict, ws=None, stream=None):
+    """Gradients of one MoE sublayer's output for dOut (float32 [T, d]) into the float32 tensors of
+    grads (keys as GRAD_NAMES; dbias and the shared ones may be absent)."""
+    if ws is None:
+        ws = workspace(layer_backward_workspace_bytes(cfg), A.device)
+    g = LayerGrads(*[None if grads.get(n) is None else grads[n].data_ptr() for n in GRAD_NAMES])
+    check("moe_layer_backward",
+          lib.moe_layer_backward(ctypes.byref(layer_desc(W)), ctypes.byref(cfg), _p(A), _p(logits), _p(topk_idx),
+                                 _p(topk_w), _p(expert_offsets), _p(sorted_src), _p(dest_row), _p(Y), _p(dOut),
+                                 ctypes.byref(g), _p(ws), ws.numel(), _s(stream)))
 
 
 def profile_enable(on: bool = True) -> None:
