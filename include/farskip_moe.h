@@ -279,6 +279,9 @@ size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
  *   expert_offsets, sorted_src, dest_row   the forward's permutation (moe_permute)
  *   Y            [T*k, d] bf16      the forward's routed expert outputs (grouped row order)
  *   dOut         [T, d] float32     gradient of the loss with respect to out
+ *   dOut_shared  [T, d] float32 or NULL: the shared experts' own output gradient when it differs
+ *                from dOut (in a FarSkip stack the shared output also feeds the next layer's
+ *                input, eq. 8b); NULL = dOut
  *   grads        host pointer to OUTPUT device pointers, all float32, overwritten:
  *                  dA [T, d] (the residual's own pass-through is not included), dW_R [E, d],
  *                  dbias [E] (or NULL: not computed), dW1, dW2 [E, c, d], dW3 [E, d, c], and
@@ -303,8 +306,33 @@ typedef struct {
 int moe_layer_backward(const moe_layer_desc_t* W, const moe_stack_cfg_t* cfg, const void* A, const float* logits,
                        const int32_t* topk_idx, const float* topk_w, const int32_t* expert_offsets,
                        const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
-                       const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream);
+                       const float* dOut_shared, const moe_layer_grads_t* grads, void* ws, size_t ws_bytes,
+                       void* stream);
 size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg);
+
+/*
+ * farskip_stack_backward -- the backward pass of the FarSkip stack of farskip_stack_forward
+ * (section 3, eqs. (8a)/(8b)) for dOL = dLoss/do_L: dO0 = dLoss/do_0 and every layer's weight
+ * gradients.  The forward is replayed on the stream keeping each layer's input, routing and expert
+ * outputs; then the layers' backward passes (moe_layer_backward) run from the last layer to the
+ * first with the gradients routed along the stack's graph: o_j feeds o_{j+1} and the next input
+ * (x_{j+1} = o_j without the skip, x_{j+2} = o_j (+ S_{j+1}) with it), and under "partial" the
+ * shared output S_j also feeds x_{j+1}, so the shared experts of layer j receive
+ * dLoss/do_j + dLoss/dx_{j+1} while the routed ones receive dLoss/do_j.  The rounding of the layer
+ * inputs to bf16 passes gradients through unchanged.  One stream; bf16 only.
+ *
+ *   layers, L, cfg, mode, skip_mask, o0   as for farskip_stack_forward
+ *   dOL    [T, d] float32   gradient of the loss with respect to o_L
+ *   dO0    [T, d] float32   OUTPUT gradient with respect to o_0 (must not alias dOL)
+ *   grads  host array [L]: each layer's gradient outputs as for moe_layer_backward; dA (optional)
+ *          receives dLoss/dx_j, the gradient with respect to that layer's input
+ *   ws     scratch of at least farskip_stack_backward_workspace_bytes(cfg, L) bytes
+ * Limits: as moe_layer_backward.
+ */
+int farskip_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                           const uint8_t* skip_mask, const float* o0, const float* dOL, float* dO0,
+                           const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream);
+size_t farskip_stack_backward_workspace_bytes(const moe_stack_cfg_t* cfg, int32_t L);
 
 /*
  * Kernel timing for measurement harnesses.  While enabled (process-wide), every kernel the

@@ -19,7 +19,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_group
            "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu_gathered", "moe_mx_quantize",
            "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
            "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
-           "moe_layer_backward_workspace_bytes", "moe_combine", "farskip_stack_forward",
+           "moe_layer_backward_workspace_bytes", "farskip_stack_backward", "farskip_stack_backward_workspace_bytes",
+           "moe_combine", "farskip_stack_forward",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect", "moe_last_error",
            "moe_version")
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
@@ -83,10 +84,15 @@ def _declare(lib):
     lib.moe_grouped_mxfp8_phase_workspace_bytes.argtypes = [i64, i32]
     lib.moe_grouped_mxfp8_phase_workspace_bytes.restype = sz
     lib.moe_layer_backward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(StackCfg), vp, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, ctypes.POINTER(LayerGrads), vp, sz, vp]
+                                       vp, vp, vp, ctypes.POINTER(LayerGrads), vp, sz, vp]
     lib.moe_layer_backward.restype = i
     lib.moe_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
     lib.moe_layer_backward_workspace_bytes.restype = sz
+    lib.farskip_stack_backward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i, vp, vp, vp, vp,
+                                           ctypes.POINTER(LayerGrads), vp, sz, vp]
+    lib.farskip_stack_backward.restype = i
+    lib.farskip_stack_backward_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg), i32]
+    lib.farskip_stack_backward_workspace_bytes.restype = sz
     lib.moe_combine.argtypes = [vp, i, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.moe_combine.restype = i
     lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,

@@ -171,41 +171,48 @@ __global__ void k_set_shared_offsets(int32_t* off, int32_t T) {
   }
 }
 
-int check_stack(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
-                const float* o0, const float* oL, const void* ws, size_t ws_bytes) {
-  if (!layers || !cfg) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layers and cfg are required");
-  if (L < 1) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: L=%d must be >= 1", L);
+// shapes, modes and pointers of a stack call (forward or backward); `who` names the entry point
+int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                     const float* o0, const float* oL, const char* who) {
+  if (!layers || !cfg) return fail(MOE_ERR_INVALID_ARG, "%s: layers and cfg are required", who);
+  if (L < 1) return fail(MOE_ERR_INVALID_ARG, "%s: L=%d must be >= 1", who, L);
   if (mode != FARSKIP_NONE && mode != FARSKIP_PARTIAL && mode != FARSKIP_OUTDATED)
-    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown mode %d", mode);
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
   const moe_stack_cfg_t& c = *cfg;
   if (c.T < 1 || c.d < 1 || c.c < 1 || c.c_shared < 0)
-    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: bad shapes");
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad shapes", who);
   if (c.E < 1 || c.k < 1 || c.k > c.E)
-    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: need 1 <= k <= E (k=%d, E=%d)", c.k, c.E);
+    return fail(MOE_ERR_INVALID_ARG, "%s: need 1 <= k <= E (k=%d, E=%d)", who, c.k, c.E);
   if (c.E > MOE_MAX_EXPERTS || c.k > MOE_MAX_TOPK)
-    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: E or k above the library limits");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E or k above the library limits", who);
   if (c.gate != MOE_GATE_SOFTMAX && c.gate != MOE_GATE_SIGMOID)
-    return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown gate %d", c.gate);
-  if (!dtype_ok(c.dtype)) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: unknown dtype %d", c.dtype);
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown gate %d", who, c.gate);
+  if (!dtype_ok(c.dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", who, c.dtype);
   if (c.dtype == MOE_BF16 && c.d % 64 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: bf16 needs d %% 64 == 0");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs d %% 64 == 0", who);
   if (c.dtype == MOE_BF16 && (c.c % 64 != 0 || c.c_shared % 64 != 0))
-    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: bf16 needs c and c_shared multiples of 64");
-  if (c.d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: needs d %% 8 == 0");
-  if (c.T * int64_t(c.k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: T*k too large");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs c and c_shared multiples of 64", who);
+  if (c.d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: needs d %% 8 == 0", who);
+  if (c.T * int64_t(c.k) > kMaxRows) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", who);
   if (c.T * c.d * int64_t(esize(c.dtype)) >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "farskip_stack_forward: a layer input above 2^31 bytes");
-  if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: o0 and oL are required");
-  if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: oL must not alias o0");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: a layer input above 2^31 bytes", who);
+  if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "%s: o0 and oL are required", who);
+  if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "%s: oL must not alias o0", who);
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
     if (!l.W_R || !l.W1 || !l.W2 || !l.W3)
-      return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layer %d is missing routed weights", j);
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing routed weights", who, j);
     if (c.c_shared && (!l.Ws1 || !l.Ws2 || !l.Ws3))
-      return fail(MOE_ERR_INVALID_ARG, "farskip_stack_forward: layer %d is missing shared weights", j);
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing shared weights", who, j);
   }
+  return MOE_OK;
+}
+
+int check_stack(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                const float* o0, const float* oL, const void* ws, size_t ws_bytes) {
+  if (int rc = check_stack_args(layers, L, cfg, mode, o0, oL, "farskip_stack_forward")) return rc;
   size_t need = 0;
-  carve_stack(nullptr, c, &need);
+  carve_stack(nullptr, *cfg, &need);
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "farskip_stack_forward: workspace %zu bytes, need %zu", ws_bytes, need);
   return MOE_OK;
@@ -510,7 +517,8 @@ size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg) {
 int moe_layer_backward(const moe_layer_desc_t* W, const moe_stack_cfg_t* cfg, const void* A, const float* logits,
                        const int32_t* topk_idx, const float* topk_w, const int32_t* expert_offsets,
                        const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
-                       const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream) {
+                       const float* dOut_shared, const moe_layer_grads_t* grads, void* ws, size_t ws_bytes,
+                       void* stream) {
   clear_error();
   const char* who = "moe_layer_backward";
   if (!W || !cfg || !grads) return fail(MOE_ERR_INVALID_ARG, "%s: W, cfg and grads are required", who);
@@ -539,7 +547,36 @@ int moe_layer_backward(const moe_layer_desc_t* W, const moe_stack_cfg_t* cfg, co
   const size_t need = layer_bwd_ws_bytes(c);
   if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
   return launch_layer_backward(*W, c, A, logits, topk_idx, topk_w, expert_offsets, sorted_src, dest_row, Y, dOut,
-                               *grads, ws, as_stream(stream));
+                               dOut_shared, *grads, ws, as_stream(stream));
+}
+
+size_t farskip_stack_backward_workspace_bytes(const moe_stack_cfg_t* cfg, int32_t L) {
+  if (!cfg || L < 1 || cfg->T < 1 || cfg->d < 1 || cfg->c < 1 || cfg->E < 1 || cfg->k < 1 || cfg->c_shared < 0)
+    return 0;
+  return stack_bwd_ws_bytes(*cfg, L);
+}
+
+int farskip_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
+                           const uint8_t* skip_mask, const float* o0, const float* dOL, float* dO0,
+                           const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  const char* who = "farskip_stack_backward";
+  if (int rc = check_stack_args(layers, L, cfg, mode, o0, dO0, who)) return rc;
+  const moe_stack_cfg_t& c = *cfg;
+  if (c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: only bf16 is implemented", who);
+  if (c.E % 8) return fail(MOE_ERR_UNSUPPORTED, "%s: needs E a multiple of 8", who);
+  if (!dOL || !grads) return fail(MOE_ERR_INVALID_ARG, "%s: dOL and grads are required", who);
+  if (dOL == dO0) return fail(MOE_ERR_INVALID_ARG, "%s: dO0 must not alias dOL", who);
+  for (int j = 0; j < L; ++j) {
+    const moe_layer_grads_t& g = grads[j];
+    if (!g.dW_R || !g.dW1 || !g.dW2 || !g.dW3)
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d needs dW_R, dW1, dW2 and dW3", who, j);
+    if (c.c_shared > 0 && (!g.dWs1 || !g.dWs2 || !g.dWs3))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d needs dWs1, dWs2 and dWs3", who, j);
+  }
+  const size_t need = stack_bwd_ws_bytes(c, L);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  return launch_stack_backward(layers, L, c, mode, skip_mask, o0, dOL, dO0, grads, ws, as_stream(stream));
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -10,12 +10,15 @@
 // each expert's rows padded to a multiple of 64 with zeros, and k_gemm_kgroup sums one expert's
 // segment per output tile.
 //
-//   k_combine_bwd    dY[dest_row[t,i]] = w[t,i] dOut[t] (bf16), dw[t,i] = <dOut[t], Y[dest_row[t,i]]>
+//   k_combine_bwd    dY[dest_row[t,i]] = w[t,i] dOut[t] (bf16), dw[t,i] = <dOut[t], Y[dest_row[t,i]]>,
+//                    and the bf16 copy of the shared experts' output gradient
 //   k_gate_bwd       dlogits from dw through the softmax / sigmoid (and renormalisation) Jacobian
 //   k_col_partial    per-expert sums of dlogits (the bias gradient), in two deterministic passes
 //   k_swiglu_bwd     dU = dH SiLU(G), dG = dH U SiLU'(G), and H = U SiLU(G) for dW3
 //   k_transpose      64 x 64 tiles through LDS, optionally gathering rows and padding segments
 //   k_gemm_kgroup    C_g = A[:, seg_g] B[:, seg_g]^T in fp32, per group g of K segments
+#include <vector>
+
 #include "common.h"
 #include "tile_kit.h"
 
@@ -40,7 +43,8 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 __global__ __launch_bounds__(256) void k_combine_bwd(const float* __restrict__ dOut, const uint16_t* __restrict__ Y,
                                                      const float* __restrict__ w, const int32_t* __restrict__ dest,
                                                      int32_t d, int32_t k, uint16_t* __restrict__ dY,
-                                                     float* __restrict__ dw, uint16_t* __restrict__ dOut_b) {
+                                                     float* __restrict__ dw, const float* __restrict__ dS,
+                                                     uint16_t* __restrict__ dS_b) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float* g = dOut + t * d;
@@ -64,10 +68,11 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const float* __restrict__ d
     const float s = block_sum_256(part, red);
     if (threadIdx.x == 0) dw[t * k + i] = s;
   }
-  if (dOut_b) {
+  if (dS_b) {   // bf16 copy of the shared experts' output gradient
+    const float* gs = dS + t * d;
     for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
-      const float4 g0 = *reinterpret_cast<const float4*>(g + col), g1 = *reinterpret_cast<const float4*>(g + col + 4);
-      *reinterpret_cast<uint4*>(dOut_b + t * d + col) =
+      const float4 g0 = *reinterpret_cast<const float4*>(gs + col), g1 = *reinterpret_cast<const float4*>(gs + col + 4);
+      *reinterpret_cast<uint4*>(dS_b + t * d + col) =
           make_uint4(pack2(g0.x, g0.y), pack2(g0.z, g0.w), pack2(g1.x, g1.y), pack2(g1.z, g1.w));
     }
   }
@@ -516,7 +521,7 @@ size_t layer_bwd_ws_bytes(const moe_stack_cfg_t& c) {
 int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, const void* A, const float* logits,
                           const int32_t* idx, const float* topk_w, const int32_t* offsets,
                           const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
-                          const moe_layer_grads_t& gr, void* ws, hipStream_t s) {
+                          const float* dOut_shared, const moe_layer_grads_t& gr, void* ws, hipStream_t s) {
   const int64_t T = c.T, d = c.d, cc = c.c, cs = c.c_shared, k = c.k, N = T * k;
   const int32_t E = c.E;
   const int64_t Tp = r64(T), Ep = r64(E), Np = r64(N) + 64 * int64_t(E);
@@ -526,7 +531,8 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
   {  // Combine and gate backward, the bias gradient, unit weights for the final sum
     ProfScope prof(MOE_K_BWD_POINTWISE, s);
     k_combine_bwd<<<unsigned(T), 256, 0, s>>>(dOut, static_cast<const uint16_t*>(Y), topk_w, dest_row, int32_t(d),
-                                              int32_t(k), w.dY, w.dw, cs > 0 ? w.dOut_b : nullptr);
+                                              int32_t(k), w.dY, w.dw, dOut_shared ? dOut_shared : dOut,
+                                              cs > 0 ? w.dOut_b : nullptr);
     FSM_TRY(check_launch("combine backward"));
     k_gate_bwd<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(logits, idx, w.dw, T, E, int32_t(k), c.gate, c.renormalize,
                                                      w.dLf, w.dL_b, int32_t(Ep));
@@ -606,6 +612,164 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
   // dA[t] = sum over t's slots of dX[dest_row] + the router's and the shared expert's parts
   return launch_combine(w.dX, MOE_BF16, w.ones, dest_row, T, d, int32_t(k), cs > 0 ? w.dXs : nullptr, w.dA_r,
                         gr.dA, nullptr, s);
+}
+#undef FSM_TRY
+
+// ---- FarSkip stack backward ---------------------------------------------------------------------------
+// The stack's forward (section 3: o_j = o_{j-1} + S_j(x_j) + R_j(x_j); x_{j+1} = o_j, or with the
+// skip on o_{j-1} + S_j(x_j) (partial, 8b) / o_{j-1} (outdated, 8a)) is replayed on the stream,
+// keeping every layer's input, routing and expert outputs; then the layers' backward passes run
+// in reverse with the gradients routed along the same graph:
+//   dS_j = G_o[j] (+ G_x[j+1] under partial with the skip on), the routed part gets G_o[j];
+//   G_o[j-1] += G_o[j]; G_x[j] goes to G_o[j-1] (x_j = o_{j-1}) or G_o[j-2] (x_j skipped o_{j-1}).
+// The layer inputs' rounding to bf16 passes the gradient through unchanged.
+__global__ __launch_bounds__(256) void k_add_f32(float* __restrict__ y, const float* __restrict__ x, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) y[i] += x[i];
+}
+__global__ __launch_bounds__(256) void k_sum2_f32(float* __restrict__ z, const float* __restrict__ a,
+                                                  const float* __restrict__ b, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) z[i] = a[i] + b[i];
+}
+__global__ void k_two_offsets(int32_t* off, int32_t T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+namespace {
+struct StackBwdWs {
+  std::vector<void*> x, Y;
+  std::vector<float*> logits, w;
+  std::vector<int32_t*> idx, off, src, dest;
+  float *o, *dS;
+  std::vector<float*> Go, Gx;   // Go[1..L] (Go[0] is the caller's dO0), Gx[1..L]
+  void *S, *perm_ws, *gemm_ws, *shared_ws, *layer_ws;
+  int32_t* shared_off;
+};
+
+StackBwdWs carve_stack_bwd(void* ws, const moe_stack_cfg_t& c, int32_t L, size_t* total) {
+  const size_t T = size_t(c.T), d = size_t(c.d), E = size_t(c.E), k = size_t(c.k), N = T * k;
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* q = base + off;
+    off = align_up(off + bytes, 256);
+    return q;
+  };
+  StackBwdWs w;
+  for (int j = 0; j < L; ++j) {
+    w.x.push_back(take(T * d * 2));
+    w.logits.push_back(static_cast<float*>(take(T * E * 4)));
+    w.idx.push_back(static_cast<int32_t*>(take(T * k * 4)));
+    w.w.push_back(static_cast<float*>(take(T * k * 4)));
+    w.off.push_back(static_cast<int32_t*>(take((E + 1) * 4)));
+    w.src.push_back(static_cast<int32_t*>(take(N * 4)));
+    w.dest.push_back(static_cast<int32_t*>(take(N * 4)));
+    w.Y.push_back(take(N * d * 2));
+  }
+  w.o = static_cast<float*>(take(T * d * 4));
+  w.dS = static_cast<float*>(take(T * d * 4));
+  w.Go.push_back(nullptr);
+  w.Gx.push_back(nullptr);
+  for (int j = 1; j <= L; ++j) {
+    w.Go.push_back(static_cast<float*>(take(T * d * 4)));
+    w.Gx.push_back(static_cast<float*>(take(T * d * 4)));
+  }
+  w.S = c.c_shared ? take(T * d * 2) : nullptr;
+  w.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
+  w.gemm_ws = take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, MOE_BF16));
+  w.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, MOE_BF16)) : nullptr;
+  w.shared_off = static_cast<int32_t*>(take(2 * 4));
+  w.layer_ws = take(layer_bwd_ws_bytes(c));
+  if (total) *total = off;
+  return w;
+}
+}  // namespace
+
+size_t stack_bwd_ws_bytes(const moe_stack_cfg_t& c, int32_t L) {
+  size_t total = 0;
+  carve_stack_bwd(nullptr, c, L, &total);
+  return total;
+}
+
+#define FSM_TRY(x)                 \
+  {                                \
+    if (int rc_ = (x)) return rc_; \
+  }
+
+int launch_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
+                          const uint8_t* mask, const float* o0, const float* dOL, float* dO0,
+                          const moe_layer_grads_t* grads, void* ws, hipStream_t s) {
+  StackBwdWs w = carve_stack_bwd(ws, c, L, nullptr);
+  const int64_t T = c.T, d = c.d, N = c.T * c.k, n = T * d;
+  const unsigned blocks = unsigned(cdiv(n, 256));
+  auto skip = [&](int j) { return mode != FARSKIP_NONE && (mask ? mask[j] != 0 : true); };   // 0-based layer
+
+  // forward replay (one stream), keeping each layer's input, routing and expert outputs
+  k_two_offsets<<<1, 64, 0, s>>>(w.shared_off, int32_t(T));
+  FSM_TRY(check_launch("stack setup"));
+  FSM_TRY(launch_make_input(o0, nullptr, MOE_BF16, T, d, w.x[0], s));
+  const float* o_prev = o0;
+  for (int j = 0; j < L; ++j) {
+    const moe_layer_desc_t& l = layers[j];
+    const bool last = j + 1 == L;
+    FSM_TRY(launch_router_logits(w.x[j], l.W_R, l.bias, MOE_BF16, T, d, c.E, w.logits[j], s));
+    FSM_TRY(launch_topk(w.logits[j], T, c.E, c.k, c.gate, c.renormalize, w.idx[j], w.w[j], s));
+    if (c.c_shared)
+      FSM_TRY(launch_grouped_swiglu(w.x[j], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, MOE_BF16, T, d, c.c_shared, w.S,
+                                    w.shared_ws, s));
+    if (skip(j) && !last)
+      FSM_TRY(launch_make_input(o_prev, mode == FARSKIP_PARTIAL ? w.S : nullptr, MOE_BF16, T, d, w.x[j + 1], s));
+    FSM_TRY(launch_permute(w.x[j], MOE_BF16, T, d, c.E, c.k, w.idx[j], w.off[j], w.src[j], w.dest[j], nullptr,
+                           w.perm_ws, s));
+    FSM_TRY(launch_grouped_swiglu(w.x[j], w.off[j], c.E, l.W1, l.W2, l.W3, MOE_BF16, N, d, c.c, w.Y[j], w.gemm_ws, s,
+                                  w.src[j], c.k, T));
+    FSM_TRY(launch_combine(w.Y[j], MOE_BF16, w.w[j], w.dest[j], T, d, c.k, c.c_shared ? w.S : nullptr, o_prev, w.o,
+                           (!skip(j) && !last) ? w.x[j + 1] : nullptr, s));
+    o_prev = w.o;
+  }
+
+  // reverse pass: Go[j] = dLoss/do_j (Go[0] is dO0), Gx[j] = dLoss/dx_j
+  std::vector<float*> Go(w.Go);
+  Go[0] = dO0;
+  {
+    ProfScope prof(MOE_K_BWD_POINTWISE, s);
+    for (int j = 0; j < L; ++j) {
+      k_fill_f32<<<blocks, 256, 0, s>>>(Go[j], n, 0.f);
+      FSM_TRY(check_launch("fill"));
+    }
+    k_fill_f32<<<blocks, 256, 0, s>>>(Go[L], n, 0.f);
+    k_add_f32<<<blocks, 256, 0, s>>>(Go[L], dOL, n);
+    FSM_TRY(check_launch("copy"));
+  }
+  for (int j = L; j >= 1; --j) {
+    const moe_layer_desc_t& l = layers[j - 1];
+    const float* dS = Go[j];
+    if (mode == FARSKIP_PARTIAL && skip(j - 1) && j < L) {
+      ProfScope prof(MOE_K_BWD_POINTWISE, s);
+      k_sum2_f32<<<blocks, 256, 0, s>>>(w.dS, Go[j], w.Gx[j + 1], n);
+      FSM_TRY(check_launch("sum"));
+      dS = w.dS;
+    }
+    moe_layer_grads_t g = grads[j - 1];
+    g.dA = w.Gx[j];
+    FSM_TRY(launch_layer_backward(l, c, w.x[j - 1], w.logits[j - 1], w.idx[j - 1], w.w[j - 1], w.off[j - 1],
+                                  w.src[j - 1], w.dest[j - 1], w.Y[j - 1], Go[j], dS, g, w.layer_ws, s));
+    ProfScope prof(MOE_K_BWD_POINTWISE, s);
+    k_add_f32<<<blocks, 256, 0, s>>>(Go[j - 1], Go[j], n);
+    float* target = j == 1 ? Go[0] : (!skip(j - 2) ? Go[j - 1] : Go[j - 2]);
+    k_add_f32<<<blocks, 256, 0, s>>>(target, w.Gx[j], n);
+    FSM_TRY(check_launch("gradient sums"));
+    if (grads[j - 1].dA) {
+      k_fill_f32<<<blocks, 256, 0, s>>>(grads[j - 1].dA, n, 0.f);
+      k_add_f32<<<blocks, 256, 0, s>>>(grads[j - 1].dA, w.Gx[j], n);
+      FSM_TRY(check_launch("layer input gradient"));
+    }
+  }
+  return MOE_OK;
 }
 #undef FSM_TRY
 

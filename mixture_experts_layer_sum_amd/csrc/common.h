@@ -92,7 +92,11 @@ size_t layer_bwd_ws_bytes(const moe_stack_cfg_t& c);
 int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, const void* A, const float* logits,
                           const int32_t* idx, const float* topk_w, const int32_t* offsets,
                           const int32_t* sorted_src, const int32_t* dest_row, const void* Y, const float* dOut,
-                          const moe_layer_grads_t& gr, void* ws, hipStream_t s);
+                          const float* dOut_shared, const moe_layer_grads_t& gr, void* ws, hipStream_t s);
+size_t stack_bwd_ws_bytes(const moe_stack_cfg_t& c, int32_t L);
+int launch_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
+                          const uint8_t* mask, const float* o0, const float* dOL, float* dO0,
+                          const moe_layer_grads_t* grads, void* ws, hipStream_t s);
 int launch_mx_quantize(const void* X, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 size_t mx_swiglu_ws_bytes(int64_t N, int32_t G, int64_t c);
 // the grouped SwiGLU MLP on MXFP8 operands (gather as in launch_grouped_swiglu); Y in bf16

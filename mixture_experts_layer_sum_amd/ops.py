@@ -223,17 +223,43 @@ def layer_backward_workspace_bytes(cfg: StackCfg) -> int:
 GRAD_NAMES = ("dA", "dW_R", "dbias", "dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3")
 
 
+def _grads(grads: dict) -> LayerGrads:
+    return LayerGrads(*[None if grads.get(n) is None else grads[n].data_ptr() for n in GRAD_NAMES])
+
+
 def moe_layer_backward(W: dict, cfg: StackCfg, A, logits, topk_idx, topk_w, expert_offsets, sorted_src, dest_row, Y,
-                       dOut, grads: dict, ws=None, stream=None):
+                       dOut, grads: dict, ws=None, stream=None, dOut_shared=None):
     """Gradients of one MoE sublayer's output for dOut (float32 [T, d]) into the float32 tensors of
-    grads (keys as GRAD_NAMES; dbias and the shared ones may be absent)."""
+    grads (keys as GRAD_NAMES; dbias and the shared ones may be absent).  dOut_shared: the shared
+    experts' own output gradient (default dOut)."""
     if ws is None:
         ws = workspace(layer_backward_workspace_bytes(cfg), A.device)
-    g = LayerGrads(*[None if grads.get(n) is None else grads[n].data_ptr() for n in GRAD_NAMES])
     check("moe_layer_backward",
           lib.moe_layer_backward(ctypes.byref(layer_desc(W)), ctypes.byref(cfg), _p(A), _p(logits), _p(topk_idx),
                                  _p(topk_w), _p(expert_offsets), _p(sorted_src), _p(dest_row), _p(Y), _p(dOut),
-                                 ctypes.byref(g), _p(ws), ws.numel(), _s(stream)))
+                                 _p(dOut_shared), ctypes.byref(_grads(grads)), _p(ws), ws.numel(), _s(stream)))
+
+
+def stack_backward_workspace_bytes(cfg: StackCfg, L: int) -> int:
+    return int(lib.farskip_stack_backward_workspace_bytes(ctypes.byref(cfg), L))
+
+
+def farskip_stack_backward(layers: Sequence[dict], cfg: StackCfg, mode, o0, dOL, dO0, grads: Sequence[dict], ws=None,
+                           skip_mask=None, stream=None):
+    """dO0 = dLoss/do_0 and each layer's gradients (grads[j] as for moe_layer_backward; its dA, if
+    given, receives dLoss/dx_j) of the FarSkip stack for dOL = dLoss/do_L."""
+    L = len(layers)
+    descs = (LayerDesc * L)(*[layer_desc(W) for W in layers])
+    gs = (LayerGrads * L)(*[_grads(g) for g in grads])
+    mask = None
+    if skip_mask is not None:
+        mask = (ctypes.c_uint8 * L)(*[1 if m else 0 for m in skip_mask])
+    if ws is None:
+        ws = workspace(stack_backward_workspace_bytes(cfg, L), o0.device)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    check("farskip_stack_backward",
+          lib.farskip_stack_backward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(dOL), _p(dO0), gs, _p(ws),
+                                     ws.numel(), _s(stream)))
 
 
 def profile_enable(on: bool = True) -> None:

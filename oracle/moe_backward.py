@@ -27,7 +27,10 @@ store=None everything is exact.
 Pins (tests/test_oracle_backward_pins.py): central finite differences of moe_oracle.moe_layer in
 float64 for every gradient separately (A, W_R, bias, W1, W2, W3, Ws1, Ws2, Ws3) over the gate
 variants, plus closed forms (an expert without rows has zero weight gradients; one expert top-1
-softmax passes no gradient to the router; dOut = 0 gives zero; linearity in dOut).
+softmax passes no gradient to the router; dOut = 0 gives zero; linearity in dOut).  The stack's
+backward (moe_stack_backward) is pinned by finite differences of moe_oracle.moe_stack for do_0 and
+every layer's weights in all three modes and with mixed skip masks, and a one-layer stack equals
+the layer plus the identity.
 """
 from __future__ import annotations
 
@@ -158,11 +161,14 @@ def shared_mlp_backward(A, Ws1, Ws2, Ws3, n_shared, c_shared, dS, store=None):
     return dA, dWs1, dWs2, dWs3
 
 
-def moe_layer_backward(A, W, k, gate, renormalize, dOut, n_shared=0, c_shared=0, store=None, fwd=None):
+def moe_layer_backward(A, W, k, gate, renormalize, dOut, n_shared=0, c_shared=0, store=None, fwd=None,
+                       dOut_shared=None):
     """Gradients of out = S(A) + R(A) (moe_oracle.moe_layer) for output gradient dOut [T, d].
 
     W as for moe_layer.  fwd: optionally the forward's dict (moe_layer's return value; its Y then
-    plays the saved expert outputs).  Returns a dict with dA, dW_R, dbias, dW1, dW2, dW3 and, with
+    plays the saved expert outputs).  dOut_shared: the shared experts' own output gradient when it
+    differs from the routed part's (in a FarSkip stack the shared output also feeds the next
+    layer's input); default dOut.  Returns a dict with dA, dW_R, dbias, dW1, dW2, dW3 and, with
     shared experts, dWs1, dWs2, dWs3; also the intermediates dY, dw and dlogits."""
     A = _f64(A)
     if fwd is None:
@@ -176,7 +182,47 @@ def moe_layer_backward(A, W, k, gate, renormalize, dOut, n_shared=0, c_shared=0,
     dA = unpermute_sum(dXp, dest, k) + dA_r
     out = dict(dA=dA, dW_R=dW_R, dbias=dbias, dW1=dW1, dW2=dW2, dW3=dW3, dY=dY, dw=dw, dlogits=dlogits)
     if n_shared:
-        dA_s, dWs1, dWs2, dWs3 = shared_mlp_backward(A, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared, dOut,
-                                                     store)
+        dS = dOut if dOut_shared is None else dOut_shared
+        dA_s, dWs1, dWs2, dWs3 = shared_mlp_backward(A, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared, dS, store)
         out.update(dA=dA + dA_s, dWs1=dWs1, dWs2=dWs2, dWs3=dWs3)
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# The FarSkip stack (section 3): o_j = o_{j-1} + S_j(x_j) + R_j(x_j), x_1 = o_0, and the next
+# input x_{j+1} = o_j (no skip), o_{j-1} + S_j(x_j) ("partial", 8b) or o_{j-1} ("outdated", 8a).
+# Reverse mode through that graph: o_j feeds o_{j+1}, and x_{j+1} (no skip at layer j) or x_{j+2}
+# (skip at layer j+1); S_j additionally feeds x_{j+1} under "partial".  The layer inputs' rounding
+# to the activation dtype passes the gradient through unchanged (reading: the cast is treated as
+# the identity, as any implementation that backpropagates through a storage cast does).
+# ---------------------------------------------------------------------------------------------
+def moe_stack_backward(o0, layer_weights, k, gate, renormalize, mode, dOL, mask=None, n_shared=0, c_shared=0,
+                       round_inputs=None, store=None):
+    """Gradients of o_L of moe_oracle.moe_stack for dOL = dLoss/do_L.  Returns a dict with do0 and
+    layers (one moe_layer_backward dict per layer, in layer order)."""
+    L = len(layer_weights)
+    mask = [1] * L if mask is None else list(mask)
+    record = []
+    om.moe_stack(o0, layer_weights, k, gate, renormalize, mode, mask, n_shared, c_shared, round_inputs, record,
+                 store)
+    zero = np.zeros_like(_f64(o0))
+    Go = [zero.copy() for _ in range(L + 1)]      # dLoss/do_j, j = 0 .. L
+    Gx = [zero.copy() for _ in range(L + 2)]      # dLoss/dx_j, j = 1 .. L (+1 unused)
+    Go[L] = _f64(dOL).copy()
+    skip = [mode != "none" and bool(mask[j]) for j in range(L)]   # skip[j-1]: x_{j+1} bypasses o_j
+    grads = [None] * L
+    for j in range(L, 0, -1):
+        W = layer_weights[j - 1]
+        dS = Go[j] + (Gx[j + 1] if (mode == "partial" and skip[j - 1] and j < L) else 0.0)
+        g = moe_layer_backward(record[j - 1][0], W, k, gate, renormalize, Go[j], n_shared, c_shared, store,
+                               dOut_shared=dS)
+        grads[j - 1] = g
+        Gx[j] = g["dA"]
+        Go[j - 1] += Go[j]
+        if j == 1:
+            Go[0] += Gx[1]
+        elif not skip[j - 2]:
+            Go[j - 1] += Gx[j]
+        else:
+            Go[j - 2] += Gx[j]
+    return dict(do0=Go[0], layers=grads)

@@ -204,3 +204,55 @@ def test_layer_backward_dsv3_full_size_sampled(ops):
             assert_parity(grads[key][e].cpu().numpy(), ref, BF, f"{key} of expert {e}")
     for key in ("dA", "dW_R", "dWs1", "dWs2", "dWs3"):
         assert torch.isfinite(grads[key]).all().item(), key
+
+
+# =================================================================================================
+# FarSkip stack backward
+# =================================================================================================
+def clean_stack_input(o0, layers64, k, gate, renorm, mode, mask, cs, delta=0.05, seed=0):
+    """Redraw the token rows whose top-k choice is within delta of a tie at any layer of the
+    oracle's forward (tokens are independent through the stack), so that both sides choose alike."""
+    o0 = o0.copy()
+    rng = np.random.default_rng(seed)
+    for _ in range(30):
+        rec = []
+        oracle.moe_stack(o0, layers64, k, gate, renorm, mode, mask, 1 if cs else 0, cs, oracle.round_to_bf16, rec,
+                         oracle.round_to_bf16)
+        gap = np.full(o0.shape[0], np.inf)
+        for j, (x, *_rest) in enumerate(rec):
+            L = oracle.router_logits(x, layers64[j]["W_R"], layers64[j].get("bias"))
+            gap = np.minimum(gap, oracle.topk_gap(L, k))
+        bad = gap < delta
+        if not bad.any():
+            return o0
+        o0[bad] = rng.standard_normal((int(bad.sum()), o0.shape[1]))
+    raise AssertionError("could not draw a stack input without near-ties")
+
+
+@pytest.mark.parametrize("mode,mask", [("none", None), ("partial", None), ("outdated", None),
+                                       ("partial", [1, 0, 1]), ("outdated", [0, 1, 1])])
+def test_stack_backward_matches_oracle(ops, mode, mask):
+    T, d, E, k, c, cs, L = 256, 128, 8, 2, 128, 128, 3
+    gate, renorm = "softmax", True
+    layers = [make_layer(mi.seed_for(87, j, 1), T, d, E, c, cs, bias=(j == 1))[1] for j in range(L)]
+    layers64 = [oracle_weights64(W) for W in layers]
+    o0 = clean_stack_input(mi.normal((T, d), 1.0, mi.seed_for(87, 0, 9)).numpy().astype(np.float64), layers64, k, gate,
+                           renorm, mode, mask, cs, seed=mi.seed_for(87, 0, 10))
+    dOL = mi.normal((T, d), 1.0, mi.seed_for(87, 0, 11)).numpy().astype(np.float64)
+    Wd = [{key: (v.to(DEV) if v is not None else None) for key, v in W.items()} for W in layers]
+    f32 = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    grads = [{"dA": f32(T, d), "dW_R": f32(E, d), "dbias": f32(E) if W["bias"] is not None else None,
+              "dW1": f32(E, c, d), "dW2": f32(E, c, d), "dW3": f32(E, d, c), "dWs1": f32(cs, d), "dWs2": f32(cs, d),
+              "dWs3": f32(d, cs)} for W in layers]
+    o0d = torch.from_numpy(o0.astype(np.float32)).to(DEV)
+    dOLd = torch.from_numpy(dOL.astype(np.float32)).to(DEV)
+    dO0 = f32(T, d)
+    cfg = ops.stack_cfg(T, d, c, cs, E, k, gate, renorm, BF)
+    ops.farskip_stack_backward(Wd, cfg, mode, o0d, dOLd, dO0, grads, skip_mask=mask)
+    torch.cuda.synchronize()
+    ref = ob.moe_stack_backward(o0, layers64, k, gate, renorm, mode, dOL, mask, n_shared=1, c_shared=cs,
+                                round_inputs=oracle.round_to_bf16, store=oracle.round_to_bf16)
+    assert_parity(to_np(dO0), ref["do0"], BF, "dO0")
+    for j in range(L):
+        for key in ("dA", "dW_R", "dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3") + (("dbias",) if j == 1 else ()):
+            assert_parity(to_np(grads[j][key]), ref["layers"][j][key], BF, f"layer {j} {key}")

@@ -106,3 +106,50 @@ def test_zero_output_gradient_and_linearity():
     g12 = ob.moe_layer_backward(A, W, 2, "sigmoid", True, 2 * d1 - d2, **kw)
     for key in ("dA", "dW_R", "dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3"):
         np.testing.assert_allclose(g12[key], 2 * g1[key] - g2[key], rtol=1e-10, atol=1e-10)
+
+
+# ---- the FarSkip stack ----------------------------------------------------------------------------
+def stack_case(seed, L=3, T=4, d=8, c=6, E=4, k=2, cs=4):
+    rng = np.random.default_rng(seed)
+    layers = []
+    for _ in range(L):
+        layers.append({"W_R": rng.standard_normal((E, d)), "bias": None,
+                       "W1": rng.standard_normal((E, c, d)) * 0.4, "W2": rng.standard_normal((E, c, d)) * 0.4,
+                       "W3": rng.standard_normal((E, d, c)) * 0.4, "Ws1": rng.standard_normal((cs, d)) * 0.4,
+                       "Ws2": rng.standard_normal((cs, d)) * 0.4, "Ws3": rng.standard_normal((d, cs)) * 0.4})
+    return rng, rng.standard_normal((T, d)), layers, rng.standard_normal((T, d))
+
+
+@pytest.mark.parametrize("mode,mask", [("none", None), ("partial", None), ("outdated", None),
+                                       ("partial", [1, 0, 1]), ("outdated", [0, 1, 1])])
+def test_stack_gradients_match_finite_differences(mode, mask):
+    rng, o0, layers, dOL = stack_case(21)
+    k, gate, renorm = 2, "softmax", True
+    kw = dict(mask=mask, n_shared=1, c_shared=4)
+    g = ob.moe_stack_backward(o0, layers, k, gate, renorm, mode, dOL, **kw)
+
+    def loss(o, lays):
+        return float(np.sum(dOL * om.moe_stack(o, lays, k, gate, renorm, mode, **kw)))
+
+    V = rng.standard_normal(o0.shape)
+    fd = (loss(o0 + EPS * V, layers) - loss(o0 - EPS * V, layers)) / (2 * EPS)
+    an = float(np.sum(g["do0"] * V))
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"do0: {fd!r} vs {an!r}"
+    for j in range(len(layers)):
+        for name, key in (("W_R", "dW_R"), ("W1", "dW1"), ("W3", "dW3"), ("Ws2", "dWs2"), ("Ws3", "dWs3")):
+            V = rng.standard_normal(layers[j][name].shape)
+            plus = [dict(l) for l in layers]
+            minus = [dict(l) for l in layers]
+            plus[j][name] = layers[j][name] + EPS * V
+            minus[j][name] = layers[j][name] - EPS * V
+            fd = (loss(o0, plus) - loss(o0, minus)) / (2 * EPS)
+            an = float(np.sum(g["layers"][j][key] * V))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"layer {j} {name}: {fd!r} vs {an!r}"
+
+
+def test_stack_of_one_layer_is_the_layer_plus_identity():
+    rng, o0, layers, dOL = stack_case(22, L=1)
+    for mode in ("none", "partial", "outdated"):
+        g = ob.moe_stack_backward(o0, layers, 2, "sigmoid", True, mode, dOL, n_shared=1, c_shared=4)
+        gl = ob.moe_layer_backward(o0, layers[0], 2, "sigmoid", True, dOL, n_shared=1, c_shared=4)
+        np.testing.assert_allclose(g["do0"], dOL + gl["dA"], rtol=1e-12, atol=1e-12)

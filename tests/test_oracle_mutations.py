@@ -268,3 +268,30 @@ def test_planted_backward_mistake_is_caught(i, monkeypatch):
     monkeypatch.setattr(ob, name, bad)
     with pytest.raises((AssertionError, ValueError, IndexError)):
         _fd_cases()
+
+
+# ---- the stack's gradient routing -----------------------------------------------------------------
+def _stack_backward_without_shared_feed(o0, layer_weights, k, gate, renormalize, mode, dOL, mask=None, n_shared=0,
+                                        c_shared=0, round_inputs=None, store=None):
+    # "partial" treated like "outdated" in the reverse pass: S_j no longer receives dLoss/dx_{j+1}
+    m = "outdated" if mode == "partial" else mode
+    g = STACK_ORIG(o0, layer_weights, k, gate, renormalize, m, dOL, mask, n_shared, c_shared, round_inputs, store)
+    return g
+
+
+def _stack_backward_skip_to_wrong_output(o0, layer_weights, k, gate, renormalize, mode, dOL, mask=None, n_shared=0,
+                                         c_shared=0, round_inputs=None, store=None):
+    # the skipped input's gradient sent to o_{j-1} as if there were no skip
+    return STACK_ORIG(o0, layer_weights, k, gate, renormalize, "none", dOL, mask, n_shared, c_shared, round_inputs,
+                      store)
+
+
+STACK_ORIG = ob.moe_stack_backward
+
+
+@pytest.mark.parametrize("bad", [_stack_backward_without_shared_feed, _stack_backward_skip_to_wrong_output],
+                         ids=["without_shared_feed", "skip_to_wrong_output"])
+def test_planted_stack_backward_mistake_is_caught(bad, monkeypatch):
+    monkeypatch.setattr(ob, "moe_stack_backward", bad)
+    with pytest.raises(AssertionError):
+        bpins.test_stack_gradients_match_finite_differences("partial", None)
