@@ -68,7 +68,7 @@ def measured_traffic():
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     lines = open(TRAFFIC_PROFILE).read().splitlines()
-    digest = next((l.split()[-1] for l in lines if l.startswith("# library source digest")), None)
+    digest = next((l.split()[5] for l in lines if l.startswith("# grouped GEMM source digest")), None)
     if digest != source_digest():
         return None
     for l in lines:

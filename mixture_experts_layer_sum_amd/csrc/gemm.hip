@@ -53,6 +53,9 @@ struct GemmArgs {
 // gathered from the token matrix through the dispatch permutation (the permuted copy of the
 // activations is then never written).
 enum { ROWS_GROUPED = 0, ROWS_SINGLE = 1, ROWS_GATHER = 2 };
+// The backward pass's products read rows as ROWS_GROUPED / ROWS_SINGLE do; their own values give
+// them their own symbols, so profilers tell them from the forward's launches.
+enum { ROWS_GROUPED_BWD = 3, ROWS_SINGLE_BWD = 4 };
 
 // ------------------------------------------------------------------------------------------------
 // M-tile table: tile_start[g] = sum_{g' < g} ceil(count_g' / BM), and tile_group[t] = the group of
@@ -675,11 +678,11 @@ int launch_bf16_product(int epi, const void* X, const int32_t* offsets, const in
   else if (epi == EPI_UG)
     k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_UG, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
   else if (epi == EPI_PLAIN && grp)
-    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_GROUPED, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_GROUPED_BWD, C.bk, C.st><<<grid, nt, 0, s>>>(a);
   else if (epi == EPI_PLAIN)
-    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_PLAIN, ROWS_SINGLE_BWD, C.bk, C.st><<<grid, nt, 0, s>>>(a);
   else
-    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_F32_BIAS, ROWS_SINGLE, C.bk, C.st><<<grid, nt, 0, s>>>(a);
+    k_gemm_bf16<C.bm, C.bn, C.wm, C.wn, EPI_F32_BIAS, ROWS_SINGLE_BWD, C.bk, C.st><<<grid, nt, 0, s>>>(a);
   return check_launch("backward product");
 }
 

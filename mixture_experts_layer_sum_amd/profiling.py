@@ -31,14 +31,18 @@ LIB_PREFIX = "fsm::"
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-def source_digest() -> str:
-    """sha1 over the library's HIP sources (names and contents), to tie a profile to a build."""
+# the sources the bf16 grouped GEMM (k_gemm_bf16, the stack's dominant kernel) is compiled from
+GEMM_SOURCES = ("common.h", "gemm.hip", "tile_kit.h")
+
+
+def source_digest(files=GEMM_SOURCES) -> str:
+    """sha1 over the named HIP sources (names and contents), to tie a profile of the kernels built
+    from them to a build."""
     h = hashlib.sha1()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in sorted(files):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -89,7 +93,7 @@ def short(name: str, width: int = 90) -> str:
 
 
 def cmd_stats(path):
-    print(f"# library source digest {source_digest()}")
+    print(f"# grouped GEMM source digest {source_digest()} (common.h, gemm.hip, tile_kit.h)")
     print(f"# rocprofv3 kernel statistics ({path.split('/')[-1]}), library kernels")
     print(f"{'kernel':<70} {'calls':>6} {'avg_us':>10} {'total_ms':>10} {'pct':>6}")
     for r in _rows(path):
@@ -134,7 +138,7 @@ def _intersect(x, y):
 
 
 def cmd_trace(path, skip_first=0):
-    print(f"# library source digest {source_digest()}")
+    print(f"# grouped GEMM source digest {source_digest()} (common.h, gemm.hip, tile_kit.h)")
     disp = []
     for r in _rows(path):
         name = _col(r, "Kernel_Name", "KernelName", "Name")
@@ -204,7 +208,7 @@ def _calibrate(per, cn, copy_gib):
 
 
 def cmd_counters(path, copy_gib=0.0):
-    print(f"# library source digest {source_digest()}")
+    print(f"# grouped GEMM source digest {source_digest()} (common.h, gemm.hip, tile_kit.h)")
     per = _per_dispatch(path)
     scale = {}
     if copy_gib > 0:
@@ -230,7 +234,7 @@ def cmd_counters(path, copy_gib=0.0):
 
 
 def cmd_traffic(fetch_path, write_path, copy_gib):
-    print(f"# library source digest {source_digest()}")
+    print(f"# grouped GEMM source digest {source_digest()} (common.h, gemm.hip, tile_kit.h)")
     pf, pw = _per_dispatch(fetch_path), _per_dispatch(write_path)
     sf, bf = _calibrate(pf, "FETCH_SIZE", copy_gib)
     sw, bw = _calibrate(pw, "WRITE_SIZE", copy_gib)

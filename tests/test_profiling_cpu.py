@@ -35,7 +35,7 @@ def test_counters_calibration(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "scale 2.0000" in out
     assert "FETCH_SIZE=2000" in out and "(0.004 GB calibrated)" in out
-    assert "library source digest" in out
+    assert "grouped GEMM source digest" in out
 
 
 def test_stats_filters_library_kernels(tmp_path, capsys):
