@@ -229,20 +229,22 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
 #define MX_FRAG_B(BUF, J, OUT) MX_FRAG(BUF, b_lo + MX_BROW(J) * RB, b_hi + MX_BROW(J) * RB, OUT)
 #define MX_SC_A(BUF, I) int(MX_SM(BUF)[a_sc + (I) * 64])
 #define MX_SC_B(BUF, J) int(MX_SM(BUF)[b_sc + MX_BROW(J) * 4])
-  // one stage: the B fragments and their scales, then per A row block the next block's fragment
-  // and scale are read before the current block's FN MFMAs; scheduling groups pin that order so
-  // an LDS read is always in flight under FN MFMAs
+  // one stage: the first A fragment, then the B fragments (so the first MFMA waits only for the
+  // first A and B fragment), then per A row block the next block's fragment and scale are read
+  // before the current block's FN MFMAs; scheduling groups pin that order so an LDS read is always
+  // in flight under FN MFMAs
 #define MX_COMPUTE(BUF)                                                                         \
   {                                                                                             \
     mx_v8i bf[FN], a_cur, a_nxt;                                                                \
     int bsc[FN], as_cur, as_nxt;                                                                \
+    MX_FRAG_A(BUF, 0, a_cur);                                                                   \
+    as_cur = MX_SC_A(BUF, 0);                                                                   \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                        \
       MX_FRAG_B(BUF, j, bf[j]);                                                                 \
       bsc[j] = MX_SC_B(BUF, j);                                                                 \
     }                                                                                           \
-    MX_FRAG_A(BUF, 0, a_cur);                                                                   \
-    as_cur = MX_SC_A(BUF, 0);                                                                   \
-    __builtin_amdgcn_sched_group_barrier(0x100, 3 * FN + 3, 0);                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                            \
       if (i + 1 < FM) {                                                                         \
         MX_FRAG_A(BUF, i + 1, a_nxt);                                                           \
