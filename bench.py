@@ -299,7 +299,46 @@ def backward(c, layers, o0, reps: int = 2) -> dict:
     out["kernels"] = kinds
     del grads, ws, Y
     torch.cuda.empty_cache()
+    out["stack"] = stack_backward(c, layers, o0, L=2)
     return out
+
+
+def stack_backward(c, layers, o0, L: int = 2, reps: int = 1) -> dict:
+    """farskip_stack_backward over the first L layers (partial inputs): the forward replay plus the
+    L layers' backward passes.  All layers write their weight gradients into one set of buffers
+    (the work is the same; 4 layers' fp32 gradients would not fit beside the weights)."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    T, d, E, cc, cs = c.T, c.d, c.E, c.c, c.shared_width
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"dW_R": f32(E, d), "dW1": f32(E, cc, d), "dW2": f32(E, cc, d), "dW3": f32(E, d, cc)}
+    if cs:
+        g.update(dWs1=f32(cs, d), dWs2=f32(cs, d), dWs3=f32(d, cs))
+    cfg = ops.stack_cfg(T, d, cc, cs, E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_backward_workspace_bytes(cfg, L), dev)
+    dOL = torch.randn((T, d), device=dev) * 0.01
+    dO0 = torch.empty_like(dOL)
+    log(f"stack backward workspace {ws.numel() / 2**30:.1f} GiB, HBM in use "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def call():
+        ops.farskip_stack_backward(layers[:L], cfg, "partial", o0, dOL, dO0, [g] * L, ws=ws)
+
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    assert torch.isfinite(dO0).all().item(), "non-finite stack gradient"
+    del g, ws
+    torch.cuda.empty_cache()
+    return {"layers": L, "mode": "partial", "ms": round(ms, 3), "ms_per_layer": round(ms / L, 3),
+            "tokens_per_s": round(T * L / (ms * 1e-3), 1),
+            "what": "forward replay (keeping inputs, routing, expert outputs) + backward of every layer"}
 
 
 def decode(layers, steps: int = 10) -> dict:

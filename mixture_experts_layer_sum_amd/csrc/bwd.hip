@@ -333,16 +333,37 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
   (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
 #define KG_LDB(BUF, KS, J) \
   (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fb0 + (J) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+// one stage (two K slices of 32): slice 0's B fragments and first A fragment, then per A row block
+// the next A fragment (and, for the first FN blocks, one of slice 1's B fragments) is read before
+// the block's FN MFMAs; slice 1 follows with its A fragments read one block ahead.  Scheduling
+// groups pin that order so an LDS read is always in flight under FN MFMAs.
 #define KG_COMPUTE(BUF)                                                                          \
-  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                             \
-    bf16x8 bf[FN], a_cur, a_nxt;                                                                 \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] = KG_LDB(BUF, ks, j);                   \
-    a_cur = KG_LDA(BUF, ks, 0);                                                                  \
+  {                                                                                              \
+    bf16x8 b0[FN], b1[FN], a_cur, a_nxt;                                                         \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) b0[j] = KG_LDB(BUF, 0, j);                    \
+    a_cur = KG_LDA(BUF, 0, 0);                                                                   \
     __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                      \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                             \
-      if (i + 1 < FM) a_nxt = KG_LDA(BUF, ks, i + 1);                                            \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                             \
+      a_nxt = KG_LDA(BUF, 0, i + 1);                                                             \
+      b1[i] = KG_LDB(BUF, 1, i);                                                                 \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], a_cur, acc[i][j], 0, 0, 0);   \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[i][j], 0, 0, 0);   \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
+      a_cur = a_nxt;                                                                             \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = FN; i < FM; ++i) {                                            \
+      a_nxt = (i + 1 < FM) ? KG_LDA(BUF, 0, i + 1) : KG_LDA(BUF, 1, 0);                          \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[i][j], 0, 0, 0);   \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
+      a_cur = a_nxt;                                                                             \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                             \
+      if (i + 1 < FM) a_nxt = KG_LDA(BUF, 1, i + 1);                                             \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[i][j], 0, 0, 0);   \
       if (i + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
       __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
       a_cur = a_nxt;                                                                             \
