@@ -299,7 +299,6 @@ def backward(c, layers, o0, reps: int = 2) -> dict:
     out["kernels"] = kinds
     del grads, ws, Y
     torch.cuda.empty_cache()
-    out["stack"] = stack_backward(c, layers, o0, L=2)
     return out
 
 
@@ -541,25 +540,44 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    def leg(name, fn):
+        """An optional measurement after the timed steps; a failure is reported in its field (and
+        on stderr) instead of costing the whole result line."""
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001
+            log(f"{name} failed: {type(e).__name__}: {e}")
+            try:
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+            except Exception:  # noqa: BLE001
+                pass
+            return {"error": f"{type(e).__name__}: {e}"}
+
     if args.decode and c.name == "dsv3-stack":
         log("timing the decode-shaped stack")
-        result["decode"] = decode(layers)
+        result["decode"] = leg("decode", lambda: decode(layers))
     if args.mxfp8 and c.name == "dsv3-stack":
         log("timing the MXFP8 routed experts")
-        result["mxfp8"] = mxfp8(c, layers, o0)
-    if args.backward and c.name == "dsv3-stack":
-        del ws
-        torch.cuda.empty_cache()
-        log("timing the backward pass of one layer")
-        result["backward"] = backward(c, layers, o0)
+        result["mxfp8"] = leg("mxfp8", lambda: mxfp8(c, layers, o0))
     if args.standalone:
         log("timing the single calls alone and the ceilings")
-        result["standalone"] = standalone(c, layers, o0)
+        result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
     if args.cpu_sample > 0:
         log("timing the CPU oracle on a token sample")
-        result["cpu_baseline"] = cpu_baseline(c, layers, o0, args.cpu_sample)
+        result["cpu_baseline"] = leg("cpu_baseline", lambda: cpu_baseline(c, layers, o0, args.cpu_sample))
     else:
         result["cpu_baseline"] = None
+    if args.backward and c.name == "dsv3-stack":
+        # last: the backward legs hold the most memory; the stack workspace and the weights of the
+        # layers they do not use are released first
+        del ws
+        del layers[2:]
+        torch.cuda.empty_cache()
+        log("timing the backward pass of one layer")
+        result["backward"] = leg("backward", lambda: backward(c, layers, o0))
+        log("timing the backward pass of the stack's first two layers")
+        result["backward"]["stack"] = leg("stack backward", lambda: stack_backward(c, layers, o0, L=2))
     print(json.dumps(result), flush=True)
 
 
