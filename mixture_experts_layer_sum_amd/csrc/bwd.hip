@@ -25,8 +25,6 @@
 namespace fsm {
 
 namespace {
-__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
-
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -76,6 +74,58 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const float* __restrict__ d
           make_uint4(pack2(g0.x, g0.y), pack2(g0.z, g0.w), pack2(g1.x, g1.y), pack2(g1.z, g1.w));
     }
   }
+}
+
+// The same with k fixed at compile time: one pass over the columns serves all k slots (dOut is read
+// once), and the k dot products are reduced together.
+template <int KK>
+__global__ __launch_bounds__(256) void k_combine_bwd_k(const float* __restrict__ dOut, const uint16_t* __restrict__ Y,
+                                                       const float* __restrict__ w, const int32_t* __restrict__ dest,
+                                                       int32_t d, uint16_t* __restrict__ dY, float* __restrict__ dw,
+                                                       const float* __restrict__ dS, uint16_t* __restrict__ dS_b) {
+  __shared__ float red[4][KK];
+  const int64_t t = blockIdx.x;
+  const float* g = dOut + t * d;
+  int64_t r[KK];
+  float wi[KK], part[KK];
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    r[i] = dest[t * KK + i];
+    wi[i] = w[t * KK + i];
+    part[i] = 0.f;
+  }
+  for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
+    const float4 g0 = *reinterpret_cast<const float4*>(g + col), g1 = *reinterpret_cast<const float4*>(g + col + 4);
+    uint4 yv[KK];
+#pragma unroll
+    for (int i = 0; i < KK; ++i) yv[i] = *reinterpret_cast<const uint4*>(Y + r[i] * d + col);
+#pragma unroll
+    for (int i = 0; i < KK; ++i) {
+      float y[8];
+      unpack8(yv[i], y);
+      part[i] += g0.x * y[0] + g0.y * y[1] + g0.z * y[2] + g0.w * y[3] + g1.x * y[4] + g1.y * y[5] + g1.z * y[6] +
+                 g1.w * y[7];
+      *reinterpret_cast<uint4*>(dY + r[i] * d + col) =
+          make_uint4(pack2(wi[i] * g0.x, wi[i] * g0.y), pack2(wi[i] * g0.z, wi[i] * g0.w),
+                     pack2(wi[i] * g1.x, wi[i] * g1.y), pack2(wi[i] * g1.z, wi[i] * g1.w));
+    }
+    if (dS_b) {
+      const float* gs = dS + t * d;
+      const float4 s0 = *reinterpret_cast<const float4*>(gs + col), s1 = *reinterpret_cast<const float4*>(gs + col + 4);
+      *reinterpret_cast<uint4*>(dS_b + t * d + col) =
+          make_uint4(pack2(s0.x, s0.y), pack2(s0.z, s0.w), pack2(s1.x, s1.y), pack2(s1.z, s1.w));
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    float v = part[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave][i] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < KK) dw[t * KK + threadIdx.x] = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
 }
 
 // ---- gate backward: one wave per token ----------------------------------------------------------
@@ -551,9 +601,22 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
 
   {  // Combine and gate backward, the bias gradient, unit weights for the final sum
     ProfScope prof(MOE_K_BWD_POINTWISE, s);
-    k_combine_bwd<<<unsigned(T), 256, 0, s>>>(dOut, static_cast<const uint16_t*>(Y), topk_w, dest_row, int32_t(d),
-                                              int32_t(k), w.dY, w.dw, dOut_shared ? dOut_shared : dOut,
-                                              cs > 0 ? w.dOut_b : nullptr);
+    const uint16_t* Yb = static_cast<const uint16_t*>(Y);
+    const float* dS = dOut_shared ? dOut_shared : dOut;
+    uint16_t* dS_b = cs > 0 ? w.dOut_b : nullptr;
+    if (k == 8)
+      k_combine_bwd_k<8><<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), w.dY, w.dw, dS, dS_b);
+    else if (k == 6)
+      k_combine_bwd_k<6><<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), w.dY, w.dw, dS, dS_b);
+    else if (k == 4)
+      k_combine_bwd_k<4><<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), w.dY, w.dw, dS, dS_b);
+    else if (k == 2)
+      k_combine_bwd_k<2><<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), w.dY, w.dw, dS, dS_b);
+    else if (k == 1)
+      k_combine_bwd_k<1><<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), w.dY, w.dw, dS, dS_b);
+    else
+      k_combine_bwd<<<unsigned(T), 256, 0, s>>>(dOut, Yb, topk_w, dest_row, int32_t(d), int32_t(k), w.dY, w.dw, dS,
+                                                dS_b);
     FSM_TRY(check_launch("combine backward"));
     k_gate_bwd<<<unsigned(cdiv(T, 4)), 256, 0, s>>>(logits, idx, w.dw, T, E, int32_t(k), c.gate, c.renormalize,
                                                      w.dLf, w.dL_b, int32_t(Ep));
@@ -661,6 +724,11 @@ __global__ void k_two_offsets(int32_t* off, int32_t T) {
 }
 
 namespace {
+int copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
+  const hipError_t e = hipMemcpyAsync(dst, src, size_t(n) * 4, hipMemcpyDeviceToDevice, s);
+  return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+}
+
 struct StackBwdWs {
   std::vector<void*> x, Y;
   std::vector<float*> logits, w;
@@ -762,10 +830,8 @@ int launch_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_s
       k_fill_f32<<<blocks, 256, 0, s>>>(Go[j], n, 0.f);
       FSM_TRY(check_launch("fill"));
     }
-    k_fill_f32<<<blocks, 256, 0, s>>>(Go[L], n, 0.f);
-    k_add_f32<<<blocks, 256, 0, s>>>(Go[L], dOL, n);
-    FSM_TRY(check_launch("copy"));
   }
+  FSM_TRY(copy_f32(Go[L], dOL, n, s));
   for (int j = L; j >= 1; --j) {
     const moe_layer_desc_t& l = layers[j - 1];
     const float* dS = Go[j];
@@ -784,11 +850,7 @@ int launch_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_s
     float* target = j == 1 ? Go[0] : (!skip(j - 2) ? Go[j - 1] : Go[j - 2]);
     k_add_f32<<<blocks, 256, 0, s>>>(target, w.Gx[j], n);
     FSM_TRY(check_launch("gradient sums"));
-    if (grads[j - 1].dA) {
-      k_fill_f32<<<blocks, 256, 0, s>>>(grads[j - 1].dA, n, 0.f);
-      k_add_f32<<<blocks, 256, 0, s>>>(grads[j - 1].dA, w.Gx[j], n);
-      FSM_TRY(check_launch("layer input gradient"));
-    }
+    if (grads[j - 1].dA) FSM_TRY(copy_f32(grads[j - 1].dA, w.Gx[j], n, s));
   }
   return MOE_OK;
 }

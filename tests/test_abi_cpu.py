@@ -193,3 +193,80 @@ def test_python_binding_refuses_unknown_dtype():
     from mixture_experts_layer_sum_amd import ops
     with pytest.raises(TypeError):
         ops.dtype_code(torch.float16)
+
+
+def test_mxfp8_argument_errors():
+    q = lib.moe_mx_quantize
+    err(q(BAD, 4, 48, BAD, BAD, None), L.MOE_ERR_UNSUPPORTED, "multiple of 32")
+    err(q(None, 4, 64, BAD, BAD, None), L.MOE_ERR_INVALID_ARG)
+    assert q(None, 0, 64, None, None, None) == L.MOE_OK   # nothing to do
+    f = lib.moe_grouped_swiglu_mxfp8
+    need = lib.moe_grouped_swiglu_mxfp8_workspace_bytes(100, 4, 256)
+    assert need >= 100 * 256 + 100 * 8
+    ok = [BAD, BAD, 100, None, 1, BAD, 4, BAD, BAD, BAD, BAD, BAD, BAD, 100, 256, 256, BAD, BAD, need, None]
+    bad = list(ok)
+    bad[14] = 192                                    # d % 128 != 0
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "128")
+    bad = list(ok)
+    bad[18] = need - 1
+    err(f(*bad), L.MOE_ERR_WORKSPACE)
+    bad = list(ok)
+    bad[2] = 99                                      # without sorted_src x_rows must equal N
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "x_rows")
+    bad = list(ok)
+    bad[3], bad[4] = BAD, 0                          # gathered with k = 0
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "k=0")
+    bad = list(ok)
+    bad[11] = None                                   # W3 codes missing
+    err(f(*bad), L.MOE_ERR_INVALID_ARG)
+    g = lib.moe_grouped_mxfp8_gate_up
+    pneed = lib.moe_grouped_mxfp8_phase_workspace_bytes(100, 4)
+    assert 0 < pneed < need
+    err(g(BAD, BAD, 100, None, 1, BAD, 4, BAD, BAD, BAD, BAD, 100, 256, 256, None, BAD, BAD, pneed, None),
+        L.MOE_ERR_INVALID_ARG, "Hq")
+    dn = lib.moe_grouped_mxfp8_down
+    err(dn(BAD, BAD, BAD, 4, BAD, BAD, 100, 256, 256, BAD, BAD, pneed - 1, None), L.MOE_ERR_WORKSPACE)
+
+
+def test_backward_argument_errors():
+    f = lib.moe_layer_backward
+    cfg = _cfg(dtype=1)
+    need = lib.moe_layer_backward_workspace_bytes(ctypes.byref(cfg))
+    assert need > 0
+    desc = L.LayerDesc(W_R=0x1000, W1=0x1000, W2=0x1000, W3=0x1000)
+    grads = L.LayerGrads(dA=0x1000, dW_R=0x1000, dW1=0x1000, dW2=0x1000, dW3=0x1000)
+    ok = [ctypes.byref(desc), ctypes.byref(cfg)] + [BAD] * 9 + [None, ctypes.byref(grads), BAD, need, None]
+    bad = list(ok)
+    bad[14] = need - 1
+    err(f(*bad), L.MOE_ERR_WORKSPACE)
+    c32 = _cfg(dtype=0)
+    bad = list(ok)
+    bad[1] = ctypes.byref(c32)
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "bf16")
+    c12 = _cfg(dtype=1, E=12)
+    bad = list(ok)
+    bad[1] = ctypes.byref(c12)
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "multiple of 8")
+    no_dw = L.LayerGrads(dA=0x1000, dW_R=0x1000, dW1=0x1000, dW2=0x1000)
+    bad = list(ok)
+    bad[12] = ctypes.byref(no_dw)
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "dW3")
+    bad = list(ok)
+    bad[10] = None                                   # dOut missing
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "dOut")
+    s = lib.farskip_stack_backward
+    sneed = lib.farskip_stack_backward_workspace_bytes(ctypes.byref(cfg), 2)
+    assert sneed > need
+    descs = (L.LayerDesc * 2)(desc, desc)
+    gs = (L.LayerGrads * 2)(grads, grads)
+    sok = [descs, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), gs, BAD, sneed,
+           None]
+    bad = list(sok)
+    bad[7] = bad[6]                                  # dO0 aliases dOL
+    err(s(*bad), L.MOE_ERR_INVALID_ARG, "alias")
+    bad = list(sok)
+    bad[10] = sneed - 1
+    err(s(*bad), L.MOE_ERR_WORKSPACE)
+    bad = list(sok)
+    bad[3] = 5
+    err(s(*bad), L.MOE_ERR_INVALID_ARG, "mode")
