@@ -41,22 +41,17 @@ __device__ __forceinline__ int mx_block_exp(float amax) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
-// Nearest E4M3 code of y (ties to the even code), saturating at +-448; the sign of zero is kept.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {                   // below 2^-6: subnormal codes m * 2^-9, m = 0 .. 8
-    code = uint32_t(rintf(a * 512.0f));  // exact scaling; rintf rounds half to even
-  } else {
-    const uint32_t bits = __float_as_uint(a);
-    const int E = int(bits >> 23) - 127;                  // -6 .. (saturated below)
-    const uint32_t man = bits & 0x7FFFFFu;
-    const uint32_t m3 = (man + 0x7FFFFu + ((man >> 20) & 1u)) >> 20;   // 3 bits, half to even
-    const int c = ((E + 7) << 3) + int(m3);              // m3 == 8 carries into the exponent
-    code = c > 0x7E ? 0x7Eu : uint32_t(c);
-  }
-  return code | sign;
+// Four E4M3 codes of a, b, c, d divided by 2^s, packed little-endian into one word. gfx950's scaled
+// pair conversion divides by its scale operand and rounds to the nearest code, ties to even, keeping
+// the sign of zero; for every value whose quotient lies within +-448 (which the block exponent makes
+// true of a whole block) that is the format's round-to-nearest-even encoding, subnormals included.
+typedef short mx_v2i16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3_word(float a, float b, float c, float d, int s) {
+  const float scale = ldexpf(1.0f, s);   // 2^s; 2^-127 is an fp32 subnormal and still exact
+  mx_v2i16 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  return uint32_t(uint16_t(w[0])) | (uint32_t(uint16_t(w[1])) << 16);
 }
 
 // ---- quantize ------------------------------------------------------------------------------
@@ -78,8 +73,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t* __restrict_
   uint32_t w[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    w[q] = e4m3_code(ldexpf(v[4 * q], -s)) | (e4m3_code(ldexpf(v[4 * q + 1], -s)) << 8) |
-           (e4m3_code(ldexpf(v[4 * q + 2], -s)) << 16) | (e4m3_code(ldexpf(v[4 * q + 3], -s)) << 24);
+    w[q] = e4m3_word(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], s);
   }
   uint4* dst = reinterpret_cast<uint4*>(codes + row * K + blk * 32);
   dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -320,7 +314,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
       }
     }
   } else {
-    // H = U . SiLU(G) in fp32, then MXFP8: a wave's 32 H columns of one row are one block, held by
+    // H = U . SiLU(G) in fp32 (the reciprocal to within one ulp), then MXFP8: a wave's 32 H columns of one row are one block, held by
     // the four lanes with the same lane % 16 (8 values each); the block maximum is a two-step
     // cross-lane max.
     uint8_t* hq = static_cast<uint8_t*>(p.out);
@@ -335,7 +329,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
         const f32x4 u = acc[i][jj], gt = acc[i][jj + FN / 2];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          h[jj][r] = u[r] * silu_f(gt[r]);
+          h[jj][r] = u[r] * gt[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[r]));
           amax = fmaxf(amax, fabsf(h[jj][r]));
         }
       }
@@ -347,8 +341,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
       const int64_t orow = int64_t(row0 + m);
 #pragma unroll
       for (int jj = 0; jj < FN / 2; ++jj) {
-        const uint32_t w = e4m3_code(ldexpf(h[jj][0], -s)) | (e4m3_code(ldexpf(h[jj][1], -s)) << 8) |
-                           (e4m3_code(ldexpf(h[jj][2], -s)) << 16) | (e4m3_code(ldexpf(h[jj][3], -s)) << 24);
+        const uint32_t w = e4m3_word(h[jj][0], h[jj][1], h[jj][2], h[jj][3], s);
         *reinterpret_cast<uint32_t*>(hq + orow * p.n_out + hcol0 + jj * 16 + nl) = w;
       }
       if (q == 0) p.out_s[orow * nb + hcol0 / 32] = uint8_t(s + 127);
