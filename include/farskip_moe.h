@@ -245,12 +245,15 @@ typedef struct {
  *     x_{j+1} = o_{j-1} + S_j(x_j)       if mode == FARSKIP_PARTIAL  (eq. 8b, f* = shared expert),
  *     x_{j+1} = o_{j-1}                  if mode == FARSKIP_OUTDATED (eq. 8a).
  * The residual o_j is kept in float32; each layer input x_j is rounded to cfg->dtype.
- * With the skip on, layer j+1's router and shared expert are enqueued on s_side while layer j's
- * permutation, routed grouped GEMM (rows gathered through the permutation) and combine run on
- * s_main (HIP events order the two).
+ * s_main runs each layer's permutation and routed grouped GEMM (rows gathered through the
+ * permutation), and nothing else.  s_side runs each layer's router and shared expert, the
+ * previous layer's combine and, with the skip on, the next layer's input; with the skip on at
+ * layer j, layer j+1's router and shared expert and layer j-1's combine all run while layer j's
+ * routed GEMM does (HIP events order the two streams).
  * s_side == s_main gives the same results with everything serialised on one stream.  Inputs
  * are taken as ordered on s_main: s_side first waits for all work enqueued on s_main before the
- * call, and the call's last kernel runs on s_main, so the result is ready when s_main is.
+ * call, and s_main's last operation waits for the final combine, so the result is ready when
+ * s_main is.
  *
  *   layers    host array [L] of device-pointer descriptors
  *   cfg       host pointer

@@ -126,10 +126,10 @@ struct StackWs {
   float* w[2];
   int32_t* offsets;
   int32_t* sorted_src;
-  int32_t* dest_row;
+  int32_t* dest_row[2];
   int32_t* shared_off;
   void* perm_ws;
-  void* Y;
+  void* Y[2];
   void* gemm_ws;
   void* shared_ws;
 };
@@ -154,10 +154,10 @@ StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   }
   s.offsets = static_cast<int32_t*>(take((E + 1) * 4));
   s.sorted_src = static_cast<int32_t*>(take(T * k * 4));
-  s.dest_row = static_cast<int32_t*>(take(T * k * 4));
+  for (int b = 0; b < 2; ++b) s.dest_row[b] = static_cast<int32_t*>(take(T * k * 4));
   s.shared_off = static_cast<int32_t*>(take(2 * 4));
   s.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
-  s.Y = take(T * k * d * es);
+  for (int b = 0; b < 2; ++b) s.Y[b] = take(T * k * d * es);
   s.gemm_ws = take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
   s.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype)) : nullptr;
   if (total) *total = off;
@@ -244,39 +244,57 @@ int wait(hipStream_t s, hipEvent_t e) {
   return r == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipStreamWaitEvent: %s", hipGetErrorString(r));
 }
 
-// Layer j (0-based) of the stack; x_j lives in x[j % 2].
-//   side stream: route_j(x_j); S_j = shared_j(x_j); if the skip is on, wait for o_{j-1} and build
-//                x_{j+1} = o_{j-1} (+ S_j when partial)        -> the next layer's router and shared
-//                expert are enqueued right behind it, so they overlap this layer's routed GEMM
-//   main stream: wait route_j; permute_j; routed grouped GEMM_j; wait side_j;
-//                combine_j: o_j = o_{j-1} + S_j + R_j (+ x_{j+1} = o_j when the skip is off)
+// Layer j (0-based) of the stack; x_j, its routing, its expert outputs Y_j and S_j live in
+// buffers [j % 2].
+//   main stream: wait route_j; permute_j; routed grouped GEMM_j (Y_j)  -- nothing else, so the
+//                routed GEMMs of consecutive layers run back to back
+//   side stream: [skip off at j-1: combine_{j-1}, which also writes x_j = o_{j-1}];
+//                route_j(x_j); S_j = shared_j(x_j);
+//                [skip on at j-1: combine_{j-1}: o_{j-1} = o_{j-2} + S_{j-1} + R_{j-1}];
+//                skip on at j: x_{j+1} = o_{j-1} (+ S_j when partial)
+// combine_{j-1} waits for GEMM_{j-1}.  With the skip on, x_{j+1} needs neither R_j nor o_j, so
+// layer j+1's router and shared expert and layer j-1's combine (HBM-bound) all run under layer j's
+// routed GEMM.  The last combine runs after the loop, and s_main waits for it.
+// Buffer reuse: permute_{j+2}, topk_{j+2} and GEMM_{j+2} rewrite what combine_j reads; the main
+// stream reaches them only after waiting for route_{j+2}, which the side stream records after
+// combine_j.  make_input_{j+1} rewrites x_{j-1}, read by GEMM_{j-1}; it follows combine_{j-1}.
 int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
                   const uint8_t* mask, const float* o0, float* oL, void* ws, hipStream_t sm,
                   hipStream_t ss) {
   StackWs w = carve_stack(ws, c, nullptr);
   const bool two = sm != ss;
-  Events E_route, E_side, E_comb, E_entry;
+  Events E_route, E_gemm, E_end;
   if (two) {
     if (int rc = E_route.make(L)) return rc;
-    if (int rc = E_side.make(L)) return rc;
-    if (int rc = E_comb.make(L)) return rc;
-    if (int rc = E_entry.make(1)) return rc;
+    if (int rc = E_gemm.make(L)) return rc;
+    if (int rc = E_end.make(2)) return rc;
     // The inputs (o0, weights) may still be in flight on s_main: s_side starts behind them.
-    if (int rc = record(E_entry.ev[0], sm)) return rc;
-    if (int rc = wait(ss, E_entry.ev[0])) return rc;
+    if (int rc = record(E_end.ev[0], sm)) return rc;
+    if (int rc = wait(ss, E_end.ev[0])) return rc;
   }
   const int64_t N = c.T * c.k;
+  auto skip_at = [&](int j) { return mode != FARSKIP_NONE && (mask ? mask[j] != 0 : true); };
+  // combine_j on the side stream: o_j = o_{j-1} + S_j + R_j into oL (o_{j-1} is o0 for j = 0, else
+  // oL itself), plus x_{j+1} = o_j when layer j has no skip and is not the last
+  auto combine = [&](int j) -> int {
+    const int b = j & 1;
+    if (two)
+      if (int rc = wait(ss, E_gemm.ev[j])) return rc;
+    void* out_x = (!skip_at(j) && j + 1 < L) ? w.x[b ^ 1] : nullptr;
+    return launch_combine(w.Y[b], c.dtype, w.w[b], w.dest_row[b], c.T, c.d, c.k, c.c_shared ? w.S[b] : nullptr,
+                          j == 0 ? o0 : oL, oL, out_x, ss);
+  };
   k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));
   if (int rc = check_launch("stack setup")) return rc;
   if (int rc = launch_make_input(o0, nullptr, c.dtype, c.T, c.d, w.x[0], ss)) return rc;
 
-  const float* o_prev = o0;
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
     const int cur = j & 1, nxt = cur ^ 1;
     const bool last = j + 1 == L;
-    const bool skip = mode != FARSKIP_NONE && (mask ? mask[j] != 0 : true);
-    // side: router and shared expert of layer j
+    // side: layer j's router and shared expert, layer j-1's combine, layer j+1's input
+    if (j > 0 && !skip_at(j - 1))
+      if (int rc = combine(j - 1)) return rc;
     if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
     if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
       return rc;
@@ -287,35 +305,28 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
                                          c.c_shared, w.S[cur], w.shared_ws, ss))
         return rc;
     }
-    if (skip && !last) {
-      if (two && j > 0)
-        if (int rc = wait(ss, E_comb.ev[j - 1])) return rc;
+    if (j > 0 && skip_at(j - 1))
+      if (int rc = combine(j - 1)) return rc;
+    if (skip_at(j) && !last) {
       const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
-      if (int rc = launch_make_input(o_prev, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
+      if (int rc = launch_make_input(j == 0 ? o0 : oL, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
     }
-    if (two)
-      if (int rc = record(E_side.ev[j], ss)) return rc;
     // main: routed path of layer j
     if (two)
       if (int rc = wait(sm, E_route.ev[j])) return rc;
     if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
-                                w.dest_row, nullptr, w.perm_ws, sm))
+                                w.dest_row[cur], nullptr, w.perm_ws, sm))
       return rc;
-    if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y,
+    if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y[cur],
                                        w.gemm_ws, sm, w.sorted_src, c.k, c.T))
       return rc;
     if (two)
-      if (int rc = wait(sm, E_side.ev[j])) return rc;
-    void* out_x = (!skip && !last) ? w.x[nxt] : nullptr;
-    if (int rc = launch_combine(w.Y, c.dtype, w.w[cur], w.dest_row, c.T, c.d, c.k, c.c_shared ? w.S[cur] : nullptr,
-                                o_prev, oL, out_x, sm))
-      return rc;
-    if (two) {
-      if (int rc = record(E_comb.ev[j], sm)) return rc;
-      if (!skip && !last)
-        if (int rc = wait(ss, E_comb.ev[j])) return rc;
-    }
-    o_prev = oL;
+      if (int rc = record(E_gemm.ev[j], sm)) return rc;
+  }
+  if (int rc = combine(L - 1)) return rc;
+  if (two) {
+    if (int rc = record(E_end.ev[1], ss)) return rc;
+    if (int rc = wait(sm, E_end.ev[1])) return rc;
   }
   return MOE_OK;
 }

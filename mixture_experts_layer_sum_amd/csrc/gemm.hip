@@ -216,6 +216,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   const int fb0 = BM * BK + (PAIRED ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
   const int sw = lds_swz<BK>(lane & 15);
 
+  // A wave whose rows all lie past the group's last row (in the ragged last M-tile of a group)
+  // skips its MFMAs and fragment reads: those rows are never stored.  It still loads its share of
+  // every stage and meets every barrier.
+  const bool live = wm * WTM < rows;
+
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   {                                                                                            \
     if (kt + S - 1 < KT) FSM_DMA_STAGE(kt + S - 1, ((J) + S - 1) % S);                         \
     __builtin_amdgcn_sched_barrier(0);                                                         \
-    FSM_COMPUTE(J);                                                                            \
+    if (live) FSM_COMPUTE(J)                                                                   \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     if (++kt >= KT) break;                                                                     \
     if (kt + S - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2)));              \
