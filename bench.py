@@ -116,6 +116,40 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
     return out
 
 
+def ep_share(c, W, A_perm, off, Y, gws, reps: int, ep: int = 8) -> dict:
+    """One GPU's share of the routed experts under expert parallelism over `ep` GPUs: the grouped
+    SwiGLU product over experts [0, E/ep) and the rows routed to them, which arrive from the
+    dispatch exchange already grouped by expert (a slice of the permuted rows)."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    E_loc = c.E // ep
+    n_loc = int(off[E_loc].item())
+    X = A_perm[:n_loc]
+    o = off[:E_loc + 1]
+    W1, W2, W3 = W["W1"][:E_loc], W["W2"][:E_loc], W["W3"][:E_loc]
+    Yl = Y[:n_loc]
+    ops.moe_grouped_swiglu(X, o, W1, W2, W3, Yl, ws=gws)
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    for _ in range(reps):
+        ops.moe_grouped_swiglu(X, o, W1, W2, W3, Yl, ws=gws)
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    prof = ops.profile_collect()
+    row = {"experts": E_loc, "rows": n_loc}
+    for kind, flop in (("gemm_gate_up", 4.0 * n_loc * c.d * c.c), ("gemm_down", 2.0 * n_loc * c.d * c.c)):
+        n, ms = prof.get(kind, (0, 0.0))
+        if n:
+            avg = ms / n
+            row[kind] = {"avg_ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+    if "gemm_gate_up" in row and "gemm_down" in row:
+        tot = row["gemm_gate_up"]["avg_ms"] + row["gemm_down"]["avg_ms"]
+        row["tflops"] = round(6.0 * n_loc * c.d * c.c / (tot * 1e-3) / 1e12, 1)
+    return row
+
+
 def standalone(c, layers, o0, reps: int = 3) -> dict:
     """After the timed steps: the layer-0 calls one at a time on the whole GPU (the stack shares it
     between two streams), including the explicit dispatch row copy that the stack folds into the
@@ -155,6 +189,7 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
     prof = ops.profile_collect()
     rep_ = kernel_report(prof, c, reps)
     out = {k_: rep_[k_] for k_ in ("permute_rows", "gemm_gate_up", "gemm_down", "combine") if k_ in rep_}
+    out["ep8_share"] = ep_share(c, W, A_perm, off, Y, gws, reps)
     del A_perm, Y, gws, pws, logits
     # ceilings: plain device-to-device copy and a large bf16 product (hipBLASLt through torch)
     a = torch.empty(2**30 // 4 * 4, dtype=torch.float32, device=dev)
