@@ -249,23 +249,27 @@ int wait(hipStream_t s, hipEvent_t e) {
 //   main stream: wait route_j; permute_j; routed grouped GEMM_j (Y_j)  -- nothing else, so the
 //                routed GEMMs of consecutive layers run back to back
 //   side stream: [skip off at j-1: combine_{j-1}, which also writes x_j = o_{j-1}];
-//                route_j(x_j); S_j = shared_j(x_j);
+//                route_j(x_j); wait permute_j; S_j = shared_j(x_j);
 //                [skip on at j-1: combine_{j-1}: o_{j-1} = o_{j-2} + S_{j-1} + R_{j-1}];
 //                skip on at j: x_{j+1} = o_{j-1} (+ S_j when partial)
-// combine_{j-1} waits for GEMM_{j-1}.  With the skip on, x_{j+1} needs neither R_j nor o_j, so
-// layer j+1's router and shared expert and layer j-1's combine (HBM-bound) all run under layer j's
-// routed GEMM.  The last combine runs after the loop, and s_main waits for it.
+// With the skip on, x_{j+1} needs neither R_j nor o_j, so layer j+1's router and shared expert
+// and layer j-1's combine (HBM-bound) all run under layer j's routed GEMM.  The side stream's
+// large grids (shared expert, combine) start only once permute_j is done: launched beside them,
+// the permutation's single-block scan would wait for the whole grid to drain, on the main
+// stream's critical path.  The last combine runs after the loop, and s_main waits for it.
 // Buffer reuse: permute_{j+2}, topk_{j+2} and GEMM_{j+2} rewrite what combine_j reads; the main
 // stream reaches them only after waiting for route_{j+2}, which the side stream records after
-// combine_j.  make_input_{j+1} rewrites x_{j-1}, read by GEMM_{j-1}; it follows combine_{j-1}.
+// combine_j.  make_input_{j+1} rewrites x_{j-1}, read by GEMM_{j-1}; it follows the wait for
+// permute_j.  Events are recorded before the waits that name them are enqueued.
 int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
                   const uint8_t* mask, const float* o0, float* oL, void* ws, hipStream_t sm,
                   hipStream_t ss) {
   StackWs w = carve_stack(ws, c, nullptr);
   const bool two = sm != ss;
-  Events E_route, E_gemm, E_end;
+  Events E_route, E_perm, E_gemm, E_end;
   if (two) {
     if (int rc = E_route.make(L)) return rc;
+    if (int rc = E_perm.make(L)) return rc;
     if (int rc = E_gemm.make(L)) return rc;
     if (int rc = E_end.make(2)) return rc;
     // The inputs (o0, weights) may still be in flight on s_main: s_side starts behind them.
@@ -292,14 +296,25 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
     const moe_layer_desc_t& l = layers[j];
     const int cur = j & 1, nxt = cur ^ 1;
     const bool last = j + 1 == L;
-    // side: layer j's router and shared expert, layer j-1's combine, layer j+1's input
+    // side: layer j's router
     if (j > 0 && !skip_at(j - 1))
       if (int rc = combine(j - 1)) return rc;
     if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
     if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
       return rc;
-    if (two)
+    // main: layer j's permutation
+    if (two) {
       if (int rc = record(E_route.ev[j], ss)) return rc;
+      if (int rc = wait(sm, E_route.ev[j])) return rc;
+    }
+    if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
+                                w.dest_row[cur], nullptr, w.perm_ws, sm))
+      return rc;
+    // side: layer j's shared expert, layer j-1's combine, layer j+1's input
+    if (two) {
+      if (int rc = record(E_perm.ev[j], sm)) return rc;
+      if (int rc = wait(ss, E_perm.ev[j])) return rc;
+    }
     if (c.c_shared) {
       if (int rc = launch_grouped_swiglu(w.x[cur], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, c.dtype, c.T, c.d,
                                          c.c_shared, w.S[cur], w.shared_ws, ss))
@@ -311,12 +326,7 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
       const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
       if (int rc = launch_make_input(j == 0 ? o0 : oL, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
     }
-    // main: routed path of layer j
-    if (two)
-      if (int rc = wait(sm, E_route.ev[j])) return rc;
-    if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
-                                w.dest_row[cur], nullptr, w.perm_ws, sm))
-      return rc;
+    // main: layer j's routed GEMMs
     if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y[cur],
                                        w.gemm_ws, sm, w.sorted_src, c.k, c.T))
       return rc;
