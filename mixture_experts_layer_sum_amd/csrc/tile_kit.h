@@ -73,12 +73,14 @@ constexpr int kXcds = 8;
 // XCD blocks of group_m x quad_nb tiles (one block per XCD at a time), ordered in 2 x 2 quads:
 // the four XCDs that run one quad at the same time pair up on M-groups (same activation rows)
 // and on N-blocks (same weight panels), so each line they share is fetched from HBM once and
-// found in the memory-side cache by the other XCD.  Returns the number of workgroups to launch
-// for at most max_mt M-tiles.
+// found in the memory-side cache by the other XCD.  Blocks go by pairs of M-groups; within a
+// pair, the quads of each pair of N-blocks, then (when the N-block count is odd) the last
+// N-block's two blocks, so that no block position is left without a tile.  Returns the number
+// of workgroups to launch for at most max_mt M-tiles.
 inline int64_t quad_grid(int64_t max_mt, int n_tiles, int group_m, int quad_nb) {
   const int64_t n_mg = (max_mt + group_m - 1) / group_m, n_nb = (n_tiles + quad_nb - 1) / quad_nb;
-  const int64_t quads = ((n_mg + 1) / 2) * ((n_nb + 1) / 2);
-  const int64_t rounds = (4 * quads + kXcds - 1) / kXcds;
+  const int64_t blocks = ((n_mg + 1) / 2) * 2 * n_nb;
+  const int64_t rounds = (blocks + kXcds - 1) / kXcds;
   return rounds * kXcds * int64_t(group_m) * quad_nb;
 }
 
@@ -90,9 +92,16 @@ __device__ __forceinline__ bool map_tile(const Args& p, int BM, int& mt, int& nt
     const int blk_tiles = p.group_m * p.quad_nb;
     const int x = b % kXcds, i = b / kXcds;
     const int blk = (i / blk_tiles) * kXcds + x, pos = i % blk_tiles;
-    const int n_nb = (p.n_tiles + p.quad_nb - 1) / p.quad_nb, nq = (n_nb + 1) / 2;
-    const int quad = blk >> 2;
-    const int mg = 2 * (quad / nq) + (blk & 1), nb = 2 * (quad % nq) + ((blk >> 1) & 1);
+    const int n_nb = (p.n_tiles + p.quad_nb - 1) / p.quad_nb, pairs = n_nb / 2;
+    const int row = blk / (2 * n_nb), at = blk % (2 * n_nb);   // M-group pair, block within it
+    int mg, nb;
+    if (at < 4 * pairs) {   // quad at / 4: M-groups 2 row + {0, 1} x N-blocks 2 (at / 4) + {0, 1}
+      mg = 2 * row + (at & 1);
+      nb = 2 * (at >> 2) + ((at >> 1) & 1);
+    } else {                // the odd last N-block: M-groups 2 row + {0, 1}
+      mg = 2 * row + (at - 4 * pairs);
+      nb = n_nb - 1;
+    }
     mt = mg * p.group_m + pos % p.group_m;
     nt = nb * p.quad_nb + pos / p.group_m;
     return mt < total_mt && nt < p.n_tiles && nt < (nb + 1) * p.quad_nb;
