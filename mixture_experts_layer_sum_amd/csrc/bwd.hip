@@ -491,8 +491,8 @@ namespace {
 int64_t r64(int64_t x) { return (x + 63) / 64 * 64; }
 
 struct BwdWs {
-  uint16_t *dY, *dOut_b, *dL_b, *dLT, *W_RT, *UG, *dH, *DUG, *H, *dX, *W3T, *W12T, *dYT, *HT, *DUGT, *XT, *AT;
-  uint16_t *UGs, *dHs, *DUGs, *Hs, *dXs, *Ws3T, *Ws12T, *dOutT, *HsT, *DUGsT;
+  uint16_t *dY, *dOut_b, *dL_b, *dLT, *UG, *dH, *DUG, *H, *dX, *dYT, *HT, *DUGT, *XT, *AT;
+  uint16_t *UGs, *dHs, *DUGs, *Hs, *dXs, *dOutT, *HsT, *DUGsT;
   float *dw, *ones, *dLf, *bias_part, *dA_r;
   int32_t *poff, *ts, *grp;
 };
@@ -520,7 +520,6 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   w.dL_b = b16(T * Ep);
   w.dLT = b16(E * Tp);
   w.bias_part = f32(kBiasChunks * E);
-  w.W_RT = b16(d * Ep);
   w.poff = static_cast<int32_t*>(take(size_t(E + 1) * 4));
   w.ts = static_cast<int32_t*>(take(size_t(E + 1) * 4));
   w.grp = static_cast<int32_t*>(take(size_t(cdiv(N, 256) + E) * 4));
@@ -529,8 +528,6 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   w.DUG = b16(N * 2 * cc);
   w.H = b16(N * cc);
   w.dX = b16(N * d);
-  w.W3T = b16(E * cc * d);
-  w.W12T = b16(E * d * 2 * cc);
   w.dYT = b16(d * Np);
   w.HT = b16(cc * Np);
   w.DUGT = b16(2 * cc * Np);
@@ -543,8 +540,6 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
     w.DUGs = b16(T * 2 * cs);
     w.Hs = b16(T * cs);
     w.dXs = b16(T * d);
-    w.Ws3T = b16(cs * d);
-    w.Ws12T = b16(d * 2 * cs);
     w.dOutT = b16(d * Tp);
     w.HsT = b16(cs * Tp);
     w.DUGsT = b16(2 * cs * Tp);
@@ -636,22 +631,17 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
   FSM_TRY(launch_tile_table(offsets, E, 256, int(cdiv(N, 256) + E), w.ts, w.grp, s));
 
   // routed experts: recompute U, G; dH = dY W3; dU, dG, H; dX = [dU | dG] [W1; W2]
-  FSM_TRY(launch_bf16_product(PRODUCT_UG, A, offsets, w.ts, w.grp, E, W.W1, W.W2, cc * d, N, d, cc, w.UG, s,
+  // (the products against weights read W3 [d, c] and W1, W2 [c, d] K-major, as stored)
+  FSM_TRY(launch_bf16_product(PRODUCT_UG, A, offsets, w.ts, w.grp, E, W.W1, W.W2, cc * d, 0, 0, 0, N, d, cc, w.UG, s,
                               sorted_src, int32_t(k), T, MOE_K_BWD_RECOMPUTE));
-  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W3), cc, d, int32_t(cc), w.W3T, d, 0, r64(d), s, nullptr, 1,
-                    nullptr, nullptr, 0, E, d * cc, cc * d));
-  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dY, offsets, w.ts, w.grp, E, w.W3T, nullptr, cc * d, N, d, cc, w.dH,
-                              s, nullptr, 1, N, MOE_K_BWD_DGRAD));
+  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dY, offsets, w.ts, w.grp, E, W.W3, nullptr, d * cc, cc, d, 0, N, d, cc,
+                              w.dH, s, nullptr, 1, N, MOE_K_BWD_DGRAD));
   {
     ProfScope prof(MOE_K_BWD_POINTWISE, s);
     k_swiglu_bwd<<<unsigned(cdiv(N * (cc / 8), 256)), 256, 0, s>>>(w.dH, w.UG, N, int32_t(cc), w.DUG, w.H);
     FSM_TRY(check_launch("swiglu backward"));
   }
-  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W1), d, cc, int32_t(d), w.W12T, 2 * cc, 0, r64(cc), s, nullptr, 1,
-                    nullptr, nullptr, 0, E, cc * d, d * 2 * cc));
-  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W2), d, cc, int32_t(d), w.W12T, 2 * cc, cc, r64(cc), s, nullptr,
-                    1, nullptr, nullptr, 0, E, cc * d, d * 2 * cc));
-  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUG, offsets, w.ts, w.grp, E, w.W12T, nullptr, d * 2 * cc, N, 2 * cc,
+  FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUG, offsets, w.ts, w.grp, E, W.W1, W.W2, cc * d, d, cc, cc, N, 2 * cc,
                               d, w.dX, s, nullptr, 1, N, MOE_K_BWD_DGRAD));
 
   // routed weight gradients over each expert's rows (segments padded to 64)
@@ -663,28 +653,24 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
   FSM_TRY(kgroup(w.DUGT, w.XT, Np, w.poff, E, 0, 2 * cc, d, gr.dW1, gr.dW2, cc, s));
 
   // router: dA_r = dlogits W_R, dW_R = dlogits^T A
-  FSM_TRY(transpose(static_cast<const uint16_t*>(W.W_R), d, E, int32_t(d), w.W_RT, Ep, 0, Ep, s));
-  FSM_TRY(launch_bf16_product(PRODUCT_F32, w.dL_b, nullptr, nullptr, nullptr, 1, w.W_RT, nullptr, 0, T, Ep, d, w.dA_r,
-                              s, nullptr, 1, T, MOE_K_BWD_DGRAD));
+  FSM_TRY(launch_bf16_product(PRODUCT_F32, w.dL_b, nullptr, nullptr, nullptr, 1, W.W_R, nullptr, 0, d, E, 0, T, Ep, d,
+                              w.dA_r, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
   FSM_TRY(transpose(w.dL_b, Ep, T, E, w.dLT, Tp, 0, Tp, s));
   FSM_TRY(transpose(Ab, d, T, int32_t(d), w.AT, Tp, 0, Tp, s));
   FSM_TRY(kgroup(w.dLT, w.AT, Tp, nullptr, 1, Tp, E, d, gr.dW_R, nullptr, E, s));
 
   // shared expert (its output gradient is dOut itself)
   if (cs > 0) {
-    FSM_TRY(launch_bf16_product(PRODUCT_UG, A, nullptr, nullptr, nullptr, 1, W.Ws1, W.Ws2, 0, T, d, cs, w.UGs, s,
-                                nullptr, 1, T, MOE_K_BWD_RECOMPUTE));
-    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws3), cs, d, int32_t(cs), w.Ws3T, d, 0, r64(d), s));
-    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dOut_b, nullptr, nullptr, nullptr, 1, w.Ws3T, nullptr, 0, T, d, cs,
-                                w.dHs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
+    FSM_TRY(launch_bf16_product(PRODUCT_UG, A, nullptr, nullptr, nullptr, 1, W.Ws1, W.Ws2, 0, 0, 0, 0, T, d, cs, w.UGs,
+                                s, nullptr, 1, T, MOE_K_BWD_RECOMPUTE));
+    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.dOut_b, nullptr, nullptr, nullptr, 1, W.Ws3, nullptr, 0, cs, d, 0, T,
+                                d, cs, w.dHs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
     {
       ProfScope prof(MOE_K_BWD_POINTWISE, s);
       k_swiglu_bwd<<<unsigned(cdiv(T * (cs / 8), 256)), 256, 0, s>>>(w.dHs, w.UGs, T, int32_t(cs), w.DUGs, w.Hs);
       FSM_TRY(check_launch("swiglu backward"));
     }
-    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws1), d, cs, int32_t(d), w.Ws12T, 2 * cs, 0, r64(cs), s));
-    FSM_TRY(transpose(static_cast<const uint16_t*>(W.Ws2), d, cs, int32_t(d), w.Ws12T, 2 * cs, cs, r64(cs), s));
-    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUGs, nullptr, nullptr, nullptr, 1, w.Ws12T, nullptr, 0, T, 2 * cs,
+    FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUGs, nullptr, nullptr, nullptr, 1, W.Ws1, W.Ws2, 0, d, cs, cs, T, 2 * cs,
                                 d, w.dXs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
     FSM_TRY(transpose(w.dOut_b, d, T, int32_t(d), w.dOutT, Tp, 0, Tp, s));
     FSM_TRY(transpose(w.Hs, cs, T, int32_t(cs), w.HsT, Tp, 0, Tp, s));

@@ -83,10 +83,13 @@ int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest
 // MXFP8 (mx.hip): rows of a bf16 matrix -> E4M3 codes + one E8M0 scale per 32 elements
 // backward-pass building blocks (gemm.hip); epi codes of the bf16 product
 enum { PRODUCT_PLAIN = 0, PRODUCT_F32 = 2, PRODUCT_UG = 3 };
+// PRODUCT_UG: B1/B2 are [n_out, K] per group (the forward's layout, ldb/b_k1/b_ksplit unused);
+// PRODUCT_PLAIN / PRODUCT_F32: B is K-major, [K, ldb] per group: rows [0, b_k1) of B1, and with
+// b_ksplit > 0 rows k >= b_ksplit from B2 (row k - b_ksplit)
 int launch_bf16_product(int epi, const void* X, const int32_t* offsets, const int32_t* ts, const int32_t* grp,
-                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t N, int64_t K,
-                        int64_t n_out, void* out, hipStream_t s, const int32_t* gather, int32_t gather_k,
-                        int64_t x_rows, int prof_kind);
+                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t ldb, int64_t b_k1,
+                        int64_t b_ksplit, int64_t N, int64_t K, int64_t n_out, void* out, hipStream_t s,
+                        const int32_t* gather, int32_t gather_k, int64_t x_rows, int prof_kind);
 // backward pass of one MoE sublayer (bwd.hip)
 size_t layer_bwd_ws_bytes(const moe_stack_cfg_t& c);
 int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, const void* A, const float* logits,

@@ -47,15 +47,23 @@ struct GemmArgs {
   int32_t gather_k;
   int64_t a_rows;             // ROWS_GATHER: rows of A (its buffer-resource extent)
   int32_t quad_nb;            // > 0: the 2 x 2 XCD-block order below, with quad_nb N-tiles per block
+  // K-major B (the backward's row modes): B1, B2 are [K rows, ldb] per group, as the weights are
+  // stored; rows [0, b_k1) of B1 hold data (later rows read as zeros), and with b_ksplit > 0,
+  // rows k >= b_ksplit are row k - b_ksplit of B2
+  int64_t ldb, b_k1;
+  int32_t b_ksplit;
 };
 
 // How a workgroup finds its A rows: contiguous rows of a grouped input, a single group, or rows
 // gathered from the token matrix through the dispatch permutation (the permuted copy of the
 // activations is then never written).
 enum { ROWS_GROUPED = 0, ROWS_SINGLE = 1, ROWS_GATHER = 2 };
-// The backward pass's products read rows as ROWS_GROUPED / ROWS_SINGLE do; their own values give
-// them their own symbols, so profilers tell them from the forward's launches.
+// The backward pass's products read rows as ROWS_GROUPED / ROWS_SINGLE do, and take their B operand
+// K-major (a weight in its stored layout, e.g. dH = dY W3 with W3 [d, c]); their own values also
+// give them their own symbols, so profilers tell them from the forward's launches.
 enum { ROWS_GROUPED_BWD = 3, ROWS_SINGLE_BWD = 4 };
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------------------------------------
 // M-tile table: tile_start[g] = sum_{g' < g} ceil(count_g' / BM), and tile_group[t] = the group of
@@ -139,6 +147,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   static_assert(FM * 16 == WTM && FN * 16 == WTN, "wave tile must be a multiple of 16");
   static_assert(FM >= FN, "the fragment pipeline prefetches one B fragment per A row block");
   static_assert(LOADS * (S - 2) < 64, "vmcnt range");
+  // K-major B: a stage's B part is BK rows of BN values (rows of BN * 2 bytes, 16-byte chunks
+  // XOR-swizzled by 2 (row mod 4)), and a 16 x 32 fragment is two transposing LDS reads
+  // (ds_read_b64_tr_b16), each giving every lane 4 consecutive K values of its column.
+  constexpr bool BKM = ROWS == ROWS_GROUPED_BWD || ROWS == ROWS_SINGLE_BWD;
+  constexpr int BR = BKM ? 2 : 1;              // LDS reads per B fragment
+  static_assert(!BKM || (!PAIRED && BK == 64 && BN == 256), "K-major B: plain products, BK 64, BN 256");
 
   // one named array per stage, so the compiler can tell the stage being filled from the one read
   __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE], s1[STAGE];
@@ -171,11 +185,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     Bg = Bu;
     nvalid = min(BN, p.n_out - n0);
   }
-  // Rows past `rows` (A) or `nvalid` (B) lie beyond the resource size and load as zeros.
+  // Rows past `rows` (A) or `nvalid` (B) lie beyond the resource size and load as zeros.  K-major
+  // B: the resources are the group's whole B1 rows [0, b_k1) and B2 rows [0, K - b_ksplit).
   const __amdgpu_buffer_rsrc_t rA =
       ROWS == ROWS_GATHER ? make_rsrc(p.A, p.a_rows * K * 2) : make_rsrc(Ab, int64_t(rows) * K * 2);
-  const __amdgpu_buffer_rsrc_t rU = make_rsrc(Bu, int64_t(nvalid) * K * 2);
-  const __amdgpu_buffer_rsrc_t rG = make_rsrc(Bg, int64_t(nvalid) * K * 2);
+  const uint16_t* B1g = static_cast<const uint16_t*>(p.B1) + g * p.b_group_stride;
+  const uint16_t* B2g = p.B2 ? static_cast<const uint16_t*>(p.B2) + g * p.b_group_stride : B1g;
+  const __amdgpu_buffer_rsrc_t rU =
+      BKM ? make_rsrc(B1g, p.b_k1 * p.ldb * 2) : make_rsrc(Bu, int64_t(nvalid) * K * 2);
+  const __amdgpu_buffer_rsrc_t rG =
+      BKM ? make_rsrc(B2g, (K - p.b_ksplit) * p.ldb * 2) : make_rsrc(Bg, int64_t(nvalid) * K * 2);
+  const uint32_t ldbB = uint32_t(p.ldb) * 2u;   // K-major B: bytes per B row
   const uint32_t rowB = uint32_t(K) * 2u;  // bytes per row of A and B
 
   // Direct-to-LDS staging: each wave fills whole 1 KB runs (RUN_ROWS tile rows) of a stage with
@@ -205,8 +225,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   const __amdgpu_buffer_rsrc_t rBw = b_gate ? rG : rU;
 #pragma unroll
   for (int i = 0; i < B_RUNS; ++i) {
-    const int r = wb_row0 + i * RUN_ROWS + d_row;
-    dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
+    if (BKM) {
+      // run i of this wave = B rows 2 (wave B_RUNS + i) + {0, 1}; lane l fills physical chunk
+      // l % 32 of its row with the logical chunk (l % 32) ^ 2 (row mod 4)
+      const int r = 2 * (wave * B_RUNS + i) + (lane >> 5);
+      const int lc = (lane & 31) ^ ((2 * r) & 7);
+      dB[i] = uint32_t(r) * ldbB + uint32_t(nt * BN) * 2u + uint32_t(lc) * 16u;
+    } else {
+      const int r = wb_row0 + i * RUN_ROWS + d_row;
+      dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * rowB + uint32_t(d_ch) * 16u;
+    }
   }
 
 
@@ -215,6 +243,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
   const int fa0 = (wm * WTM + (lane & 15)) * BK;
   const int fb0 = BM * BK + (PAIRED ? wn * (WTN / 2) : wn * WTN) * BK + (lane & 15) * BK;
   const int sw = lds_swz<BK>(lane & 15);
+  // K-major B fragment reads: lane (q = lane / 16, j = lane % 16) reads row 8q + j/4 (+ 4 for the
+  // upper half of its K values) at columns 4 (j % 4) .. + 3 of the fragment's 16; the swizzle of
+  // those rows is 2 (j / 4)
+  const int tr_base = (8 * (lane >> 4) + ((lane & 15) >> 2)) * BN + 4 * (lane & 1);
+  const int tr_cb = (wn * WTN) / 8 + ((lane & 3) >> 1), tr_swz = 2 * ((lane & 15) >> 2);
 
   // A wave whose rows all lie past the group's last row (in the ragged last M-tile of a group)
   // skips its MFMAs and fragment reads: those rows are never stored.  It still loads its share of
@@ -233,15 +266,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     const uint32_t kb = uint32_t(KT) * BK * 2u;                                                    \
     _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                             \
       FSM_LDS_DMA16(rA, &FSM_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * BK], dA[i] + kb);             \
-    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                             \
-      FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);        \
+    if (BKM) {                                                                                     \
+      const int k0 = (KT) * BK;                                                                    \
+      const bool second = p.b_ksplit > 0 && k0 >= p.b_ksplit;                                      \
+      const uint32_t kbb = uint32_t(second ? k0 - p.b_ksplit : k0) * ldbB;                         \
+      _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
+        FSM_LDS_DMA16(second ? rG : rU, &FSM_SM(BUF)[BM * BK + (wave * B_RUNS + i) * 512], dB[i] + kbb); \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
+        FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);      \
+    }                                                                                              \
   }
 #define FSM_BROW(J) \
   ((PAIRED) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
 #define FSM_LDA(BUF, KS, I) \
   (*reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
-#define FSM_LDB(BUF, KS, J) \
-  (*reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define FSM_LDB_TR(BUF, KS, J, H)                                                                \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(              \
+      &FSM_SM(BUF)[BM * BK + tr_base + ((KS) * 32 + 4 * (H)) * BN + (((tr_cb + 2 * (J)) ^ tr_swz) << 3)]))
+#define FSM_LDB(BUF, KS, J)                                                                        \
+  (BKM ? __builtin_bit_cast(bf16x8, __builtin_shufflevector(FSM_LDB_TR(BUF, KS, J, 0),             \
+                                                            FSM_LDB_TR(BUF, KS, J, 1), 0, 1, 2, 3, 4, 5, 6, 7)) \
+       : *reinterpret_cast<const bf16x8*>(&FSM_SM(BUF)[fb0 + FSM_BROW(J) * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
   // One stage's MFMAs with the fragment reads software-pipelined: the A fragment for row block
   // i+1 (and, when the stage has a second K slice, that slice's B fragments) are read before the
   // MFMAs of row block i, and scheduling groups pin that order, so an LDS read is always in flight
@@ -252,7 +298,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     if (WITH_B) b1[I] = FSM_LDB(BUF, 1, I);                                                    \
     _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
       acc[I][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[I][j], 0, 0, 0);   \
-    __builtin_amdgcn_sched_group_barrier(0x100, (WITH_B) ? 2 : 1, 0);                          \
+    __builtin_amdgcn_sched_group_barrier(0x100, (WITH_B) ? 1 + BR : 1, 0);                     \
     __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
     a_cur = a_nxt;                                                                             \
   }
@@ -261,7 +307,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
     bf16x8 b0[FN], b1[FN], a_cur, a_nxt;                                                       \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) b0[j] = FSM_LDB(BUF, 0, j);                 \
     a_cur = FSM_LDA(BUF, 0, 0);                                                                \
-    __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                    \
+    __builtin_amdgcn_sched_group_barrier(0x100, FN * BR + 1, 0);                               \
     if (KSL == 2) {                                                                            \
       _Pragma("unroll") for (int i = 0; i < FN; ++i) FSM_STEP0(BUF, i, true);                  \
       _Pragma("unroll") for (int i = FN; i < FM; ++i) FSM_STEP0(BUF, i, false);                \
@@ -339,6 +385,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 #undef FSM_BROW
 #undef FSM_LDA
 #undef FSM_LDB
+#undef FSM_LDB_TR
 #undef FSM_SM
 #undef FSM_STEP0
 #undef FSM_COMPUTE
@@ -662,16 +709,22 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
 // EPI_PLAIN: bf16 out [N, n_out]; EPI_F32_BIAS (one group, no bias): fp32 out [N, n_out].  ts / grp:
 // the group tile table for 256-row tiles (null with one group).
 int launch_bf16_product(int epi, const void* X, const int32_t* offsets, const int32_t* ts, const int32_t* grp,
-                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t N, int64_t K,
-                        int64_t n_out, void* out, hipStream_t s, const int32_t* gather, int32_t gather_k,
-                        int64_t x_rows, int prof_kind) {
+                        int32_t G, const void* B1, const void* B2, int64_t b_stride, int64_t ldb, int64_t b_k1,
+                        int64_t b_ksplit, int64_t N, int64_t K, int64_t n_out, void* out, hipStream_t s,
+                        const int32_t* gather, int32_t gather_k, int64_t x_rows, int prof_kind) {
   if (N == 0) return MOE_OK;
   constexpr TileCfg C = kP1;
+  if (epi != EPI_UG) {   // K-major B: 32-bit buffer offsets within one group's B1 / B2
+    if (ldb < n_out || b_k1 > K || b_ksplit < 0 || b_ksplit % C.bk != 0 || K % C.bk != 0 ||
+        (b_ksplit > 0 && !B2) || (b_k1 > K - b_ksplit ? b_k1 : K - b_ksplit) * ldb * 2 >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "backward product: B layout out of range");
+  }
   GemmArgs a{};
   a.A = X; a.B1 = B1; a.B2 = B2; a.out = out; a.bias = nullptr;
   a.offsets = offsets; a.tile_start = ts; a.tile_group = grp; a.b_group_stride = b_stride;
   a.K = int32_t(K); a.n_out = int32_t(n_out); a.M = int32_t(N); a.G = G; a.group_m = C.gm;
   a.gather = gather; a.gather_k = gather_k; a.a_rows = x_rows;
+  a.ldb = ldb; a.b_k1 = b_k1; a.b_ksplit = int32_t(b_ksplit);
   a.n_tiles = int32_t(cdiv(n_out, epi == EPI_UG ? C.bn / 2 : C.bn));
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
   const int64_t mt = grp ? cdiv(N, C.bm) + G : cdiv(N, C.bm);
