@@ -4,18 +4,18 @@
 // Dispatch and Combine, the shared expert) with respect to A and every weight: the chain rule of
 // the forward, in reverse.  The three products that give activation gradients (dH = dY W3,
 // dX = [dU | dG] [W1; W2], and the router's dlogits W_R) run on the forward's grouped bf16 kernel
-// against weights transposed once per call; U and G are recomputed by that kernel's gate/up loads
-// (nothing of the forward beyond its outputs is kept).  The weight gradients are products whose
-// reduction runs over each expert's rows: the operands are transposed into K-contiguous rows,
-// each expert's rows padded to a multiple of 64 with zeros, and k_gemm_kgroup sums one expert's
-// segment per output tile.
+// with the weights read as stored (K-major, through transposing LDS reads); U and G are recomputed
+// by that kernel's gate/up loads (nothing of the forward beyond its outputs is kept).  The weight
+// gradients are products whose reduction runs over each expert's rows: k_gemm_kgroup sums one
+// expert's segment per output tile, reading dY, H, [dU | dG] and the dense operands as stored; only
+// the gathered layer input is copied, transposed, with each expert's rows padded to 64.
 //
 //   k_combine_bwd    dY[dest_row[t,i]] = w[t,i] dOut[t] (bf16), dw[t,i] = <dOut[t], Y[dest_row[t,i]]>,
 //                    and the bf16 copy of the shared experts' output gradient
 //   k_gate_bwd       dlogits from dw through the softmax / sigmoid (and renormalisation) Jacobian
 //   k_col_partial    per-expert sums of dlogits (the bias gradient), in two deterministic passes
 //   k_swiglu_bwd     dU = dH SiLU(G), dG = dH U SiLU'(G), and H = U SiLU(G) for dW3
-//   k_transpose      64 x 64 tiles through LDS, optionally gathering rows and padding segments
+//   k_transpose      64 x 64 tiles through LDS, gathering rows and padding segments
 //   k_gemm_kgroup    C_g = A[:, seg_g] B[:, seg_g]^T in fp32, per group g of K segments
 #include <vector>
 
@@ -315,26 +315,38 @@ __global__ __launch_bounds__(256) void k_transpose(TrArgs p) {
 }
 
 // ---- K-grouped product -----------------------------------------------------------------------------
-// C_g[m][n] = sum over K segment g of A[m][k] B[n][k] (fp32 out), A [M, ldk] and B [N, ldk] bf16
-// with K contiguous; segment g is [koff[g], koff[g+1]) (multiples of 64; koff null: one segment
-// [0, K)).  Output rows m < split go to out1 + g * split * N, the rest to out2 + g * (M - split) * N
-// (row m - split).  256 x 256 tiles, 8 waves (2 x 4), v_mfma_f32_16x16x32_bf16 with the B fragment
-// first so a lane holds four consecutive output columns; two direct-to-LDS stages of 64 K values.
+// C_g[m][n] = sum over group g's K segment of A[m][k] B[n][k] (fp32 out).  Each operand comes in one
+// of two layouts:
+//   K-contiguous (a transposed copy): rows [M or N, ld] with K along the row; group g's segment
+//     starts at column koff_t[g] (koff_t null: koff[g]) and runs into zero padding up to a
+//     multiple of 64;
+//   row-major in K ("RM", the activations as the forward keeps them): [K rows, ld], column m (or
+//     n); group g's segment is rows [koff[g], koff[g+1]), and rows past it read as zeros (they lie
+//     beyond the buffer resource).  Stage rows are 512 bytes with 16-byte chunks XOR-swizzled by
+//     2 (row mod 4), and a 16 x 32 fragment is two transposing LDS reads (ds_read_b64_tr_b16).
+// The segment of group g holds koff[g+1] - koff[g] K values (koff null: one segment of K).  Output
+// rows m < split go to out1 + g * split * N, the rest to out2 + g * (M - split) * N (row m - split).
+// 256 x 256 tiles, 8 waves (2 x 4), v_mfma_f32_16x16x32_bf16 with the B fragment first so a lane
+// holds four consecutive output columns; two direct-to-LDS stages of 64 K values.
+typedef short kg_v4i16 __attribute__((ext_vector_type(4)));
 struct KgArgs {
   const uint16_t* A;
   const uint16_t* B;
   float* out1;
   float* out2;
-  const int32_t* koff;
-  int64_t ldk;
+  const int32_t* koff;     // [G+1] segment bounds along K, or null (one segment [0, K))
+  const int32_t* koff_t;   // [G+1] segment starts of a K-contiguous operand, or null (= koff)
+  int64_t lda, ldb;        // elements per operand row
   int32_t K, M, N, G, split, tm, tn;
 };
 
+template <bool ARM, bool BRM>
 __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
-  constexpr int BM = 256, BN = 256, WAVES_N = 4, BK = 64, RB = BK * 2;   // RB: bytes per LDS row
+  constexpr int BM = 256, BN = 256, WAVES_N = 4, BK = 64, RB = BK * 2;   // RB: bytes per K-contiguous LDS row
   constexpr int WTM = 128, WTN = 64, FM = 8, FN = 4, NW = 8, RUN_ROWS = 8;
-  constexpr int A_RUNS = BM / RUN_ROWS / NW, B_RUNS = BN / RUN_ROWS / NW;
+  constexpr int A_RUNS = BM / RUN_ROWS / NW, B_RUNS = BN / RUN_ROWS / NW;   // 1 KB runs per wave per stage
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements
+  constexpr int AR = ARM ? 2 : 1, BR = BRM ? 2 : 1;   // LDS reads per fragment
   __shared__ __attribute__((aligned(16))) uint16_t s0[STAGE], s1[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -346,22 +358,46 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
   if (i8 >= q8 + (x < r8 ? 1 : 0)) return;
   const int L = x * q8 + min(x, r8) + i8;
   const int g = L / (p.tm * p.tn), rem = L - g * (p.tm * p.tn), mt = rem / p.tn, nt = rem - mt * p.tn;
-  const int64_t k0 = p.koff ? p.koff[g] : 0;
-  const int K = p.koff ? int(p.koff[g + 1] - k0) : p.K;
+  const int64_t seg0 = p.koff ? p.koff[g] : 0;
+  const int K = p.koff ? int(p.koff[g + 1] - seg0) : p.K;
+  const int64_t segt = p.koff_t ? p.koff_t[g] : seg0;
   const int m0 = mt * BM, n0 = nt * BN;
   const int mrows = min(BM, p.M - m0), nrows = min(BN, p.N - n0);
-  const uint32_t ldb = uint32_t(p.ldk) * 2u;   // bytes per operand row
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + int64_t(m0) * p.ldk + k0, int64_t(mrows) * p.ldk * 2);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + int64_t(n0) * p.ldk + k0, int64_t(nrows) * p.ldk * 2);
+  const uint32_t lda = uint32_t(p.lda) * 2u, ldb = uint32_t(p.ldb) * 2u;   // bytes per operand row
+  const __amdgpu_buffer_rsrc_t rA = ARM ? make_rsrc(p.A + seg0 * p.lda, int64_t(K) * p.lda * 2)
+                                        : make_rsrc(p.A + int64_t(m0) * p.lda + segt, int64_t(mrows) * p.lda * 2);
+  const __amdgpu_buffer_rsrc_t rB = BRM ? make_rsrc(p.B + seg0 * p.ldb, int64_t(K) * p.ldb * 2)
+                                        : make_rsrc(p.B + int64_t(n0) * p.ldb + segt, int64_t(nrows) * p.ldb * 2);
+  // direct-to-LDS: K-contiguous runs are 8 rows of 128 bytes (lane l: row l / 8, chunk (l % 8) ^ row);
+  // RM runs are 2 rows of 512 bytes (lane l: row l / 32, chunk (l % 32) ^ 2 (row mod 4))
   const int d_row = lane >> 3, d_ch = (lane & 7) ^ d_row;
   uint32_t dA[A_RUNS], dB[B_RUNS];
 #pragma unroll
-  for (int i = 0; i < A_RUNS; ++i) dA[i] = uint32_t((wave * A_RUNS + i) * RUN_ROWS + d_row) * ldb + uint32_t(d_ch) * 16u;
+  for (int i = 0; i < A_RUNS; ++i) {
+    if (ARM) {
+      const int r = 2 * (wave * A_RUNS + i) + (lane >> 5), lc = (lane & 31) ^ ((2 * r) & 7);
+      dA[i] = uint32_t(r) * lda + uint32_t(m0) * 2u + uint32_t(lc) * 16u;
+    } else {
+      dA[i] = uint32_t((wave * A_RUNS + i) * RUN_ROWS + d_row) * lda + uint32_t(d_ch) * 16u;
+    }
+  }
 #pragma unroll
-  for (int i = 0; i < B_RUNS; ++i) dB[i] = uint32_t((wave * B_RUNS + i) * RUN_ROWS + d_row) * ldb + uint32_t(d_ch) * 16u;
+  for (int i = 0; i < B_RUNS; ++i) {
+    if (BRM) {
+      const int r = 2 * (wave * B_RUNS + i) + (lane >> 5), lc = (lane & 31) ^ ((2 * r) & 7);
+      dB[i] = uint32_t(r) * ldb + uint32_t(n0) * 2u + uint32_t(lc) * 16u;
+    } else {
+      dB[i] = uint32_t((wave * B_RUNS + i) * RUN_ROWS + d_row) * ldb + uint32_t(d_ch) * 16u;
+    }
+  }
 
-  // fragment reads: row (base + 16 i + lane % 16), K slice ks: chunk ((4 ks + lane / 16) ^ (lane & 7))
+  // K-contiguous fragment reads: row (base + 16 i + lane % 16), K slice ks: chunk ((4 ks + lane / 16) ^ (lane & 7))
   const int sw = lane & 7, fa0 = (wm * WTM + (lane & 15)) * BK, fb0 = BM * BK + (wn * WTN + (lane & 15)) * BK;
+  // RM fragment reads: lane (q = lane / 16, j = lane % 16) reads row 8q + j/4 (+ 4 for its upper K
+  // values) at columns 4 (j % 4) .. + 3 of the fragment's 16; those rows' swizzle is 2 (j / 4)
+  const int tr_row = (8 * (lane >> 4) + ((lane & 15) >> 2)) * 256 + 4 * (lane & 1);
+  const int tr_swz = 2 * ((lane & 15) >> 2);
+  const int tr_ca = (wm * WTM) / 8 + ((lane & 3) >> 1), tr_cb = (wn * WTN) / 8 + ((lane & 3) >> 1);
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -373,16 +409,24 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
 #define KG_SM(BUF) ((BUF) ? s1 : s0)
 #define KG_STAGE(KT, BUF)                                                                        \
   {                                                                                              \
-    const uint32_t kb = uint32_t(KT) * RB + kb_zero;                                             \
+    const uint32_t kba = (ARM ? uint32_t(KT) * BK * lda : uint32_t(KT) * RB) + kb_zero;          \
+    const uint32_t kbb = (BRM ? uint32_t(KT) * BK * ldb : uint32_t(KT) * RB) + kb_zero;          \
     _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                           \
-      FSM_LDS_DMA16(rA, &KG_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * BK], dA[i] + kb);            \
+      FSM_LDS_DMA16(rA, &KG_SM(BUF)[(wave * A_RUNS + i) * 512], dA[i] + kba);                     \
     _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
-      FSM_LDS_DMA16(rB, &KG_SM(BUF)[BM * BK + (wave * B_RUNS + i) * RUN_ROWS * BK], dB[i] + kb);  \
+      FSM_LDS_DMA16(rB, &KG_SM(BUF)[BM * BK + (wave * B_RUNS + i) * 512], dB[i] + kbb);           \
   }
-#define KG_LDA(BUF, KS, I) \
-  (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
-#define KG_LDB(BUF, KS, J) \
-  (*reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fb0 + (J) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define KG_TR(BUF, OFF, KS, CB, H)                                                               \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) kg_v4i16*)(         \
+      &KG_SM(BUF)[(OFF) + tr_row + ((KS) * 32 + 4 * (H)) * 256 + (((CB) ^ tr_swz) << 3)]))
+#define KG_TRF(BUF, OFF, KS, CB) \
+  __builtin_bit_cast(bf16x8, __builtin_shufflevector(KG_TR(BUF, OFF, KS, CB, 0), KG_TR(BUF, OFF, KS, CB, 1), 0, 1, 2, 3, 4, 5, 6, 7))
+#define KG_LDA(BUF, KS, I)                                                                       \
+  (ARM ? KG_TRF(BUF, 0, KS, tr_ca + 2 * (I))                                                     \
+       : *reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fa0 + (I) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
+#define KG_LDB(BUF, KS, J)                                                                       \
+  (BRM ? KG_TRF(BUF, BM * BK, KS, tr_cb + 2 * (J))                                               \
+       : *reinterpret_cast<const bf16x8*>(&KG_SM(BUF)[fb0 + (J) * 16 * BK + ((((KS) * 4 + (lane >> 4)) ^ sw) << 3)]))
 // one stage (two K slices of 32): slice 0's B fragments and first A fragment, then per A row block
 // the next A fragment (and, for the first FN blocks, one of slice 1's B fragments) is read before
 // the block's FN MFMAs; slice 1 follows with its A fragments read one block ahead.  Scheduling
@@ -392,13 +436,13 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
     bf16x8 b0[FN], b1[FN], a_cur, a_nxt;                                                         \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) b0[j] = KG_LDB(BUF, 0, j);                    \
     a_cur = KG_LDA(BUF, 0, 0);                                                                   \
-    __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);                                      \
+    __builtin_amdgcn_sched_group_barrier(0x100, FN * BR + AR, 0);                                \
     _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                             \
       a_nxt = KG_LDA(BUF, 0, i + 1);                                                             \
       b1[i] = KG_LDB(BUF, 1, i);                                                                 \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[i][j], 0, 0, 0);   \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, AR + BR, 0);                                   \
       __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
       a_cur = a_nxt;                                                                             \
     }                                                                                            \
@@ -406,7 +450,7 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
       a_nxt = (i + 1 < FM) ? KG_LDA(BUF, 0, i + 1) : KG_LDA(BUF, 1, 0);                          \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a_cur, acc[i][j], 0, 0, 0);   \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, AR, 0);                                        \
       __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
       a_cur = a_nxt;                                                                             \
     }                                                                                            \
@@ -414,7 +458,7 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
       if (i + 1 < FM) a_nxt = KG_LDA(BUF, 1, i + 1);                                             \
       _Pragma("unroll") for (int j = 0; j < FN; ++j)                                             \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a_cur, acc[i][j], 0, 0, 0);   \
-      if (i + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
+      if (i + 1 < FM) __builtin_amdgcn_sched_group_barrier(0x100, AR, 0);                        \
       __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);                                        \
       a_cur = a_nxt;                                                                             \
     }                                                                                            \
@@ -426,7 +470,7 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
     asm volatile("" ::: "memory");      \
   }
 
-  const int KT = K / BK;
+  const int KT = (K + BK - 1) / BK;   // the last stage's rows past the segment read as zeros
   if (KT == 0) {   // an empty segment: the gradient block is zero (uniform across the workgroup)
     for (int e = tid; e < BM * BN; e += 512) {
       const int m = m0 + e / BN, n = n0 + e % BN;
@@ -461,6 +505,8 @@ __global__ __launch_bounds__(512) void k_gemm_kgroup(KgArgs p) {
 #undef KG_STAGE
 #undef KG_LDA
 #undef KG_LDB
+#undef KG_TR
+#undef KG_TRF
 #undef KG_COMPUTE
 #undef KG_BARRIER
 
@@ -491,8 +537,8 @@ namespace {
 int64_t r64(int64_t x) { return (x + 63) / 64 * 64; }
 
 struct BwdWs {
-  uint16_t *dY, *dOut_b, *dL_b, *dLT, *UG, *dH, *DUG, *H, *dX, *dYT, *HT, *DUGT, *XT, *AT;
-  uint16_t *UGs, *dHs, *DUGs, *Hs, *dXs, *dOutT, *HsT, *DUGsT;
+  uint16_t *dY, *dOut_b, *dL_b, *UG, *dH, *DUG, *H, *dX, *XT;
+  uint16_t *UGs, *dHs, *DUGs, *Hs, *dXs;
   float *dw, *ones, *dLf, *bias_part, *dA_r;
   int32_t *poff, *ts, *grp;
 };
@@ -501,7 +547,7 @@ constexpr int kBiasChunks = 64;
 
 BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   const int64_t T = c.T, d = c.d, cc = c.c, cs = c.c_shared, E = c.E, k = c.k, N = T * k;
-  const int64_t Tp = r64(T), Ep = r64(E), Np = r64(N) + 64 * E;
+  const int64_t Ep = r64(E), Np = r64(N) + 64 * E;
   char* base = static_cast<char*>(ws);
   size_t off = 0;
   auto take = [&](size_t bytes) -> void* {
@@ -518,7 +564,6 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   w.ones = f32(T * k);
   w.dLf = f32(T * E);
   w.dL_b = b16(T * Ep);
-  w.dLT = b16(E * Tp);
   w.bias_part = f32(kBiasChunks * E);
   w.poff = static_cast<int32_t*>(take(size_t(E + 1) * 4));
   w.ts = static_cast<int32_t*>(take(size_t(E + 1) * 4));
@@ -528,11 +573,7 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   w.DUG = b16(N * 2 * cc);
   w.H = b16(N * cc);
   w.dX = b16(N * d);
-  w.dYT = b16(d * Np);
-  w.HT = b16(cc * Np);
-  w.DUGT = b16(2 * cc * Np);
   w.XT = b16(d * Np);
-  w.AT = b16(d * Tp);
   w.dA_r = f32(T * d);
   if (cs > 0) {
     w.UGs = b16(T * 2 * cs);
@@ -540,9 +581,6 @@ BwdWs carve_bwd(void* ws, const moe_stack_cfg_t& c, size_t* total) {
     w.DUGs = b16(T * 2 * cs);
     w.Hs = b16(T * cs);
     w.dXs = b16(T * d);
-    w.dOutT = b16(d * Tp);
-    w.HsT = b16(cs * Tp);
-    w.DUGsT = b16(2 * cs * Tp);
   }
   if (total) *total = off;
   return w;
@@ -560,15 +598,24 @@ int transpose(const uint16_t* X, int64_t ldx, int64_t R, int32_t C, uint16_t* ou
   return check_launch("transpose");
 }
 
-int kgroup(const uint16_t* A, const uint16_t* B, int64_t ldk, const int32_t* koff, int32_t G, int64_t K, int64_t M,
-           int64_t N, float* out1, float* out2, int64_t split, hipStream_t s) {
+// A is row-major in K ([K rows, lda]); B is row-major in K ([K rows, ldb], b_rm) or a K-contiguous
+// copy ([N, ldb] with segments at koff_t).  max_rows bounds a segment's rows (32-bit buffer offsets).
+int kgroup(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, bool b_rm, const int32_t* koff,
+           const int32_t* koff_t, int32_t G, int64_t K, int64_t max_rows, int64_t M, int64_t N, float* out1,
+           float* out2, int64_t split, hipStream_t s) {
+  if ((max_rows + 64) * lda * 2 >= (int64_t(1) << 31) || (b_rm && (max_rows + 64) * ldb * 2 >= (int64_t(1) << 31)))
+    return fail(MOE_ERR_UNSUPPORTED, "weight-gradient product: operand rows above 2^31 bytes");
   KgArgs a{};
-  a.A = A; a.B = B; a.out1 = out1; a.out2 = out2 ? out2 : out1; a.koff = koff; a.ldk = ldk;
+  a.A = A; a.B = B; a.out1 = out1; a.out2 = out2 ? out2 : out1; a.koff = koff; a.koff_t = koff_t;
+  a.lda = lda; a.ldb = ldb;
   a.K = int32_t(K); a.M = int32_t(M); a.N = int32_t(N); a.G = G; a.split = int32_t(split);
   a.tm = int32_t(cdiv(M, 256)); a.tn = int32_t(cdiv(N, 256));
   const int64_t total = int64_t(G) * a.tm * a.tn;
   ProfScope prof(MOE_K_BWD_WGRAD, s);
-  k_gemm_kgroup<<<dim3(unsigned(total)), 512, 0, s>>>(a);
+  if (b_rm)
+    k_gemm_kgroup<true, true><<<dim3(unsigned(total)), 512, 0, s>>>(a);
+  else
+    k_gemm_kgroup<true, false><<<dim3(unsigned(total)), 512, 0, s>>>(a);
   return check_launch("weight-gradient product");
 }
 }  // namespace
@@ -590,7 +637,7 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
                           const float* dOut_shared, const moe_layer_grads_t& gr, void* ws, hipStream_t s) {
   const int64_t T = c.T, d = c.d, cc = c.c, cs = c.c_shared, k = c.k, N = T * k;
   const int32_t E = c.E;
-  const int64_t Tp = r64(T), Ep = r64(E), Np = r64(N) + 64 * int64_t(E);
+  const int64_t Ep = r64(E), Np = r64(N) + 64 * int64_t(E);
   BwdWs w = carve_bwd(ws, c, nullptr);
   const uint16_t* Ab = static_cast<const uint16_t*>(A);
 
@@ -644,20 +691,16 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
   FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUG, offsets, w.ts, w.grp, E, W.W1, W.W2, cc * d, d, cc, cc, N, 2 * cc,
                               d, w.dX, s, nullptr, 1, N, MOE_K_BWD_DGRAD));
 
-  // routed weight gradients over each expert's rows (segments padded to 64)
-  FSM_TRY(transpose(w.dY, d, N, int32_t(d), w.dYT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
-  FSM_TRY(transpose(w.H, cc, N, int32_t(cc), w.HT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
-  FSM_TRY(transpose(w.DUG, 2 * cc, N, int32_t(2 * cc), w.DUGT, Np, 0, Np, s, nullptr, 1, offsets, w.poff, E));
+  // routed weight gradients over each expert's rows: dY, H and [dU | dG] are read as stored; the
+  // gathered layer input is copied once, transposed, with each expert's rows padded to 64
   FSM_TRY(transpose(Ab, d, N, int32_t(d), w.XT, Np, 0, Np, s, sorted_src, int32_t(k), offsets, w.poff, E));
-  FSM_TRY(kgroup(w.dYT, w.HT, Np, w.poff, E, 0, d, cc, gr.dW3, nullptr, d, s));
-  FSM_TRY(kgroup(w.DUGT, w.XT, Np, w.poff, E, 0, 2 * cc, d, gr.dW1, gr.dW2, cc, s));
+  FSM_TRY(kgroup(w.dY, d, w.H, cc, true, offsets, nullptr, E, 0, T, d, cc, gr.dW3, nullptr, d, s));
+  FSM_TRY(kgroup(w.DUG, 2 * cc, w.XT, Np, false, offsets, w.poff, E, 0, T, 2 * cc, d, gr.dW1, gr.dW2, cc, s));
 
   // router: dA_r = dlogits W_R, dW_R = dlogits^T A
   FSM_TRY(launch_bf16_product(PRODUCT_F32, w.dL_b, nullptr, nullptr, nullptr, 1, W.W_R, nullptr, 0, d, E, 0, T, Ep, d,
                               w.dA_r, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
-  FSM_TRY(transpose(w.dL_b, Ep, T, E, w.dLT, Tp, 0, Tp, s));
-  FSM_TRY(transpose(Ab, d, T, int32_t(d), w.AT, Tp, 0, Tp, s));
-  FSM_TRY(kgroup(w.dLT, w.AT, Tp, nullptr, 1, Tp, E, d, gr.dW_R, nullptr, E, s));
+  FSM_TRY(kgroup(w.dL_b, Ep, Ab, d, true, nullptr, nullptr, 1, T, T, E, d, gr.dW_R, nullptr, E, s));
 
   // shared expert (its output gradient is dOut itself)
   if (cs > 0) {
@@ -672,11 +715,8 @@ int launch_layer_backward(const moe_layer_desc_t& W, const moe_stack_cfg_t& c, c
     }
     FSM_TRY(launch_bf16_product(PRODUCT_PLAIN, w.DUGs, nullptr, nullptr, nullptr, 1, W.Ws1, W.Ws2, 0, d, cs, cs, T, 2 * cs,
                                 d, w.dXs, s, nullptr, 1, T, MOE_K_BWD_DGRAD));
-    FSM_TRY(transpose(w.dOut_b, d, T, int32_t(d), w.dOutT, Tp, 0, Tp, s));
-    FSM_TRY(transpose(w.Hs, cs, T, int32_t(cs), w.HsT, Tp, 0, Tp, s));
-    FSM_TRY(transpose(w.DUGs, 2 * cs, T, int32_t(2 * cs), w.DUGsT, Tp, 0, Tp, s));
-    FSM_TRY(kgroup(w.dOutT, w.HsT, Tp, nullptr, 1, Tp, d, cs, gr.dWs3, nullptr, d, s));
-    FSM_TRY(kgroup(w.DUGsT, w.AT, Tp, nullptr, 1, Tp, 2 * cs, d, gr.dWs1, gr.dWs2, cs, s));
+    FSM_TRY(kgroup(w.dOut_b, d, w.Hs, cs, true, nullptr, nullptr, 1, T, T, d, cs, gr.dWs3, nullptr, d, s));
+    FSM_TRY(kgroup(w.DUGs, 2 * cs, Ab, d, true, nullptr, nullptr, 1, T, T, 2 * cs, d, gr.dWs1, gr.dWs2, cs, s));
   }
 
   // dA[t] = sum over t's slots of dX[dest_row] + the router's and the shared expert's parts
