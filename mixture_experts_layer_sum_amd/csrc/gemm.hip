@@ -390,14 +390,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
 #undef FSM_STEP0
 #undef FSM_COMPUTE
 
-  // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4*(lane >> 4) + {0..3}
-  const int ml = lane & 15, nl = (lane >> 4) * 4;
+  // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4*(lane >> 4) + {0..3}.
+  // Where the tile's columns all lie below n_out (every tile but a ragged last N-tile), the bf16
+  // epilogues pair adjacent fragments into 16-byte stores (pair_words); partner lanes share their
+  // row, so they skip or store it together.
+  const int ml = lane & 15, nl = (lane >> 4) * 4, pc = pair_col(lane);
+  constexpr int TILE_N = PAIRED ? BN / 2 : BN;
+  const bool full_n = (FN / (PAIRED ? 2 : 1)) % 2 == 0 && (nt + 1) * TILE_N <= p.n_out;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = wm * WTM + i * 16 + ml;
     if (m >= rows) continue;
     const int64_t orow = int64_t(row0 + m);
-    if (EPI == EPI_SWIGLU) {
+    if (EPI == EPI_SWIGLU && full_n) {
+      uint16_t* out = static_cast<uint16_t*>(p.out) + orow * p.n_out + nt * (BN / 2) + wn * (WTN / 2) + pc;
+#pragma unroll
+      for (int j = 0; j + 1 < FN / 2; j += 2) {
+        const f32x4 u0 = acc[i][j], g0 = acc[i][j + FN / 2], u1 = acc[i][j + 1], g1 = acc[i][j + 1 + FN / 2];
+        *reinterpret_cast<st_u32x4*>(out + j * 16) =
+            pair_words(pack2(u0[0] * silu_f(g0[0]), u0[1] * silu_f(g0[1])), pack2(u0[2] * silu_f(g0[2]), u0[3] * silu_f(g0[3])),
+                       pack2(u1[0] * silu_f(g1[0]), u1[1] * silu_f(g1[1])), pack2(u1[2] * silu_f(g1[2]), u1[3] * silu_f(g1[3])));
+      }
+    } else if (EPI == EPI_SWIGLU) {
       uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j) {
@@ -409,6 +423,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
         v.y = pack2(u[2] * silu_f(gt[2]), u[3] * silu_f(gt[3]));
         *reinterpret_cast<uint2*>(out + orow * p.n_out + col) = v;
       }
+    } else if (EPI == EPI_UG && full_n) {
+      const int64_t ld = 2 * int64_t(p.n_out);
+      uint16_t* out = static_cast<uint16_t*>(p.out) + orow * ld + nt * (BN / 2) + wn * (WTN / 2) + pc;
+#pragma unroll
+      for (int j = 0; j + 1 < FN / 2; j += 2) {
+        const f32x4 u0 = acc[i][j], g0 = acc[i][j + FN / 2], u1 = acc[i][j + 1], g1 = acc[i][j + 1 + FN / 2];
+        *reinterpret_cast<st_u32x4*>(out + j * 16) =
+            pair_words(pack2(u0[0], u0[1]), pack2(u0[2], u0[3]), pack2(u1[0], u1[1]), pack2(u1[2], u1[3]));
+        *reinterpret_cast<st_u32x4*>(out + p.n_out + j * 16) =
+            pair_words(pack2(g0[0], g0[1]), pack2(g0[2], g0[3]), pack2(g1[0], g1[1]), pack2(g1[2], g1[3]));
+      }
     } else if (EPI == EPI_UG) {
       uint16_t* out = static_cast<uint16_t*>(p.out);
       const int64_t ld = 2 * int64_t(p.n_out);
@@ -419,6 +444,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
         const f32x4 u = acc[i][j], gt = acc[i][j + FN / 2];
         *reinterpret_cast<uint2*>(out + orow * ld + col) = make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3]));
         *reinterpret_cast<uint2*>(out + orow * ld + p.n_out + col) = make_uint2(pack2(gt[0], gt[1]), pack2(gt[2], gt[3]));
+      }
+    } else if (EPI == EPI_PLAIN && full_n) {
+      uint16_t* out = static_cast<uint16_t*>(p.out) + orow * p.n_out + nt * BN + wn * WTN + pc;
+#pragma unroll
+      for (int j = 0; j + 1 < FN; j += 2) {
+        const f32x4 a = acc[i][j], b = acc[i][j + 1];
+        *reinterpret_cast<st_u32x4*>(out + j * 16) =
+            pair_words(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3]));
       }
     } else if (EPI == EPI_PLAIN) {
       uint16_t* out = static_cast<uint16_t*>(p.out);

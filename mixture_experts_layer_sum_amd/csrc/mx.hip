@@ -295,7 +295,22 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
 
   // epilogue: lane holds rows m = .. + (lane & 15), columns n = .. + 4 (lane >> 4) + {0..3}
   const int ml = lane & 15, nl = q * 4;
-  if (EPI == MX_PLAIN) {
+  if (EPI == MX_PLAIN && FN % 2 == 0 && (nt + 1) * BN <= p.n_out) {
+    // adjacent fragments paired into 16-byte stores (pair_words); partner lanes share their row
+    const int pc = pair_col(lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = wm * WTM + i * 16 + ml;
+      if (m >= rows) continue;
+      uint16_t* out = static_cast<uint16_t*>(p.out) + int64_t(row0 + m) * p.n_out + nt * BN + wn * WTN + pc;
+#pragma unroll
+      for (int j = 0; j + 1 < FN; j += 2) {
+        const f32x4 a = acc[i][j], b = acc[i][j + 1];
+        *reinterpret_cast<st_u32x4*>(out + j * 16) =
+            pair_words(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3]));
+      }
+    }
+  } else if (EPI == MX_PLAIN) {
     uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {

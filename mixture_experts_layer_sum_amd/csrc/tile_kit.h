@@ -33,6 +33,30 @@ __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, const void
 #define FSM_LDS_DMA4(RSRC, LDS, VOFF) ((void)(RSRC), (void)(LDS), (void)(VOFF))
 #endif
 
+// 16-byte output stores.  A product issued with the weight fragment first leaves lane group
+// q = lane / 16 holding columns 4q .. 4q + 3 of each 16-column fragment (as packed bf16 pairs, two
+// dwords).  For two adjacent fragments a (columns 0-15) and b (16-31), one gfx950 permlane16 swap
+// per dword trades b's words in groups 0 and 2 for a's words in groups 1 and 3 (the lanes it pairs,
+// l and l + 16, hold the same row).  Each lane then holds 8 consecutive columns, starting at
+// pair_col(lane) of the 32, and one 16-byte store per lane replaces two 8-byte stores: measured on
+// the routed down product, 5% faster, with the same bytes written.
+typedef unsigned int st_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int pair_col(int lane) { return ((lane >> 4) & 1) * 16 + (lane >> 5) * 8; }
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ st_u32x4 pair_words(uint32_t a01, uint32_t a23, uint32_t b01, uint32_t b23) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(a01, b01, false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(a23, b23, false, false);
+  st_u32x4 v;
+  v[0] = s0[0];
+  v[1] = s1[0];
+  v[2] = s0[1];
+  v[3] = s1[1];
+  return v;
+}
+#else
+__device__ __forceinline__ st_u32x4 pair_words(uint32_t, uint32_t, uint32_t, uint32_t) { return st_u32x4{}; }
+#endif
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
 // outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
