@@ -78,6 +78,21 @@ def measured_traffic():
     return None
 
 
+def stream_overlap(launches, main_stream) -> dict:
+    """Cross-stream overlap of the timed stack steps from the per-launch HIP-event intervals: M = the
+    main stream's busy time (permutations, routed GEMMs), S = the side stream's (routers, top-k,
+    shared experts, combines, next-layer inputs)."""
+    from mixture_experts_layer_sum_amd.profiling import overlap
+    main = [(a, b) for _, s, a, b in launches if s == main_stream]
+    side = [(a, b) for _, s, a, b in launches if s != main_stream]
+    ov = overlap(main, side)
+    r = lambda v: None if v is None else round(v, 4)  # noqa: E731
+    return {"side_hidden_frac": r(ov["side_hidden"]), "main_covered_frac": r(ov["main_covered"]),
+            "main_busy_ms": round(ov["main"], 2), "side_busy_ms": round(ov["side"], 2),
+            "both_busy_ms": round(ov["both"], 2), "launches": len(launches),
+            "what": "|M n S| / |S| and |M n S| / |M| over the timed steps (HIP events around each launch)"}
+
+
 def kernel_report(prof: dict, c, steps: int) -> dict:
     """Per-kind averages and the algorithmic throughput of each kernel kind."""
     T, d, E, k, c_, cs = c.T, c.d, c.E, c.k, c.c, c.shared_width
@@ -526,7 +541,7 @@ def main():
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ops.profile_enable(False)
-    prof = ops.profile_collect()
+    prof, launches = ops.profile_collect_intervals()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step")
     assert torch.isfinite(oL).all().item(), "non-finite stack output"
@@ -574,6 +589,7 @@ def main():
         "two_stream_speedup": None if single_ms is None else round(single_ms / ms_per_step, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "overlap": stream_overlap(launches, main_s.cuda_stream),
     }
     def leg(name, fn):
         """An optional measurement after the timed steps; a failure is reported in its field (and

@@ -376,6 +376,28 @@ typedef struct {
 int moe_profile_enable(int on);
 int moe_profile_collect(moe_kernel_time_t* out /* [MOE_KERNEL_KINDS] */);
 
+/*
+ * One recorded launch on a common time axis, for the cross-stream overlap of the FarSkip stack
+ * (the share of the second queue's work that runs while the first queue's runs).
+ */
+typedef struct {
+  int32_t kind;     /* moe_kernel_kind_t */
+  int32_t pad;
+  uint64_t stream;  /* the hipStream_t it was launched on, as an opaque id */
+  double start_ms;  /* start event, ms after the first recorded start event of this collection */
+  double end_ms;    /* end event, same origin */
+} moe_kernel_interval_t;
+
+/*
+ * moe_profile_collect, plus each recorded launch's interval in record order.
+ *   out       [MOE_KERNEL_KINDS] per-kind totals, as moe_profile_collect
+ *   iv        host array of cap entries; the first min(cap, launches) launches are written
+ *   n         receives the number of recorded launches (may exceed cap)
+ * Clears the records.  Errors: out, iv (with cap > 0) or n null -> MOE_ERR_INVALID_ARG; a failed
+ * event query -> MOE_ERR_HIP (records are still released).
+ */
+int moe_profile_collect_intervals(moe_kernel_time_t* out, moe_kernel_interval_t* iv, int32_t cap, int32_t* n);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

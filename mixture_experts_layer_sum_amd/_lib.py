@@ -21,7 +21,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_group
            "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
            "moe_layer_backward_workspace_bytes", "farskip_stack_backward", "farskip_stack_backward_workspace_bytes",
            "moe_combine", "farskip_stack_forward",
-           "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect", "moe_last_error",
+           "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect",
+           "moe_profile_collect_intervals", "moe_last_error",
            "moe_version")
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
                 "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
@@ -46,6 +47,11 @@ class LayerGrads(ctypes.Structure):
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("count", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
+class KernelInterval(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("pad", ctypes.c_int32), ("stream", ctypes.c_uint64),
+                ("start_ms", ctypes.c_double), ("end_ms", ctypes.c_double)]
 
 
 class FarSkipMoEError(RuntimeError):
@@ -104,6 +110,9 @@ def _declare(lib):
     lib.moe_profile_enable.restype = i
     lib.moe_profile_collect.argtypes = [ctypes.POINTER(KernelTime)]
     lib.moe_profile_collect.restype = i
+    lib.moe_profile_collect_intervals.argtypes = [ctypes.POINTER(KernelTime), ctypes.POINTER(KernelInterval), i32,
+                                                  ctypes.POINTER(i32)]
+    lib.moe_profile_collect_intervals.restype = i
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []

@@ -10,6 +10,7 @@ namespace fsm {
 namespace {
 struct Rec {
   int kind;
+  hipStream_t s;
   hipEvent_t a, b;
 };
 std::atomic<bool> g_on{false};
@@ -38,7 +39,7 @@ ProfScope::~ProfScope() {
     return;
   }
   std::lock_guard<std::mutex> g(g_mu);
-  g_recs.push_back({kind_, a_, b_});
+  g_recs.push_back({kind_, s_, a_, b_});
 }
 
 }  // namespace fsm
@@ -50,31 +51,53 @@ int moe_profile_enable(int on) {
   return MOE_OK;
 }
 
-int moe_profile_collect(moe_kernel_time_t* out) {
-  if (!out) return fsm::fail(MOE_ERR_INVALID_ARG, "moe_profile_collect: out is required");
+int moe_profile_collect_intervals(moe_kernel_time_t* out, moe_kernel_interval_t* iv, int32_t cap, int32_t* n) {
+  if (!out || !n || (cap > 0 && !iv))
+    return fsm::fail(MOE_ERR_INVALID_ARG, "moe_profile_collect_intervals: out, n (and iv with cap > 0) are required");
   for (int i = 0; i < MOE_KERNEL_KINDS; ++i) out[i] = moe_kernel_time_t{0, 0.0};
   std::vector<fsm::Rec> recs;
   {
     std::lock_guard<std::mutex> g(fsm::g_mu);
     recs.swap(fsm::g_recs);
   }
+  *n = int32_t(recs.size());
   int rc = MOE_OK;
+  // every end event has completed once the last one of each stream has; wait for all of them
   for (const fsm::Rec& r : recs) {
-    float ms = 0.f;
-    if (rc == MOE_OK) {
-      hipError_t e = hipEventSynchronize(r.b);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
-      if (e != hipSuccess) {
-        rc = fsm::fail(MOE_ERR_HIP, "moe_profile_collect: %s", hipGetErrorString(e));
-      } else if (r.kind >= 0 && r.kind < MOE_KERNEL_KINDS) {
-        out[r.kind].count += 1;
-        out[r.kind].total_ms += ms;
-      }
+    if (rc != MOE_OK) break;
+    const hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) rc = fsm::fail(MOE_ERR_HIP, "moe_profile_collect: %s", hipGetErrorString(e));
+  }
+  for (size_t i = 0; i < recs.size() && rc == MOE_OK; ++i) {
+    const fsm::Rec& r = recs[i];
+    float ms = 0.f, t0 = 0.f, t1 = 0.f;
+    hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e == hipSuccess && int64_t(i) < cap) {
+      e = hipEventElapsedTime(&t0, recs[0].a, r.a);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t1, recs[0].a, r.b);
     }
+    if (e != hipSuccess) {
+      rc = fsm::fail(MOE_ERR_HIP, "moe_profile_collect: %s", hipGetErrorString(e));
+      break;
+    }
+    if (r.kind >= 0 && r.kind < MOE_KERNEL_KINDS) {
+      out[r.kind].count += 1;
+      out[r.kind].total_ms += ms;
+    }
+    if (int64_t(i) < cap)
+      iv[i] = moe_kernel_interval_t{r.kind, 0, uint64_t(reinterpret_cast<uintptr_t>(r.s)), double(t0), double(t1)};
+  }
+  for (const fsm::Rec& r : recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
   }
   return rc;
+}
+
+int moe_profile_collect(moe_kernel_time_t* out) {
+  if (!out) return fsm::fail(MOE_ERR_INVALID_ARG, "moe_profile_collect: out is required");
+  int32_t n = 0;
+  return moe_profile_collect_intervals(out, nullptr, 0, &n);
 }
 
 }  // extern "C"

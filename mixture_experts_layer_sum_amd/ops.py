@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
-                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelTime, LayerDesc, LayerGrads, StackCfg, check, lib)
+                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelInterval, KernelTime, LayerDesc, LayerGrads, StackCfg, check, lib)
 
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
 MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
@@ -272,6 +272,19 @@ def profile_collect() -> dict:
     out = (KernelTime * len(KERNEL_KINDS))()
     check("moe_profile_collect", lib.moe_profile_collect(out))
     return {name: (out[i].count, out[i].total_ms) for i, name in enumerate(KERNEL_KINDS)}
+
+
+def profile_collect_intervals(cap: int = 16384):
+    """profile_collect, plus every recorded launch as (kind, stream id, start ms, end ms) on one time
+    axis (the first recorded launch's start event is 0)."""
+    out = (KernelTime * len(KERNEL_KINDS))()
+    iv = (KernelInterval * cap)()
+    n = ctypes.c_int32(0)
+    check("moe_profile_collect_intervals", lib.moe_profile_collect_intervals(out, iv, cap, ctypes.byref(n)))
+    totals = {name: (out[i].count, out[i].total_ms) for i, name in enumerate(KERNEL_KINDS)}
+    launches = [(KERNEL_KINDS[r.kind] if 0 <= r.kind < len(KERNEL_KINDS) else str(r.kind), int(r.stream),
+                 r.start_ms, r.end_ms) for r in iv[:min(n.value, cap)]]
+    return totals, launches
 
 
 # ---------------------------------------------------------------------------------------------

@@ -137,6 +137,17 @@ def _intersect(x, y):
     return tot
 
 
+def overlap(main, side) -> dict:
+    """Cross-stream overlap of two lists of (start, end) busy intervals (any one unit): the lengths
+    of their unions |M| and |S|, of the intersection |M n S|, and the fractions |M n S| / |S| (the
+    share of the side queue's work that ran while the main queue was busy) and |M n S| / |M|."""
+    M, S = _union(main), _union(side)
+    both = _intersect(M, S)
+    lm, ls = _length(M), _length(S)
+    return {"main": lm, "side": ls, "both": both,
+            "side_hidden": both / ls if ls else None, "main_covered": both / lm if lm else None}
+
+
 def cmd_trace(path, skip_first=0):
     print(f"# grouped GEMM source digest {source_digest()} (common.h, gemm.hip, tile_kit.h)")
     disp = []
@@ -166,16 +177,14 @@ def cmd_trace(path, skip_first=0):
         print("# overlap: could not identify a single main queue")
         return
     mq = main_q.pop()
-    M = _union([(t0, t1) for t0, t1, q, _ in lib if q == mq])
-    S = _union([(t0, t1) for t0, t1, q, _ in lib if q != mq])
-    if not S:
+    ov = overlap([(t0, t1) for t0, t1, q, _ in lib if q == mq], [(t0, t1) for t0, t1, q, _ in lib if q != mq])
+    if not ov["side"]:
         print("# overlap: no side-queue work (single stream)")
         return
-    both = _intersect(M, S)
     span = max(d[1] for d in lib) - min(d[0] for d in lib)
-    print(f"# overlap: main queue {mq}; |M| = {_length(M) / 1e6:.2f} ms, |S| = {_length(S) / 1e6:.2f} ms, "
-          f"|M n S| = {both / 1e6:.2f} ms, span = {span / 1e6:.2f} ms")
-    print(f"# overlap fraction |M n S|/|S| = {both / _length(S):.4f}   |M n S|/|M| = {both / _length(M):.4f}")
+    print(f"# overlap: main queue {mq}; |M| = {ov['main'] / 1e6:.2f} ms, |S| = {ov['side'] / 1e6:.2f} ms, "
+          f"|M n S| = {ov['both'] / 1e6:.2f} ms, span = {span / 1e6:.2f} ms")
+    print(f"# overlap fraction |M n S|/|S| = {ov['side_hidden']:.4f}   |M n S|/|M| = {ov['main_covered']:.4f}")
 
 
 def _per_dispatch(path):

@@ -197,3 +197,33 @@ def test_stack_dsv3_full_size_sampled(ops, name):
         assert_parity((o_new - o_prev)[keep], res["out"][keep], torch.bfloat16, f"{name} layer {j} S + R")
         if x_next is not None:  # partial: x_{j+1} = bf16(o_{j-1} + S_j)
             assert_parity(x_next[keep], rnd(o_prev + res["S"])[keep], torch.bfloat16, f"{name} layer {j} x_next")
+
+
+def test_profile_intervals_of_a_two_stream_stack(ops):
+    """The per-launch intervals behind bench.py's overlap figure: one per recorded launch, on both
+    streams, consistent with the per-kind totals of the same collection."""
+    c = MID_STACK
+    layers, o0 = make_stack(c)
+    run_stack(ops, c, layers, o0, "partial")   # warm-up outside the recording
+    ops.profile_collect()
+    ops.profile_enable(True)
+    try:
+        run_stack(ops, c, layers, o0, "partial")
+    finally:
+        ops.profile_enable(False)
+    totals, launches = ops.profile_collect_intervals()
+    assert len(launches) == sum(n for n, _ in totals.values()) > 0
+    assert all(b >= a for _, _, a, b in launches)
+    streams = {s for _, s, _, _ in launches}
+    assert len(streams) == 2
+    main = torch.cuda.current_stream().cuda_stream
+    routed = {s for k, s, _, _ in launches if k in ("gemm_gate_up", "gemm_down", "permute_index")}
+    assert routed == {main}
+    for kind, (n, ms) in totals.items():
+        mine = [b - a for k, _, a, b in launches if k == kind]
+        assert len(mine) == n
+        # both are differences of float event times (about 1 us resolution)
+        assert abs(sum(mine) - ms) <= 2e-3 * n + 1e-4 * ms
+    # nothing left behind: the next collection is empty
+    totals2, launches2 = ops.profile_collect_intervals()
+    assert launches2 == [] and all(n == 0 for n, _ in totals2.values())

@@ -73,3 +73,15 @@ def test_gemm_symbol_classification():
     shared = "void fsm::k_gemm_bf16<256, 256, 2, 4, 1, 1, 64, 2>(fsm::GemmArgs)"
     assert not profiling.is_routed_gate_up(shared) and not profiling.is_routed(shared)
     assert not profiling.is_routed(R) and profiling.gemm_args("fsm::k_combine(int)") is None
+
+
+def test_overlap_of_intervals():
+    # main busy [0, 10) and [20, 30); side busy [5, 25) (two pieces that touch): 10 of side's 20 hidden
+    ov = profiling.overlap([(0, 10), (20, 30)], [(5, 15), (15, 25)])
+    assert (ov["main"], ov["side"], ov["both"]) == (20, 20, 10)
+    assert ov["side_hidden"] == 0.5 and ov["main_covered"] == 0.5
+    # nested and repeated intervals are merged before measuring
+    ov = profiling.overlap([(0, 4), (1, 2), (0, 4)], [(3, 8)])
+    assert (ov["main"], ov["side"], ov["both"]) == (4, 5, 1)
+    # one stream only: no side fraction
+    assert profiling.overlap([(0, 1)], [])["side_hidden"] is None
