@@ -20,7 +20,7 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_group
            "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
            "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
            "moe_layer_backward_workspace_bytes", "farskip_stack_backward", "farskip_stack_backward_workspace_bytes",
-           "moe_combine", "farskip_stack_forward",
+           "moe_combine", "farskip_stack_forward", "farskip_stack_forward_mxfp8", "farskip_stack_mxfp8_workspace_bytes",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect",
            "moe_profile_collect_intervals", "moe_last_error",
            "moe_version")
@@ -33,6 +33,10 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("W_R", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("W1", ctypes.c_void_p),
                 ("W2", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("Ws1", ctypes.c_void_p),
                 ("Ws2", ctypes.c_void_p), ("Ws3", ctypes.c_void_p)]
+
+
+class LayerMx(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s")]
 
 
 class StackCfg(ctypes.Structure):
@@ -104,6 +108,12 @@ def _declare(lib):
     lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,
                                           ctypes.POINTER(ctypes.c_uint8), vp, vp, vp, sz, vp, vp]
     lib.farskip_stack_forward.restype = i
+    lib.farskip_stack_forward_mxfp8.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerMx), i32,
+                                                ctypes.POINTER(StackCfg), i, ctypes.POINTER(ctypes.c_uint8), vp, vp,
+                                                vp, sz, vp, vp]
+    lib.farskip_stack_forward_mxfp8.restype = i
+    lib.farskip_stack_mxfp8_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
+    lib.farskip_stack_mxfp8_workspace_bytes.restype = sz
     lib.farskip_stack_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
     lib.farskip_stack_workspace_bytes.restype = sz
     lib.moe_profile_enable.argtypes = [i]

@@ -132,9 +132,13 @@ struct StackWs {
   void* Y[2];
   void* gemm_ws;
   void* shared_ws;
+  uint8_t* xq[2];   // MXFP8 stack: codes and scales of the layer inputs
+  uint8_t* xs[2];
 };
 
-StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total) {
+// mx: the MXFP8 stack's buffers (layer-input codes and scales, the MXFP8 product's workspace) in
+// place of the bf16 product's workspace
+StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total, bool mx = false) {
   const size_t es = esize(c.dtype);
   const size_t T = size_t(c.T), d = size_t(c.d), E = size_t(c.E), k = size_t(c.k);
   char* base = static_cast<char*>(ws);
@@ -158,8 +162,14 @@ StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total) {
   s.shared_off = static_cast<int32_t*>(take(2 * 4));
   s.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
   for (int b = 0; b < 2; ++b) s.Y[b] = take(T * k * d * es);
-  s.gemm_ws = take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
+  s.gemm_ws = mx ? take(mx_swiglu_ws_bytes(c.T * c.k, c.E, c.c)) : take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
   s.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype)) : nullptr;
+  if (mx) {
+    for (int b = 0; b < 2; ++b) {
+      s.xq[b] = static_cast<uint8_t*>(take(T * d));
+      s.xs[b] = static_cast<uint8_t*>(take(T * d / 32));
+    }
+  }
   if (total) *total = off;
   return s;
 }
@@ -173,7 +183,7 @@ __global__ void k_set_shared_offsets(int32_t* off, int32_t T) {
 
 // shapes, modes and pointers of a stack call (forward or backward); `who` names the entry point
 int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
-                     const float* o0, const float* oL, const char* who) {
+                     const float* o0, const float* oL, const char* who, const moe_layer_mx_t* mx = nullptr) {
   if (!layers || !cfg) return fail(MOE_ERR_INVALID_ARG, "%s: layers and cfg are required", who);
   if (L < 1) return fail(MOE_ERR_INVALID_ARG, "%s: L=%d must be >= 1", who, L);
   if (mode != FARSKIP_NONE && mode != FARSKIP_PARTIAL && mode != FARSKIP_OUTDATED)
@@ -198,10 +208,17 @@ int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_
     return fail(MOE_ERR_UNSUPPORTED, "%s: a layer input above 2^31 bytes", who);
   if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "%s: o0 and oL are required", who);
   if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "%s: oL must not alias o0", who);
+  if (mx && c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs bf16 layers", who);
+  if (mx && (c.d % 128 != 0 || c.c % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs d and c multiples of 128", who);
+  if (mx && c.T * c.k * c.c >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T * k * c must be below 2^31", who);
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
-    if (!l.W_R || !l.W1 || !l.W2 || !l.W3)
+    if (!l.W_R || (!mx && (!l.W1 || !l.W2 || !l.W3)))
       return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing routed weights", who, j);
+    if (mx && (!mx[j].W1q || !mx[j].W1s || !mx[j].W2q || !mx[j].W2s || !mx[j].W3q || !mx[j].W3s))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing MXFP8 expert codes or scales", who, j);
     if (c.c_shared && (!l.Ws1 || !l.Ws2 || !l.Ws3))
       return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing shared weights", who, j);
   }
@@ -260,11 +277,18 @@ int wait(hipStream_t s, hipEvent_t e) {
 // Buffer reuse: permute_{j+2}, topk_{j+2} and GEMM_{j+2} rewrite what combine_j reads; the main
 // stream reaches them only after waiting for route_{j+2}, which the side stream records after
 // combine_j.  make_input_{j+1} rewrites x_{j-1}, read by GEMM_{j-1}; it follows the wait for
-// permute_j.  Events are recorded before the waits that name them are enqueued.
+// permute_j.  Events are recorded before the waits that name them are enqueued.  The MXFP8
+// stack's layer-input codes and scales [j % 2] are written right after x_j, on the same stream,
+// and read only by GEMM_j, so they follow x_j's reuse rule.
 int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
                   const uint8_t* mask, const float* o0, float* oL, void* ws, hipStream_t sm,
-                  hipStream_t ss) {
-  StackWs w = carve_stack(ws, c, nullptr);
+                  hipStream_t ss, const moe_layer_mx_t* mx = nullptr) {
+  StackWs w = carve_stack(ws, c, nullptr, mx != nullptr);
+  // MXFP8 stack: each layer input is quantised on s_side as soon as it is formed (before the
+  // router that s_main's permutation waits for)
+  auto quantize_input = [&](int b) -> int {
+    return mx ? launch_mx_quantize(w.x[b], c.T, c.d, w.xq[b], w.xs[b], ss) : MOE_OK;
+  };
   const bool two = sm != ss;
   Events E_route, E_perm, E_gemm, E_end;
   if (two) {
@@ -291,14 +315,17 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
   k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));
   if (int rc = check_launch("stack setup")) return rc;
   if (int rc = launch_make_input(o0, nullptr, c.dtype, c.T, c.d, w.x[0], ss)) return rc;
+  if (int rc = quantize_input(0)) return rc;
 
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
     const int cur = j & 1, nxt = cur ^ 1;
     const bool last = j + 1 == L;
     // side: layer j's router
-    if (j > 0 && !skip_at(j - 1))
-      if (int rc = combine(j - 1)) return rc;
+    if (j > 0 && !skip_at(j - 1)) {
+      if (int rc = combine(j - 1)) return rc;   // also forms x_j
+      if (int rc = quantize_input(cur)) return rc;
+    }
     if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
     if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
       return rc;
@@ -325,11 +352,19 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
     if (skip_at(j) && !last) {
       const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
       if (int rc = launch_make_input(j == 0 ? o0 : oL, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
+      if (int rc = quantize_input(nxt)) return rc;
     }
     // main: layer j's routed GEMMs
-    if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y[cur],
-                                       w.gemm_ws, sm, w.sorted_src, c.k, c.T))
+    if (mx) {
+      const moe_layer_mx_t& q = mx[j];
+      if (int rc = launch_grouped_swiglu_mx(w.xq[cur], w.xs[cur], w.offsets, c.E, q.W1q, q.W1s, q.W2q, q.W2s, q.W3q,
+                                            q.W3s, N, c.d, c.c, w.Y[cur], w.gemm_ws, sm, w.sorted_src, c.k, c.T, 3,
+                                            nullptr, nullptr))
+        return rc;
+    } else if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c,
+                                              w.Y[cur], w.gemm_ws, sm, w.sorted_src, c.k, c.T)) {
       return rc;
+    }
     if (two)
       if (int rc = record(E_gemm.ev[j], sm)) return rc;
   }
@@ -512,6 +547,27 @@ int moe_combine(const void* Y, int dtype, const float* topk_w, const int32_t* de
   clear_error();
   if (int rc = check_combine(Y, dtype, topk_w, dest_row, T, d, k, out)) return rc;
   return launch_combine(Y, dtype, topk_w, dest_row, T, d, k, addend, residual, out, out_x, as_stream(stream));
+}
+
+size_t farskip_stack_mxfp8_workspace_bytes(const moe_stack_cfg_t* cfg) {
+  if (!cfg || cfg->T < 1 || cfg->d < 1 || cfg->c < 1 || cfg->E < 1 || cfg->k < 1 || cfg->dtype != MOE_BF16)
+    return 0;
+  size_t total = 0;
+  carve_stack(nullptr, *cfg, &total, true);
+  return total;
+}
+
+int farskip_stack_forward_mxfp8(const moe_layer_desc_t* layers, const moe_layer_mx_t* mx, int32_t L,
+                                const moe_stack_cfg_t* cfg, int mode, const uint8_t* skip_mask, const float* o0,
+                                float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side) {
+  clear_error();
+  const char* who = "farskip_stack_forward_mxfp8";
+  if (!mx) return fail(MOE_ERR_INVALID_ARG, "%s: mx is required", who);
+  if (int rc = check_stack_args(layers, L, cfg, mode, o0, oL, who, mx)) return rc;
+  size_t need = 0;
+  carve_stack(nullptr, *cfg, &need, true);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  return stack_forward(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side), mx);
 }
 
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg) {

@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
-                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelInterval, KernelTime, LayerDesc, LayerGrads, StackCfg, check, lib)
+                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelInterval, KernelTime, LayerDesc, LayerMx, LayerGrads, StackCfg, check, lib)
 
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
 MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
@@ -193,12 +193,44 @@ def stack_workspace_bytes(cfg: StackCfg) -> int:
     return int(lib.farskip_stack_workspace_bytes(ctypes.byref(cfg)))
 
 
-def layer_desc(W: dict) -> LayerDesc:
+def layer_desc(W: dict, routed: bool = True) -> LayerDesc:
+    """Device-pointer descriptor of one layer; routed=False leaves W1-W3 out (the MXFP8 stack)."""
+    rp = lambda name: W[name].data_ptr() if routed else None  # noqa: E731
     return LayerDesc(W_R=W["W_R"].data_ptr(), bias=W["bias"].data_ptr() if W.get("bias") is not None else None,
-                     W1=W["W1"].data_ptr(), W2=W["W2"].data_ptr(), W3=W["W3"].data_ptr(),
+                     W1=rp("W1"), W2=rp("W2"), W3=rp("W3"),
                      Ws1=W["Ws1"].data_ptr() if W.get("Ws1") is not None else None,
                      Ws2=W["Ws2"].data_ptr() if W.get("Ws2") is not None else None,
                      Ws3=W["Ws3"].data_ptr() if W.get("Ws3") is not None else None)
+
+
+def stack_mxfp8_workspace_bytes(cfg: StackCfg) -> int:
+    return int(lib.farskip_stack_mxfp8_workspace_bytes(ctypes.byref(cfg)))
+
+
+def layer_mx(W: dict) -> dict:
+    """MXFP8 (codes, scales) of one layer's routed experts W1, W2 [E, c, d] and W3 [E, d, c]."""
+    return {name: mx_quantized(W[name]) for name in ("W1", "W2", "W3")}
+
+
+def farskip_stack_forward_mxfp8(layers: Sequence[dict], mx_layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws,
+                                skip_mask=None, s_main=None, s_side=None):
+    """farskip_stack_forward with the routed experts on MXFP8 operands; mx_layers[j] as layer_mx()."""
+    L = len(layers)
+    if len(mx_layers) != L:
+        raise ValueError("one MXFP8 expert set per layer is required")
+    descs = (LayerDesc * L)(*[layer_desc(W, routed=False) for W in layers])
+    mxd = (LayerMx * L)(*[LayerMx(W1q=q["W1"][0].data_ptr(), W1s=q["W1"][1].data_ptr(), W2q=q["W2"][0].data_ptr(),
+                                  W2s=q["W2"][1].data_ptr(), W3q=q["W3"][0].data_ptr(), W3s=q["W3"][1].data_ptr())
+                          for q in mx_layers])
+    mask = None
+    if skip_mask is not None:
+        mask = (ctypes.c_uint8 * L)(*[1 if m else 0 for m in skip_mask])
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    sm = _s(s_main)
+    ss = _s(s_side) if s_side is not None else sm
+    check("farskip_stack_forward_mxfp8",
+          lib.farskip_stack_forward_mxfp8(descs, mxd, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(),
+                                          sm, ss))
 
 
 def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws, skip_mask=None,

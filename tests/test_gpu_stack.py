@@ -52,13 +52,17 @@ def make_stack(c):
     return layers, o0
 
 
-def run_stack(ops, c, layers, o0, mode, mask=None, two_streams=True):
+def run_stack(ops, c, layers, o0, mode, mask=None, two_streams=True, mx_layers=None):
     cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
-    ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
     oL = torch.full_like(o0, float("nan"))
     sm = torch.cuda.current_stream()
     ss = torch.cuda.Stream() if two_streams else sm
-    ops.farskip_stack_forward(layers, cfg, mode, o0, oL, ws, skip_mask=mask, s_main=sm, s_side=ss)
+    if mx_layers is not None:
+        ws = ops.workspace(ops.stack_mxfp8_workspace_bytes(cfg), DEV)
+        ops.farskip_stack_forward_mxfp8(layers, mx_layers, cfg, mode, o0, oL, ws, skip_mask=mask, s_main=sm, s_side=ss)
+    else:
+        ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
+        ops.farskip_stack_forward(layers, cfg, mode, o0, oL, ws, skip_mask=mask, s_main=sm, s_side=ss)
     torch.cuda.synchronize()
     return oL
 
@@ -125,9 +129,11 @@ def test_stack_two_streams_equals_one_stream(ops, mode, mask):
     assert torch.equal(a, c2)  # bitwise repeatable
 
 
-def composed(ops, c, layers, o0, mode, mask, rows=None, record=None):
+def composed(ops, c, layers, o0, mode, mask, rows=None, record=None, mx_layers=None):
     """The stack recursion written with the single ABI calls on one stream.  With rows and a record
-    list, each layer appends (x_j, o_{j-1}, o_j, topk_idx_j, x_{j+1} or None) for those rows."""
+    list, each layer appends (x_j, o_{j-1}, o_j, topk_idx_j, x_{j+1} or None) for those rows.  With
+    mx_layers, the routed experts are moe_grouped_swiglu_mxfp8 on moe_mx_quantize of x_j, rows
+    gathered through the permutation."""
     from mixture_experts_layer_sum_amd.ops import LayerBuffers
     dt = c.torch_dtype
     buf = LayerBuffers(c.T, c.d, c.E, c.k, c.c, c.shared_width, dt, DEV)
@@ -136,9 +142,15 @@ def composed(ops, c, layers, o0, mode, mask, rows=None, record=None):
     L = len(layers)
     for j, W in enumerate(layers):
         ops.moe_route(x, W["W_R"], c.k, c.gate, c.renormalize, buf.logits, buf.topk_idx, buf.topk_w, bias=W["bias"])
-        ops.moe_permute(buf.topk_idx, c.E, buf.offsets, buf.sorted_src, buf.dest_row, A=x, A_perm=buf.A_perm,
-                        ws=buf.perm_ws)
-        ops.moe_grouped_swiglu(buf.A_perm, buf.offsets, W["W1"], W["W2"], W["W3"], buf.Y, ws=buf.gemm_ws)
+        if mx_layers is not None:
+            q = mx_layers[j]
+            ops.moe_permute(buf.topk_idx, c.E, buf.offsets, buf.sorted_src, buf.dest_row, ws=buf.perm_ws)
+            ops.moe_grouped_swiglu_mxfp8(ops.mx_quantized(x), buf.offsets, q["W1"], q["W2"], q["W3"], buf.Y,
+                                         sorted_src=buf.sorted_src, k=c.k)
+        else:
+            ops.moe_permute(buf.topk_idx, c.E, buf.offsets, buf.sorted_src, buf.dest_row, A=x, A_perm=buf.A_perm,
+                            ws=buf.perm_ws)
+            ops.moe_grouped_swiglu(buf.A_perm, buf.offsets, W["W1"], W["W2"], W["W3"], buf.Y, ws=buf.gemm_ws)
         S = None
         if c.shared_width:
             ops.moe_grouped_swiglu(x, buf.shared_off, W["Ws1"], W["Ws2"], W["Ws3"], buf.S, ws=buf.shared_ws)
@@ -227,3 +239,58 @@ def test_profile_intervals_of_a_two_stream_stack(ops):
     # nothing left behind: the next collection is empty
     totals2, launches2 = ops.profile_collect_intervals()
     assert launches2 == [] and all(n == 0 for n, _ in totals2.values())
+
+
+# ---- the stack with MXFP8 routed experts ---------------------------------------------------------
+MID_STACK_NOSH = MID_STACK.scaled(cfg_id=13, name="mid-bf16-stack-no-shared", n_shared=0, c_shared=0)
+
+
+@pytest.mark.parametrize("mode,mask", MODES[:4])
+def test_mxfp8_stack_equals_composed_ops_and_one_stream(ops, mode, mask):
+    c = MID_STACK
+    layers, o0 = make_stack(c)
+    mxl = [ops.layer_mx(W) for W in layers]
+    a = run_stack(ops, c, layers, o0, mode, mask, mx_layers=mxl)
+    assert not torch.isnan(a).any().item()
+    assert torch.equal(a, run_stack(ops, c, layers, o0, mode, mask, two_streams=False, mx_layers=mxl))
+    assert torch.equal(a, composed(ops, c, layers, o0, mode, mask, mx_layers=mxl))
+    assert torch.equal(a, run_stack(ops, c, layers, o0, mode, mask, mx_layers=mxl))  # repeatable
+
+
+def test_mxfp8_stack_vs_oracle_teacher_forced(ops):
+    """Each layer's routed output on the GPU's own layer inputs (64 seeded tokens) against the
+    MXFP8 oracle: selection identical away from near-ties; o_j - o_{j-1} = sum_i w_i MLP_mx(x_j)
+    within the MXFP8 end-to-end bar (mean |err| <= 2^-8 mean |ref|); partial inputs bf16(o_{j-1})."""
+    from tests.mx_bound import fp32_store
+    mx = oracle.mxfp8
+    c = MID_STACK_NOSH
+    layers, o0 = make_stack(c)
+    mxl = [ops.layer_mx(W) for W in layers]
+    oL = run_stack(ops, c, layers, o0, "partial", mx_layers=mxl)
+    rows = mi.sample_rows(c.T, 64, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 5))
+    rec = []
+    assert torch.equal(oL, composed(ops, c, layers, o0, "partial", None, rows=rows, record=rec, mx_layers=mxl))
+    for j, W in enumerate(layers):
+        x, o_prev, o_new, idx, x_next = rec[j]
+        W_R = to_np(W["W_R"]).astype(np.float64)
+        logits = oracle.router_logits(x, W_R, None if W.get("bias") is None else to_np(W["bias"]).astype(np.float64))
+        ref_idx = oracle.select_topk(logits, c.k)
+        keep = oracle.topk_gap(logits, c.k) >= NEAR_TIE
+        assert keep.sum() >= 48
+        np.testing.assert_array_equal(idx[keep], ref_idx[keep])
+        w = oracle.gate_weights(logits, ref_idx, c.gate, c.renormalize)
+        q = {n: {} for n in ("W1", "W2", "W3")}
+        ref = np.zeros_like(x)
+        for t in np.nonzero(keep)[0]:
+            for i in range(c.k):
+                e = int(ref_idx[t, i])
+                for n in q:
+                    if e not in q[n]:
+                        q[n][e] = mx.mx_quantize(to_np(W[n][e]).astype(np.float64))
+                ref[t] += w[t, i] * mx.mlp_mxfp8(x[t:t + 1], q["W1"][e], q["W2"][e], q["W3"][e],
+                                                 hidden_store=fp32_store)[0]
+        err = np.abs((o_new - o_prev) - ref)[keep]
+        r = float(err.mean() / np.abs(ref[keep]).mean())
+        assert r <= 2.0 ** -8, f"layer {j}: mean|err|/mean|ref| = {r:.3e}"
+        if x_next is not None:
+            np.testing.assert_array_equal(x_next, oracle.round_to_bf16(o_prev))
