@@ -280,6 +280,46 @@ def mxfp8(c, layers, o0, reps: int = 3) -> dict:
     return out
 
 
+def mxfp8_stack(c, layers, o0, steps: int = 5) -> dict:
+    """The same 4-layer FarSkip stack with the routed experts on MXFP8 operands
+    (farskip_stack_forward_mxfp8): all layers' routed weights quantised once (as at load time,
+    untimed), then one warm-up and `steps` timed steps on the same two streams; per-kernel times and
+    the cross-stream overlap from HIP events."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    mxl = [ops.layer_mx(W) for W in layers]
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_mxfp8_workspace_bytes(cfg), dev)
+    oL = torch.empty_like(o0)
+    main_s, side_s = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def step():
+        ops.farskip_stack_forward_mxfp8(layers, mxl, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=side_s)
+
+    step()
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ops.profile_enable(False)
+    prof, launches = ops.profile_collect_intervals()
+    assert torch.isfinite(oL).all().item(), "non-finite MXFP8 stack output"
+    ms = (t1 - t0) * 1e3 / steps
+    out = {"layers": c.layers, "steps": steps, "ms_per_step": round(ms, 3),
+           "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
+           "kernels": kernel_report(prof, c, steps), "overlap": stream_overlap(launches, main_s.cuda_stream),
+           "what": "routed experts MXFP8 (E4M3, E8M0 per 32); router, shared expert and combine bf16 / fp32"}
+    del mxl, ws, oL
+    torch.cuda.empty_cache()
+    return out
+
+
 def backward(c, layers, o0, reps: int = 2) -> dict:
     """Layer 0's backward pass (moe_layer_backward) for a random output gradient, after its forward
     (router, permutation, gathered grouped product) on the same input.  Per kind of kernel: the
@@ -611,6 +651,8 @@ def main():
     if args.mxfp8 and c.name == "dsv3-stack":
         log("timing the MXFP8 routed experts")
         result["mxfp8"] = leg("mxfp8", lambda: mxfp8(c, layers, o0))
+        log("timing the stack with MXFP8 routed experts")
+        result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, o0))
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
