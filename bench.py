@@ -111,6 +111,8 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
         "mx_quantize": (T * d * (2.0 + 1.0 + 1.0 / 32), "byte"),   # the token rows, once per layer
         "mx_gate_up": (4.0 * N * d * c_, "flop_fp8"),
         "mx_down": (2.0 * N * d * c_, "flop_fp8"),
+        "mx_dense_gate_up": (4.0 * T * d * cs, "flop_fp8"),
+        "mx_dense_down": (2.0 * T * d * cs, "flop_fp8"),
     }
     out = {}
     for kind, (n, ms) in prof.items():
@@ -281,8 +283,8 @@ def mxfp8(c, layers, o0, reps: int = 3) -> dict:
 
 
 def mxfp8_stack(c, layers, o0, steps: int = 5) -> dict:
-    """The same 4-layer FarSkip stack with the routed experts on MXFP8 operands
-    (farskip_stack_forward_mxfp8): all layers' routed weights quantised once (as at load time,
+    """The same 4-layer FarSkip stack with the expert MLPs on MXFP8 operands
+    (farskip_stack_forward_mxfp8): all layers' expert weights quantised once (as at load time,
     untimed), then one warm-up and `steps` timed steps on the same two streams; per-kernel times and
     the cross-stream overlap from HIP events."""
     import torch
@@ -314,7 +316,7 @@ def mxfp8_stack(c, layers, o0, steps: int = 5) -> dict:
     out = {"layers": c.layers, "steps": steps, "ms_per_step": round(ms, 3),
            "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
            "kernels": kernel_report(prof, c, steps), "overlap": stream_overlap(launches, main_s.cuda_stream),
-           "what": "routed experts MXFP8 (E4M3, E8M0 per 32); router, shared expert and combine bf16 / fp32"}
+           "what": "routed and shared experts MXFP8 (E4M3, E8M0 per 32); router and combine bf16 / fp32"}
     del mxl, ws, oL
     torch.cuda.empty_cache()
     return out

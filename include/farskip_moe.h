@@ -266,30 +266,37 @@ int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_s
                           size_t ws_bytes, void* s_main, void* s_side);
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
 
-/* MXFP8 codes and scales of one layer's routed experts, as moe_mx_quantize writes them. */
+/* MXFP8 codes and scales of one layer's expert weights, as moe_mx_quantize writes them. */
 typedef struct {
-  const uint8_t* W1q; /* [E, c, d] E4M3 codes */
-  const uint8_t* W1s; /* [E, c, d / 32] E8M0 scales */
-  const uint8_t* W2q; /* [E, c, d] */
-  const uint8_t* W2s; /* [E, c, d / 32] */
-  const uint8_t* W3q; /* [E, d, c] */
-  const uint8_t* W3s; /* [E, d, c / 32] */
+  const uint8_t* W1q;  /* [E, c, d] E4M3 codes */
+  const uint8_t* W1s;  /* [E, c, d / 32] E8M0 scales */
+  const uint8_t* W2q;  /* [E, c, d] */
+  const uint8_t* W2s;  /* [E, c, d / 32] */
+  const uint8_t* W3q;  /* [E, d, c] */
+  const uint8_t* W3s;  /* [E, d, c / 32] */
+  const uint8_t* Ws1q; /* [c_shared, d] shared experts (NULL when c_shared == 0) */
+  const uint8_t* Ws1s; /* [c_shared, d / 32] */
+  const uint8_t* Ws2q; /* [c_shared, d] */
+  const uint8_t* Ws2s; /* [c_shared, d / 32] */
+  const uint8_t* Ws3q; /* [d, c_shared] */
+  const uint8_t* Ws3s; /* [d, c_shared / 32] */
 } moe_layer_mx_t;
 
 /*
- * farskip_stack_forward_mxfp8 -- farskip_stack_forward with each layer's routed experts run on
- * MXFP8 operands (FarSkip-Collective section 5 serves its converted models with FP8 quantisation
- * and fused MoE kernels; the format is OCP MXFP8).  Per layer, on top of the bf16 stack: the layer
- * input x_j (bf16) is quantised to MXFP8 rows on s_side right after it is formed, and s_main's
- * routed products are moe_grouped_swiglu_mxfp8 with rows gathered through the permutation
- * (Y in bf16).  The router, top-k, shared experts, combine and the residual bookkeeping are those
- * of farskip_stack_forward, in bf16 / fp32.  The result equals the same single calls composed on
- * one stream, bit for bit.
- *   layers  as farskip_stack_forward, except that W1, W2, W3 are not read (may be NULL)
- *   mx      host array [L]: the routed experts' MXFP8 codes and scales
+ * farskip_stack_forward_mxfp8 -- farskip_stack_forward with each layer's expert MLPs (routed and
+ * shared) run on MXFP8 operands (FarSkip-Collective section 5 serves its converted models with FP8
+ * quantisation and fused MoE kernels; the format is OCP MXFP8).  Per layer, on top of the bf16
+ * stack: the layer input x_j (bf16) is quantised to MXFP8 rows on s_side right after it is formed;
+ * s_main's routed products are moe_grouped_swiglu_mxfp8 with rows gathered through the permutation
+ * and s_side's shared expert is moe_grouped_swiglu_mxfp8 over all T rows as one group (outputs in
+ * bf16).  The router, top-k, combine and the residual bookkeeping are those of
+ * farskip_stack_forward, in bf16 / fp32.  The result equals the same single calls composed on one
+ * stream, bit for bit.
+ *   layers  as farskip_stack_forward, except that W1-W3 and Ws1-Ws3 are not read (may be NULL)
+ *   mx      host array [L]: the experts' MXFP8 codes and scales
  *   ws      scratch of at least farskip_stack_mxfp8_workspace_bytes(cfg) bytes
- * Requires cfg->dtype == MOE_BF16, d and c multiples of 128.  Errors and stream contract as
- * farskip_stack_forward.
+ * Requires cfg->dtype == MOE_BF16, d, c and c_shared multiples of 128.  Errors and stream contract
+ * as farskip_stack_forward.
  */
 int farskip_stack_forward_mxfp8(const moe_layer_desc_t* layers, const moe_layer_mx_t* mx, int32_t L,
                                 const moe_stack_cfg_t* cfg, int mode, const uint8_t* skip_mask, const float* o0,
@@ -395,7 +402,9 @@ typedef enum {
   MOE_K_BWD_WGRAD = 16,   /* backward: weight-gradient products (reduction over rows) */
   MOE_K_TRANSPOSE = 17,   /* backward: weight and activation transposes */
   MOE_K_BWD_POINTWISE = 18, /* backward: combine, gate, SwiGLU and bias-sum kernels */
-  MOE_KERNEL_KINDS = 19
+  MOE_K_MX_DENSE_GATE_UP = 19, /* MXFP8 phase 1 of a single-group call (the shared expert) */
+  MOE_K_MX_DENSE_DOWN = 20,    /* MXFP8 phase 2 of a single-group call */
+  MOE_KERNEL_KINDS = 21
 } moe_kernel_kind_t;
 
 typedef struct {

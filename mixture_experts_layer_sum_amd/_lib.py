@@ -26,7 +26,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_group
            "moe_version")
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
                 "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
-                "mx_down", "bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise")
+                "mx_down", "bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise",
+                "mx_dense_gate_up", "mx_dense_down")
 
 
 class LayerDesc(ctypes.Structure):
@@ -36,7 +37,8 @@ class LayerDesc(ctypes.Structure):
 
 
 class LayerMx(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s",
+                                                "Ws1q", "Ws1s", "Ws2q", "Ws2s", "Ws3q", "Ws3s")]
 
 
 class StackCfg(ctypes.Structure):

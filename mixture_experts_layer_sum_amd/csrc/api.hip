@@ -163,7 +163,8 @@ StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total, bool mx =
   s.perm_ws = take(permute_ws_bytes(c.T, c.E, c.k));
   for (int b = 0; b < 2; ++b) s.Y[b] = take(T * k * d * es);
   s.gemm_ws = mx ? take(mx_swiglu_ws_bytes(c.T * c.k, c.E, c.c)) : take(swiglu_ws_bytes(c.T * c.k, c.E, c.c, c.dtype));
-  s.shared_ws = c.c_shared ? take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype)) : nullptr;
+  s.shared_ws = !c.c_shared ? nullptr
+                : mx ? take(mx_swiglu_ws_bytes(c.T, 1, c.c_shared)) : take(swiglu_ws_bytes(c.T, 1, c.c_shared, c.dtype));
   if (mx) {
     for (int b = 0; b < 2; ++b) {
       s.xq[b] = static_cast<uint8_t*>(take(T * d));
@@ -209,8 +210,8 @@ int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_
   if (!o0 || !oL) return fail(MOE_ERR_INVALID_ARG, "%s: o0 and oL are required", who);
   if (o0 == oL) return fail(MOE_ERR_INVALID_ARG, "%s: oL must not alias o0", who);
   if (mx && c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs bf16 layers", who);
-  if (mx && (c.d % 128 != 0 || c.c % 128 != 0))
-    return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs d and c multiples of 128", who);
+  if (mx && (c.d % 128 != 0 || c.c % 128 != 0 || c.c_shared % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs d, c and c_shared multiples of 128", who);
   if (mx && c.T * c.k * c.c >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "%s: T * k * c must be below 2^31", who);
   for (int j = 0; j < L; ++j) {
@@ -219,8 +220,11 @@ int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_
       return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing routed weights", who, j);
     if (mx && (!mx[j].W1q || !mx[j].W1s || !mx[j].W2q || !mx[j].W2s || !mx[j].W3q || !mx[j].W3s))
       return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing MXFP8 expert codes or scales", who, j);
-    if (c.c_shared && (!l.Ws1 || !l.Ws2 || !l.Ws3))
+    if (c.c_shared && !mx && (!l.Ws1 || !l.Ws2 || !l.Ws3))
       return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing shared weights", who, j);
+    if (c.c_shared && mx &&
+        (!mx[j].Ws1q || !mx[j].Ws1s || !mx[j].Ws2q || !mx[j].Ws2s || !mx[j].Ws3q || !mx[j].Ws3s))
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing MXFP8 shared-expert codes or scales", who, j);
   }
   return MOE_OK;
 }
@@ -342,7 +346,13 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
       if (int rc = record(E_perm.ev[j], sm)) return rc;
       if (int rc = wait(ss, E_perm.ev[j])) return rc;
     }
-    if (c.c_shared) {
+    if (c.c_shared && mx) {
+      const moe_layer_mx_t& q = mx[j];
+      if (int rc = launch_grouped_swiglu_mx(w.xq[cur], w.xs[cur], w.shared_off, 1, q.Ws1q, q.Ws1s, q.Ws2q, q.Ws2s,
+                                            q.Ws3q, q.Ws3s, c.T, c.d, c.c_shared, w.S[cur], w.shared_ws, ss,
+                                            nullptr, 1, c.T, 3, nullptr, nullptr))
+        return rc;
+    } else if (c.c_shared) {
       if (int rc = launch_grouped_swiglu(w.x[cur], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, c.dtype, c.T, c.d,
                                          c.c_shared, w.S[cur], w.shared_ws, ss))
         return rc;

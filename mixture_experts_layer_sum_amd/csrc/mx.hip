@@ -407,7 +407,7 @@ int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int
   a.n_tiles = int32_t(cdiv(c, MX_BN / 2));
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
   a.gather = gather; a.gather_k = gather_k; a.a_rows = x_rows;
-  ProfScope prof(MOE_K_MX_GATE_UP, s);
+  ProfScope prof(G > 1 ? MOE_K_MX_GATE_UP : MOE_K_MX_DENSE_GATE_UP, s);
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G), a.n_tiles, a.group_m, a.quad_nb)));
   if (gather)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER><<<grid, 512, 0, s>>>(a);
@@ -426,7 +426,7 @@ int mx_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* offsets, int32_
   a.K = int32_t(c); a.n_out = int32_t(d); a.M = int32_t(N); a.G = G; a.group_m = MX_GROUP_M;
   a.n_tiles = int32_t(cdiv(d, MX_BN));
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
-  ProfScope prof(MOE_K_MX_DOWN, s);
+  ProfScope prof(G > 1 ? MOE_K_MX_DOWN : MOE_K_MX_DENSE_DOWN, s);
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G), a.n_tiles, a.group_m, a.quad_nb)));
   k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
   return check_launch("mx grouped gemm phase 2");

@@ -193,14 +193,12 @@ def stack_workspace_bytes(cfg: StackCfg) -> int:
     return int(lib.farskip_stack_workspace_bytes(ctypes.byref(cfg)))
 
 
-def layer_desc(W: dict, routed: bool = True) -> LayerDesc:
-    """Device-pointer descriptor of one layer; routed=False leaves W1-W3 out (the MXFP8 stack)."""
-    rp = lambda name: W[name].data_ptr() if routed else None  # noqa: E731
+def layer_desc(W: dict, experts: bool = True) -> LayerDesc:
+    """Device-pointer descriptor of one layer; experts=False leaves the expert weights W1-W3 and
+    Ws1-Ws3 out (the MXFP8 stack takes them quantised)."""
+    rp = lambda name: W[name].data_ptr() if experts and W.get(name) is not None else None  # noqa: E731
     return LayerDesc(W_R=W["W_R"].data_ptr(), bias=W["bias"].data_ptr() if W.get("bias") is not None else None,
-                     W1=rp("W1"), W2=rp("W2"), W3=rp("W3"),
-                     Ws1=W["Ws1"].data_ptr() if W.get("Ws1") is not None else None,
-                     Ws2=W["Ws2"].data_ptr() if W.get("Ws2") is not None else None,
-                     Ws3=W["Ws3"].data_ptr() if W.get("Ws3") is not None else None)
+                     W1=rp("W1"), W2=rp("W2"), W3=rp("W3"), Ws1=rp("Ws1"), Ws2=rp("Ws2"), Ws3=rp("Ws3"))
 
 
 def stack_mxfp8_workspace_bytes(cfg: StackCfg) -> int:
@@ -208,8 +206,10 @@ def stack_mxfp8_workspace_bytes(cfg: StackCfg) -> int:
 
 
 def layer_mx(W: dict) -> dict:
-    """MXFP8 (codes, scales) of one layer's routed experts W1, W2 [E, c, d] and W3 [E, d, c]."""
-    return {name: mx_quantized(W[name]) for name in ("W1", "W2", "W3")}
+    """MXFP8 (codes, scales) of one layer's expert weights: routed W1, W2 [E, c, d], W3 [E, d, c] and,
+    when present, shared Ws1, Ws2 [c_shared, d], Ws3 [d, c_shared] (each along its last dimension)."""
+    return {name: mx_quantized(W[name]) for name in ("W1", "W2", "W3", "Ws1", "Ws2", "Ws3")
+            if W.get(name) is not None}
 
 
 def farskip_stack_forward_mxfp8(layers: Sequence[dict], mx_layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws,
@@ -218,10 +218,14 @@ def farskip_stack_forward_mxfp8(layers: Sequence[dict], mx_layers: Sequence[dict
     L = len(layers)
     if len(mx_layers) != L:
         raise ValueError("one MXFP8 expert set per layer is required")
-    descs = (LayerDesc * L)(*[layer_desc(W, routed=False) for W in layers])
-    mxd = (LayerMx * L)(*[LayerMx(W1q=q["W1"][0].data_ptr(), W1s=q["W1"][1].data_ptr(), W2q=q["W2"][0].data_ptr(),
-                                  W2s=q["W2"][1].data_ptr(), W3q=q["W3"][0].data_ptr(), W3s=q["W3"][1].data_ptr())
-                          for q in mx_layers])
+    descs = (LayerDesc * L)(*[layer_desc(W, experts=False) for W in layers])
+    def mx_desc(q):
+        f = {}
+        for name in ("W1", "W2", "W3", "Ws1", "Ws2", "Ws3"):
+            f[name + "q"], f[name + "s"] = (q[name][0].data_ptr(), q[name][1].data_ptr()) if name in q else (None, None)
+        return LayerMx(**f)
+
+    mxd = (LayerMx * L)(*[mx_desc(q) for q in mx_layers])
     mask = None
     if skip_mask is not None:
         mask = (ctypes.c_uint8 * L)(*[1 if m else 0 for m in skip_mask])

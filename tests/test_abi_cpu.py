@@ -271,3 +271,16 @@ def test_backward_argument_errors():
     bad = list(sok)
     bad[3] = 5
     err(s(*bad), L.MOE_ERR_INVALID_ARG, "mode")
+
+
+def test_kernel_kinds_match_the_header():
+    """The binding's kernel-kind names follow moe_kernel_kind_t, in order and in number."""
+    import re
+
+    from mixture_experts_layer_sum_amd._lib import KERNEL_KINDS
+    text = open(os.path.join(ROOT, "include", "farskip_moe.h")).read()
+    body = text[text.index("MOE_K_ROUTER_GEMM"):text.index("} moe_kernel_kind_t;")]
+    kinds = {int(v): n.lower() for n, v in re.findall(r"MOE_K_(\w+)\s*=\s*(\d+)", body)}
+    count = int(re.search(r"MOE_KERNEL_KINDS\s*=\s*(\d+)", body).group(1))
+    assert sorted(kinds) == list(range(count))
+    assert tuple(kinds[i] for i in range(count)) == KERNEL_KINDS
