@@ -231,6 +231,14 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
         "device_copy_GBps": round(2 * a.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
     }
+    # each kernel against the box's measured ceiling of its kind, beside its fraction of the peak
+    for kind, v in out.items():
+        if not isinstance(v, dict):
+            continue
+        if "tflops" in v and kind != "ep8_share":
+            v["frac_of_hipblaslt"] = round(v["tflops"] / out["ceilings"]["hipblaslt_bf16_8192cubed_TFLOPs"], 4)
+        if "gbs" in v:
+            v["frac_of_device_copy"] = round(v["gbs"] / out["ceilings"]["device_copy_GBps"], 4)
     del a, b, m, n
     return out
 

@@ -212,8 +212,8 @@ int check_stack_args(const moe_layer_desc_t* layers, int32_t L, const moe_stack_
   if (mx && c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs bf16 layers", who);
   if (mx && (c.d % 128 != 0 || c.c % 128 != 0 || c.c_shared % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "%s: the MXFP8 stack needs d, c and c_shared multiples of 128", who);
-  if (mx && c.T * c.k * c.c >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "%s: T * k * c must be below 2^31", who);
+  if (mx && (c.T * c.k * c.c >= (int64_t(1) << 31) || c.T * c.c_shared >= (int64_t(1) << 31)))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T * k * c and T * c_shared must be below 2^31", who);
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
     if (!l.W_R || (!mx && (!l.W1 || !l.W2 || !l.W3)))

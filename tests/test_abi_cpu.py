@@ -284,3 +284,35 @@ def test_kernel_kinds_match_the_header():
     count = int(re.search(r"MOE_KERNEL_KINDS\s*=\s*(\d+)", body).group(1))
     assert sorted(kinds) == list(range(count))
     assert tuple(kinds[i] for i in range(count)) == KERNEL_KINDS
+
+
+def test_mxfp8_stack_argument_errors():
+    """farskip_stack_forward_mxfp8 rejects bad calls on the host, before any launch."""
+    f = lib.farskip_stack_forward_mxfp8
+    cfg = _cfg(d=128, c=256, c_shared=128, dtype=1)
+    need = lib.farskip_stack_mxfp8_workspace_bytes(ctypes.byref(cfg))
+    assert need > lib.farskip_stack_workspace_bytes(ctypes.byref(cfg)) - 64 * 8 * 128 * 2 * 4
+    assert lib.farskip_stack_mxfp8_workspace_bytes(ctypes.byref(_cfg(dtype=0))) == 0   # fp32: no MXFP8 stack
+    desc = (L.LayerDesc * 2)(*[L.LayerDesc(W_R=0x1000) for _ in range(2)])   # expert weights not read
+    full = {n: 0x1000 for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s", "Ws1q", "Ws1s", "Ws2q", "Ws2s", "Ws3q", "Ws3s")}
+    mx = (L.LayerMx * 2)(*[L.LayerMx(**full) for _ in range(2)])
+    ok_args = [desc, mx, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None]
+    bad = list(ok_args)
+    bad[1] = None
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "mx")
+    bad = list(ok_args)
+    bad[9] = need - 1
+    err(f(*bad), L.MOE_ERR_WORKSPACE)
+    no_shared = dict(full, Ws3s=None)
+    bad = list(ok_args)
+    bad[1] = (L.LayerMx * 2)(L.LayerMx(**full), L.LayerMx(**no_shared))
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "shared")
+    no_routed = dict(full, W2q=None)
+    bad = list(ok_args)
+    bad[1] = (L.LayerMx * 2)(L.LayerMx(**no_routed), L.LayerMx(**full))
+    err(f(*bad), L.MOE_ERR_INVALID_ARG, "layer 0")
+    for c_bad in (_cfg(d=128, c=192, c_shared=128, dtype=1), _cfg(d=128, c=256, c_shared=192, dtype=1),
+                  _cfg(d=128, c=256, c_shared=0, dtype=0)):
+        bad = list(ok_args)
+        bad[3] = ctypes.byref(c_bad)
+        err(f(*bad), L.MOE_ERR_UNSUPPORTED)
