@@ -539,7 +539,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU expert-parallel "
-              "path is not part of this build.", file=sys.stderr)
+              "path (collectives across GPUs) is not implemented in this library.", file=sys.stderr)
         sys.exit(2)
 
     import torch
