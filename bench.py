@@ -290,16 +290,19 @@ def mxfp8(c, layers, o0, reps: int = 3) -> dict:
     return out
 
 
-def mxfp8_stack(c, layers, o0, steps: int = 5) -> dict:
+def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
     """The same 4-layer FarSkip stack with the expert MLPs on MXFP8 operands
-    (farskip_stack_forward_mxfp8): all layers' expert weights quantised once (as at load time,
-    untimed), then one warm-up and `steps` timed steps on the same two streams; per-kernel times and
-    the cross-stream overlap from HIP events."""
+    (farskip_stack_forward_mxfp8) for workload c: the experts' weights quantised once beforehand (as
+    at load time, untimed: mxl), then one warm-up and `steps` timed steps on the same two streams;
+    per-kernel times and the cross-stream overlap from HIP events, and the weight stream per step
+    against the HBM peak (the bound of a decode-sized batch)."""
     import torch
 
+    import moe_inputs as mi
     from mixture_experts_layer_sum_amd import ops
-    dev = o0.device
-    mxl = [ops.layer_mx(W) for W in layers]
+    dev = layers[0]["W_R"].device
+    if o0 is None:
+        o0 = mi.activations(c, dev).float()
     cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
     ws = ops.workspace(ops.stack_mxfp8_workspace_bytes(cfg), dev)
     oL = torch.empty_like(o0)
@@ -321,11 +324,15 @@ def mxfp8_stack(c, layers, o0, steps: int = 5) -> dict:
     prof, launches = ops.profile_collect_intervals()
     assert torch.isfinite(oL).all().item(), "non-finite MXFP8 stack output"
     ms = (t1 - t0) * 1e3 / steps
-    out = {"layers": c.layers, "steps": steps, "ms_per_step": round(ms, 3),
+    weight_bytes = c.layers * ((3 * c.E * c.c * c.d + 3 * c.shared_width * c.d) * (1 + 1 / 32) + 2 * c.E * c.d)
+    gbs = weight_bytes / (ms * 1e-3) / 1e9
+    out = {"workload": c.name, "tokens": c.T, "layers": c.layers, "steps": steps, "ms_per_step": round(ms, 3),
            "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
+           "weight_stream": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": round(weight_bytes)},
            "kernels": kernel_report(prof, c, steps), "overlap": stream_overlap(launches, main_s.cuda_stream),
            "what": "routed and shared experts MXFP8 (E4M3, E8M0 per 32); router and combine bf16 / fp32"}
-    del mxl, ws, oL
+    del ws, oL
     torch.cuda.empty_cache()
     return out
 
@@ -661,8 +668,14 @@ def main():
     if args.mxfp8 and c.name == "dsv3-stack":
         log("timing the MXFP8 routed experts")
         result["mxfp8"] = leg("mxfp8", lambda: mxfp8(c, layers, o0))
-        log("timing the stack with MXFP8 routed experts")
-        result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, o0))
+        mxl = [ops.layer_mx(W) for W in layers]
+        log("timing the stack with MXFP8 expert MLPs")
+        result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, mxl, o0))
+        log("timing the decode-shaped stack with MXFP8 expert MLPs")
+        result["mxfp8"]["decode_stack"] = leg("mxfp8 decode stack",
+                                              lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10))
+        del mxl
+        torch.cuda.empty_cache()
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))

@@ -261,20 +261,24 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   }
 
   const int KT = K / RB;
+  // A wave whose rows all lie past the group's last row (the ragged last M-tile of a group; most of
+  // the tile for a decode batch of a few dozen rows per expert) skips its fragment reads and MFMAs.
+  // It still loads its share of every stage and meets every barrier; its rows are never stored.
+  const bool live = wm * WTM < rows;
   MX_STAGE(0, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   MX_BARRIER();
   for (int kt = 0;;) {   // two stages, unrolled by two so each half names its buffer
     if (kt + 1 < KT) MX_STAGE(kt + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    MX_COMPUTE(0);
+    if (live) MX_COMPUTE(0)
     __builtin_amdgcn_sched_barrier(0);
     if (++kt >= KT) break;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     MX_BARRIER();
     if (kt + 1 < KT) MX_STAGE(kt + 1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    MX_COMPUTE(1);
+    if (live) MX_COMPUTE(1)
     __builtin_amdgcn_sched_barrier(0);
     if (++kt >= KT) break;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));

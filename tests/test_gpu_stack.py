@@ -304,12 +304,13 @@ def test_mxfp8_stack_vs_oracle_teacher_forced(ops):
             assert r <= 2.0 ** -8, f"layer {j} x_next: mean|err|/mean|ref| = {r:.3e}"
 
 
-def test_mxfp8_stack_dsv3_full_size(ops):
-    """The DeepSeek-V3-shaped layers (T = 65536, d = 7168, 256 experts, top-8) through the MXFP8
-    stack in the bench launch configuration (two streams, partial inputs; two layers here): equal
-    bit for bit to the composed single calls, whose MXFP8 grouped product the full-size tests of
-    that call check against the oracle; finite."""
-    c = mi.BY_NAME["dsv3-stack"].scaled(layers=2)
+@pytest.mark.parametrize("name", ["dsv3-stack", "dsv3-decode"])
+def test_mxfp8_stack_dsv3_full_size(ops, name):
+    """The DeepSeek-V3-shaped layers (d = 7168, 256 experts, top-8; prefill T = 65536 and a decode
+    batch T = 1024) through the MXFP8 stack in the bench launch configuration (two streams, partial
+    inputs; two layers here): equal bit for bit to the composed single calls, whose MXFP8 grouped
+    product the full-size tests of that call check against the oracle; finite."""
+    c = mi.BY_NAME[name].scaled(layers=2)
     layers, o0 = make_stack(c)
     mxl = [ops.layer_mx(W) for W in layers]
     oL = run_stack(ops, c, layers, o0, "partial", mx_layers=mxl)
