@@ -50,6 +50,8 @@ def parse():
                    help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
     p.add_argument("--mxfp8", type=int, default=1,
                    help="after the steps, time the layer-0 routed experts with MXFP8 operands; 0 = skip")
+    p.add_argument("--mxfp8-stack", type=int, default=1,
+                   help="with --mxfp8: also time the prefill and decode stacks with MXFP8 expert MLPs")
     p.add_argument("--backward", type=int, default=1,
                    help="after the steps, time the backward pass of layer 0 (one MoE sublayer); 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -668,12 +670,17 @@ def main():
     if args.mxfp8 and c.name == "dsv3-stack":
         log("timing the MXFP8 routed experts")
         result["mxfp8"] = leg("mxfp8", lambda: mxfp8(c, layers, o0))
-        mxl = [ops.layer_mx(W) for W in layers]
-        log("timing the stack with MXFP8 expert MLPs")
-        result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, mxl, o0))
-        log("timing the decode-shaped stack with MXFP8 expert MLPs")
-        result["mxfp8"]["decode_stack"] = leg("mxfp8 decode stack",
-                                              lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10))
+    if args.mxfp8 and args.mxfp8_stack and c.name == "dsv3-stack":
+        log("quantising every layer's expert weights to MXFP8")
+        mxl = leg("mxfp8 weights", lambda: [ops.layer_mx(W) for W in layers])
+        if isinstance(mxl, dict):   # the quantisation failed: report it in place of both stack legs
+            result["mxfp8"]["stack"] = result["mxfp8"]["decode_stack"] = mxl
+        else:
+            log("timing the stack with MXFP8 expert MLPs")
+            result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, mxl, o0))
+            log("timing the decode-shaped stack with MXFP8 expert MLPs")
+            result["mxfp8"]["decode_stack"] = leg(
+                "mxfp8 decode stack", lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10))
         del mxl
         torch.cuda.empty_cache()
     if args.standalone:
