@@ -105,24 +105,35 @@ struct MxArgs {
   int64_t a_rows;            // rows of A (the gathered form's resource extent)
 };
 
-template <int EPI, int ROWS>
-__global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
-  constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, NW = 8;
+// Tilings: BM x 256 output tiles, WAVES_M x 4 waves, S LDS stages.  256 x 256 with 8 waves and two
+// stages for the prefill-sized groups; 64 x 256 with 4 waves and three stages for groups of a few
+// dozen rows (a decode batch), where the product streams the weights and more bytes in flight per
+// CU matter more than the MFMA work.  Both sum every output over K in the same order.
+template <int EPI, int ROWS, int BM_ = 256, int WAVES_M_ = 2, int S_ = 2>
+__global__ __launch_bounds__(256 * WAVES_M_) void k_gemm_mx(MxArgs p) {
+  constexpr int BM = BM_, BN = 256, WAVES_M = WAVES_M_, WAVES_N = 4, NW = WAVES_M * WAVES_N, S = S_;
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
   constexpr int RB = 128;                       // bytes (K values) per LDS row per stage
   constexpr int RUN_ROWS = 8;                   // rows of one wave's 1 KB direct-to-LDS run
   constexpr int A_RUNS = BM / RUN_ROWS / NW, B_RUNS = BN / RUN_ROWS / NW;
-  constexpr int LOADS = A_RUNS + B_RUNS + 1;    // + one 4-byte scale load per wave
-  constexpr int DATA = (BM + BN) * RB, SCL = (BM + BN) * 4;
+  // scale bytes: the BM + BN rows' 4 bytes per stage, in runs of 64 rows (one 4-byte load per
+  // lane); wave w loads runs w, w + NW, ...  Runs past the last row load zeros into padding, so
+  // every wave issues the same number of loads per stage.
+  constexpr int SROWS = BM + BN, SL = (SROWS + 64 * NW - 1) / (64 * NW);
+  constexpr int LOADS = A_RUNS + B_RUNS + SL;   // vector-memory operations per wave per stage
+  constexpr int DATA = (BM + BN) * RB, SCL = SL * NW * 64 * 4;
   static_assert(EPI != MX_SWIGLU || (FN % 2) == 0, "SwiGLU needs paired fragments");
   static_assert(EPI != MX_SWIGLU || (WTN / 2) == 32, "a wave's H columns of a row must be one MX block");
-  static_assert(BM + BN == 64 * NW, "one scale row per lane");
+  static_assert(A_RUNS * RUN_ROWS * NW == BM && B_RUNS * RUN_ROWS * NW == BN, "runs must tile the stage");
+  static_assert(BM % 64 == 0 && (BN / 2) % 64 == 0, "scale runs must not straddle A / B / gate rows");
+  static_assert(S == 2 || S == 3, "two or three stages");
+  static_assert(LOADS * (S - 2) < 64, "vmcnt range");
 
   // one LDS array per stage (data rows, then their scale bytes): separate objects let the compiler
   // see that the loads filling one stage never alias the reads of the other
   constexpr int STAGE = DATA + SCL;
-  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE], st1[STAGE];
-#define MX_SM(BUF) ((BUF) ? st1 : st0)
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE], st1[STAGE], st2[S > 2 ? STAGE : 16];
+#define MX_SM(BUF) ((BUF) == 0 ? st0 : (BUF) == 1 ? st1 : st2)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -143,18 +154,17 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   const bool b_gate = EPI == MX_SWIGLU && wb_row0 >= BN / 2;
   const __amdgpu_buffer_rsrc_t rB = make_rsrc((b_gate ? p.B2 : p.B1) + g * p.b_group_stride + int64_t(n0) * K,
                                               int64_t(nvalid) * K);
-  // scale rows: waves 0-3 load A rows wave * 64 + lane, waves 4-7 load B rows (wave - 4) * 64 + lane
-  const bool s_is_a = wave < NW / 2;
-  const int s_row0 = (s_is_a ? wave : wave - NW / 2) * 64, s_row = s_row0 + lane;
-  const bool s_gate = EPI == MX_SWIGLU && !s_is_a && s_row0 >= BN / 2;   // uniform: whole waves
-  const __amdgpu_buffer_rsrc_t rBs = make_rsrc((s_gate ? p.B2s : p.B1s) + g * p.bs_group_stride + int64_t(n0) * KB,
-                                               int64_t(nvalid) * KB);
-  const __amdgpu_buffer_rsrc_t rS = s_is_a ? rAs : rBs;
+  // scale rows: run i of this wave covers tile rows 64 (i NW + wave) + lane (A rows first, then B
+  // rows); a run lies wholly in A, in B1's half or in B2's half (uniform over the wave)
+  const __amdgpu_buffer_rsrc_t rB1s = make_rsrc(p.B1s + g * p.bs_group_stride + int64_t(n0) * KB, int64_t(nvalid) * KB);
+  const __amdgpu_buffer_rsrc_t rB2s =
+      EPI == MX_SWIGLU ? make_rsrc(p.B2s + g * p.bs_group_stride + int64_t(n0) * KB, int64_t(nvalid) * KB) : rB1s;
 
   // this lane's load offsets at k = 0 (lane l writes physical chunk l % 8 of row l / 8 of a run,
   // so it loads logical chunk (l % 8) ^ (row & 7): the XOR swizzle the fragment reads undo)
   const int d_row = lane >> 3, d_ch = (lane & 7) ^ d_row;
-  uint32_t dA[A_RUNS], dB[B_RUNS], dS;
+  uint32_t dA[A_RUNS], dB[B_RUNS], dS[SL];
+  __amdgpu_buffer_rsrc_t rS[SL];
   if (ROWS == MX_ROWS_GATHER) {
     int src[A_RUNS];
 #pragma unroll
@@ -174,13 +184,24 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
     const int r = wb_row0 + i * RUN_ROWS + d_row;
     dB[i] = uint32_t(b_gate ? r - BN / 2 : r) * uint32_t(K) + uint32_t(d_ch) * 16u;
   }
-  if (s_is_a) {
-    if (ROWS == MX_ROWS_GATHER)
-      dS = s_row < rows ? uint32_t(p.gather[row0 + s_row] / p.gather_k) * uint32_t(KB) : 0x80000000u;
-    else
-      dS = uint32_t(s_row) * uint32_t(KB);
-  } else {
-    dS = uint32_t(s_gate ? s_row - BN / 2 : s_row) * uint32_t(KB);
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const int s_row0 = (i * NW + wave) * 64, s_row = s_row0 + lane;   // s_row0 is wave-uniform
+    if (s_row0 >= SROWS) {          // padding run: beyond every resource, loads zeros
+      rS[i] = rAs;
+      dS[i] = 0x80000000u;
+    } else if (s_row0 < BM) {       // A rows
+      rS[i] = rAs;
+      if (ROWS == MX_ROWS_GATHER)
+        dS[i] = s_row < rows ? uint32_t(p.gather[row0 + s_row] / p.gather_k) * uint32_t(KB) : 0x80000000u;
+      else
+        dS[i] = uint32_t(s_row) * uint32_t(KB);
+    } else {                        // B rows (the gate half reads B2's scales)
+      const int b_row = s_row - BM;
+      const bool s_gate = EPI == MX_SWIGLU && s_row0 - BM >= BN / 2;
+      rS[i] = s_gate ? rB2s : rB1s;
+      dS[i] = uint32_t(s_gate ? b_row - BN / 2 : b_row) * uint32_t(KB);
+    }
   }
 
   // fragment reads: A rows (wm * WTM + 16 i + lane % 16), B rows likewise; lane group q = lane / 16
@@ -209,7 +230,8 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
       FSM_LDS_DMA16(rA, &MX_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * RB], dA[i] + kb); \
     _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                          \
       FSM_LDS_DMA16(rB, &MX_SM(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb);  \
-    FSM_LDS_DMA4(rS, &MX_SM(BUF)[DATA + wave * 64 * 4], dS + uint32_t(KT) * 4u + kb_zero); \
+    _Pragma("unroll") for (int i = 0; i < SL; ++i)                                              \
+      FSM_LDS_DMA4(rS[i], &MX_SM(BUF)[DATA + (i * NW + wave) * 64 * 4], dS[i] + uint32_t(KT) * 4u + kb_zero); \
   }
 #define MX_BROW(J) \
   ((EPI == MX_SWIGLU) ? ((J) < FN / 2 ? (J) * 16 : BN / 2 + ((J) - FN / 2) * 16) : (J) * 16)
@@ -265,25 +287,38 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
   // the tile for a decode batch of a few dozen rows per expert) skips its fragment reads and MFMAs.
   // It still loads its share of every stage and meets every barrier; its rows are never stored.
   const bool live = wm * WTM < rows;
-  MX_STAGE(0, 0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  MX_BARRIER();
-  for (int kt = 0;;) {   // two stages, unrolled by two so each half names its buffer
-    if (kt + 1 < KT) MX_STAGE(kt + 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (live) MX_COMPUTE(0)
-    __builtin_amdgcn_sched_barrier(0);
-    if (++kt >= KT) break;
+  // ring of S stages: stages 0 .. S-2 in flight, then wait for stage 0 (straight-line branches, so
+  // the compiler's own wait-count tracking sees which stages are pending)
+  if (KT >= S - 1) {
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) MX_STAGE(st, st);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2)));
+  } else {
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (st < KT) MX_STAGE(st, st);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    MX_BARRIER();
-    if (kt + 1 < KT) MX_STAGE(kt + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (live) MX_COMPUTE(1)
-    __builtin_amdgcn_sched_barrier(0);
-    if (++kt >= KT) break;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    MX_BARRIER();
   }
+  MX_BARRIER();
+  // one ring step on buffer J: refill the buffer read one step earlier with stage kt + S - 1, run
+  // this stage's MFMAs, then wait until the next stage is in LDS for every wave
+#define MX_RING_STEP(J)                                                                         \
+  {                                                                                             \
+    if (kt + S - 1 < KT) MX_STAGE(kt + S - 1, ((J) + S - 1) % S);                               \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    if (live) MX_COMPUTE(J)                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    if (++kt >= KT) break;                                                                      \
+    if (kt + S - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS * (S - 2)));               \
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                             \
+    MX_BARRIER();                                                                               \
+  }
+  for (int kt = 0;;) {   // unrolled S times so each step names its buffers as constants
+    MX_RING_STEP(0);
+    MX_RING_STEP(1);
+    if (S > 2) MX_RING_STEP(2 % S);
+  }
+#undef MX_RING_STEP
   (void)LOADS;
 #undef MX_SM
 #undef MX_STAGE
@@ -370,9 +405,15 @@ __global__ __launch_bounds__(512) void k_gemm_mx(MxArgs p) {
 
 // ---- host launchers ------------------------------------------------------------------------
 namespace {
-constexpr int MX_BM = 256, MX_BN = 256, MX_GROUP_M = 4;
+constexpr int MX_BM = 256, MX_BN = 256, MX_GROUP_M = 4, MX_SMALL_BM = 64, MX_SMALL_ROWS = 96;
 
-int64_t mx_max_tiles(int64_t N, int32_t G) { return cdiv(N, MX_BM) + G; }
+// 64-row tiles where groups average at most MX_SMALL_ROWS rows, or where 256-row tiles would not
+// give every CU a workgroup (the rule of the bf16 product)
+bool mx_small(int64_t N, int32_t G, int64_t c) {
+  return N <= int64_t(MX_SMALL_ROWS) * G || (cdiv(N, MX_BM) + G) * cdiv(c, MX_BN / 2) < 256;
+}
+int mx_bm(int64_t N, int32_t G, int64_t c) { return mx_small(N, G, c) ? MX_SMALL_BM : MX_BM; }
+int64_t mx_max_tiles(int64_t N, int32_t G, int bm) { return cdiv(N, bm) + G; }
 
 // workspace: the M-tile table, then (fused call only) H's codes and scales
 struct MxWs {
@@ -389,7 +430,7 @@ MxWs carve_mx(void* ws, int32_t G, int64_t N, int64_t c, size_t* total) {
   w.ts = reinterpret_cast<int32_t*>(base + off);
   off = align_up(off + size_t(G + 1) * 4, 256);
   w.grp = reinterpret_cast<int32_t*>(base + off);
-  off = align_up(off + size_t(mx_max_tiles(N, G)) * 4, 256);
+  off = align_up(off + size_t(mx_max_tiles(N, G, MX_SMALL_BM)) * 4, 256);   // room for either tiling
   w.Hq = reinterpret_cast<uint8_t*>(base + off);
   off = align_up(off + size_t(N) * size_t(c), 256);
   w.Hs = reinterpret_cast<uint8_t*>(base + off);
@@ -401,7 +442,7 @@ MxWs carve_mx(void* ws, int32_t G, int64_t N, int64_t c, size_t* total) {
 int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int32_t G, const uint8_t* W1q,
                const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s, int64_t N, int64_t d, int64_t c,
                uint8_t* Hq, uint8_t* Hs, const MxWs& w, hipStream_t s, const int32_t* gather, int32_t gather_k,
-               int64_t x_rows) {
+               int64_t x_rows, int bm) {
   MxArgs a{};
   a.A = Xq; a.As = Xs; a.B1 = W1q; a.B1s = W1s; a.B2 = W2q; a.B2s = W2s;
   a.out = Hq; a.out_s = Hs;
@@ -412,8 +453,12 @@ int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
   a.gather = gather; a.gather_k = gather_k; a.a_rows = x_rows;
   ProfScope prof(G > 1 ? MOE_K_MX_GATE_UP : MOE_K_MX_DENSE_GATE_UP, s);
-  const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G), a.n_tiles, a.group_m, a.quad_nb)));
-  if (gather)
+  const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
+  if (bm == MX_SMALL_BM && gather)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (gather)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER><<<grid, 512, 0, s>>>(a);
   else
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
@@ -421,7 +466,7 @@ int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int
 }
 
 int mx_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* offsets, int32_t G, const uint8_t* W3q,
-            const uint8_t* W3s, int64_t N, int64_t c, int64_t d, void* Y, const MxWs& w, hipStream_t s) {
+            const uint8_t* W3s, int64_t N, int64_t c, int64_t d, void* Y, const MxWs& w, hipStream_t s, int bm) {
   MxArgs a{};
   a.A = Hq; a.As = Hs; a.B1 = W3q; a.B1s = W3s; a.B2 = nullptr; a.B2s = nullptr;
   a.out = Y; a.out_s = nullptr;
@@ -431,8 +476,11 @@ int mx_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* offsets, int32_
   a.n_tiles = int32_t(cdiv(d, MX_BN));
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
   ProfScope prof(G > 1 ? MOE_K_MX_DOWN : MOE_K_MX_DENSE_DOWN, s);
-  const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G), a.n_tiles, a.group_m, a.quad_nb)));
-  k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
+  const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
+  if (bm == MX_SMALL_BM)
+    k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else
+    k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
   return check_launch("mx grouped gemm phase 2");
 }
 }  // namespace
@@ -463,11 +511,15 @@ int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t
     Hq = w.Hq;
     Hs = w.Hs;
   }
-  if (int rc = launch_tile_table(offsets, G, MX_BM, int(mx_max_tiles(N, G)), w.ts, w.grp, s)) return rc;
+  // the tiling follows the group sizes and the hidden width, so the two calls of a split product
+  // (phases 1 then 2) pick the same one
+  const int bm = mx_bm(N, G, c);
+  if (int rc = launch_tile_table(offsets, G, bm, int(mx_max_tiles(N, G, bm)), w.ts, w.grp, s)) return rc;
   if (phases & 1)
-    if (int rc = mx_gate_up(Xq, Xs, offsets, G, W1q, W1s, W2q, W2s, N, d, c, Hq, Hs, w, s, gather, gather_k, x_rows))
+    if (int rc = mx_gate_up(Xq, Xs, offsets, G, W1q, W1s, W2q, W2s, N, d, c, Hq, Hs, w, s, gather, gather_k, x_rows,
+                            bm))
       return rc;
-  if (phases & 2) return mx_down(Hq, Hs, offsets, G, W3q, W3s, N, c, d, Y, w, s);
+  if (phases & 2) return mx_down(Hq, Hs, offsets, G, W3q, W3s, N, c, d, Y, w, s, bm);
   return MOE_OK;
 }
 

@@ -266,6 +266,42 @@ def test_grouped_mxfp8_gathered(ops, T, E, k, d, c):
             check_end_to_end(to_np(Ygf[a:b]), Xp[a:b], o1[g], o2[g], o3[g], f"group {g}")
 
 
+def test_grouped_mxfp8_small_tiles_bitwise_equal_large(ops):
+    """Groups averaging at most 96 rows (or grids too small to give every CU a workgroup) run on
+    64-row tiles with three stages, the rest on 256-row tiles with two.  The same rows and weights
+    with empty groups appended (which moves the average below the switch) must give bit-identical
+    H and Y: both tilings sum every output over K in the same order.  Then the 64-row result
+    against the oracle's bars."""
+    d, c = 256, 2048
+    sizes = [2500, 0, 3100, 2592]                   # 2048 rows per group, 640 big tiles: 256-row tiles
+    extra = [0] * 100                               # 8192 rows over 104 groups: 64-row tiles
+    N = sum(sizes)
+    seed = mi.seed_for(89, N, d, c)
+    A = mi.block_scaled_normal((N, d), 1.0, seed, DEV, spread=3)
+    G = len(sizes) + len(extra)
+    W1, W2, W3 = make_weights(G, d, c, seed)
+    Aq = ops.mx_quantized(A)
+    g = len(sizes)
+    big = [ops.mx_quantized(W[:g].contiguous()) for W in (W1, W2, W3)]
+    small = [ops.mx_quantized(W) for W in (W1, W2, W3)]
+    off_big = torch.from_numpy(offsets_of(sizes)).to(DEV)
+    off_small = torch.from_numpy(offsets_of(sizes + extra)).to(DEV)
+    H_big, _, Y_big = run_phases_and_fused(ops, Aq, off_big, *big, N, c, d)
+    H_small, _, Y_small = run_phases_and_fused(ops, Aq, off_small, *small, N, c, d)
+    assert torch.equal(H_big[0], H_small[0]) and torch.equal(H_big[1], H_small[1])
+    assert torch.equal(Y_big, Y_small)
+    A_np = to_np(A).astype(np.float64)
+    o1, o2, o3 = oracle_stack(W1[:g]), oracle_stack(W2[:g]), oracle_stack(W3[:g])
+    off_np = offsets_of(sizes)
+    for e in range(g):
+        a, b = int(off_np[e]), int(off_np[e + 1])
+        if b > a:
+            rows = np.array(list(range(a, min(a + 40, b))) + list(range(max(a, b - 40), b)))
+            check_hidden(H_small[0][rows].cpu().numpy(), H_small[1][rows].cpu().numpy(), A_np[rows], o1[e], o2[e],
+                         f"H of group {e}")
+            check_end_to_end(to_np(Y_small[rows]), A_np[rows], o1[e], o2[e], o3[e], f"group {e}")
+
+
 DSV3 = {c.name: c for c in mi.CONFIGS}["dsv3-stack"]
 
 
