@@ -95,8 +95,19 @@ def stream_overlap(launches, main_stream) -> dict:
             "what": "|M n S| / |S| and |M n S| / |M| over the timed steps (HIP events around each launch)"}
 
 
-def kernel_report(prof: dict, c, steps: int) -> dict:
-    """Per-kind averages and the algorithmic throughput of each kernel kind."""
+def fused_input_bytes(c, mode: str = "partial") -> float:
+    """Bytes per stack step that the combine moves beyond its own formula: with the skip on at
+    consecutive layers, combine_{j-1} also forms x_{j+1} = cast(o_{j-1} (+ S_j)) (L - 2 of the L
+    combines of a step): one bf16 write of x, plus one read of S for partial inputs."""
+    if mode == "none" or c.layers < 3:
+        return 0.0
+    per = c.T * c.d * 2.0 * (2 if (mode == "partial" and c.shared_width) else 1)
+    return (c.layers - 2) * per
+
+
+def kernel_report(prof: dict, c, steps: int, extra_bytes: dict = None) -> dict:
+    """Per-kind averages and the algorithmic throughput of each kernel kind; extra_bytes adds
+    bytes per step to a kind's per-launch formula (work that some of its launches also do)."""
     T, d, E, k, c_, cs = c.T, c.d, c.E, c.k, c.c, c.shared_width
     N = T * k
     per_launch = {  # (algorithmic work per launch, unit)
@@ -129,7 +140,8 @@ def kernel_report(prof: dict, c, steps: int) -> dict:
                 peak = PEAK_FP8_TFLOPS if unit == "flop_fp8" else PEAK_BF16_TFLOPS
                 row["frac_mfma_peak"] = round(row["tflops"] / peak, 4)
             else:
-                row["gbs"] = round(work / (avg * 1e-3) / 1e9, 1)
+                total = work * n + (extra_bytes or {}).get(kind, 0.0) * steps
+                row["gbs"] = round(total / (ms * 1e-3) / 1e9, 1)
                 row["frac_hbm_peak"] = round(row["gbs"] / PEAK_HBM_GBS, 4)
         out[kind] = row
     return out
@@ -332,7 +344,8 @@ def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
            "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
            "weight_stream": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": round(weight_bytes)},
-           "kernels": kernel_report(prof, c, steps), "overlap": stream_overlap(launches, main_s.cuda_stream),
+           "kernels": kernel_report(prof, c, steps, {"combine": fused_input_bytes(c)}),
+           "overlap": stream_overlap(launches, main_s.cuda_stream),
            "what": "routed and shared experts MXFP8 (E4M3, E8M0 per 32); router and combine bf16 / fp32"}
     del ws, oL
     torch.cuda.empty_cache()
@@ -480,7 +493,7 @@ def decode(layers, steps: int = 10) -> dict:
         ms = (time.perf_counter() - t0) * 1e3 / steps
         if label == "two_streams":
             ops.profile_enable(False)
-            out["kernels"] = kernel_report(ops.profile_collect(), c, steps)
+            out["kernels"] = kernel_report(ops.profile_collect(), c, steps, {"combine": fused_input_bytes(c)})
         out[label] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1)}
     assert torch.isfinite(oL).all().item(), "non-finite decode output"
     esz = 2
@@ -615,7 +628,7 @@ def main():
         single_ms = (time.perf_counter() - t1) * 1e3 / args.single_stream_steps
         log(f"one-stream reference: {single_ms:.2f} ms/step")
 
-    kernels = kernel_report(prof, c, args.steps)
+    kernels = kernel_report(prof, c, args.steps, {"combine": fused_input_bytes(c, args.mode)})
     g = kernels.get("gemm_gate_up", {})
     flops_launch = 4.0 * c.T * c.k * c.d * c.c
     traffic = measured_traffic()

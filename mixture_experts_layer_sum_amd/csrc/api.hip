@@ -271,8 +271,9 @@ int wait(hipStream_t s, hipEvent_t e) {
 //                routed GEMMs of consecutive layers run back to back
 //   side stream: [skip off at j-1: combine_{j-1}, which also writes x_j = o_{j-1}];
 //                route_j(x_j); wait permute_j; S_j = shared_j(x_j);
-//                [skip on at j-1: combine_{j-1}: o_{j-1} = o_{j-2} + S_{j-1} + R_{j-1}];
-//                skip on at j: x_{j+1} = o_{j-1} (+ S_j when partial)
+//                [skip on at j-1: combine_{j-1}: o_{j-1} = o_{j-2} + S_{j-1} + R_{j-1}, which also
+//                writes x_{j+1} = o_{j-1} (+ S_j when partial) if the skip is on at j];
+//                skip on at j and no such combine (j = 0, or skip off at j-1): x_{j+1} from o_{j-1}
 // With the skip on, x_{j+1} needs neither R_j nor o_j, so layer j+1's router and shared expert
 // and layer j-1's combine (HBM-bound) all run under layer j's routed GEMM.  The side stream's
 // large grids (shared expert, combine) start only once permute_j is done: launched beside them,
@@ -280,8 +281,8 @@ int wait(hipStream_t s, hipEvent_t e) {
 // stream's critical path.  The last combine runs after the loop, and s_main waits for it.
 // Buffer reuse: permute_{j+2}, topk_{j+2} and GEMM_{j+2} rewrite what combine_j reads; the main
 // stream reaches them only after waiting for route_{j+2}, which the side stream records after
-// combine_j.  make_input_{j+1} rewrites x_{j-1}, read by GEMM_{j-1}; it follows the wait for
-// permute_j.  Events are recorded before the waits that name them are enqueued.  The MXFP8
+// combine_j.  Forming x_{j+1} (combine_{j-1} or make_input_{j+1}) rewrites x_{j-1}, read by
+// GEMM_{j-1}; it follows the wait for permute_j.  Events are recorded before the waits that name them are enqueued.  The MXFP8
 // stack's layer-input codes and scales [j % 2] are written right after x_j, on the same stream,
 // and read only by GEMM_j, so they follow x_j's reuse rule.
 int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
@@ -308,13 +309,16 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
   auto skip_at = [&](int j) { return mode != FARSKIP_NONE && (mask ? mask[j] != 0 : true); };
   // combine_j on the side stream: o_j = o_{j-1} + S_j + R_j into oL (o_{j-1} is o0 for j = 0, else
   // oL itself), plus x_{j+1} = o_j when layer j has no skip and is not the last
-  auto combine = [&](int j) -> int {
+  // With the skip on at j, the combine can also form layer j+2's input from o_j while it is in
+  // registers: next_x = cast(o_j + next_add) (next_add = S_{j+1} for partial inputs, null for
+  // outdated ones), the same values the layer-input kernel would form from o_j read back.
+  auto combine = [&](int j, void* next_x = nullptr, const void* next_add = nullptr) -> int {
     const int b = j & 1;
     if (two)
       if (int rc = wait(ss, E_gemm.ev[j])) return rc;
-    void* out_x = (!skip_at(j) && j + 1 < L) ? w.x[b ^ 1] : nullptr;
+    void* out_x = (!skip_at(j) && j + 1 < L) ? w.x[b ^ 1] : next_x;
     return launch_combine(w.Y[b], c.dtype, w.w[b], w.dest_row[b], c.T, c.d, c.k, c.c_shared ? w.S[b] : nullptr,
-                          j == 0 ? o0 : oL, oL, out_x, ss);
+                          j == 0 ? o0 : oL, oL, out_x, ss, (out_x && out_x == next_x) ? next_add : nullptr);
   };
   k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));
   if (int rc = check_launch("stack setup")) return rc;
@@ -357,13 +361,16 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
                                          c.c_shared, w.S[cur], w.shared_ws, ss))
         return rc;
     }
-    if (j > 0 && skip_at(j - 1))
-      if (int rc = combine(j - 1)) return rc;
-    if (skip_at(j) && !last) {
-      const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
+    // x_{j+1} = o_{j-1} (+ S_j): formed by combine_{j-1} when it runs here, else from o_{j-1} in HBM
+    const bool input_next = skip_at(j) && !last;
+    const void* add = (mode == FARSKIP_PARTIAL) ? w.S[cur] : nullptr;
+    if (j > 0 && skip_at(j - 1)) {
+      if (int rc = combine(j - 1, input_next ? w.x[nxt] : nullptr, add)) return rc;
+    } else if (input_next) {
       if (int rc = launch_make_input(j == 0 ? o0 : oL, add, c.dtype, c.T, c.d, w.x[nxt], ss)) return rc;
-      if (int rc = quantize_input(nxt)) return rc;
     }
+    if (input_next)
+      if (int rc = quantize_input(nxt)) return rc;
     // main: layer j's routed GEMMs
     if (mx) {
       const moe_layer_mx_t& q = mx[j];

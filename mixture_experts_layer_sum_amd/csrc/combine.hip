@@ -6,7 +6,9 @@
 // as a per-token gather in float32, slots in order, so the result is deterministic and needs no
 // float atomics.  Each thread owns 8 consecutive columns of one token (16-byte bf16 / 32-byte fp32
 // vectors); a workgroup of 128 threads covers 1024 columns of one token.  The optional rounded
-// copy out_x is the next layer's input when the skip is off (x_{j+1} = o_j).
+// copy out_x is a next layer's input: x_{j+1} = o_j when the skip is off, or, with x_addend, the
+// FarSkip input of the layer after, x_{j+2} = cast(o_j + S_{j+1}) (partial; outdated without
+// x_addend), formed while o_j is in registers instead of being read back.
 //
 // Layer input (section 3, eqs. (8a)/(8b)): x = cast(o) or x = cast(o + S), the "outdated" and
 // "partial" FarSkip inputs built from the float32 residual stream and the shared-expert output.
@@ -48,7 +50,8 @@ __global__ __launch_bounds__(CB_THR) void k_combine(const void* __restrict__ Y, 
                                                     const float* __restrict__ w,
                                                     const int32_t* __restrict__ dest_row, int64_t d, int k,
                                                     int col_blocks, const void* __restrict__ addend,
-                                                    const float* residual, float* out, void* out_x) {
+                                                    const float* residual, float* out, void* out_x,
+                                                    const void* __restrict__ x_addend) {
   const int64_t t = blockIdx.x / col_blocks;
   const int64_t col = int64_t(blockIdx.x % col_blocks) * CB_COLS + threadIdx.x * 8;
   if (col >= d) return;
@@ -79,7 +82,15 @@ __global__ __launch_bounds__(CB_THR) void k_combine(const void* __restrict__ Y, 
   }
   *reinterpret_cast<float4*>(out + o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   *reinterpret_cast<float4*>(out + o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  if (out_x) store8(out_x, dtype, o, acc);
+  if (out_x && x_addend) {
+    float s[8];
+    load8(x_addend, dtype, o, s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s[q] += acc[q];
+    store8(out_x, dtype, o, s);
+  } else if (out_x) {
+    store8(out_x, dtype, o, acc);
+  }
 }
 
 // bf16 combine with k fixed at compile time: every Y row of the token is requested before the
@@ -95,7 +106,8 @@ __global__ __launch_bounds__(CB_THR) void k_combine_bf16(const uint16_t* __restr
                                                          const int32_t* __restrict__ dest_row, int64_t d,
                                                          int col_blocks, const uint16_t* __restrict__ addend,
                                                          const float* residual, float* out,
-                                                         uint16_t* __restrict__ out_x) {
+                                                         uint16_t* __restrict__ out_x,
+                                                         const uint16_t* __restrict__ x_addend) {
   const int64_t t = blockIdx.x / col_blocks;
   const int64_t col = int64_t(blockIdx.x % col_blocks) * CB_COLS + threadIdx.x * 8;
   if (col >= d) return;
@@ -113,8 +125,9 @@ __global__ __launch_bounds__(CB_THR) void k_combine_bf16(const uint16_t* __restr
     ra = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(residual + o));
     rb = __builtin_nontemporal_load(reinterpret_cast<const cb_f32x4*>(residual + o + 4));
   }
-  cb_u32x4 av = {0u, 0u, 0u, 0u};
+  cb_u32x4 av = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
   if (addend) av = __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(addend + o));
+  if (x_addend) xv = __builtin_nontemporal_load(reinterpret_cast<const cb_u32x4*>(x_addend + o));
   float acc[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
   if (addend) {
     float s[8];
@@ -132,11 +145,20 @@ __global__ __launch_bounds__(CB_THR) void k_combine_bf16(const uint16_t* __restr
   __builtin_nontemporal_store(cb_f32x4{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<cb_f32x4*>(out + o));
   __builtin_nontemporal_store(cb_f32x4{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<cb_f32x4*>(out + o + 4));
   if (out_x) {
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = acc[q];
+    if (x_addend) {
+      float s[8];
+      unpack8(make_uint4(xv[0], xv[1], xv[2], xv[3]), s);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] += s[q];
+    }
     uint4 v;
-    v.x = pack2(acc[0], acc[1]);
-    v.y = pack2(acc[2], acc[3]);
-    v.z = pack2(acc[4], acc[5]);
-    v.w = pack2(acc[6], acc[7]);
+    v.x = pack2(x[0], x[1]);
+    v.y = pack2(x[2], x[3]);
+    v.z = pack2(x[4], x[5]);
+    v.w = pack2(x[6], x[7]);
     *reinterpret_cast<uint4*>(out_x + o) = v;
   }
 }
@@ -167,7 +189,7 @@ __global__ __launch_bounds__(256) void k_make_input(const float* __restrict__ o,
 
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
-                   void* out_x, hipStream_t s) {
+                   void* out_x, hipStream_t s, const void* x_addend) {
   if (T == 0) return MOE_OK;
   const int col_blocks = int(cdiv(d, CB_COLS));
   ProfScope prof(MOE_K_COMBINE, s);
@@ -175,17 +197,18 @@ int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest
     const auto* Yb = static_cast<const uint16_t*>(Y);
     const auto* Ab = static_cast<const uint16_t*>(addend);
     auto* Xb = static_cast<uint16_t*>(out_x);
+    const auto* XAb = static_cast<const uint16_t*>(x_addend);
     const unsigned grid = unsigned(T * col_blocks);
     if (k == 8)
-      k_combine_bf16<8><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+      k_combine_bf16<8><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb, XAb);
     else if (k == 6)
-      k_combine_bf16<6><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+      k_combine_bf16<6><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb, XAb);
     else
-      k_combine_bf16<1><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb);
+      k_combine_bf16<1><<<grid, CB_THR, 0, s>>>(Yb, w, dest_row, d, col_blocks, Ab, residual, out, Xb, XAb);
     return check_launch("combine");
   }
   k_combine<<<unsigned(T * col_blocks), CB_THR, 0, s>>>(Y, dtype, w, dest_row, d, k, col_blocks, addend,
-                                                         residual, out, out_x);
+                                                         residual, out, out_x, x_addend);
   return check_launch("combine");
 }
 

@@ -77,9 +77,10 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
                           void* Y, void* ws, hipStream_t s, const int32_t* gather = nullptr,
                           int32_t gather_k = 1, int64_t x_rows = 0);
+// out_x (optional) = cast(out), or cast(out + x_addend) with x_addend [T, d] dtype
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
-                   void* out_x, hipStream_t s);
+                   void* out_x, hipStream_t s, const void* x_addend = nullptr);
 // MXFP8 (mx.hip): rows of a bf16 matrix -> E4M3 codes + one E8M0 scale per 32 elements
 // backward-pass building blocks (gemm.hip); epi codes of the bf16 product
 enum { PRODUCT_PLAIN = 0, PRODUCT_F32 = 2, PRODUCT_UG = 3 };
