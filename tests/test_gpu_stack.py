@@ -316,3 +316,32 @@ def test_mxfp8_stack_dsv3_full_size(ops, name):
     oL = run_stack(ops, c, layers, o0, "partial", mx_layers=mxl)
     assert torch.isfinite(oL).all().item()
     assert torch.equal(oL, composed(ops, c, layers, o0, "partial", None, mx_layers=mxl))
+
+
+MAX_EK = mi.MoEConfig(14, "max-experts-topk", T=256, d=256, E=1024, k=32, c=128, n_shared=1, c_shared=128,
+                      gate="softmax", renormalize=True, dtype="bf16", layers=3)
+
+
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
+def test_stack_at_the_expert_and_topk_limits(ops, mx):
+    """E = 1024 experts and k = 32 (the library's limits) through a 3-layer partial stack: the
+    general combine kernel (k outside its fixed-k forms) also forms the next layer's input; the
+    stack equals the composed single calls and one stream, bit for bit, bf16 and MXFP8 experts;
+    the bf16 layer 0 against the oracle on 32 sampled tokens."""
+    c = MAX_EK
+    layers, o0 = make_stack(c)
+    mxl = [ops.layer_mx(W) for W in layers] if mx else None
+    a = run_stack(ops, c, layers, o0, "partial", mx_layers=mxl)
+    assert torch.isfinite(a).all().item()
+    assert torch.equal(a, run_stack(ops, c, layers, o0, "partial", two_streams=False, mx_layers=mxl))
+    rows = mi.sample_rows(c.T, 32, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 7))
+    rec = []
+    assert torch.equal(a, composed(ops, c, layers, o0, "partial", None, rows=rows, record=rec, mx_layers=mxl))
+    if not mx:   # layer 0 against the oracle on the sampled tokens (the bf16 bar, near-ties excluded)
+        x, o_prev, o_new, idx, _ = rec[0]
+        res = oracle.moe_layer(x, oracle_weights(layers[0]), c.k, c.gate, c.renormalize, c.n_shared, c.c_shared,
+                               store=oracle.round_to_bf16)
+        keep = oracle.topk_gap(res["logits"], c.k) >= NEAR_TIE
+        assert keep.sum() >= 16
+        np.testing.assert_array_equal(idx[keep], res["topk_idx"][keep])
+        assert_parity((o_new - o_prev)[keep], res["out"][keep], torch.bfloat16, "E=1024 k=32 layer 0")
