@@ -83,6 +83,8 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t* __restrict_
 
 // ---- grouped product -----------------------------------------------------------------------
 enum { MX_PLAIN = 0, MX_SWIGLU = 1 };
+// MX_ROWS_SINGLE reads rows as MX_ROWS_GROUPED does; a single-group call (the shared expert) uses it
+// so that profilers report it apart from the routed products
 enum { MX_ROWS_GROUPED = 0, MX_ROWS_SINGLE = 1, MX_ROWS_GATHER = 2 };
 
 struct MxArgs {
@@ -456,10 +458,14 @@ int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
   if (bm == MX_SMALL_BM && gather)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM && G == 1)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_SINGLE, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
   else if (bm == MX_SMALL_BM)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
   else if (gather)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER><<<grid, 512, 0, s>>>(a);
+  else if (G == 1)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_SINGLE><<<grid, 512, 0, s>>>(a);
   else
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
   return check_launch("mx grouped gemm phase 1");
@@ -477,8 +483,12 @@ int mx_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* offsets, int32_
   a.quad_nb = quad_width(a.n_tiles, a.group_m);
   ProfScope prof(G > 1 ? MOE_K_MX_DOWN : MOE_K_MX_DENSE_DOWN, s);
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
-  if (bm == MX_SMALL_BM)
+  if (bm == MX_SMALL_BM && G == 1)
+    k_gemm_mx<MX_PLAIN, MX_ROWS_SINGLE, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM)
     k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (G == 1)
+    k_gemm_mx<MX_PLAIN, MX_ROWS_SINGLE><<<grid, 512, 0, s>>>(a);
   else
     k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED><<<grid, 512, 0, s>>>(a);
   return check_launch("mx grouped gemm phase 2");
