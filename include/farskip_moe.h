@@ -423,7 +423,8 @@ typedef struct {
   int32_t kind;     /* moe_kernel_kind_t */
   int32_t pad;
   uint64_t stream;  /* the hipStream_t it was launched on, as an opaque id */
-  double start_ms;  /* start event, ms after the first recorded start event of this collection */
+  double start_ms;  /* start event, ms relative to the first recorded launch's start event (negative
+                       for a launch on another stream that started before it) */
   double end_ms;    /* end event, same origin */
 } moe_kernel_interval_t;
 
