@@ -72,11 +72,12 @@ int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, in
 int launch_tile_table(const int32_t* offsets, int G, int BM, int max_tiles, int32_t* tile_start,
                       int32_t* tile_group, hipStream_t s);
 size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype);
-// gather != null: row r of the grouped input is X[gather[r] / gather_k], X having x_rows rows
+// gather != null: row r of the grouped input is X[gather[r] / gather_k], X having x_rows rows.
+// mid != null: recorded on s between the gate/up and the down product.
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
                           void* Y, void* ws, hipStream_t s, const int32_t* gather = nullptr,
-                          int32_t gather_k = 1, int64_t x_rows = 0);
+                          int32_t gather_k = 1, int64_t x_rows = 0, hipEvent_t mid = nullptr);
 // out_x (optional) = cast(out), or cast(out + x_addend) with x_addend [T, d] dtype
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
@@ -108,7 +109,7 @@ int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t
                              const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s,
                              const uint8_t* W3q, const uint8_t* W3s, int64_t N, int64_t d, int64_t c, void* Y,
                              void* ws, hipStream_t s, const int32_t* gather, int32_t gather_k, int64_t x_rows,
-                             int phases, uint8_t* Hq, uint8_t* Hs);
+                             int phases, uint8_t* Hq, uint8_t* Hs, hipEvent_t mid = nullptr);
 // x = cast(o [+ S]) : the FarSkip layer input from the fp32 residual (and the shared output)
 int launch_make_input(const float* o, const void* S, int dtype, int64_t T, int64_t d, void* x,
                       hipStream_t s);

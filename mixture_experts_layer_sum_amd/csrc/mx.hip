@@ -513,10 +513,13 @@ int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t
                              const uint8_t* W1q, const uint8_t* W1s, const uint8_t* W2q, const uint8_t* W2s,
                              const uint8_t* W3q, const uint8_t* W3s, int64_t N, int64_t d, int64_t c, void* Y,
                              void* ws, hipStream_t s, const int32_t* gather, int32_t gather_k, int64_t x_rows,
-                             int phases, uint8_t* Hq, uint8_t* Hs) {
+                             int phases, uint8_t* Hq, uint8_t* Hs, hipEvent_t mid) {
   // phases: 3 = both (H in the workspace), 1 = gate/up into the caller's Hq / Hs, 2 = down from them
   MxWs w = carve_mx(ws, G, N, phases == 3 ? c : 0, nullptr);
-  if (N == 0) return MOE_OK;
+  if (N == 0) {   // nothing to compute; the phase event still marks this point of the stream
+    const hipError_t e = mid ? hipEventRecord(mid, s) : hipSuccess;
+    return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
   if (phases == 3) {
     Hq = w.Hq;
     Hs = w.Hs;
@@ -529,6 +532,10 @@ int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t
     if (int rc = mx_gate_up(Xq, Xs, offsets, G, W1q, W1s, W2q, W2s, N, d, c, Hq, Hs, w, s, gather, gather_k, x_rows,
                             bm))
       return rc;
+  if (mid) {
+    const hipError_t e = hipEventRecord(mid, s);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
   if (phases & 2) return mx_down(Hq, Hs, offsets, G, W3q, W3s, N, c, d, Y, w, s, bm);
   return MOE_OK;
 }
