@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +29,7 @@ METRIC = "routed tokens/s + MFMA util, bf16 MoE layer (DeepSeek-V3 shape), 1 GPU
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 
 
 def log(msg):
@@ -52,6 +54,9 @@ def parse():
                    help="after the steps, time the layer-0 routed experts with MXFP8 operands; 0 = skip")
     p.add_argument("--mxfp8-stack", type=int, default=1,
                    help="with --mxfp8: also time the prefill and decode stacks with MXFP8 expert MLPs")
+    p.add_argument("--configs", type=int, default=1,
+                   help="1 = also time one FarSkip layer of each smaller workload (tiny fp32, DSV2-Lite, "
+                        "Qwen3-30B-A3B, Llama-4-Scout)")
     p.add_argument("--backward", type=int, default=1,
                    help="after the steps, time the backward pass of layer 0 (one MoE sublayer); 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -346,6 +351,9 @@ def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": round(weight_bytes)},
            "kernels": kernel_report(prof, c, steps, {"combine": fused_input_bytes(c)}),
            "overlap": stream_overlap(launches, main_s.cuda_stream),
+           # a batch with fewer than one 256-row tile of rows per expert streams its weights; a
+           # prefill batch is bound by the fp8 products (kernels.mx_gate_up.frac_mfma_peak)
+           "bound": "hbm (weight_stream)" if c.T * c.k < 256 * c.E else "mfma fp8 (kernels.mx_gate_up)",
            "what": "routed and shared experts MXFP8 (E4M3, E8M0 per 32); router and combine bf16 / fp32"}
     del ws, oL
     torch.cuda.empty_cache()
@@ -503,6 +511,73 @@ def decode(layers, steps: int = 10) -> dict:
     out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                        "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": weight_bytes,
                        "what": "expert, shared and router weights read once per layer / step time"}
+    return out
+
+
+SMALL_WORKLOADS = ("tiny-fp32", "dsv2-lite", "qwen3-30b-a3b", "llama4-scout")
+
+
+def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
+    """One FarSkip layer (router, top-k, permutation, routed and shared experts, combine; two
+    streams) of each smaller workload: the median of `reps` calls bracketed by HIP events on the
+    main stream (the call ends on that stream), then `reps` more calls with per-launch events for
+    the kernel report.  Each workload's weights are released before the next one's are drawn."""
+    import torch
+
+    import moe_inputs as mi
+    from mixture_experts_layer_sum_amd import ops
+
+    dev = "cuda:0"
+    out = {}
+    for name in names:
+        c = mi.BY_NAME[name]
+        layers = [mi.layer_weights(c, j, dev) for j in range(c.layers)]
+        o0 = mi.activations(c, dev).float()
+        cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+        ws = ops.workspace(ops.stack_workspace_bytes(cfg), dev)
+        oL = torch.empty_like(o0)
+        main_s, side_s = torch.cuda.current_stream(), torch.cuda.Stream()
+
+        def call():
+            ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=side_s)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(main_s)
+            call()
+            b.record(main_s)
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+        ops.profile_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        ops.profile_enable(False)
+        prof, _ = ops.profile_collect_intervals()
+        assert torch.isfinite(oL).all().item(), f"non-finite output ({name})"
+        kernels = kernel_report(prof, c, reps)
+        peak = PEAK_F32_TFLOPS if c.dtype == "f32" else PEAK_BF16_TFLOPS
+        if c.dtype == "f32":   # fp32 products: fractions against the fp32 MFMA peak
+            for row in kernels.values():
+                if "tflops" in row:
+                    row["frac_mfma_peak"] = round(row["tflops"] / peak, 4)
+        flop = c.layers * c.T * c.flops_per_token()["total"]
+        out[name] = {
+            "shape": {"T": c.T, "d": c.d, "E": c.E, "k": c.k, "c": c.c, "shared": c.shared_width,
+                      "gate": c.gate, "renormalize": c.renormalize, "dtype": c.dtype},
+            "ms_per_layer": round(ms / c.layers, 4), "reps": reps,
+            "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
+            "routed_assignments_per_s": round(c.T * c.k * c.layers / (ms * 1e-3), 1),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / peak, 4),
+            "kernels": kernels,
+        }
+        log(f"{name}: {ms:.3f} ms per layer, {out[name]['tflops']} TFLOP/s")
+        del layers, o0, ws, oL
+        torch.cuda.empty_cache()
     return out
 
 
@@ -699,6 +774,9 @@ def main():
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
+    if args.configs and c.name == "dsv3-stack":
+        log("timing one layer of each smaller workload")
+        result["configs"] = leg("configs", lambda: per_config())
     if args.cpu_sample > 0:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = leg("cpu_baseline", lambda: cpu_baseline(c, layers, o0, args.cpu_sample))
