@@ -215,6 +215,32 @@ def test_stack_dsv3_full_size_sampled(ops, name):
             assert_parity(x_next[keep], rnd(o_prev + res["S"])[keep], torch.bfloat16, f"{name} layer {j} x_next")
 
 
+@pytest.mark.parametrize("name,n_sample", [("tiny-fp32", 64), ("dsv2-lite", 128), ("qwen3-30b-a3b", 128),
+                                           ("llama4-scout", 64)])
+def test_stack_one_layer_each_workload(ops, name, n_sample):
+    """One FarSkip layer of each smaller workload at its full size, launched as bench.py times it
+    (farskip_stack_forward, L = 1, partial, two streams): bitwise equal to the composed single calls,
+    and o_1 - o_0 on seeded tokens against the oracle's layer output (S + R), with exact routing
+    away from top-k near-ties."""
+    c = mi.BY_NAME[name]
+    layers, o0 = make_stack(c)
+    oL = run_stack(ops, c, layers, o0, "partial")
+    assert not torch.isnan(oL).any().item()
+    rows = mi.sample_rows(c.T, n_sample, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 4))
+    rec = []
+    assert torch.equal(oL, composed(ops, c, layers, o0, "partial", None, rows=rows, record=rec))
+    x, o_prev, o_new, idx, x_next = rec[0]
+    assert x_next is None
+    np.testing.assert_array_equal(x, to_np(o0[rows.to(DEV)]))   # x_1 = o_0 (bf16-valued inputs)
+    rnd = oracle.round_to_bf16 if c.dtype == "bf16" else None
+    res = oracle.moe_layer(x, oracle_weights(layers[0]), c.k, c.gate, c.renormalize, c.n_shared, c.c_shared,
+                           store=rnd)
+    keep = oracle.topk_gap(res["logits"], c.k) >= NEAR_TIE
+    assert keep.mean() > 0.9
+    np.testing.assert_array_equal(idx[keep], res["topk_idx"][keep])
+    assert_parity((o_new - o_prev)[keep], res["out"][keep], c.torch_dtype, f"{name} one-layer stack S + R")
+
+
 def test_profile_intervals_of_a_two_stream_stack(ops):
     """The per-launch intervals behind bench.py's overlap figure: one per recorded launch, on both
     streams, consistent with the per-kind totals of the same collection."""
