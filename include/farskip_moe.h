@@ -248,8 +248,9 @@ typedef struct {
  * s_main runs each layer's permutation and routed grouped GEMM (rows gathered through the
  * permutation), and nothing else.  s_side runs each layer's router and shared expert, the
  * previous layer's combine and, with the skip on, the next layer's input; with the skip on at
- * layer j, layer j+1's router and shared expert and layer j-1's combine all run while layer j's
- * routed GEMM does (HIP events order the two streams).
+ * layer j, layer j's shared expert, layer j-1's combine (which also forms x_{j+1}) and layer
+ * j+1's router all run while layer j's routed GEMMs do: they wait until layer j's routed gate/up
+ * product is done and run beside its down product (HIP events order the two streams).
  * s_side == s_main gives the same results with everything serialised on one stream.  Inputs
  * are taken as ordered on s_main: s_side first waits for all work enqueued on s_main before the
  * call, and s_main's last operation waits for the final combine, so the result is ready when

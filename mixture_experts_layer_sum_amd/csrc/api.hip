@@ -274,8 +274,8 @@ int wait(hipStream_t s, hipEvent_t e) {
 //                [skip on at j-1: combine_{j-1}: o_{j-1} = o_{j-2} + S_{j-1} + R_{j-1}, which also
 //                writes x_{j+1} = o_{j-1} (+ S_j when partial) if the skip is on at j];
 //                skip on at j and no such combine (j = 0, or skip off at j-1): x_{j+1} from o_{j-1}
-// With the skip on, x_{j+1} needs neither R_j nor o_j, so layer j+1's router and shared expert
-// and layer j-1's combine (HBM-bound) all run beside layer j's routed GEMMs.  They start once
+// With the skip on, x_{j+1} needs neither R_j nor o_j, so layer j's shared expert, layer j-1's
+// combine (HBM-bound) and layer j+1's router all run beside layer j's routed GEMMs.  They start once
 // layer j's gate/up product is done and run beside its down product: measured on the
 // DeepSeek-V3-shaped stack, 1.1% faster than beside the gate/up product, whose tiles share weight
 // panels and activation rows in each XCD's L2 and lose more to a second kernel on the same CUs.
