@@ -503,6 +503,10 @@ def decode(layers, steps: int = 10) -> dict:
             ops.profile_enable(False)
             out["kernels"] = kernel_report(ops.profile_collect(), c, steps, {"combine": fused_input_bytes(c)})
         out[label] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1)}
+    # the same two-stream step captured once into a HIP graph and replayed
+    gms = graph_replay_ms(lambda sm: ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=sm,
+                                                               s_side=side_s))
+    out["graph_replay"] = {"ms_per_step": round(gms, 3), "tokens_per_s": round(c.T * c.layers / (gms * 1e-3), 1)}
     assert torch.isfinite(oL).all().item(), "non-finite decode output"
     esz = 2
     weight_bytes = c.layers * esz * (3 * c.E * c.c * c.d + 3 * c.shared_width * c.d + c.E * c.d)
@@ -514,6 +518,29 @@ def decode(layers, steps: int = 10) -> dict:
     return out
 
 
+def graph_replay_ms(enqueue, reps: int = 20) -> float:
+    """Capture one call into a HIP graph (enqueue(s_main) puts the call on s_main, the capture
+    stream; its side stream joins the capture through the call's own events) and return the median
+    of `reps` replays between HIP events."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        enqueue(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+    del g
+    return ms
+
+
 SMALL_WORKLOADS = ("tiny-fp32", "dsv2-lite", "qwen3-30b-a3b", "llama4-scout")
 
 
@@ -521,7 +548,8 @@ def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
     """One FarSkip layer (router, top-k, permutation, routed and shared experts, combine; two
     streams) of each smaller workload: the median of `reps` calls bracketed by HIP events on the
     main stream (the call ends on that stream), then `reps` more calls with per-launch events for
-    the kernel report.  Each workload's weights are released before the next one's are drawn."""
+    the kernel report, then `reps` replays of the call captured into a HIP graph.  Each
+    workload's weights are released before the next one's are drawn."""
     import torch
 
     import moe_inputs as mi
@@ -557,6 +585,9 @@ def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
         torch.cuda.synchronize()
         ops.profile_enable(False)
         prof, _ = ops.profile_collect_intervals()
+        # the same call captured once into a HIP graph: what the launches themselves cost
+        gms = graph_replay_ms(lambda sm: ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=sm,
+                                                                   s_side=side_s), reps)
         assert torch.isfinite(oL).all().item(), f"non-finite output ({name})"
         kernels = kernel_report(prof, c, reps)
         peak = PEAK_F32_TFLOPS if c.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -569,13 +600,14 @@ def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
             "shape": {"T": c.T, "d": c.d, "E": c.E, "k": c.k, "c": c.c, "shared": c.shared_width,
                       "gate": c.gate, "renormalize": c.renormalize, "dtype": c.dtype},
             "ms_per_layer": round(ms / c.layers, 4), "reps": reps,
+            "graph_replay_ms_per_layer": round(gms / c.layers, 4),
             "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
             "routed_assignments_per_s": round(c.T * c.k * c.layers / (ms * 1e-3), 1),
             "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / peak, 4),
             "kernels": kernels,
         }
-        log(f"{name}: {ms:.3f} ms per layer, {out[name]['tflops']} TFLOP/s")
+        log(f"{name}: {ms:.3f} ms per layer ({gms:.3f} ms as a graph replay), {out[name]['tflops']} TFLOP/s")
         del layers, o0, ws, oL
         torch.cuda.empty_cache()
     return out

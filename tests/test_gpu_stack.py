@@ -241,6 +241,44 @@ def test_stack_one_layer_each_workload(ops, name, n_sample):
     assert_parity((o_new - o_prev)[keep], res["out"][keep], c.torch_dtype, f"{name} one-layer stack S + R")
 
 
+@pytest.mark.parametrize("c", [TINY_STACK, MID_STACK], ids=lambda c: c.name)
+def test_stack_graph_replay(ops, c):
+    """The two-stream stack captured into one HIP graph (the side stream joins the capture through
+    the call's first event wait and rejoins the main stream at its end) and replayed three times,
+    with eager calls and new input values in place between the replays: every replay equals the
+    eager call on the same input, bitwise."""
+    layers, o0 = make_stack(c)
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
+    o_in = o0.clone()
+    o_graph = torch.full_like(o0, float("nan"))
+    side = torch.cuda.Stream()
+
+    def call(out):
+        ops.farskip_stack_forward(layers, cfg, "partial", o_in, out, ws, s_main=torch.cuda.current_stream(),
+                                  s_side=side)
+
+    call(o_graph)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        call(o_graph)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(7)
+    for r in range(3):
+        # new input values (the workload dtype's grid), then the eager reference on a fresh buffer
+        o_in.copy_((o0.cpu() * (1.0 + 0.25 * r) + torch.randn(o0.shape, generator=gen) * 0.01)
+                   .to(c.torch_dtype).float())
+        ref = torch.full_like(o0, float("nan"))
+        call(ref)
+        torch.cuda.synchronize()
+        o_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert not torch.isnan(ref).any().item()
+        assert torch.equal(o_graph, ref), f"replay {r}"
+
+
 def test_profile_intervals_of_a_two_stream_stack(ops):
     """The per-launch intervals behind bench.py's overlap figure: one per recorded launch, on both
     streams, consistent with the per-kind totals of the same collection."""
