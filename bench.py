@@ -309,7 +309,7 @@ def mxfp8(c, layers, o0, reps: int = 3) -> dict:
     return out
 
 
-def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
+def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5, graph: bool = False) -> dict:
     """The same 4-layer FarSkip stack with the expert MLPs on MXFP8 operands
     (farskip_stack_forward_mxfp8) for workload c: the experts' weights quantised once beforehand (as
     at load time, untimed: mxl), then one warm-up and `steps` timed steps on the same two streams;
@@ -341,6 +341,10 @@ def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
     t1 = time.perf_counter()
     ops.profile_enable(False)
     prof, launches = ops.profile_collect_intervals()
+    gms = None
+    if graph:   # the same two-stream step captured once into a HIP graph and replayed
+        gms = graph_replay_ms(lambda sm: ops.farskip_stack_forward_mxfp8(layers, mxl, cfg, "partial", o0, oL, ws,
+                                                                         s_main=sm, s_side=side_s))
     assert torch.isfinite(oL).all().item(), "non-finite MXFP8 stack output"
     ms = (t1 - t0) * 1e3 / steps
     weight_bytes = c.layers * ((3 * c.E * c.c * c.d + 3 * c.shared_width * c.d) * (1 + 1 / 32) + 2 * c.E * c.d)
@@ -351,6 +355,8 @@ def mxfp8_stack(c, layers, mxl, o0=None, steps: int = 5) -> dict:
                              "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": round(weight_bytes)},
            "kernels": kernel_report(prof, c, steps, {"combine": fused_input_bytes(c)}),
            "overlap": stream_overlap(launches, main_s.cuda_stream),
+           "graph_replay": None if gms is None else {
+               "ms_per_step": round(gms, 3), "tokens_per_s": round(c.T * c.layers / (gms * 1e-3), 1)},
            # a batch with fewer than one 256-row tile of rows per expert streams its weights; a
            # prefill batch is bound by the fp8 products (kernels.mx_gate_up.frac_mfma_peak)
            "bound": "hbm (weight_stream)" if c.T * c.k < 256 * c.E else "mfma fp8 (kernels.mx_gate_up)",
@@ -800,7 +806,7 @@ def main():
             result["mxfp8"]["stack"] = leg("mxfp8 stack", lambda: mxfp8_stack(c, layers, mxl, o0))
             log("timing the decode-shaped stack with MXFP8 expert MLPs")
             result["mxfp8"]["decode_stack"] = leg(
-                "mxfp8 decode stack", lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10))
+                "mxfp8 decode stack", lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10, graph=True))
         del mxl
         torch.cuda.empty_cache()
     if args.standalone:

@@ -241,22 +241,28 @@ def test_stack_one_layer_each_workload(ops, name, n_sample):
     assert_parity((o_new - o_prev)[keep], res["out"][keep], c.torch_dtype, f"{name} one-layer stack S + R")
 
 
-@pytest.mark.parametrize("c", [TINY_STACK, MID_STACK], ids=lambda c: c.name)
-def test_stack_graph_replay(ops, c):
-    """The two-stream stack captured into one HIP graph (the side stream joins the capture through
-    the call's first event wait and rejoins the main stream at its end) and replayed three times,
-    with eager calls and new input values in place between the replays: every replay equals the
-    eager call on the same input, bitwise."""
+@pytest.mark.parametrize("c,mx", [(TINY_STACK, False), (MID_STACK, False), (MID_STACK, True)],
+                         ids=["tiny-fp32-stack", "mid-bf16-stack", "mid-mxfp8-stack"])
+def test_stack_graph_replay(ops, c, mx):
+    """The two-stream stack (bf16 / fp32, or with MXFP8 expert MLPs) captured into one HIP graph (the
+    side stream joins the capture through the call's first event wait and rejoins the main stream
+    at its end) and replayed three times, with eager calls and new input values in place between
+    the replays: every replay equals the eager call on the same input, bitwise."""
     layers, o0 = make_stack(c)
     cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
-    ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
+    mxl = [ops.layer_mx(W) for W in layers] if mx else None
+    nbytes = ops.stack_mxfp8_workspace_bytes(cfg) if mx else ops.stack_workspace_bytes(cfg)
+    ws = ops.workspace(nbytes, DEV)
     o_in = o0.clone()
     o_graph = torch.full_like(o0, float("nan"))
     side = torch.cuda.Stream()
 
     def call(out):
-        ops.farskip_stack_forward(layers, cfg, "partial", o_in, out, ws, s_main=torch.cuda.current_stream(),
-                                  s_side=side)
+        sm = torch.cuda.current_stream()
+        if mx:
+            ops.farskip_stack_forward_mxfp8(layers, mxl, cfg, "partial", o_in, out, ws, s_main=sm, s_side=side)
+        else:
+            ops.farskip_stack_forward(layers, cfg, "partial", o_in, out, ws, s_main=sm, s_side=side)
 
     call(o_graph)   # warm-up outside the capture
     torch.cuda.synchronize()
