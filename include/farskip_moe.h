@@ -254,7 +254,10 @@ typedef struct {
  * s_side == s_main gives the same results with everything serialised on one stream.  Inputs
  * are taken as ordered on s_main: s_side first waits for all work enqueued on s_main before the
  * call, and s_main's last operation waits for the final combine, so the result is ready when
- * s_main is.
+ * s_main is.  The call allocates no device memory, does not synchronise with the host and issues
+ * no memset, so it may be captured into a HIP graph on s_main (s_side then joins the capture
+ * through the call's first event wait); each replay recomputes o_L from the current contents of
+ * o0, the weights and the workspace pointers given at capture.
  *
  *   layers    host array [L] of device-pointer descriptors
  *   cfg       host pointer
@@ -292,7 +295,7 @@ typedef struct {
  * and s_side's shared expert is moe_grouped_swiglu_mxfp8 over all T rows as one group (outputs in
  * bf16).  The router, top-k, combine and the residual bookkeeping are those of
  * farskip_stack_forward, in bf16 / fp32.  The result equals the same single calls composed on one
- * stream, bit for bit.
+ * stream, bit for bit.  Streams, events and graph capture as for farskip_stack_forward.
  *   layers  as farskip_stack_forward, except that W1-W3 and Ws1-Ws3 are not read (may be NULL)
  *   mx      host array [L]: the experts' MXFP8 codes and scales
  *   ws      scratch of at least farskip_stack_mxfp8_workspace_bytes(cfg) bytes
