@@ -62,3 +62,14 @@ def test_small_workloads_are_single_layers_of_known_shape():
     assert mi.BY_NAME["dsv2-lite"].flops_per_token()["total"] == 262144 + 103809024 + 34603008
     assert mi.BY_NAME["llama4-scout"].flops_per_token()["total"] == 163840 + 251658240 + 251658240
     assert not math.isnan(bench.PEAK_F32_TFLOPS)
+
+
+def test_stream_overlap_from_launch_intervals():
+    # main stream 1: [0, 10) and [12, 20); side stream 2: [5, 14) and [30, 31)
+    launches = [("gemm_gate_up", 1, 0.0, 10.0), ("router_gemm", 2, 5.0, 14.0), ("gemm_down", 1, 12.0, 20.0),
+                ("combine", 2, 30.0, 31.0)]
+    ov = bench.stream_overlap(launches, 1)
+    # |M| = 18, |S| = 10, |M n S| = [5, 10) + [12, 14) = 7
+    assert ov["main_busy_ms"] == 18.0 and ov["side_busy_ms"] == 10.0 and ov["both_busy_ms"] == 7.0
+    assert ov["side_hidden_frac"] == 0.7 and ov["main_covered_frac"] == round(7 / 18, 4)
+    assert ov["launches"] == 4
