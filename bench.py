@@ -43,9 +43,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="dsv3-stack")
     p.add_argument("--mode", default="partial", choices=["none", "partial", "outdated"])
-    p.add_argument("--single-stream-steps", type=int, default=3,
-                   help="extra steps with both streams merged into one (overlap reference); 0 = skip")
-    p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--cpu-sample", type=int, default=1024, help="tokens in the CPU-oracle sample; 0 = skip")
+    p.add_argument("--cpu-configs", type=int, default=1,
+                   help="with --configs: also time the CPU oracle on one layer of each smaller workload at full T")
+    p.add_argument("--compare-steps", type=int, default=3,
+                   help="interleaved two-stream / one-stream steps, profiling off for both; 0 = skip")
     p.add_argument("--decode", type=int, default=1,
                    help="after the steps, time a 1024-token decode step through the same layers; 0 = skip")
     p.add_argument("--standalone", type=int, default=1,
@@ -150,6 +152,22 @@ def kernel_report(prof: dict, c, steps: int, extra_bytes: dict = None) -> dict:
                 row["frac_hbm_peak"] = round(row["gbs"] / PEAK_HBM_GBS, 4)
         out[kind] = row
     return out
+
+
+def route_report(kernels: dict, c) -> dict:
+    """The route step per layer (router logits + top-k gating): its time, and its algorithmic bytes
+    (read the layer input and W_R once, write the logits the call returns, write the top-k ids and
+    weights) and FLOP over that time, against the HBM and bf16 MFMA peaks."""
+    if "router_gemm" not in kernels or "topk" not in kernels:
+        return None
+    ms = (kernels["router_gemm"]["ms_per_step"] + kernels["topk"]["ms_per_step"]) / c.layers
+    nbytes = c.T * c.d * 2.0 + c.E * c.d * 2.0 + c.T * c.E * 4.0 + c.T * c.k * 8.0
+    flop = 2.0 * c.T * c.d * c.E
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms_per_layer": round(ms, 4), "bytes_per_layer": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(tf, 1),
+            "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def ep_share(c, W, A_perm, off, Y, gws, reps: int, ep: int = 8) -> dict:
@@ -476,6 +494,21 @@ def stack_backward(c, layers, o0, L: int = 2, reps: int = 1) -> dict:
             "what": "forward replay (keeping inputs, routing, expert outputs) + backward of every layer"}
 
 
+def interleaved(fns: dict, n: int) -> dict:
+    """Median wall time (ms) of each callable in fns, alternated call by call n times (the device is
+    synchronised before and after every call), so that both see the same clocks and temperature."""
+    import torch
+    times = {k: [] for k in fns}
+    for _ in range(n):
+        for k, fn in fns.items():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            times[k].append((time.perf_counter() - t0) * 1e3)
+    return {k: statistics.median(v) for k, v in times.items()}
+
+
 def decode(layers, steps: int = 10) -> dict:
     """One decode step of a 1024-sequence batch through the same 4 layers and weights (the
     dsv3-decode workload): the FarSkip stack with T = 1024.  About 32 rows per expert, so a layer
@@ -493,22 +526,26 @@ def decode(layers, steps: int = 10) -> dict:
     ws = ops.workspace(ops.stack_workspace_bytes(cfg), dev)
     main_s, side_s = torch.cuda.current_stream(), torch.cuda.Stream()
     out = {"workload": c.name, "tokens": c.T, "layers": c.layers}
-    for label, ss in (("two_streams", side_s), ("one_stream", main_s)):
-        for _ in range(2):
-            ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=ss)
-        torch.cuda.synchronize()
-        if label == "two_streams":
-            ops.profile_collect()
-            ops.profile_enable(True)
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=ss)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        if label == "two_streams":
-            ops.profile_enable(False)
-            out["kernels"] = kernel_report(ops.profile_collect(), c, steps, {"combine": fused_input_bytes(c)})
+
+    def step(ss):
+        ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=main_s, s_side=ss)
+
+    for ss in (side_s, main_s, side_s):
+        step(ss)
+    # step times with profiling off, two streams and one stream alternated step by step
+    med = interleaved({"two_streams": lambda: step(side_s), "one_stream": lambda: step(main_s)}, steps)
+    for label, ms in med.items():
         out[label] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1)}
+    out["two_stream_speedup"] = round(med["one_stream"] / med["two_streams"], 4)
+    # per-kernel times from a separate pass with HIP events around every launch
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    for _ in range(steps):
+        step(side_s)
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    out["kernels"] = kernel_report(ops.profile_collect(), c, steps, {"combine": fused_input_bytes(c)})
     # the same two-stream step captured once into a HIP graph and replayed
     gms = graph_replay_ms(lambda sm: ops.farskip_stack_forward(layers, cfg, "partial", o0, oL, ws, s_main=sm,
                                                                s_side=side_s))
@@ -550,7 +587,7 @@ def graph_replay_ms(enqueue, reps: int = 20) -> float:
 SMALL_WORKLOADS = ("tiny-fp32", "dsv2-lite", "qwen3-30b-a3b", "llama4-scout")
 
 
-def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
+def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3, cpu: bool = True) -> dict:
     """One FarSkip layer (router, top-k, permutation, routed and shared experts, combine; two
     streams) of each smaller workload: the median of `reps` calls bracketed by HIP events on the
     main stream (the call ends on that stream), then `reps` more calls with per-launch events for
@@ -614,60 +651,121 @@ def per_config(names=SMALL_WORKLOADS, reps: int = 20, warmup: int = 3) -> dict:
             "kernels": kernels,
         }
         log(f"{name}: {ms:.3f} ms per layer ({gms:.3f} ms as a graph replay), {out[name]['tflops']} TFLOP/s")
+        if cpu:   # the CPU oracle on the same layer at full T
+            try:
+                out[name]["cpu_baseline"] = cpu_baseline_full(c, layers, o0)
+                log(f"{name}: CPU oracle {out[name]['cpu_baseline']['oracle_s']} s per layer")
+            except Exception as e:  # noqa: BLE001
+                out[name]["cpu_baseline"] = {"error": f"{type(e).__name__}: {e}"}
         del layers, o0, ws, oL
         torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(c, layers, o0, n_tokens: int) -> dict:
-    """The CPU oracle as it stands, on n_tokens seeded tokens through all layers of the stack.
-    Expert weights are copied from the device on demand; the copy time is measured and excluded."""
-    import numpy as np
+def host_cpu() -> dict:
+    """The host's CPU model and the threads the oracle's BLAS uses."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cores": threads or len(os.sched_getaffinity(0)), "cpu_model": model,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+class _TimedSlices:
+    """W[e] -> expert e's weights as float64, copied from the device when first asked for (bf16
+    moved as is, widened on the host) and kept while `keep`; the copy time is accumulated in
+    self.clock[0] so that it can be excluded from the oracle's time."""
+
+    def __init__(self, t, clock, keep: bool):
+        self.t, self.clock, self.cache = t, clock, ({} if keep else None)
+
+    def __getitem__(self, e):
+        import torch
+        e = int(e)
+        if self.cache is not None and e in self.cache:
+            return self.cache[e]
+        t0 = time.perf_counter()
+        host = self.t[e].detach().cpu().to(torch.float64).numpy()
+        self.clock[0] += time.perf_counter() - t0
+        if self.cache is not None:
+            self.cache[e] = host
+        return host
+
+
+def _oracle_weights(W, clock, keep: bool):
     import torch
-
-    import moe_inputs as mi
-    import oracle
-
-    fetch = [0.0]
-
-    class Slices:
-        def __init__(self, t):
-            self.t = t
-
-        def __getitem__(self, e):
-            t0 = time.perf_counter()
-            host = self.t[int(e)].float().cpu().numpy()
-            fetch[0] += time.perf_counter() - t0
-            return host
 
     def small(t):
         if t is None:
             return None
         t0 = time.perf_counter()
-        a = t.float().cpu().numpy()
-        fetch[0] += time.perf_counter() - t0
+        a = t.detach().cpu().to(torch.float64).numpy()
+        clock[0] += time.perf_counter() - t0
         return a
+    return {"W_R": small(W["W_R"]), "bias": small(W.get("bias")), "W1": _TimedSlices(W["W1"], clock, keep),
+            "W2": _TimedSlices(W["W2"], clock, keep), "W3": _TimedSlices(W["W3"], clock, keep),
+            "Ws1": small(W.get("Ws1")), "Ws2": small(W.get("Ws2")), "Ws3": small(W.get("Ws3"))}
 
-    Wo = [{"W_R": small(W["W_R"]), "bias": small(W["bias"]), "W1": Slices(W["W1"]), "W2": Slices(W["W2"]),
-           "W3": Slices(W["W3"]), "Ws1": small(W["Ws1"]), "Ws2": small(W["Ws2"]), "Ws3": small(W["Ws3"])}
-          for W in layers]
+
+def cpu_baseline(c, layers, o0, n_tokens: int) -> dict:
+    """The CPU oracle as it stands, on n_tokens seeded tokens through all layers of the stack.
+    Each expert's weights are copied from the device once per layer (when the oracle first asks
+    for them) and not kept; the copy time is measured and excluded."""
+    import moe_inputs as mi
+    import oracle
+
+    fetch = [0.0]
+    Wo = [_oracle_weights(W, fetch, keep=False) for W in layers]
     rows = mi.sample_rows(c.T, n_tokens, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 7))
     x0 = o0[rows.to(o0.device)].cpu().numpy()
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
-    except Exception:
-        pass
     t0 = time.perf_counter()
     oracle.moe_stack(x0, Wo, c.k, c.gate, c.renormalize, "partial", None, c.n_shared, c.c_shared)
     wall = time.perf_counter() - t0
     compute = max(wall - fetch[0], 1e-9)
-    return {"value": round(n_tokens * c.layers / compute, 3), "unit": "tokens/s", "cores":
-            threads or len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{n_tokens} seeded tokens of the {c.name} workload through all {c.layers} layers "
-                      f"(float64 NumPy oracle; {compute:.1f} s compute, {fetch[0]:.1f} s of device-to-host "
-                      f"weight copies excluded)"}
+    host = host_cpu()
+    return {"value": round(n_tokens * c.layers / compute, 3), "unit": "tokens/s", "cores": host["cores"],
+            "kind": "oracle", "cpu_model": host["cpu_model"], "oracle_s": round(compute, 2),
+            "weight_copy_s": round(fetch[0], 2),
+            "sample": f"{n_tokens} seeded tokens of the {c.name} workload through all {c.layers} layers, "
+                      f"every expert's weights copied once per layer (float64 NumPy oracle; {compute:.1f} s of "
+                      f"oracle work; {fetch[0]:.1f} s of device-to-host weight copies excluded)"}
+
+
+def cpu_baseline_full(c, layers, o0, long_run_s: float = 10.0) -> dict:
+    """The CPU oracle on one layer of workload c at its full T: the median of 3 runs (1 run when the
+    first takes longer than long_run_s).  Weights are copied to the host once, before the timing."""
+    import statistics as st
+
+    import oracle
+    fetch = [0.0]
+    Wo = _oracle_weights(layers[0], fetch, keep=True)
+    for e in range(c.E):      # copy and widen every expert before the clock starts
+        Wo["W1"][e], Wo["W2"][e], Wo["W3"][e]
+    x = o0.cpu().numpy()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, Wo, c.k, c.gate, c.renormalize, c.n_shared, c.c_shared)
+        times.append(time.perf_counter() - t0)
+        if times[0] > long_run_s:
+            break
+    med = st.median(times)
+    host = host_cpu()
+    return {"value": round(c.T / med, 1), "unit": "tokens/s", "cores": host["cores"], "kind": "oracle",
+            "cpu_model": host["cpu_model"], "runs": len(times), "oracle_s": round(med, 3),
+            "sample": f"one layer of {c.name} at its full T = {c.T} (float64 NumPy oracle; median of "
+                      f"{len(times)} run(s); weight copies excluded)"}
 
 
 def main():
@@ -731,15 +829,18 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step")
     assert torch.isfinite(oL).all().item(), "non-finite stack output"
 
-    single_ms = None
-    if args.single_stream_steps > 0:
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.single_stream_steps):
-            step(main_s)
-        torch.cuda.synchronize()
-        single_ms = (time.perf_counter() - t1) * 1e3 / args.single_stream_steps
-        log(f"one-stream reference: {single_ms:.2f} ms/step")
+    compare = None
+    if args.compare_steps > 0:
+        # the two schedules with profiling off for both, alternated step by step
+        med = interleaved({"two_streams": lambda: step(side_s), "one_stream": lambda: step(main_s)},
+                          args.compare_steps)
+        compare = {"steps_each": args.compare_steps, "two_streams_ms": round(med["two_streams"], 3),
+                   "one_stream_ms": round(med["one_stream"], 3),
+                   "two_stream_speedup": round(med["one_stream"] / med["two_streams"], 4),
+                   "timing_events_cost_frac": round(ms_per_step / med["two_streams"] - 1.0, 4),
+                   "what": "median step times, profiling off, two-stream and one-stream steps alternated; "
+                           "timing_events_cost_frac compares the timed (event-bracketed) steps with them"}
+        log(f"interleaved: two streams {med['two_streams']:.2f} ms, one stream {med['one_stream']:.2f} ms")
 
     kernels = kernel_report(prof, c, args.steps, {"combine": fused_input_bytes(c, args.mode)})
     g = kernels.get("gemm_gate_up", {})
@@ -757,6 +858,7 @@ def main():
         # rows are gathered from x (read once: T*d), W1/W2 read once, H written once
         roofline["algorithmic_bytes_per_launch"] = 2 * (c.T * c.d + 2 * c.E * c.c * c.d + c.T * c.k * c.c)
 
+    route = route_report(kernels, c)
     total_flop = c.layers * c.T * c.flops_per_token()["total"]
     value = c.T * c.layers / (ms_per_step * 1e-3)
     result = {
@@ -770,9 +872,11 @@ def main():
         "routed_assignments_per_s": round(c.T * c.k * c.layers / (ms_per_step * 1e-3), 1),
         "stack_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "stack_frac_mfma_peak": round(total_flop / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "one_stream_ms_per_step": None if single_ms is None else round(single_ms, 3),
-        "two_stream_speedup": None if single_ms is None else round(single_ms / ms_per_step, 4),
+        "one_stream_ms_per_step": None if compare is None else compare["one_stream_ms"],
+        "two_stream_speedup": None if compare is None else compare["two_stream_speedup"],
+        "stream_comparison": compare,
         "roofline": roofline,
+        "route": route,
         "kernels": kernels,
         "overlap": stream_overlap(launches, main_s.cuda_stream),
     }
@@ -814,7 +918,7 @@ def main():
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
     if args.configs and c.name == "dsv3-stack":
         log("timing one layer of each smaller workload")
-        result["configs"] = leg("configs", lambda: per_config())
+        result["configs"] = leg("configs", lambda: per_config(cpu=bool(args.cpu_configs and args.cpu_sample)))
     if args.cpu_sample > 0:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = leg("cpu_baseline", lambda: cpu_baseline(c, layers, o0, args.cpu_sample))

@@ -65,6 +65,8 @@ typedef enum { FARSKIP_NONE = 0, FARSKIP_PARTIAL = 1, FARSKIP_OUTDATED = 2 } far
  *                             d and bias are then ignored).
  *   topk_idx [T, k] int32     OUTPUT: per token the k experts with the largest logits, in
  *                             descending logit order; equal logits go to the lower expert index.
+ *                             A NaN logit ranks below every number (it is taken as -infinity), so
+ *                             every id is in [0, E) whatever the logits hold.
  *   topk_w  [T, k] float32    OUTPUT gate weights: gate = MOE_GATE_SOFTMAX -> softmax over all E
  *                             logits, evaluated at the selected experts; MOE_GATE_SIGMOID ->
  *                             1/(1+exp(-logit)).  renormalize != 0 divides by their sum over k.
@@ -238,6 +240,23 @@ typedef struct {
 } moe_stack_cfg_t;
 
 /*
+ * Timing of one stack call, measured on the device with events around each of its kernels (the
+ * analogue of the share of communication hidden behind computation that section 4 of the page
+ * reports: here the second queue's kernel time that runs while the first queue's does).  Times are
+ * milliseconds; M is the union of s_main's kernel intervals and S that of s_side's.
+ */
+typedef struct {
+  double wall_ms;          /* first kernel start to last kernel end, both streams */
+  double main_busy_ms;     /* |M| */
+  double side_busy_ms;     /* |S| */
+  double overlap_ms;       /* |M intersect S| */
+  double overlap_of_side;  /* |M intersect S| / |S| (0 when S is empty) */
+  double overlap_of_main;  /* |M intersect S| / |M| (0 when M is empty) */
+  int32_t launches_main;   /* kernels on s_main */
+  int32_t launches_side;   /* kernels on s_side (0 when s_side == s_main) */
+} moe_stack_stats_t;
+
+/*
  * farskip_stack_forward -- L MoE sublayers f_j = S_j + R_j (shared + routed) on the residual
  * stream, wired as section 3 of the page describes:
  *     o_j = o_{j-1} + S_j(x_j) + R_j(x_j),  x_1 = o_0, and
@@ -264,10 +283,15 @@ typedef struct {
  *   skip_mask host array [L] of 0/1, or NULL = skip on for every layer
  *   o0        [T, d] float32 input o_0;  oL [T, d] float32 OUTPUT o_L (must not alias o0)
  *   ws        scratch of at least farskip_stack_workspace_bytes(cfg) bytes
+ *   stats     host pointer or NULL.  NULL: the call is asynchronous, as described above.  Non-NULL:
+ *             every kernel of this call is bracketed by timing events on its own stream, the call
+ *             waits until s_main (and so the whole stack) has finished, and fills *stats (see
+ *             moe_stack_stats_t).  Those launches are not seen by moe_profile_collect.  A non-NULL
+ *             stats while s_main is being captured into a graph returns MOE_ERR_INVALID_ARG.
  */
 int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg,
                           int mode, const uint8_t* skip_mask, const float* o0, float* oL, void* ws,
-                          size_t ws_bytes, void* s_main, void* s_side);
+                          size_t ws_bytes, void* s_main, void* s_side, moe_stack_stats_t* stats);
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
 
 /* MXFP8 codes and scales of one layer's expert weights, as moe_mx_quantize writes them. */
@@ -299,12 +323,13 @@ typedef struct {
  *   layers  as farskip_stack_forward, except that W1-W3 and Ws1-Ws3 are not read (may be NULL)
  *   mx      host array [L]: the experts' MXFP8 codes and scales
  *   ws      scratch of at least farskip_stack_mxfp8_workspace_bytes(cfg) bytes
- * Requires cfg->dtype == MOE_BF16, d, c and c_shared multiples of 128.  Errors and stream contract
- * as farskip_stack_forward.
+ * Requires cfg->dtype == MOE_BF16, d, c and c_shared multiples of 128.  Errors, stream contract and
+ * stats as farskip_stack_forward.
  */
 int farskip_stack_forward_mxfp8(const moe_layer_desc_t* layers, const moe_layer_mx_t* mx, int32_t L,
                                 const moe_stack_cfg_t* cfg, int mode, const uint8_t* skip_mask, const float* o0,
-                                float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side);
+                                float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side,
+                                moe_stack_stats_t* stats);
 size_t farskip_stack_mxfp8_workspace_bytes(const moe_stack_cfg_t* cfg);
 
 /*
@@ -377,6 +402,39 @@ int farskip_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_
                            const uint8_t* skip_mask, const float* o0, const float* dOL, float* dO0,
                            const moe_layer_grads_t* grads, void* ws, size_t ws_bytes, void* stream);
 size_t farskip_stack_backward_workspace_bytes(const moe_stack_cfg_t* cfg, int32_t L);
+
+/*
+ * moe_workspace_bytes -- the scratch size of any entry point, as one call: a dispatch over the
+ * per-call queries above.  The sizes are those of one MoE layer (section 2.1: T tokens of width d,
+ * E routed experts of hidden width c, k experts per token, shared experts of total hidden width
+ * c_shared) and of an L-layer stack:
+ *   MOE_OP_PERMUTE                moe_permute for T tokens, E experts, k slots
+ *   MOE_OP_GROUPED_SWIGLU         moe_grouped_swiglu(_gathered) over the layer's routed rows:
+ *                                 N = T * k rows in G = E groups of hidden width c, dtype
+ *                                 (the shared expert: E = 1, k = 1, c = c_shared)
+ *   MOE_OP_GROUPED_SWIGLU_MXFP8   moe_grouped_swiglu_mxfp8, same N, G, c
+ *   MOE_OP_MXFP8_PHASE            moe_grouped_mxfp8_gate_up / _down, same N, G
+ *   MOE_OP_STACK                  farskip_stack_forward (L is not needed: buffers are reused)
+ *   MOE_OP_STACK_MXFP8            farskip_stack_forward_mxfp8
+ *   MOE_OP_LAYER_BACKWARD         moe_layer_backward
+ *   MOE_OP_STACK_BACKWARD         farskip_stack_backward with L layers
+ * The first seven arguments follow the order (op, T, d, E, k, c, L); c_shared and dtype (a
+ * moe_dtype_t) complete the layer description.  The gate does not change any size.  Returns 0 for
+ * an unknown op or sizes the op rejects (as the per-call queries do).
+ */
+typedef enum {
+  MOE_OP_PERMUTE = 0,
+  MOE_OP_GROUPED_SWIGLU = 1,
+  MOE_OP_GROUPED_SWIGLU_MXFP8 = 2,
+  MOE_OP_MXFP8_PHASE = 3,
+  MOE_OP_STACK = 4,
+  MOE_OP_STACK_MXFP8 = 5,
+  MOE_OP_LAYER_BACKWARD = 6,
+  MOE_OP_STACK_BACKWARD = 7
+} moe_op_t;
+
+size_t moe_workspace_bytes(int op, int64_t T, int64_t d, int32_t E, int32_t k, int64_t c, int32_t L,
+                           int64_t c_shared, int dtype);
 
 /*
  * Kernel timing for measurement harnesses.  While enabled (process-wide), every kernel the

@@ -22,8 +22,11 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_group
            "moe_layer_backward_workspace_bytes", "farskip_stack_backward", "farskip_stack_backward_workspace_bytes",
            "moe_combine", "farskip_stack_forward", "farskip_stack_forward_mxfp8", "farskip_stack_mxfp8_workspace_bytes",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect",
-           "moe_profile_collect_intervals", "moe_last_error",
+           "moe_profile_collect_intervals", "moe_workspace_bytes", "moe_last_error",
            "moe_version")
+# moe_op_t: the operations moe_workspace_bytes knows
+MOE_OPS = {"permute": 0, "grouped_swiglu": 1, "grouped_swiglu_mxfp8": 2, "mxfp8_phase": 3, "stack": 4,
+           "stack_mxfp8": 5, "layer_backward": 6, "stack_backward": 7}
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
                 "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
                 "mx_down", "bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise",
@@ -58,6 +61,13 @@ class KernelTime(ctypes.Structure):
 class KernelInterval(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("pad", ctypes.c_int32), ("stream", ctypes.c_uint64),
                 ("start_ms", ctypes.c_double), ("end_ms", ctypes.c_double)]
+
+
+class StackStats(ctypes.Structure):
+    _fields_ = [("wall_ms", ctypes.c_double), ("main_busy_ms", ctypes.c_double), ("side_busy_ms", ctypes.c_double),
+                ("overlap_ms", ctypes.c_double), ("overlap_of_side", ctypes.c_double),
+                ("overlap_of_main", ctypes.c_double), ("launches_main", ctypes.c_int32),
+                ("launches_side", ctypes.c_int32)]
 
 
 class FarSkipMoEError(RuntimeError):
@@ -108,11 +118,12 @@ def _declare(lib):
     lib.moe_combine.argtypes = [vp, i, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.moe_combine.restype = i
     lib.farskip_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(StackCfg), i,
-                                          ctypes.POINTER(ctypes.c_uint8), vp, vp, vp, sz, vp, vp]
+                                          ctypes.POINTER(ctypes.c_uint8), vp, vp, vp, sz, vp, vp,
+                                          ctypes.POINTER(StackStats)]
     lib.farskip_stack_forward.restype = i
     lib.farskip_stack_forward_mxfp8.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerMx), i32,
                                                 ctypes.POINTER(StackCfg), i, ctypes.POINTER(ctypes.c_uint8), vp, vp,
-                                                vp, sz, vp, vp]
+                                                vp, sz, vp, vp, ctypes.POINTER(StackStats)]
     lib.farskip_stack_forward_mxfp8.restype = i
     lib.farskip_stack_mxfp8_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg)]
     lib.farskip_stack_mxfp8_workspace_bytes.restype = sz
@@ -125,6 +136,8 @@ def _declare(lib):
     lib.moe_profile_collect_intervals.argtypes = [ctypes.POINTER(KernelTime), ctypes.POINTER(KernelInterval), i32,
                                                   ctypes.POINTER(i32)]
     lib.moe_profile_collect_intervals.restype = i
+    lib.moe_workspace_bytes.argtypes = [i, i64, i64, i32, i32, i64, i32, i64, i]
+    lib.moe_workspace_bytes.restype = sz
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []

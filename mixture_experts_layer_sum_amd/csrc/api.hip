@@ -393,6 +393,21 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
   return MOE_OK;
 }
 
+// the stack with an optional moe_stack_stats_t: the call's own launches are timed and, once they have
+// finished, summarised per stream
+int stack_forward_stats(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t& c, int mode,
+                        const uint8_t* mask, const float* o0, float* oL, void* ws, hipStream_t sm, hipStream_t ss,
+                        const moe_layer_mx_t* mx, moe_stack_stats_t* stats, const char* who) {
+  if (stats) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(sm, &st) == hipSuccess && st != hipStreamCaptureStatusNone)
+      return fail(MOE_ERR_INVALID_ARG, "%s: stats cannot be measured while s_main is being captured", who);
+  }
+  StatsScope scope(stats, sm);
+  if (int rc = stack_forward(layers, L, c, mode, mask, o0, oL, ws, sm, ss, mx)) return rc;
+  return scope.finish();
+}
+
 }  // namespace
 }  // namespace fsm
 
@@ -576,7 +591,8 @@ size_t farskip_stack_mxfp8_workspace_bytes(const moe_stack_cfg_t* cfg) {
 
 int farskip_stack_forward_mxfp8(const moe_layer_desc_t* layers, const moe_layer_mx_t* mx, int32_t L,
                                 const moe_stack_cfg_t* cfg, int mode, const uint8_t* skip_mask, const float* o0,
-                                float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side) {
+                                float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side,
+                                moe_stack_stats_t* stats) {
   clear_error();
   const char* who = "farskip_stack_forward_mxfp8";
   if (!mx) return fail(MOE_ERR_INVALID_ARG, "%s: mx is required", who);
@@ -584,7 +600,8 @@ int farskip_stack_forward_mxfp8(const moe_layer_desc_t* layers, const moe_layer_
   size_t need = 0;
   carve_stack(nullptr, *cfg, &need, true);
   if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
-  return stack_forward(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side), mx);
+  return stack_forward_stats(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side), mx,
+                             stats, who);
 }
 
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg) {
@@ -597,10 +614,11 @@ size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg) {
 
 int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg_t* cfg, int mode,
                           const uint8_t* skip_mask, const float* o0, float* oL, void* ws, size_t ws_bytes,
-                          void* s_main, void* s_side) {
+                          void* s_main, void* s_side, moe_stack_stats_t* stats) {
   clear_error();
   if (int rc = check_stack(layers, L, cfg, mode, o0, oL, ws, ws_bytes)) return rc;
-  return stack_forward(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side));
+  return stack_forward_stats(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side),
+                             nullptr, stats, "farskip_stack_forward");
 }
 
 size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg) {
@@ -671,6 +689,32 @@ int farskip_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_
   const size_t need = stack_bwd_ws_bytes(c, L);
   if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
   return launch_stack_backward(layers, L, c, mode, skip_mask, o0, dOL, dO0, grads, ws, as_stream(stream));
+}
+
+size_t moe_workspace_bytes(int op, int64_t T, int64_t d, int32_t E, int32_t k, int64_t c, int32_t L,
+                           int64_t c_shared, int dtype) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  moe_stack_cfg_t cfg{};
+  cfg.T = T;
+  cfg.d = d;
+  cfg.c = c;
+  cfg.c_shared = c_shared;
+  cfg.E = E;
+  cfg.k = k;
+  cfg.gate = MOE_GATE_SOFTMAX;
+  cfg.renormalize = 0;
+  cfg.dtype = dtype;
+  switch (op) {
+    case MOE_OP_PERMUTE: return moe_permute_workspace_bytes(T, E, k);
+    case MOE_OP_GROUPED_SWIGLU: return moe_grouped_swiglu_workspace_bytes(T * k, E, c, dtype);
+    case MOE_OP_GROUPED_SWIGLU_MXFP8: return moe_grouped_swiglu_mxfp8_workspace_bytes(T * k, E, c);
+    case MOE_OP_MXFP8_PHASE: return moe_grouped_mxfp8_phase_workspace_bytes(T * k, E);
+    case MOE_OP_STACK: return farskip_stack_workspace_bytes(&cfg);
+    case MOE_OP_STACK_MXFP8: return farskip_stack_mxfp8_workspace_bytes(&cfg);
+    case MOE_OP_LAYER_BACKWARD: return moe_layer_backward_workspace_bytes(&cfg);
+    case MOE_OP_STACK_BACKWARD: return farskip_stack_backward_workspace_bytes(&cfg, L);
+    default: return 0;
+  }
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

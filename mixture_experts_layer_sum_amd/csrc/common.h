@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <vector>
+
 #include "../../include/farskip_moe.h"
 
 namespace fsm {
@@ -57,6 +59,28 @@ class ProfScope {
   int kind_;
   hipStream_t s_;
   hipEvent_t a_, b_;
+};
+
+// Collects the timing events of every launch made on this thread while it lives (instead of the
+// process-wide profiler), for a stack call's moe_stack_stats_t.  A null out records nothing.
+// finish() waits for the recorded launches and fills *out.
+struct ProfRec {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a, b;   // timing events recorded before and after the launch
+};
+class StatsScope {
+ public:
+  StatsScope(moe_stack_stats_t* out, hipStream_t main);
+  ~StatsScope();
+  StatsScope(const StatsScope&) = delete;
+  StatsScope& operator=(const StatsScope&) = delete;
+  int finish();
+
+ private:
+  moe_stack_stats_t* out_;
+  hipStream_t main_;
+  std::vector<ProfRec> recs_;
 };
 
 // ---- internal launchers (defined in the kernel files) -----------------------------------------

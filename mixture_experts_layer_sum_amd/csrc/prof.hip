@@ -1,6 +1,8 @@
 // Opt-in kernel timing: timing events recorded on the launch stream around each library kernel.
+#include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -8,20 +10,18 @@
 namespace fsm {
 
 namespace {
-struct Rec {
-  int kind;
-  hipStream_t s;
-  hipEvent_t a, b;
-};
+using Rec = ProfRec;
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Rec> g_recs;
+// a stack call that fills moe_stack_stats_t collects its own launches here (this thread only)
+thread_local std::vector<Rec>* t_sink = nullptr;
 }  // namespace
 
 bool prof_on() { return g_on.load(std::memory_order_relaxed); }
 
 ProfScope::ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s), a_(nullptr), b_(nullptr) {
-  if (!prof_on()) return;
+  if (!prof_on() && !t_sink) return;
   if (hipEventCreate(&a_) != hipSuccess) { a_ = nullptr; return; }
   if (hipEventCreate(&b_) != hipSuccess) { (void)hipEventDestroy(a_); a_ = nullptr; b_ = nullptr; return; }
   if (hipEventRecord(a_, s_) != hipSuccess) {
@@ -38,8 +38,77 @@ ProfScope::~ProfScope() {
     (void)hipEventDestroy(b_);
     return;
   }
+  if (t_sink) {
+    t_sink->push_back({kind_, s_, a_, b_});
+    return;
+  }
   std::lock_guard<std::mutex> g(g_mu);
   g_recs.push_back({kind_, s_, a_, b_});
+}
+
+namespace {
+// total length of the union of intervals (sorted by start)
+double union_len(std::vector<std::pair<double, double>> v) {
+  std::sort(v.begin(), v.end());
+  double total = 0.0, a = 0.0, b = 0.0;
+  bool open = false;
+  for (const auto& iv : v) {
+    if (!open || iv.first > b) {
+      if (open) total += b - a;
+      a = iv.first;
+      b = iv.second;
+      open = true;
+    } else if (iv.second > b) {
+      b = iv.second;
+    }
+  }
+  return open ? total + (b - a) : 0.0;
+}
+}  // namespace
+
+StatsScope::StatsScope(moe_stack_stats_t* out, hipStream_t main) : out_(out), main_(main) {
+  if (out_) t_sink = &recs_;
+}
+
+StatsScope::~StatsScope() {
+  if (out_) t_sink = nullptr;
+  for (const Rec& r : recs_) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+}
+
+int StatsScope::finish() {
+  if (!out_) return MOE_OK;
+  t_sink = nullptr;
+  *out_ = moe_stack_stats_t{};
+  for (const Rec& r : recs_) {
+    const hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stack stats: %s", hipGetErrorString(e));
+  }
+  std::vector<std::pair<double, double>> m, s, all;
+  double lo = 0.0, hi = 0.0;
+  for (size_t i = 0; i < recs_.size(); ++i) {
+    const Rec& r = recs_[i];
+    float t0 = 0.f, t1 = 0.f;
+    hipError_t e = hipEventElapsedTime(&t0, recs_[0].a, r.a);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, recs_[0].a, r.b);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stack stats: %s", hipGetErrorString(e));
+    (r.s == main_ ? m : s).push_back({double(t0), double(t1)});
+    all.push_back({double(t0), double(t1)});
+    lo = i == 0 ? t0 : std::min(lo, double(t0));
+    hi = i == 0 ? t1 : std::max(hi, double(t1));
+  }
+  const double um = union_len(m), us = union_len(s), ua = union_len(all);
+  out_->wall_ms = hi - lo;
+  out_->main_busy_ms = um;
+  out_->side_busy_ms = us;
+  out_->overlap_ms = std::max(0.0, um + us - ua);   // |M n S| = |M| + |S| - |M u S|
+  out_->overlap_of_side = us > 0.0 ? out_->overlap_ms / us : 0.0;
+  out_->overlap_of_main = um > 0.0 ? out_->overlap_ms / um : 0.0;
+  out_->launches_main = int32_t(m.size());
+  out_->launches_side = int32_t(s.size());
+  return MOE_OK;
 }
 
 }  // namespace fsm

@@ -6,7 +6,8 @@
 // butterfly over the wavefront picks the winner under the total order
 //     a before b  <=>  logit_a > logit_b, or logit_a == logit_b and index_a < index_b,
 // so ties go to the lower expert index and every lane agrees on the winner.  Lane i keeps
-// winner i.  Weights: softmax over all E logits (wave max and wave sum), or sigmoid, optionally
+// winner i.  A NaN logit is read as -infinity: it ranks below every number, so each round still
+// returns an expert index in [0, E) (the ids feed the permutation's histogram and scatter).  Weights: softmax over all E logits (wave max and wave sum), or sigmoid, optionally
 // renormalised over the k winners.
 #include "common.h"
 
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   for (int j = 0; j < VPL; ++j) {
     const int e = j * 64 + lane;
     if (e < E) {
-      v[j] = row[e];
+      const float x = row[e];
+      v[j] = x != x ? -INFINITY : x;
     } else {
       v[j] = -INFINITY;
       taken |= 1u << j;

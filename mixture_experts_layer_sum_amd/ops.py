@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
-                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, KernelInterval, KernelTime, LayerDesc, LayerMx, LayerGrads, StackCfg, check, lib)
+                   MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, MOE_OPS, KernelInterval, KernelTime, LayerDesc, LayerMx,
+                   LayerGrads, StackCfg, StackStats, check, lib)
 
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
 MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
@@ -212,8 +213,12 @@ def layer_mx(W: dict) -> dict:
             if W.get(name) is not None}
 
 
+def _stats_dict(st: StackStats) -> dict:
+    return {name: getattr(st, name) for name, _ in StackStats._fields_}
+
+
 def farskip_stack_forward_mxfp8(layers: Sequence[dict], mx_layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws,
-                                skip_mask=None, s_main=None, s_side=None):
+                                skip_mask=None, s_main=None, s_side=None, stats: bool = False):
     """farskip_stack_forward with the routed experts on MXFP8 operands; mx_layers[j] as layer_mx()."""
     L = len(layers)
     if len(mx_layers) != L:
@@ -232,14 +237,18 @@ def farskip_stack_forward_mxfp8(layers: Sequence[dict], mx_layers: Sequence[dict
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     sm = _s(s_main)
     ss = _s(s_side) if s_side is not None else sm
+    st = StackStats() if stats else None
     check("farskip_stack_forward_mxfp8",
           lib.farskip_stack_forward_mxfp8(descs, mxd, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(),
-                                          sm, ss))
+                                          sm, ss, ctypes.byref(st) if stats else None))
+    return _stats_dict(st) if stats else None
 
 
 def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, ws, skip_mask=None,
-                          s_main=None, s_side=None):
-    """o_L of the FarSkip stack (mode "none" | "partial" | "outdated").  s_side defaults to s_main."""
+                          s_main=None, s_side=None, stats: bool = False):
+    """o_L of the FarSkip stack (mode "none" | "partial" | "outdated").  s_side defaults to s_main.
+    stats=True: the call blocks until the stack is done and returns the library's per-stream kernel
+    timing (moe_stack_stats_t as a dict); otherwise it is asynchronous and returns None."""
     L = len(layers)
     descs = (LayerDesc * L)(*[layer_desc(W) for W in layers])
     mask = None
@@ -248,8 +257,18 @@ def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, w
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     sm = _s(s_main)
     ss = _s(s_side) if s_side is not None else sm
+    st = StackStats() if stats else None
     check("farskip_stack_forward",
-          lib.farskip_stack_forward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(), sm, ss))
+          lib.farskip_stack_forward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(), sm, ss,
+                                    ctypes.byref(st) if stats else None))
+    return _stats_dict(st) if stats else None
+
+
+def workspace_bytes(op: str, T: int, d: int, E: int, k: int, c: int, L: int = 1, c_shared: int = 0,
+                    dtype=torch.bfloat16) -> int:
+    """moe_workspace_bytes: scratch bytes of the call named by op (a key of MOE_OPS)."""
+    return int(lib.moe_workspace_bytes(MOE_OPS[op], T, d, E, k, c, L, c_shared,
+                                       dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)))
 
 
 def layer_backward_workspace_bytes(cfg: StackCfg) -> int:

@@ -144,7 +144,7 @@ def test_stack_argument_errors():
     need = lib.farskip_stack_workspace_bytes(ctypes.byref(cfg))
     assert need > 64 * 2 * 128 * 4 * 2
     desc = (L.LayerDesc * 2)(*[L.LayerDesc(W_R=0x1000, W1=0x1000, W2=0x1000, W3=0x1000) for _ in range(2)])
-    ok_args = (desc, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None)
+    ok_args = (desc, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None, None)
     bad = list(ok_args)
     bad[8] = need - 1
     err(f(*bad), L.MOE_ERR_WORKSPACE)
@@ -296,7 +296,7 @@ def test_mxfp8_stack_argument_errors():
     desc = (L.LayerDesc * 2)(*[L.LayerDesc(W_R=0x1000) for _ in range(2)])   # expert weights not read
     full = {n: 0x1000 for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s", "Ws1q", "Ws1s", "Ws2q", "Ws2s", "Ws3q", "Ws3s")}
     mx = (L.LayerMx * 2)(*[L.LayerMx(**full) for _ in range(2)])
-    ok_args = [desc, mx, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None]
+    ok_args = [desc, mx, 2, ctypes.byref(cfg), 1, None, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None, None]
     bad = list(ok_args)
     bad[1] = None
     err(f(*bad), L.MOE_ERR_INVALID_ARG, "mx")
@@ -316,3 +316,37 @@ def test_mxfp8_stack_argument_errors():
         bad = list(ok_args)
         bad[3] = ctypes.byref(c_bad)
         err(f(*bad), L.MOE_ERR_UNSUPPORTED)
+
+
+def test_workspace_bytes_dispatch():
+    """moe_workspace_bytes(op, T, d, E, k, c, L, c_shared, dtype) returns what each per-call query
+    returns for the same layer sizes (routed rows N = T * k in E groups), and 0 for an unknown op
+    or sizes the op rejects."""
+    T, d, E, k, c, cs = 4096, 2048, 64, 6, 1408, 2816
+    for dt in (L.MOE_BF16, L.MOE_F32):
+        cfg = _cfg(T=T, d=d, E=E, k=k, c=c, c_shared=cs, dtype=dt)
+        ws = lambda op, Ls=1: lib.moe_workspace_bytes(L.MOE_OPS[op], T, d, E, k, c, Ls, cs, dt)  # noqa: E731
+        assert ws("permute") == lib.moe_permute_workspace_bytes(T, E, k) > 0
+        assert ws("grouped_swiglu") == lib.moe_grouped_swiglu_workspace_bytes(T * k, E, c, dt) > 0
+        assert ws("grouped_swiglu_mxfp8") == lib.moe_grouped_swiglu_mxfp8_workspace_bytes(T * k, E, c) > 0
+        assert ws("mxfp8_phase") == lib.moe_grouped_mxfp8_phase_workspace_bytes(T * k, E) > 0
+        assert ws("stack") == lib.farskip_stack_workspace_bytes(ctypes.byref(cfg)) > 0
+        assert ws("stack_mxfp8") == lib.farskip_stack_mxfp8_workspace_bytes(ctypes.byref(cfg))
+        assert ws("layer_backward") == lib.moe_layer_backward_workspace_bytes(ctypes.byref(cfg)) > 0
+        assert ws("stack_backward", 3) == lib.farskip_stack_backward_workspace_bytes(ctypes.byref(cfg), 3) > 0
+    assert lib.moe_workspace_bytes(L.MOE_OPS["stack_mxfp8"], T, d, E, k, c, 1, cs, L.MOE_BF16) > 0
+    assert lib.moe_workspace_bytes(L.MOE_OPS["stack_mxfp8"], T, d, E, k, c, 1, cs, L.MOE_F32) == 0
+    assert lib.moe_workspace_bytes(99, T, d, E, k, c, 1, cs, L.MOE_BF16) == 0
+    assert lib.moe_workspace_bytes(L.MOE_OPS["permute"], -1, d, E, k, c, 1, cs, L.MOE_BF16) == 0
+    assert lib.moe_workspace_bytes(L.MOE_OPS["stack"], T, d, 0, k, c, 1, cs, L.MOE_BF16) == 0
+    assert lib.moe_workspace_bytes(L.MOE_OPS["stack_backward"], T, d, E, k, c, 0, cs, L.MOE_BF16) == 0
+    # the binding's wrapper passes the same arguments
+    from mixture_experts_layer_sum_amd import ops
+    assert ops.workspace_bytes("grouped_swiglu", T, d, E, k, c) == \
+        lib.moe_grouped_swiglu_workspace_bytes(T * k, E, c, L.MOE_BF16)
+
+
+def test_stack_stats_struct_layout():
+    """moe_stack_stats_t: six doubles then two int32 (56 bytes), as the header declares it."""
+    assert ctypes.sizeof(L.StackStats) == 56
+    assert L.StackStats.launches_main.offset == 48 and L.StackStats.launches_side.offset == 52

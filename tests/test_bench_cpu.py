@@ -73,3 +73,21 @@ def test_stream_overlap_from_launch_intervals():
     assert ov["main_busy_ms"] == 18.0 and ov["side_busy_ms"] == 10.0 and ov["both_busy_ms"] == 7.0
     assert ov["side_hidden_frac"] == 0.7 and ov["main_covered_frac"] == round(7 / 18, 4)
     assert ov["launches"] == 4
+
+
+def test_route_report_per_layer():
+    c = mi.BY_NAME["dsv3-stack"]
+    kernels = {"router_gemm": {"ms_per_step": 1.8, "launches": 40}, "topk": {"ms_per_step": 0.44, "launches": 40}}
+    r = bench.route_report(kernels, c)
+    assert r["ms_per_layer"] == pytest.approx((1.8 + 0.44) / c.layers)
+    nbytes = c.T * c.d * 2 + c.E * c.d * 2 + c.T * c.E * 4 + c.T * c.k * 8
+    assert r["bytes_per_layer"] == nbytes
+    assert r["gbs"] == pytest.approx(nbytes / (r["ms_per_layer"] * 1e-3) / 1e9, abs=0.1)
+    assert r["frac_mfma_peak"] == pytest.approx(2.0 * c.T * c.d * c.E / (r["ms_per_layer"] * 1e-3) / 1e12
+                                                / bench.PEAK_BF16_TFLOPS, abs=1e-4)
+    assert bench.route_report({"topk": {"ms_per_step": 1.0, "launches": 4}}, c) is None
+
+
+def test_host_cpu_reports_cores():
+    h = bench.host_cpu()
+    assert h["cores"] >= 1 and h["affinity_cpus"] >= 1
