@@ -26,3 +26,17 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    # achieved errors of the float parity comparisons (tests/helpers.py report()), one line each
+    try:
+        from tests.helpers import RESULTS
+    except Exception:  # pragma: no cover
+        return
+    if not RESULTS:
+        return
+    tr = terminalreporter
+    tr.section("achieved parity errors (max|err|/max|ref|; of_bar = share of the element-wise bar used)")
+    for test, what, vals in RESULTS:
+        tr.write_line(f"{test} | {what} | " + ", ".join(f"{k}={v:.3e}" for k, v in vals.items()))

@@ -26,7 +26,8 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.helpers import NEAR_TIE, ExpertSlices, assert_parity, oracle_weights, to_np
+from tests.helpers import (NEAR_TIE, ExpertSlices, assert_mirror, assert_parity, bf16_ulp, combine_bound,
+                           mirror_bound, oracle_weights, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -129,11 +130,12 @@ def test_stack_two_streams_equals_one_stream(ops, mode, mask):
     assert torch.equal(a, c2)  # bitwise repeatable
 
 
-def composed(ops, c, layers, o0, mode, mask, rows=None, record=None, mx_layers=None):
+def composed(ops, c, layers, o0, mode, mask, rows=None, record=None, mx_layers=None, keep=None):
     """The stack recursion written with the single ABI calls on one stream.  With rows and a record
     list, each layer appends (x_j, o_{j-1}, o_j, topk_idx_j, x_{j+1} or None) for those rows.  With
-    mx_layers, the expert MLPs are moe_grouped_swiglu_mxfp8 on moe_mx_quantize of x_j (routed: rows
-    gathered through the permutation; shared: all rows as one group)."""
+    a keep list instead, each layer appends the same five tensors for all tokens, on the device.
+    With mx_layers, the expert MLPs are moe_grouped_swiglu_mxfp8 on moe_mx_quantize of x_j (routed:
+    rows gathered through the permutation; shared: all rows as one group)."""
     from mixture_experts_layer_sum_amd.ops import LayerBuffers
     dt = c.torch_dtype
     buf = LayerBuffers(c.T, c.d, c.E, c.k, c.c, c.shared_width, dt, DEV)
@@ -171,6 +173,8 @@ def composed(ops, c, layers, o0, mode, mask, rows=None, record=None, mx_layers=N
             rd = rows.to(DEV)
             record.append((to_np(x[rd]), to_np(o_prev[rd]), to_np(o_new[rd]), buf.topk_idx[rd].cpu().numpy(),
                            None if x_next is None else to_np(x_next[rd])))
+        if keep is not None:
+            keep.append((x.clone(), o_prev, o_new, buf.topk_idx.clone(), x_next))
         o_prev, x = o_new, x_next
     torch.cuda.synchronize()
     return o_prev
@@ -187,32 +191,65 @@ def test_stack_equals_composed_ops(ops, c, mode, mask):
     assert torch.equal(a, b)
 
 
+def cover_rows(n_sample, topk_all, E, seed):
+    """A seeded sample of n_sample tokens plus, for every layer and every expert that the sample
+    does not reach there, one seeded token routed to it (topk_all: each layer's [T, k] routing)."""
+    T = topk_all[0].shape[0]
+    rows = set(mi.sample_rows(T, n_sample, seed).numpy().tolist())
+    g = np.random.default_rng(seed)
+    for idx in topk_all:
+        hit = np.zeros(E, bool)
+        hit[np.unique(idx[sorted(rows)])] = True
+        for e in np.nonzero(~hit)[0]:
+            cand = np.nonzero((idx == e).any(axis=1))[0]
+            if cand.size:
+                t = int(g.choice(cand))
+                rows.add(t)
+                hit[np.unique(idx[t])] = True
+    return torch.from_numpy(np.array(sorted(rows), dtype=np.int64))
+
+
 @pytest.mark.parametrize("name", ["dsv3-stack", "dsv3-decode"])
 def test_stack_dsv3_full_size_sampled(ops, name):
     """The DeepSeek-V3-shaped 4-layer partial stack in the bench launch configuration (two streams),
     for the prefill batch (T = 65536, 256-row tiles) and one decode step (T = 1024, 64-row tiles).
-    The stack output equals the composed single calls bitwise; 16 seeded tokens are then checked
-    layer by layer against the oracle on the GPU's own layer inputs (teacher-forced)."""
+    The stack output equals the composed single calls bitwise.  Then, at every layer, 256 seeded
+    tokens plus tokens added until every expert of that layer is reached are checked against the
+    oracle on the GPU's own layer inputs (teacher-forced): routing, S + R and the next input, each
+    against the spec bar and against the store-mirrored oracle's element-wise bar."""
     c = mi.BY_NAME[name]
     layers, o0 = make_stack(c)
     oL = run_stack(ops, c, layers, o0, "partial")
     assert not torch.isnan(oL).any().item()
-    rows = mi.sample_rows(c.T, 16, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 3))
-    rec = []
-    assert torch.equal(oL, composed(ops, c, layers, o0, "partial", None, rows=rows, record=rec))
+    kept = []
+    assert torch.equal(oL, composed(ops, c, layers, o0, "partial", None, keep=kept))
+    rows = cover_rows(256, [k_[3].cpu().numpy() for k_ in kept], c.E, mi.seed_for(c.cfg_id, 0, mi.T_SAMPLE, 3))
+    rd = rows.to(DEV)
     rnd = oracle.round_to_bf16
     for j, W in enumerate(layers):
-        # fetch expert weights on demand, one layer at a time, without caching (22.5 GB per layer)
+        x, o_prev, o_new, idx, x_next = (None if t is None else t[rd] for t in kept[j])
+        x, o_prev, o_new, idx = to_np(x), to_np(o_prev), to_np(o_new), idx.cpu().numpy()
+        x_next = None if x_next is None else to_np(x_next)
+        # every expert is fetched once per layer and not kept (22.5 GB per layer)
         Wo = oracle_weights(W, cache=False)
-        x, o_prev, o_new, idx, x_next = rec[j]
         res = oracle.moe_layer(x, Wo, c.k, c.gate, c.renormalize, c.n_shared, c.c_shared, store=rnd)
+        assert len(Wo["W1"].fetched) == c.E or set(np.unique(kept[j][3].cpu().numpy())) == Wo["W1"].fetched
         keep = oracle.topk_gap(res["logits"], c.k) >= NEAR_TIE
-        assert keep.sum() >= 12
+        assert keep.sum() >= 240
         np.testing.assert_array_equal(idx[keep], res["topk_idx"][keep])
+        what = f"{name} layer {j} ({len(rows)} tokens, {len(Wo['W1'].fetched)} experts)"
         # o_j = o_{j-1} + S_j + R_j, summed in fp32 on the GPU
-        assert_parity((o_new - o_prev)[keep], res["out"][keep], torch.bfloat16, f"{name} layer {j} S + R")
+        got = (o_new.astype(np.float64) - o_prev)[keep]
+        assert_parity(got, res["out"][keep], torch.bfloat16, what + " S + R")
+        bound = combine_bound(res["S"], res["Y"], res["topk_w"], res["dest_row"].reshape(len(rows), c.k), o_prev)
+        assert_mirror(got, res["out"][keep], what + " S + R", bound=bound[keep])
         if x_next is not None:  # partial: x_{j+1} = bf16(o_{j-1} + S_j)
-            assert_parity(x_next[keep], rnd(o_prev + res["S"])[keep], torch.bfloat16, f"{name} layer {j} x_next")
+            ref_x = rnd(o_prev + res["S"])
+            assert_parity(x_next[keep], ref_x[keep], torch.bfloat16, what + " x_next")
+            # one bf16 unit of x, plus S's own bar, plus two fp32 roundings of o_{j-1} + S
+            bx = bf16_ulp(ref_x) + mirror_bound(res["S"]) + 2.0 ** -23 * (np.abs(o_prev) + np.abs(res["S"]))
+            assert_mirror(x_next[keep], ref_x[keep], what + " x_next", bound=bx[keep])
+    del kept
 
 
 @pytest.mark.parametrize("name,n_sample", [("tiny-fp32", 64), ("dsv2-lite", 128), ("qwen3-30b-a3b", 128),
@@ -238,7 +275,11 @@ def test_stack_one_layer_each_workload(ops, name, n_sample):
     keep = oracle.topk_gap(res["logits"], c.k) >= NEAR_TIE
     assert keep.mean() > 0.9
     np.testing.assert_array_equal(idx[keep], res["topk_idx"][keep])
-    assert_parity((o_new - o_prev)[keep], res["out"][keep], c.torch_dtype, f"{name} one-layer stack S + R")
+    got = (o_new.astype(np.float64) - o_prev)[keep]
+    assert_parity(got, res["out"][keep], c.torch_dtype, f"{name} one-layer stack S + R")
+    if rnd is not None:
+        bound = combine_bound(res["S"], res["Y"], res["topk_w"], res["dest_row"].reshape(len(x), c.k), o_prev)
+        assert_mirror(got, res["out"][keep], f"{name} one-layer stack S + R", bound=bound[keep])
 
 
 @pytest.mark.parametrize("c,mx", [(TINY_STACK, False), (MID_STACK, False), (MID_STACK, True)],
@@ -283,6 +324,40 @@ def test_stack_graph_replay(ops, c, mx):
         torch.cuda.synchronize()
         assert not torch.isnan(ref).any().item()
         assert torch.equal(o_graph, ref), f"replay {r}"
+
+
+@pytest.mark.parametrize("two", [True, False], ids=["two-streams", "one-stream"])
+def test_stack_stats_out_parameter(ops, two):
+    """farskip_stack_forward's stats: the call blocks, fills per-stream busy times and the overlap of
+    its own kernels, leaves the result bitwise unchanged, and records nothing for the process-wide
+    profiler.  On one stream there is no side-stream work and no overlap."""
+    c = MID_STACK
+    layers, o0 = make_stack(c)
+    ref = run_stack(ops, c, layers, o0, "partial", two_streams=two)
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.stack_workspace_bytes(cfg), DEV)
+    out = torch.full_like(o0, float("nan"))
+    sm = torch.cuda.current_stream()
+    ss = torch.cuda.Stream() if two else sm
+    ops.profile_collect()
+    ops.profile_enable(True)
+    try:
+        st = ops.farskip_stack_forward(layers, cfg, "partial", o0, out, ws, s_main=sm, s_side=ss, stats=True)
+    finally:
+        ops.profile_enable(False)
+    assert sum(n for n, _ in ops.profile_collect().values()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    print(f"[stats] {'two' if two else 'one'} stream(s): {st}", flush=True)
+    assert st["launches_main"] >= 2 * c.layers
+    assert st["main_busy_ms"] > 0 and st["wall_ms"] >= max(st["main_busy_ms"], st["side_busy_ms"]) - 1e-6
+    assert 0.0 <= st["overlap_of_side"] <= 1.0 and 0.0 <= st["overlap_of_main"] <= 1.0
+    # |M u S| = |M| + |S| - |M n S| cannot exceed the span from the first start to the last end
+    assert st["main_busy_ms"] + st["side_busy_ms"] - st["overlap_ms"] <= st["wall_ms"] + 1e-6
+    if two:
+        assert st["launches_side"] >= 2 * c.layers and st["side_busy_ms"] > 0
+    else:
+        assert st["launches_side"] == 0 and st["overlap_ms"] == 0.0 and st["side_busy_ms"] == 0.0
 
 
 def test_profile_intervals_of_a_two_stream_stack(ops):
