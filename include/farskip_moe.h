@@ -96,6 +96,24 @@ int moe_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32
 size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t k);
 
 /*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device memory or pass a
+ * workspace: code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments and outputs as moe_permute, bit for bit, without ws / ws_bytes: the
+ * scratch (the per-chunk expert counts and their prefix sums, moe_permute_workspace_bytes(T, E, k)
+ * bytes) lives in a fixed device array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends.  The call allocates and frees nothing; its first call on a
+ * device looks up that device's array (the current device must be the stream's device).
+ * Sizes whose scratch exceeds the array (roughly T * k * E > 4096 * 2^20) return MOE_ERR_UNSUPPORTED
+ * with a message; other errors as moe_permute.  Nothing in the array has to start at zero.  All calls
+ * on one GPU share its array: two such calls that may run at the same time on that GPU (on
+ * different streams, or from different host threads) race and must be ordered by the caller.
+ */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_permute_noalloc(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                        const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_src,
+                        int32_t* dest_row, void* A_perm, void* stream);
+
+/*
  * moe_grouped_swiglu -- the modern MLP of section 2.1 applied per group (expert):
  * for rows r in [group_offsets[g], group_offsets[g+1]):
  *     H[r] = (X[r] W1[g]^T) . SiLU(X[r] W2[g]^T)      (H kept in dtype, in the workspace)

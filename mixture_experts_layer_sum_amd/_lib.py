@@ -14,8 +14,9 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 FARSKIP_NONE, FARSKIP_PARTIAL, FARSKIP_OUTDATED = 0, 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 1024, 32
+MOE_PERMUTE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
-EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_grouped_swiglu",
+EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_permute_noalloc", "moe_grouped_swiglu",
            "moe_grouped_swiglu_workspace_bytes", "moe_grouped_swiglu_gathered", "moe_mx_quantize",
            "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
            "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
@@ -82,6 +83,8 @@ def _declare(lib):
     lib.moe_route.restype = i
     lib.moe_permute.argtypes = [vp, i, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.restype = i
+    lib.moe_permute_noalloc.argtypes = [vp, i, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_permute_noalloc.restype = i
     lib.moe_permute_workspace_bytes.argtypes = [i64, i32, i32]
     lib.moe_permute_workspace_bytes.restype = sz
     lib.moe_grouped_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i, i64, i64, i64, vp, vp, sz, vp]

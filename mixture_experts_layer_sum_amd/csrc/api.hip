@@ -443,6 +443,19 @@ int moe_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32
                         as_stream(stream));
 }
 
+int moe_permute_noalloc(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                        const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_src, int32_t* dest_row,
+                        void* A_perm, void* stream) {
+  clear_error();
+  // the same checks as moe_permute, with the fixed scratch standing in for the workspace
+  const size_t need = permute_ws_bytes(T < 0 ? 0 : T, E < 1 ? 1 : E, k < 1 ? 1 : k);
+  if (int rc = check_permute(A, dtype, T, d, E, k, topk_idx, expert_offsets, sorted_src, dest_row, A_perm,
+                             reinterpret_cast<void*>(uintptr_t(1)), need))
+    return rc;
+  return launch_permute_noalloc(A, dtype, T, d, E, k, topk_idx, expert_offsets, sorted_src, dest_row, A_perm,
+                                as_stream(stream));
+}
+
 size_t moe_grouped_swiglu_workspace_bytes(int64_t N, int32_t G, int64_t c, int dtype) {
   if (N < 0 || G < 1 || c < 1 || !dtype_ok(dtype)) return 0;
   return swiglu_ws_bytes(N, G, c, dtype);

@@ -14,6 +14,8 @@
 //                    dest_row[f] = offsets[e] + (earlier slots of e); sorted_src is its inverse
 //   4. k_perm_rows   one wavefront per token reads its row once and writes it to its k
 //                    destination rows (16-byte vectors): the row copy reads A exactly once
+#include <mutex>
+
 #include "common.h"
 
 namespace fsm {
@@ -170,6 +172,58 @@ int launch_permute(const void* A, int dtype, int64_t T, int64_t d, int32_t E, in
     if (int rc = check_launch("permute rows")) return rc;
   }
   return MOE_OK;
+}
+
+// ---- the permutation without a caller workspace (moe_permute_noalloc) ---------------------------
+// The two per-chunk count arrays live in a fixed device array instead of a workspace argument.
+// Every GPU the library runs on holds its own copy of the array until the process ends; host code
+// reaches it only through the address that hipGetSymbolAddress returns for the current device (the
+// array's name in host code is a host-side stand-in, not a device address).
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;   // MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes == MOE_PERMUTE_NOALLOC_SCRATCH_BYTES, "header and library agree");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (looked up once per device, with that device current)
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_permute_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: device %d beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MOE_ERR_HIP, "moe_permute_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+size_t permute_noalloc_limit() { return kNoAllocScratchBytes; }
+
+int launch_permute_noalloc(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
+                           const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
+                           void* A_perm, hipStream_t s) {
+  const size_t need = permute_ws_bytes(T, E, k);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_permute_noalloc: T*k = %lld slots over E = %d experts need %zu bytes of scratch, above the "
+                "fixed %zu (use moe_permute with a workspace)", (long long)(T * k), E, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  // k_perm_hist writes every count of every chunk and k_perm_scan every prefix before they are read,
+  // so nothing in the scratch has to start at zero
+  return launch_permute(A, dtype, T, d, E, k, topk_idx, offsets, sorted_src, dest_row, A_perm, ws, s);
 }
 
 }  // namespace fsm

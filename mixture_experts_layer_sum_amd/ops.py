@@ -78,6 +78,16 @@ def moe_permute(topk_idx, E: int, expert_offsets, sorted_src, dest_row, A=None, 
                                          _p(dest_row), _p(A_perm), _p(ws), ws.numel(), _s(stream)))
 
 
+def moe_permute_noalloc(topk_idx, E: int, expert_offsets, sorted_src, dest_row, A=None, A_perm=None, stream=None):
+    """moe_permute without a workspace: the library's fixed device scratch holds the counts (for
+    callers that cannot allocate; calls that may overlap on one GPU race)."""
+    T, k = topk_idx.shape
+    d = A.shape[1] if A is not None else 0
+    dt = dtype_code(A.dtype) if A is not None else MOE_BF16
+    check("moe_permute_noalloc", lib.moe_permute_noalloc(_p(A), dt, T, d, E, k, _p(topk_idx), _p(expert_offsets),
+                                                         _p(sorted_src), _p(dest_row), _p(A_perm), _s(stream)))
+
+
 def grouped_swiglu_workspace_bytes(N: int, G: int, c: int, dtype) -> int:
     return int(lib.moe_grouped_swiglu_workspace_bytes(N, G, c, dtype_code(dtype)))
 

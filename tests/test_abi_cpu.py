@@ -350,3 +350,18 @@ def test_stack_stats_struct_layout():
     """moe_stack_stats_t: six doubles then two int32 (56 bytes), as the header declares it."""
     assert ctypes.sizeof(L.StackStats) == 56
     assert L.StackStats.launches_main.offset == 48 and L.StackStats.launches_side.offset == 52
+
+
+def test_permute_noalloc_rejects_oversize_before_any_launch():
+    """moe_permute_noalloc checks its arguments, and that the fixed scratch is large enough, on the
+    host before touching the device."""
+    f = lib.moe_permute_noalloc
+    cap = L.MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
+    # 2^22 slots over 1024 experts need 2 x 1024 chunks x 1024 experts x 4 bytes = 8 MiB + 256 > cap
+    T, k, E = 1 << 17, 32, 1024
+    assert lib.moe_permute_workspace_bytes(T, E, k) > cap
+    err(f(None, 1, T, 0, E, k, BAD, BAD, BAD, BAD, None, None), L.MOE_ERR_UNSUPPORTED, "scratch")
+    err(f(None, 1, 10, 0, 8, 2, None, BAD, BAD, BAD, None, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 1, 10, 0, 0, 2, BAD, BAD, BAD, BAD, None, None), L.MOE_ERR_INVALID_ARG)
+    err(f(None, 1, 10, 64, 8, 2, BAD, BAD, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "A_perm")
+    assert lib.moe_permute_workspace_bytes(1 << 16, 256, 8) < cap   # the DSV3 batch fits
