@@ -273,6 +273,65 @@ def moe_stack(o0, layer_weights, k, gate, renormalize, mode, mask=None, n_shared
 
 
 # ---------------------------------------------------------------------------------------------
+# Section 3, the wiring of a model whose layers are an attention sub-block followed by an MoE
+# sub-block (shared experts S_k and routed experts R_k).  The page gives the attention input as
+# the "partial" activation of (8b), everything the residual holds after layer k-1 except that
+# layer's routed-expert output,
+#     attn-in_k = o_{k-2} + attn-out_{k-1} + shared-out_{k-1}        (attn-in_1 = o_0),
+# and the MoE input as the "outdated" activation of (8a), the previous layer's full output, which
+# lacks only layer k's own attention output,
+#     mlp-in_k = o_{k-1} = attn-in_k + routed-out_{k-1}.
+# Every sub-block output still enters the residual: o_k = o_{k-1} + attn-out_k + S_k + R_k, with
+# S_k and R_k computed from mlp-in_k.  Mode "none" is the standard residual stream of section 3's
+# first equation: attn-in_k = o_{k-1}, mlp-in_k = o_{k-1} + attn-out_k.  (The equation for mlp-in_k
+# is missing from the page; its stated decomposition and the (8a) reading agree on o_{k-1}.)
+# ---------------------------------------------------------------------------------------------
+def attn_moe_stack(o0, layers, mode, round_inputs=None, record=None):
+    """layers: list of (attn_fn, shared_fn, routed_fn), each mapping x [T,d] -> [T,d].
+    mode: "farskip" (the wiring above) | "none".  round_inputs: optional function applied to every
+    sub-block input (the implementation's activation dtype).  record: optional list that receives
+    (attn_in, mlp_in, attn_out, S, R, o) per layer, the inputs as the sub-blocks saw them."""
+    if mode not in ("farskip", "none"):
+        raise ValueError(mode)
+    rnd = (lambda x: x) if round_inputs is None else (lambda x: _f64(round_inputs(x)))
+    o_prev = _f64(o0)
+    partial = o_prev      # attn-in of the next layer: o_{k-1} without R_{k-1}
+    for attn_fn, shared_fn, routed_fn in layers:
+        a_in = rnd(partial if mode == "farskip" else o_prev)
+        A = _f64(attn_fn(a_in))
+        m_in = rnd(o_prev if mode == "farskip" else o_prev + A)
+        S = _f64(shared_fn(m_in))
+        R = _f64(routed_fn(m_in))
+        o = o_prev + A + S + R
+        partial = o_prev + A + S
+        if record is not None:
+            record.append((a_in, m_in, A, S, R, o))
+        o_prev = o
+    return o_prev
+
+
+def attn_moe_layer_stack(o0, layer_weights, attn_weights, k, gate, renormalize, mode, n_shared=0, c_shared=0,
+                         round_inputs=None, record=None, store=None):
+    """attn_moe_stack with MoE sublayers (shared + routed experts, as moe_layer) and, standing in for
+    each attention sub-block, a dense per-token SwiGLU block with its own weights: attn_weights[j] =
+    (Wa1, Wa2 [c_a, d], Wa3 [d, c_a]) and attn-out = mlp(x, Wa1, Wa2, Wa3).  `store` as in mlp()."""
+    layers = []
+    for W, Wa in zip(layer_weights, attn_weights):
+        def attn_fn(x, Wa=Wa):
+            return mlp(x, Wa[0], Wa[1], Wa[2], store)
+
+        def shared_fn(x, W=W):
+            if n_shared:
+                return shared_mlp(x, W["Ws1"], W["Ws2"], W["Ws3"], n_shared, c_shared, store)
+            return np.zeros_like(_f64(x))
+
+        def routed_fn(x, W=W):
+            return moe_layer(x, W, k, gate, renormalize, store=store)["R"]
+        layers.append((attn_fn, shared_fn, routed_fn))
+    return attn_moe_stack(o0, layers, mode, round_inputs, record)
+
+
+# ---------------------------------------------------------------------------------------------
 # Precision helpers used by the comparisons.
 # ---------------------------------------------------------------------------------------------
 def round_to_bf16(x):

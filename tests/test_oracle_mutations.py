@@ -101,11 +101,49 @@ def _stack_dropped_o0(o0, layers, mode, mask=None, round_inputs=None, record=Non
     return ORIG["farskip_stack"](o0, layers, mode, mask, round_inputs, record) - np.asarray(o0, np.float64)
 
 
+def _attn_input_not_skipped(o0, layers, mode, round_inputs=None, record=None):
+    # attention fed the full o_{k-1} (the routed output not skipped), MoE input as the page's
+    o_prev = np.asarray(o0, np.float64)
+    for af, sf, rf in layers:
+        A = af(o_prev)
+        S, R = sf(o_prev), rf(o_prev)
+        o_prev = o_prev + A + S + R
+    return o_prev
+
+
+def _mlp_input_without_routed(o0, layers, mode, round_inputs=None, record=None):
+    # MoE fed the partial activation too (routed-out_{k-1} dropped from mlp-in_k)
+    o_prev = np.asarray(o0, np.float64)
+    partial = o_prev
+    for af, sf, rf in layers:
+        A = af(partial)
+        S, R = sf(partial), rf(partial)
+        o = o_prev + A + S + R
+        partial = o_prev + A + S
+        o_prev = o
+    return o_prev
+
+
+def _attn_partial_with_routed_not_shared(o0, layers, mode, round_inputs=None, record=None):
+    # the partial activation built from the routed output instead of the shared one
+    o_prev = np.asarray(o0, np.float64)
+    partial = o_prev
+    for af, sf, rf in layers:
+        A = af(partial if mode == "farskip" else o_prev)
+        m = o_prev if mode == "farskip" else o_prev + A
+        S, R = sf(m), rf(m)
+        o = o_prev + A + S + R
+        partial = o_prev + A + R
+        o_prev = o
+    return o_prev
+
+
 ORIG = {name: getattr(om, name) for name in ("select_topk", "permute", "combine", "farskip_stack", "mlp",
-                                            "gate_scores", "gate_weights")}
+                                            "gate_scores", "gate_weights", "attn_moe_stack")}
 
 GOLDEN_ROUTED = [lambda c=c: pins.test_routed_layer_golden(c) for c in range(6)]
 GOLDEN_STACK = [lambda c=c: pins.test_stack_golden_scalar(c) for c in range(5)]
+GOLDEN_ATTN = [lambda c=c: pins.test_attn_moe_stack_golden_scalar(c) for c in range(2)]
 
 CASES = [
     ("mlp", _mlp_gate_up_swapped, [pins.test_mlp_golden]),
@@ -122,6 +160,9 @@ CASES = [
     ("farskip_stack", _stack_partial_without_residual, GOLDEN_STACK),
     ("farskip_stack", _stack_outdated_as_current, GOLDEN_STACK),
     ("farskip_stack", _stack_dropped_o0, GOLDEN_STACK),
+    ("attn_moe_stack", _attn_input_not_skipped, GOLDEN_ATTN),
+    ("attn_moe_stack", _mlp_input_without_routed, GOLDEN_ATTN),
+    ("attn_moe_stack", _attn_partial_with_routed_not_shared, GOLDEN_ATTN),
 ]
 
 

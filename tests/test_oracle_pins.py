@@ -325,6 +325,109 @@ def test_stack_record_has_the_layer_inputs():
 
 
 # ------------------------------------------------------------------------------------------
+# Attention + MoE wiring of section 3 (attn-in_k partial, mlp-in_k outdated)
+# ------------------------------------------------------------------------------------------
+def _scalar_attn_layers(g):
+    return [(lambda x, v=v: v * x, lambda x, a=a: a * x, lambda x, b=b: b * x)
+            for v, a, b in zip(g["alpha"], g["a"], g["b"])]
+
+
+@pytest.mark.parametrize("case", range(len(GOLDEN["attn_moe_stack"]["cases"])))
+def test_attn_moe_stack_golden_scalar(case):
+    g = GOLDEN["attn_moe_stack"]
+    c = g["cases"][case]
+    rec = []
+    oL = oracle.attn_moe_stack(np.array([[g["o0"]]]), _scalar_attn_layers(g), c["mode"], record=rec)
+    assert [float(r[0][0, 0]) for r in rec] == c["attn_in"]
+    assert [float(r[1][0, 0]) for r in rec] == c["mlp_in"]
+    assert [float(r[5][0, 0]) for r in rec] == c["o"]
+    assert float(oL[0, 0]) == c["o"][-1]
+
+
+def attn_setup(L=3, T=11, d=6, E=4, c=5, k=2, seed=90):
+    o0, Ws, kw = moe_stack_setup(L=L, T=T, d=d, E=E, c=c, k=k, seed=seed)
+    Wa = [(mi.normal((c, d), 0.3, seed + 100 + 3 * j).double().numpy(),
+           mi.normal((c, d), 0.3, seed + 101 + 3 * j).double().numpy(),
+           mi.normal((d, c), 0.3, seed + 102 + 3 * j).double().numpy()) for j in range(L)]
+    return o0, Ws, Wa, kw
+
+
+def _attn_fn(Wa):
+    return lambda x: oracle.mlp(x, *Wa)
+
+
+def test_attn_moe_none_is_the_residual_sum_over_interleaved_sub_blocks():
+    """Mode none is section 3's first equation over the 2L sub-blocks attn_1, moe_1, attn_2, ...:
+    the (already pinned) MoE-only stack with skipping disabled, fed the interleaved blocks."""
+    o0, Ws, Wa, kw = attn_setup()
+    zero = lambda x: np.zeros_like(np.asarray(x, np.float64))  # noqa: E731
+    blocks = []
+    for W, A in zip(Ws, Wa):
+        blocks.append((_attn_fn(A), zero))
+        blocks.append((lambda x, W=W: oracle.shared_mlp(x, W["Ws1"], W["Ws2"], W["Ws3"], 1, kw["c_shared"]),
+                       lambda x, W=W: oracle.moe_layer(x, W, kw["k"], kw["gate"], kw["renormalize"])["R"]))
+    ref = oracle.farskip_stack(o0, blocks, "none")
+    got = oracle.attn_moe_layer_stack(o0, Ws, Wa, kw["k"], kw["gate"], kw["renormalize"], "none", 1, kw["c_shared"])
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+def test_attn_moe_farskip_without_attention_is_the_standard_moe_stack():
+    """With every attention output zero, mlp-in_k = o_{k-1} is the full residual: the MoE-only
+    stack with skipping disabled."""
+    o0, Ws, Wa, kw = attn_setup()
+    Wa0 = [(a, b, np.zeros_like(c)) for a, b, c in Wa]
+    got = oracle.attn_moe_layer_stack(o0, Ws, Wa0, kw["k"], kw["gate"], kw["renormalize"], "farskip", 1,
+                                      kw["c_shared"])
+    np.testing.assert_allclose(got, oracle.moe_stack(o0, Ws, mode="none", **kw), rtol=1e-12)
+
+
+def test_attn_moe_farskip_without_routed_experts_is_parallel_blocks():
+    """With every routed output zero, attn-in_k = mlp-in_k = o_{k-1}: each layer adds the attention
+    and the shared experts of the same input, o_k = o_{k-1} + A_k(o_{k-1}) + S_k(o_{k-1})."""
+    o0, Ws, Wa, kw = attn_setup()
+    for W in Ws:
+        W["W3"] = np.zeros_like(W["W3"])
+    o = o0.copy()
+    for W, A in zip(Ws, Wa):
+        o = o + oracle.mlp(o, *A) + oracle.shared_mlp(o, W["Ws1"], W["Ws2"], W["Ws3"], 1, kw["c_shared"])
+    got = oracle.attn_moe_layer_stack(o0, Ws, Wa, kw["k"], kw["gate"], kw["renormalize"], "farskip", 1,
+                                      kw["c_shared"])
+    np.testing.assert_allclose(got, o, rtol=1e-12)
+
+
+def test_attn_moe_farskip_inputs_follow_the_page():
+    """attn-in_k = o_{k-2} + attn-out_{k-1} + shared-out_{k-1}, mlp-in_k = o_{k-1}, and the page's
+    decomposition mlp-in_k = attn-in_k + routed-out_{k-1}; every sub-block output enters o_L."""
+    o0, Ws, Wa, kw = attn_setup(L=3)
+    rec = []
+    oracle.attn_moe_layer_stack(o0, Ws, Wa, kw["k"], kw["gate"], kw["renormalize"], "farskip", 1, kw["c_shared"],
+                                record=rec)
+    np.testing.assert_array_equal(rec[0][0], o0)
+    np.testing.assert_array_equal(rec[0][1], o0)
+    o_prev = o0
+    for j in range(1, 3):
+        a_in, m_in = rec[j][0], rec[j][1]
+        A, S, R, o = rec[j - 1][2], rec[j - 1][3], rec[j - 1][4], rec[j - 1][5]
+        np.testing.assert_allclose(a_in, o_prev + A + S, rtol=1e-14)
+        np.testing.assert_array_equal(m_in, o)
+        np.testing.assert_allclose(m_in, a_in + R, rtol=1e-12, atol=1e-14)
+        o_prev = o
+    total = o0 + sum(r[2] + r[3] + r[4] for r in rec)
+    np.testing.assert_allclose(rec[-1][5], total, rtol=1e-12)
+
+
+def test_attn_moe_one_layer():
+    o0, Ws, Wa, kw = attn_setup(L=1)
+    W = Ws[0]
+    moe = oracle.moe_layer(o0, W, kw["k"], kw["gate"], kw["renormalize"])["R"] + \
+        oracle.shared_mlp(o0, W["Ws1"], W["Ws2"], W["Ws3"], 1, kw["c_shared"])
+    A = oracle.mlp(o0, *Wa[0])
+    far = oracle.attn_moe_layer_stack(o0, Ws, Wa, kw["k"], kw["gate"], kw["renormalize"], "farskip", 1,
+                                      kw["c_shared"])
+    np.testing.assert_allclose(far, o0 + A + moe, rtol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------
 # Precision helpers
 # ------------------------------------------------------------------------------------------
 def test_round_to_bf16_matches_torch():
