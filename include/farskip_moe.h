@@ -47,7 +47,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate_t;
-typedef enum { FARSKIP_NONE = 0, FARSKIP_PARTIAL = 1, FARSKIP_OUTDATED = 2 } farskip_mode_t;
+typedef enum {
+  FARSKIP_NONE = 0,     /* the standard residual stream (no skip) */
+  FARSKIP_PARTIAL = 1,  /* MoE-only stack: next input o_{j-1} + shared output (eq. 8b) */
+  FARSKIP_OUTDATED = 2, /* MoE-only stack: next input o_{j-1} (eq. 8a) */
+  FARSKIP_PAPER = 3     /* attention + MoE stack: attention input partial, MoE input outdated */
+} farskip_mode_t;
 
 /* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 1024
@@ -312,6 +317,42 @@ int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_s
                           size_t ws_bytes, void* s_main, void* s_side, moe_stack_stats_t* stats);
 size_t farskip_stack_workspace_bytes(const moe_stack_cfg_t* cfg);
 
+/* The weights of the dense SwiGLU block that stands in for a layer's attention sub-block in
+ * farskip_attn_moe_stack_forward (device pointers): Wa1, Wa2 [c_attn, d], Wa3 [d, c_attn]. */
+typedef struct {
+  const void* Wa1;
+  const void* Wa2;
+  const void* Wa3;
+} moe_attn_desc_t;
+
+/*
+ * farskip_attn_moe_stack_forward -- L layers, each an attention sub-block followed by an MoE
+ * sub-block (shared experts S_j plus routed experts R_j), on the residual stream, wired as section 3
+ * of the page gives it for such models:
+ *   mode FARSKIP_PAPER: the attention input is the partial activation (eq. 8b) and the MoE input the
+ *       outdated one (eq. 8a):
+ *         attn-in_j = o_{j-2} + attn-out_{j-1} + S_{j-1}   (everything in o_{j-1} but R_{j-1}; o_0 at j = 1)
+ *         mlp-in_j  = o_{j-1} = attn-in_j + R_{j-1}
+ *   mode FARSKIP_NONE: the standard stream, attn-in_j = o_{j-1}, mlp-in_j = o_{j-1} + attn-out_j;
+ *   in both: o_j = o_{j-1} + attn-out_j + S_j(mlp-in_j) + R_j(mlp-in_j).
+ * No attention block is in this library: each attention sub-block is computed by a dense SwiGLU
+ * block of hidden width c_attn with the layer's attn[j] weights (the wiring does not depend on what
+ * the sub-block computes).  The residual is float32; every sub-block input is rounded to
+ * cfg->dtype.  Streams: s_main runs each layer's permutation and routed GEMMs; s_side runs the
+ * routers, shared experts, combines and attention blocks -- in FARSKIP_PAPER mode layer j+1's
+ * attention runs while layer j's routed experts do.  s_side == s_main serialises everything with the
+ * same results.  Stream contract, graph capture and stats as farskip_stack_forward.
+ *   layers, L, cfg, o0, oL   as farskip_stack_forward
+ *   attn     host array [L] of the attention stand-ins' weights
+ *   c_attn   their hidden width (bf16: a multiple of 64)
+ *   ws       scratch of at least farskip_attn_moe_stack_workspace_bytes(cfg, c_attn) bytes
+ */
+int farskip_attn_moe_stack_forward(const moe_layer_desc_t* layers, const moe_attn_desc_t* attn, int32_t L,
+                                   const moe_stack_cfg_t* cfg, int64_t c_attn, int mode, const float* o0,
+                                   float* oL, void* ws, size_t ws_bytes, void* s_main, void* s_side,
+                                   moe_stack_stats_t* stats);
+size_t farskip_attn_moe_stack_workspace_bytes(const moe_stack_cfg_t* cfg, int64_t c_attn);
+
 /* MXFP8 codes and scales of one layer's expert weights, as moe_mx_quantize writes them. */
 typedef struct {
   const uint8_t* W1q;  /* [E, c, d] E4M3 codes */
@@ -422,8 +463,9 @@ int farskip_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_
 size_t farskip_stack_backward_workspace_bytes(const moe_stack_cfg_t* cfg, int32_t L);
 
 /*
- * moe_workspace_bytes -- the scratch size of any entry point, as one call: a dispatch over the
- * per-call queries above.  The sizes are those of one MoE layer (section 2.1: T tokens of width d,
+ * moe_workspace_bytes -- the scratch size of the MoE entry points, as one call: a dispatch over the
+ * per-call queries above (farskip_attn_moe_stack_forward, which also needs the attention width, has
+ * its own query).  The sizes are those of one MoE layer (section 2.1: T tokens of width d,
  * E routed experts of hidden width c, k experts per token, shared experts of total hidden width
  * c_shared) and of an L-layer stack:
  *   MOE_OP_PERMUTE                moe_permute for T tokens, E experts, k slots
@@ -484,7 +526,9 @@ typedef enum {
   MOE_K_BWD_POINTWISE = 18, /* backward: combine, gate, SwiGLU and bias-sum kernels */
   MOE_K_MX_DENSE_GATE_UP = 19, /* MXFP8 phase 1 of a single-group call (the shared expert) */
   MOE_K_MX_DENSE_DOWN = 20,    /* MXFP8 phase 2 of a single-group call */
-  MOE_KERNEL_KINDS = 21
+  MOE_K_ATTN_GATE_UP = 21,     /* attention stand-in block (farskip_attn_moe_stack_forward), phase 1 */
+  MOE_K_ATTN_DOWN = 22,        /* attention stand-in block, phase 2 */
+  MOE_KERNEL_KINDS = 23
 } moe_kernel_kind_t;
 
 typedef struct {

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfarskip_
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
-FARSKIP_NONE, FARSKIP_PARTIAL, FARSKIP_OUTDATED = 0, 1, 2
+FARSKIP_NONE, FARSKIP_PARTIAL, FARSKIP_OUTDATED, FARSKIP_PAPER = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_TOPK = 1024, 32
 MOE_PERMUTE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -21,7 +21,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_permu
            "moe_grouped_swiglu_mxfp8", "moe_grouped_swiglu_mxfp8_workspace_bytes", "moe_grouped_mxfp8_gate_up",
            "moe_grouped_mxfp8_down", "moe_grouped_mxfp8_phase_workspace_bytes", "moe_layer_backward",
            "moe_layer_backward_workspace_bytes", "farskip_stack_backward", "farskip_stack_backward_workspace_bytes",
-           "moe_combine", "farskip_stack_forward", "farskip_stack_forward_mxfp8", "farskip_stack_mxfp8_workspace_bytes",
+           "moe_combine", "farskip_stack_forward", "farskip_attn_moe_stack_forward",
+           "farskip_attn_moe_stack_workspace_bytes", "farskip_stack_forward_mxfp8", "farskip_stack_mxfp8_workspace_bytes",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect",
            "moe_profile_collect_intervals", "moe_workspace_bytes", "moe_last_error",
            "moe_version")
@@ -31,7 +32,7 @@ MOE_OPS = {"permute": 0, "grouped_swiglu": 1, "grouped_swiglu_mxfp8": 2, "mxfp8_
 KERNEL_KINDS = ("router_gemm", "topk", "permute_index", "permute_rows", "tile_table", "gemm_gate_up",
                 "gemm_down", "combine", "layer_input", "dense_gate_up", "dense_down", "mx_quantize", "mx_gate_up",
                 "mx_down", "bwd_recompute", "bwd_dgrad", "bwd_wgrad", "transpose", "bwd_pointwise",
-                "mx_dense_gate_up", "mx_dense_down")
+                "mx_dense_gate_up", "mx_dense_down", "attn_gate_up", "attn_down")
 
 
 class LayerDesc(ctypes.Structure):
@@ -43,6 +44,10 @@ class LayerDesc(ctypes.Structure):
 class LayerMx(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("W1q", "W1s", "W2q", "W2s", "W3q", "W3s",
                                                 "Ws1q", "Ws1s", "Ws2q", "Ws2s", "Ws3q", "Ws3s")]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("Wa1", ctypes.c_void_p), ("Wa2", ctypes.c_void_p), ("Wa3", ctypes.c_void_p)]
 
 
 class StackCfg(ctypes.Structure):
@@ -124,6 +129,12 @@ def _declare(lib):
                                           ctypes.POINTER(ctypes.c_uint8), vp, vp, vp, sz, vp, vp,
                                           ctypes.POINTER(StackStats)]
     lib.farskip_stack_forward.restype = i
+    lib.farskip_attn_moe_stack_forward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AttnDesc), i32,
+                                                   ctypes.POINTER(StackCfg), i64, i, vp, vp, vp, sz, vp, vp,
+                                                   ctypes.POINTER(StackStats)]
+    lib.farskip_attn_moe_stack_forward.restype = i
+    lib.farskip_attn_moe_stack_workspace_bytes.argtypes = [ctypes.POINTER(StackCfg), i64]
+    lib.farskip_attn_moe_stack_workspace_bytes.restype = sz
     lib.farskip_stack_forward_mxfp8.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerMx), i32,
                                                 ctypes.POINTER(StackCfg), i, ctypes.POINTER(ctypes.c_uint8), vp, vp,
                                                 vp, sz, vp, vp, ctypes.POINTER(StackStats)]

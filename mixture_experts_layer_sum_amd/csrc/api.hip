@@ -134,11 +134,14 @@ struct StackWs {
   void* shared_ws;
   uint8_t* xq[2];   // MXFP8 stack: codes and scales of the layer inputs
   uint8_t* xs[2];
+  void* xa[2];      // attention + MoE stack: the attention sub-blocks' inputs and outputs
+  void* A[2];
+  void* attn_ws;
 };
 
 // mx: the MXFP8 stack's buffers (layer-input codes and scales, the MXFP8 product's workspace) in
 // place of the bf16 product's workspace
-StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total, bool mx = false) {
+StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total, bool mx = false, int64_t c_attn = 0) {
   const size_t es = esize(c.dtype);
   const size_t T = size_t(c.T), d = size_t(c.d), E = size_t(c.E), k = size_t(c.k);
   char* base = static_cast<char*>(ws);
@@ -170,6 +173,13 @@ StackWs carve_stack(void* ws, const moe_stack_cfg_t& c, size_t* total, bool mx =
       s.xq[b] = static_cast<uint8_t*>(take(T * d));
       s.xs[b] = static_cast<uint8_t*>(take(T * d / 32));
     }
+  }
+  if (c_attn > 0) {
+    for (int b = 0; b < 2; ++b) {
+      s.xa[b] = take(T * d * es);
+      s.A[b] = take(T * d * es);
+    }
+    s.attn_ws = take(swiglu_ws_bytes(c.T, 1, c_attn, c.dtype));
   }
   if (total) *total = off;
   return s;
@@ -386,6 +396,110 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
       if (int rc = quantize_input(nxt)) return rc;
   }
   if (int rc = combine(L - 1)) return rc;
+  if (two) {
+    if (int rc = record(E_end.ev[1], ss)) return rc;
+    if (int rc = wait(sm, E_end.ev[1])) return rc;
+  }
+  return MOE_OK;
+}
+
+// ---- the attention + MoE stack ----------------------------------------------------------------------
+// Section 3's wiring of layers made of an attention sub-block and an MoE sub-block (shared S_j and
+// routed R_j experts): mode FARSKIP_PAPER takes the attention input as the partial activation
+// (eq. 8b) and the MoE input as the outdated one (eq. 8a),
+//     attn-in_j = P_{j-1} = o_{j-2} + attn-out_{j-1} + S_{j-1}     (attn-in_0 = o_0)
+//     mlp-in_j  = o_{j-1}                                          (mlp-in_0 = o_0)
+//     o_j = o_{j-1} + attn-out_j + S_j + R_j;
+// mode FARSKIP_NONE is the standard stream (attn-in_j = o_{j-1}, mlp-in_j = o_{j-1} + attn-out_j).  A
+// dense SwiGLU block stands in for each attention sub-block.  The residual is float32; sub-block
+// inputs are rounded to cfg.dtype.  Buffers [j % 2]: xm (MoE inputs, the workspace's x), xa / A
+// (attention inputs / outputs), S, logits, top-k, dest_row, Y.
+//   paper mode, per layer j:
+//     side: router_j(xm[j]), top-k_j; record route_j
+//     main: wait route_j; permute_j; routed gate/up_j, down_j; record gemm_j -- nothing else
+//     side: S_j = shared(xm[j]); P_j = o_{j-1} + A_j + S_j into oL (in place; o_0 for j = 0) and
+//           xa[j+1] = cast(P_j); A_{j+1} = attn_{j+1}(xa[j+1]) -- layer j+1's attention runs beside
+//           layer j's routed experts, the one-GPU form of the overlap the wiring is for;
+//           wait gemm_j; combine_j: oL += sum_i w Y_j (in place), xm[j+1] = cast(o_j)
+//   none mode, per layer j: side: A_j = attn_j(xa[j]); P_j = o_{j-1} + A_j into oL, xm[j] =
+//     cast(P_j); router_j; main: as above; side: S_j; wait gemm_j; combine_j: oL += S_j +
+//     sum_i w Y_j, xa[j+1] = cast(o_j).
+// Reuse: xm[j+1] (rewritten by combine_j) was last read by layer j-1's gathered gate/up on main,
+// which precedes gemm_j; Y / top-k / dest_row [j % 2] are rewritten by layer j+2's kernels, which
+// main reaches only after route_{j+2}, recorded on side after combine_j; oL, xa, A, S and the side
+// workspaces are touched by the side stream only.
+int attn_stack_forward(const moe_layer_desc_t* layers, const moe_attn_desc_t* attn, int32_t L,
+                       const moe_stack_cfg_t& c, int64_t c_attn, int mode, const float* o0, float* oL, void* ws,
+                       hipStream_t sm, hipStream_t ss) {
+  StackWs w = carve_stack(ws, c, nullptr, false, c_attn);
+  const bool two = sm != ss;
+  const bool paper = mode == FARSKIP_PAPER;
+  static const int kAttnKinds[2] = {MOE_K_ATTN_GATE_UP, MOE_K_ATTN_DOWN};
+  Events E_route, E_gemm, E_end;
+  if (two) {
+    if (int rc = E_route.make(L)) return rc;
+    if (int rc = E_gemm.make(L)) return rc;
+    if (int rc = E_end.make(2)) return rc;
+    if (int rc = record(E_end.ev[0], sm)) return rc;
+    if (int rc = wait(ss, E_end.ev[0])) return rc;
+  }
+  const int64_t N = c.T * c.k;
+  auto attention = [&](int j, int b) -> int {
+    const moe_attn_desc_t& a = attn[j];
+    return launch_grouped_swiglu(w.xa[b], w.shared_off, 1, a.Wa1, a.Wa2, a.Wa3, c.dtype, c.T, c.d, c_attn, w.A[b],
+                                 w.attn_ws, ss, nullptr, 1, 0, nullptr, kAttnKinds);
+  };
+  k_set_shared_offsets<<<1, 64, 0, ss>>>(w.shared_off, int32_t(c.T));
+  if (int rc = check_launch("stack setup")) return rc;
+  if (int rc = launch_make_input(o0, nullptr, c.dtype, c.T, c.d, w.xa[0], ss)) return rc;
+  if (paper) {
+    if (int rc = launch_make_input(o0, nullptr, c.dtype, c.T, c.d, w.x[0], ss)) return rc;
+    if (int rc = attention(0, 0)) return rc;
+  }
+  for (int j = 0; j < L; ++j) {
+    const moe_layer_desc_t& l = layers[j];
+    const int cur = j & 1, nxt = cur ^ 1;
+    const bool last = j + 1 == L;
+    const float* o_prev = j == 0 ? o0 : oL;
+    if (!paper) {   // mlp-in_j = o_{j-1} + A_j
+      if (int rc = attention(j, cur)) return rc;
+      if (int rc = launch_residual_add(o_prev, w.A[cur], nullptr, c.dtype, c.T, c.d, oL, w.x[cur], ss)) return rc;
+    }
+    if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
+    if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
+      return rc;
+    if (two) {
+      if (int rc = record(E_route.ev[j], ss)) return rc;
+      if (int rc = wait(sm, E_route.ev[j])) return rc;
+    }
+    if (int rc = launch_permute(w.x[cur], c.dtype, c.T, c.d, c.E, c.k, w.idx[cur], w.offsets, w.sorted_src,
+                                w.dest_row[cur], nullptr, w.perm_ws, sm))
+      return rc;
+    if (int rc = launch_grouped_swiglu(w.x[cur], w.offsets, c.E, l.W1, l.W2, l.W3, c.dtype, N, c.d, c.c, w.Y[cur],
+                                       w.gemm_ws, sm, w.sorted_src, c.k, c.T))
+      return rc;
+    if (two)
+      if (int rc = record(E_gemm.ev[j], sm)) return rc;
+    // side, beside the routed experts: the shared experts, and in paper mode the partial stream and
+    // the next layer's attention
+    if (c.c_shared)
+      if (int rc = launch_grouped_swiglu(w.x[cur], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, c.dtype, c.T, c.d,
+                                         c.c_shared, w.S[cur], w.shared_ws, ss))
+        return rc;
+    if (paper) {
+      if (int rc = launch_residual_add(o_prev, w.A[cur], c.c_shared ? w.S[cur] : nullptr, c.dtype, c.T, c.d, oL,
+                                       last ? nullptr : w.xa[nxt], ss))
+        return rc;
+      if (!last)
+        if (int rc = attention(j + 1, nxt)) return rc;
+    }
+    if (two)
+      if (int rc = wait(ss, E_gemm.ev[j])) return rc;
+    const void* add = (!paper && c.c_shared) ? w.S[cur] : nullptr;
+    void* out_x = last ? nullptr : (paper ? w.x[nxt] : w.xa[nxt]);
+    if (int rc = launch_combine(w.Y[cur], c.dtype, w.w[cur], w.dest_row[cur], c.T, c.d, c.k, add, oL, oL, out_x, ss))
+      return rc;
+  }
   if (two) {
     if (int rc = record(E_end.ev[1], ss)) return rc;
     if (int rc = wait(sm, E_end.ev[1])) return rc;
@@ -632,6 +746,43 @@ int farskip_stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_s
   if (int rc = check_stack(layers, L, cfg, mode, o0, oL, ws, ws_bytes)) return rc;
   return stack_forward_stats(layers, L, *cfg, mode, skip_mask, o0, oL, ws, as_stream(s_main), as_stream(s_side),
                              nullptr, stats, "farskip_stack_forward");
+}
+
+size_t farskip_attn_moe_stack_workspace_bytes(const moe_stack_cfg_t* cfg, int64_t c_attn) {
+  if (!cfg || cfg->T < 1 || cfg->d < 1 || cfg->c < 1 || cfg->E < 1 || cfg->k < 1 || c_attn < 1 || !dtype_ok(cfg->dtype))
+    return 0;
+  size_t total = 0;
+  carve_stack(nullptr, *cfg, &total, false, c_attn);
+  return total;
+}
+
+int farskip_attn_moe_stack_forward(const moe_layer_desc_t* layers, const moe_attn_desc_t* attn, int32_t L,
+                                   const moe_stack_cfg_t* cfg, int64_t c_attn, int mode, const float* o0, float* oL,
+                                   void* ws, size_t ws_bytes, void* s_main, void* s_side, moe_stack_stats_t* stats) {
+  clear_error();
+  const char* who = "farskip_attn_moe_stack_forward";
+  if (mode != FARSKIP_NONE && mode != FARSKIP_PAPER)
+    return fail(MOE_ERR_INVALID_ARG, "%s: mode must be FARSKIP_NONE or FARSKIP_PAPER (got %d)", who, mode);
+  if (int rc = check_stack_args(layers, L, cfg, FARSKIP_NONE, o0, oL, who)) return rc;
+  if (!attn) return fail(MOE_ERR_INVALID_ARG, "%s: attn is required", who);
+  if (c_attn < 1) return fail(MOE_ERR_INVALID_ARG, "%s: c_attn=%lld must be >= 1", who, (long long)c_attn);
+  if (cfg->dtype == MOE_BF16 && c_attn % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs c_attn %% 64 == 0", who);
+  for (int j = 0; j < L; ++j)
+    if (!attn[j].Wa1 || !attn[j].Wa2 || !attn[j].Wa3)
+      return fail(MOE_ERR_INVALID_ARG, "%s: layer %d is missing attention weights", who, j);
+  size_t need = 0;
+  carve_stack(nullptr, *cfg, &need, false, c_attn);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  const hipStream_t sm = as_stream(s_main), ss = as_stream(s_side);
+  if (stats) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(sm, &st) == hipSuccess && st != hipStreamCaptureStatusNone)
+      return fail(MOE_ERR_INVALID_ARG, "%s: stats cannot be measured while s_main is being captured", who);
+  }
+  StatsScope scope(stats, sm);
+  if (int rc = attn_stack_forward(layers, attn, L, *cfg, c_attn, mode, o0, oL, ws, sm, ss)) return rc;
+  return scope.finish();
 }
 
 size_t moe_layer_backward_workspace_bytes(const moe_stack_cfg_t* cfg) {

@@ -187,6 +187,42 @@ __global__ __launch_bounds__(256) void k_make_input(const float* __restrict__ o,
   store8(x, dtype, off, f);
 }
 
+// out = o + A (+ S) in float32 (out may alias o) and, optionally, x = cast(out): the partial
+// residual of the attention + MoE wiring (everything except the routed-expert output) and the next
+// attention sub-block's input.  A and S are in the workload dtype; S may be null.  The sums run in
+// the order (o + A) + S.
+__global__ __launch_bounds__(256) void k_residual_add(const float* o, const void* __restrict__ A,
+                                                      const void* __restrict__ S, int dtype, int64_t n8, float* out,
+                                                      void* __restrict__ x) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t off = i * 8;
+  const cb_f32x4 a = *reinterpret_cast<const cb_f32x4*>(o + off);
+  const cb_f32x4 b = *reinterpret_cast<const cb_f32x4*>(o + off + 4);
+  float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  float t[8];
+  load8(A, dtype, off, t);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] += t[q];
+  if (S) {
+    load8(S, dtype, off, t);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f[q] += t[q];
+  }
+  *reinterpret_cast<cb_f32x4*>(out + off) = cb_f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<cb_f32x4*>(out + off + 4) = cb_f32x4{f[4], f[5], f[6], f[7]};
+  if (x) store8(x, dtype, off, f);
+}
+
+int launch_residual_add(const float* o, const void* A, const void* S, int dtype, int64_t T, int64_t d, float* out,
+                        void* x, hipStream_t s) {
+  const int64_t n8 = T * d / 8;
+  if (n8 == 0) return MOE_OK;
+  ProfScope prof(MOE_K_LAYER_INPUT, s);
+  k_residual_add<<<unsigned(cdiv(n8, 256)), 256, 0, s>>>(o, A, S, dtype, n8, out, x);
+  return check_launch("residual add");
+}
+
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
                    void* out_x, hipStream_t s, const void* x_addend) {

@@ -102,10 +102,12 @@ int launch_tile_table(const int32_t* offsets, int G, int BM, int max_tiles, int3
 size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype);
 // gather != null: row r of the grouped input is X[gather[r] / gather_k], X having x_rows rows.
 // mid != null: recorded on s between the gate/up and the down product.
+// kinds (optional): the two profiler kinds of its products (default: routed or single-group ones)
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
                           void* Y, void* ws, hipStream_t s, const int32_t* gather = nullptr,
-                          int32_t gather_k = 1, int64_t x_rows = 0, hipEvent_t mid = nullptr);
+                          int32_t gather_k = 1, int64_t x_rows = 0, hipEvent_t mid = nullptr,
+                          const int* kinds = nullptr);
 // out_x (optional) = cast(out), or cast(out + x_addend) with x_addend [T, d] dtype
 int launch_combine(const void* Y, int dtype, const float* w, const int32_t* dest_row, int64_t T,
                    int64_t d, int32_t k, const void* addend, const float* residual, float* out,
@@ -141,5 +143,8 @@ int launch_grouped_swiglu_mx(const uint8_t* Xq, const uint8_t* Xs, const int32_t
 // x = cast(o [+ S]) : the FarSkip layer input from the fp32 residual (and the shared output)
 int launch_make_input(const float* o, const void* S, int dtype, int64_t T, int64_t d, void* x,
                       hipStream_t s);
+// out = (o + A) + S in float32 (out may alias o; S may be null), and x = cast(out) when x is set
+int launch_residual_add(const float* o, const void* A, const void* S, int dtype, int64_t T, int64_t d, float* out,
+                        void* x, hipStream_t s);
 
 }  // namespace fsm

@@ -590,14 +590,14 @@ void tile_rows(int64_t N, int32_t G, int64_t c, int dtype, int& bm1, int& bm2) {
 // Both phases of the bf16 grouped product with tile configurations C1 (gate/up) and C2 (down).
 template <const TileCfg& C1, const TileCfg& C2>
 int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t mt1, int64_t mt2, int64_t c,
-                     int64_t d, int32_t G, hipStream_t s, hipEvent_t mid) {
+                     int64_t d, int32_t G, hipStream_t s, hipEvent_t mid, const int* kinds) {
   a1.group_m = C1.gm;
   a1.n_tiles = int32_t(cdiv(c, C1.bn / 2));
   a1.quad_nb = quad_width(a1.n_tiles, a1.group_m);
   const dim3 grid1(unsigned(quad_grid(mt1, a1.n_tiles, a1.group_m, a1.quad_nb)));
   constexpr int nt1 = 64 * C1.wm * C1.wn;
   {
-    ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
+    ProfScope prof(kinds ? kinds[0] : G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
     if (rows1 == ROWS_GATHER)
       k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GATHER, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
     else if (rows1 == ROWS_GROUPED)
@@ -615,7 +615,7 @@ int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t m
   a2.quad_nb = quad_width(a2.n_tiles, a2.group_m);
   const dim3 grid2(unsigned(quad_grid(mt2, a2.n_tiles, a2.group_m, a2.quad_nb)));
   constexpr int nt2 = 64 * C2.wm * C2.wn;
-  ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
+  ProfScope prof(kinds ? kinds[1] : G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
   if (rows2 == ROWS_GROUPED)
     k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_GROUPED, C2.bk, C2.st><<<grid2, nt2, 0, s>>>(a2);
   else
@@ -663,7 +663,7 @@ size_t swiglu_ws_bytes(int64_t N, int32_t G, int64_t c, int dtype) {
 int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, const void* W1,
                           const void* W2, const void* W3, int dtype, int64_t N, int64_t d, int64_t c,
                           void* Y, void* ws, hipStream_t s, const int32_t* gather, int32_t gather_k,
-                          int64_t x_rows, hipEvent_t mid) {
+                          int64_t x_rows, hipEvent_t mid, const int* kinds) {
   SwigluWs w = carve(ws, G, N, c, dtype, nullptr);
   if (N == 0) {   // nothing to compute; the phase event still marks this point of the stream
     const hipError_t e = mid ? hipEventRecord(mid, s) : hipSuccess;
@@ -701,11 +701,11 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
   const int rows1 = gather ? ROWS_GATHER : (G > 1 ? ROWS_GROUPED : ROWS_SINGLE);
   const int rows2 = G > 1 ? ROWS_GROUPED : ROWS_SINGLE;
   if (bf && small_tiles(N, G, c, dtype))
-    return launch_bf16_pair<kS1, kS2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid);
-  if (bf) return launch_bf16_pair<kP1, kP2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid);
+    return launch_bf16_pair<kS1, kS2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds);
+  if (bf) return launch_bf16_pair<kP1, kP2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds);
   a1.n_tiles = int32_t(cdiv(c, F_BN));
   {
-    ProfScope prof(G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
+    ProfScope prof(kinds ? kinds[0] : G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
     if (rows1 == ROWS_GATHER)
       k_gemm_f32<EPI_SWIGLU, ROWS_GATHER><<<dim3(unsigned(mt1 * a1.n_tiles)), 256, 0, s>>>(a1);
     else
@@ -717,7 +717,7 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
   a2.n_tiles = int32_t(cdiv(d, F_BN));
-  ProfScope prof(G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
+  ProfScope prof(kinds ? kinds[1] : G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
   k_gemm_f32<EPI_PLAIN, ROWS_GROUPED><<<dim3(unsigned(mt2 * a2.n_tiles)), 256, 0, s>>>(a2);
   return check_launch("grouped gemm phase 2 (f32)");
 }

@@ -11,12 +11,12 @@ from typing import Optional, Sequence
 
 import torch
 
-from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PARTIAL, KERNEL_KINDS, MOE_BF16, MOE_F32,
+from ._lib import (FARSKIP_NONE, FARSKIP_OUTDATED, FARSKIP_PAPER, FARSKIP_PARTIAL, KERNEL_KINDS, AttnDesc, MOE_BF16, MOE_F32,
                    MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, MOE_OPS, KernelInterval, KernelTime, LayerDesc, LayerMx,
                    LayerGrads, StackCfg, StackStats, check, lib)
 
 GATES = {"softmax": MOE_GATE_SOFTMAX, "sigmoid": MOE_GATE_SIGMOID}
-MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED}
+MODES = {"none": FARSKIP_NONE, "partial": FARSKIP_PARTIAL, "outdated": FARSKIP_OUTDATED, "farskip": FARSKIP_PAPER}
 
 
 def dtype_code(dt: torch.dtype) -> int:
@@ -271,6 +271,30 @@ def farskip_stack_forward(layers: Sequence[dict], cfg: StackCfg, mode, o0, oL, w
     check("farskip_stack_forward",
           lib.farskip_stack_forward(descs, L, ctypes.byref(cfg), m, mask, _p(o0), _p(oL), _p(ws), ws.numel(), sm, ss,
                                     ctypes.byref(st) if stats else None))
+    return _stats_dict(st) if stats else None
+
+
+def attn_stack_workspace_bytes(cfg: StackCfg, c_attn: int) -> int:
+    return int(lib.farskip_attn_moe_stack_workspace_bytes(ctypes.byref(cfg), c_attn))
+
+
+def farskip_attn_moe_stack_forward(layers: Sequence[dict], attn: Sequence[dict], cfg: StackCfg, c_attn: int, mode,
+                                   o0, oL, ws, s_main=None, s_side=None, stats: bool = False):
+    """o_L of the attention + MoE stack (mode "farskip": attention input partial, MoE input outdated;
+    "none": the standard stream).  attn[j]: the layer's attention stand-in weights Wa1, Wa2, Wa3."""
+    L = len(layers)
+    if len(attn) != L:
+        raise ValueError("one attention block per layer is required")
+    descs = (LayerDesc * L)(*[layer_desc(W) for W in layers])
+    ad = (AttnDesc * L)(*[AttnDesc(Wa1=a["Wa1"].data_ptr(), Wa2=a["Wa2"].data_ptr(), Wa3=a["Wa3"].data_ptr())
+                          for a in attn])
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    sm = _s(s_main)
+    ss = _s(s_side) if s_side is not None else sm
+    st = StackStats() if stats else None
+    check("farskip_attn_moe_stack_forward",
+          lib.farskip_attn_moe_stack_forward(descs, ad, L, ctypes.byref(cfg), c_attn, m, _p(o0), _p(oL), _p(ws),
+                                             ws.numel(), sm, ss, ctypes.byref(st) if stats else None))
     return _stats_dict(st) if stats else None
 
 

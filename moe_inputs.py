@@ -35,6 +35,7 @@ BASE_SEED = 20251101
 # tensor ids used in the seed derivation
 T_ACT, T_WR, T_BIAS, T_W1, T_W2, T_W3, T_WS1, T_WS2, T_WS3 = 0, 1, 2, 3, 4, 5, 6, 7, 8
 T_LOGITS, T_TOPK, T_GROUPS, T_GATEW, T_PERM, T_Y, T_SAMPLE, T_MISC = 10, 11, 12, 13, 14, 15, 16, 17
+T_WA1, T_WA2, T_WA3 = 18, 19, 20   # the dense block standing in for a layer's attention sub-block
 
 
 @dataclasses.dataclass(frozen=True)
@@ -189,6 +190,16 @@ def layer_weights(cfg: MoEConfig, layer: int = 0, device="cpu") -> dict:
     else:
         w["Ws1"] = w["Ws2"] = w["Ws3"] = None
     return w
+
+
+def attn_weights(cfg: MoEConfig, layer: int, c_attn: int, device="cpu") -> dict:
+    """Weights of the dense SwiGLU block that stands in for a layer's attention sub-block in the
+    attention + MoE stack: Wa1, Wa2 [c_attn, d] ~ N(0, w_std^2), Wa3 [d, c_attn] ~ N(0, w3_std^2),
+    in the workload dtype."""
+    dt, cid = cfg.torch_dtype, weights_id(cfg)
+    return {"Wa1": normal((c_attn, cfg.d), cfg.w_std, seed_for(cid, layer, T_WA1), device, dt),
+            "Wa2": normal((c_attn, cfg.d), cfg.w_std, seed_for(cid, layer, T_WA2), device, dt),
+            "Wa3": normal((cfg.d, c_attn), cfg.w3_std, seed_for(cid, layer, T_WA3), device, dt)}
 
 
 def logits(T: int, E: int, seed: int, device="cpu", bias: Optional[torch.Tensor] = None,

@@ -365,3 +365,33 @@ def test_permute_noalloc_rejects_oversize_before_any_launch():
     err(f(None, 1, 10, 0, 0, 2, BAD, BAD, BAD, BAD, None, None), L.MOE_ERR_INVALID_ARG)
     err(f(None, 1, 10, 64, 8, 2, BAD, BAD, BAD, BAD, BAD, None), L.MOE_ERR_INVALID_ARG, "A_perm")
     assert lib.moe_permute_workspace_bytes(1 << 16, 256, 8) < cap   # the DSV3 batch fits
+
+
+def test_attn_stack_argument_errors():
+    """farskip_attn_moe_stack_forward rejects bad calls on the host, before any launch."""
+    f = lib.farskip_attn_moe_stack_forward
+    cfg = _cfg(c_shared=256)
+    need = lib.farskip_attn_moe_stack_workspace_bytes(ctypes.byref(cfg), 128)
+    assert need > lib.farskip_stack_workspace_bytes(ctypes.byref(cfg))
+    assert lib.farskip_attn_moe_stack_workspace_bytes(ctypes.byref(cfg), 0) == 0
+    full = dict(W_R=0x1000, W1=0x1000, W2=0x1000, W3=0x1000, Ws1=0x1000, Ws2=0x1000, Ws3=0x1000)
+    desc = (L.LayerDesc * 2)(*[L.LayerDesc(**full) for _ in range(2)])
+    attn = (L.AttnDesc * 2)(*[L.AttnDesc(Wa1=0x1000, Wa2=0x1000, Wa3=0x1000) for _ in range(2)])
+    ok = [desc, attn, 2, ctypes.byref(cfg), 128, L.FARSKIP_PAPER, BAD, ctypes.c_void_p(0x2000), BAD, need, None, None,
+          None]
+    for i, v, code, needle in ((5, L.FARSKIP_PARTIAL, L.MOE_ERR_INVALID_ARG, "mode"),
+                               (1, None, L.MOE_ERR_INVALID_ARG, "attn"),
+                               (4, 0, L.MOE_ERR_INVALID_ARG, "c_attn"),
+                               (9, need - 1, L.MOE_ERR_WORKSPACE, None),
+                               (7, BAD, L.MOE_ERR_INVALID_ARG, "alias"),
+                               (1, (L.AttnDesc * 2)(L.AttnDesc(Wa1=0x1000, Wa2=0x1000, Wa3=0x1000), L.AttnDesc()),
+                                L.MOE_ERR_INVALID_ARG, "layer 1")):
+        bad = list(ok)
+        bad[i] = v
+        err(f(*bad), code, needle)
+    c_bf = _cfg(c_shared=256, dtype=1)
+    bad = list(ok)
+    bad[3] = ctypes.byref(c_bf)
+    bad[4] = 96
+    bad[9] = lib.farskip_attn_moe_stack_workspace_bytes(ctypes.byref(c_bf), 96)
+    err(f(*bad), L.MOE_ERR_UNSUPPORTED, "c_attn")
