@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--configs", type=int, default=1,
                    help="1 = also time one FarSkip layer of each smaller workload (tiny fp32, DSV2-Lite, "
                         "Qwen3-30B-A3B, Llama-4-Scout)")
+    p.add_argument("--attn", type=int, default=1,
+                   help="after the steps, time the attention + MoE stack over the same layers; 0 = skip")
     p.add_argument("--backward", type=int, default=1,
                    help="after the steps, time the backward pass of layer 0 (one MoE sublayer); 0 = skip")
     p.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -126,6 +128,8 @@ def kernel_report(prof: dict, c, steps: int, extra_bytes: dict = None) -> dict:
         "gemm_down": (2.0 * N * d * c_, "flop"),
         "dense_gate_up": (4.0 * T * d * cs, "flop"),
         "dense_down": (2.0 * T * d * cs, "flop"),
+        "attn_gate_up": (4.0 * T * d * (cs or c_), "flop"),   # the attention stand-in: width of the shared expert
+        "attn_down": (2.0 * T * d * (cs or c_), "flop"),
         "combine": (N * d * 2.0 + N * 8.0 + T * d * (2.0 + 4.0 + 4.0), "byte"),
         "layer_input": (T * d * (4.0 + 2.0 + 2.0), "byte"),
         "mx_quantize": (T * d * (2.0 + 1.0 + 1.0 / 32), "byte"),   # the token rows, once per layer
@@ -155,12 +159,13 @@ def kernel_report(prof: dict, c, steps: int, extra_bytes: dict = None) -> dict:
 
 
 def route_report(kernels: dict, c) -> dict:
-    """The route step per layer (router logits + top-k gating): its time, and its algorithmic bytes
+    """The route step per layer (router logits + top-k gating, one launch or two): its time, and its algorithmic bytes
     (read the layer input and W_R once, write the logits the call returns, write the top-k ids and
     weights) and FLOP over that time, against the HBM and bf16 MFMA peaks."""
-    if "router_gemm" not in kernels or "topk" not in kernels:
+    if "router_gemm" not in kernels:
         return None
-    ms = (kernels["router_gemm"]["ms_per_step"] + kernels["topk"]["ms_per_step"]) / c.layers
+    # where one router tile holds a token's logits the top-k runs in the router GEMM's epilogue
+    ms = (kernels["router_gemm"]["ms_per_step"] + kernels.get("topk", {}).get("ms_per_step", 0.0)) / c.layers
     nbytes = c.T * c.d * 2.0 + c.E * c.d * 2.0 + c.T * c.E * 4.0 + c.T * c.k * 8.0
     flop = 2.0 * c.T * c.d * c.E
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -561,6 +566,58 @@ def decode(layers, steps: int = 10) -> dict:
     return out
 
 
+def attn_stack(c, layers, o0, steps: int = 3) -> dict:
+    """The attention + MoE stack (farskip_attn_moe_stack_forward) over the same layers, with a dense
+    SwiGLU block of the shared expert's width standing in for each attention sub-block.  The
+    section-3 wiring (attention input partial, MoE input outdated: layer j+1's attention runs beside
+    layer j's routed experts) and the standard stream, each on two streams and on one, alternated
+    step by step with profiling off; then the wiring's cross-stream overlap from one profiled pass."""
+    import torch
+
+    import moe_inputs as mi
+    from mixture_experts_layer_sum_amd import ops
+    dev = o0.device
+    ca = c.shared_width or c.c
+    attn = [mi.attn_weights(c, j, ca, dev) for j in range(c.layers)]
+    cfg = ops.stack_cfg(c.T, c.d, c.c, c.shared_width, c.E, c.k, c.gate, c.renormalize, c.torch_dtype)
+    ws = ops.workspace(ops.attn_stack_workspace_bytes(cfg, ca), dev)
+    oL = torch.empty_like(o0)
+    main_s, side_s = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def step(mode, ss):
+        ops.farskip_attn_moe_stack_forward(layers, attn, cfg, ca, mode, o0, oL, ws, s_main=main_s, s_side=ss)
+
+    runs = {"farskip_two_streams": lambda: step("farskip", side_s), "farskip_one_stream": lambda: step("farskip", main_s),
+            "none_two_streams": lambda: step("none", side_s), "none_one_stream": lambda: step("none", main_s)}
+    for fn in runs.values():
+        fn()
+    med = interleaved(runs, steps)
+    flop = c.layers * c.T * (c.flops_per_token()["total"] + 6 * c.d * ca)
+    out = {"workload": c.name, "attn_stand_in_hidden": ca, "layers": c.layers, "steps_each": steps}
+    for k_, ms in med.items():
+        out[k_] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(c.T * c.layers / (ms * 1e-3), 1),
+                   "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    out["two_stream_speedup_farskip"] = round(med["farskip_one_stream"] / med["farskip_two_streams"], 4)
+    out["two_stream_speedup_none"] = round(med["none_one_stream"] / med["none_two_streams"], 4)
+    out["farskip_vs_none_two_streams"] = round(med["none_two_streams"] / med["farskip_two_streams"], 4)
+    torch.cuda.synchronize()
+    ops.profile_collect()
+    ops.profile_enable(True)
+    step("farskip", side_s)
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    prof, launches = ops.profile_collect_intervals()
+    out["overlap"] = stream_overlap(launches, main_s.cuda_stream)
+    out["kernels"] = {k_: v for k_, v in kernel_report(prof, c, 1).items()
+                      if k_ in ("attn_gate_up", "attn_down", "gemm_gate_up", "gemm_down", "combine", "layer_input")}
+    assert torch.isfinite(oL).all().item(), "non-finite attention stack output"
+    out["what"] = ("a dense SwiGLU block stands in for attention; farskip = attention input partial (eq. 8b), MoE "
+                   "input outdated (eq. 8a); none = the standard stream")
+    del attn, ws, oL
+    torch.cuda.empty_cache()
+    return out
+
+
 def graph_replay_ms(enqueue, reps: int = 20) -> float:
     """Capture one call into a HIP graph (enqueue(s_main) puts the call on s_main, the capture
     stream; its side stream joins the capture through the call's own events) and return the median
@@ -913,6 +970,9 @@ def main():
                 "mxfp8 decode stack", lambda: mxfp8_stack(mi.BY_NAME["dsv3-decode"], layers, mxl, steps=10, graph=True))
         del mxl
         torch.cuda.empty_cache()
+    if args.attn and c.name == "dsv3-stack":
+        log("timing the attention + MoE stack")
+        result["attn_stack"] = leg("attn_stack", lambda: attn_stack(c, layers, o0))
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))

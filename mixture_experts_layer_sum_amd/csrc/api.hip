@@ -345,8 +345,8 @@ int stack_forward(const moe_layer_desc_t* layers, int32_t L, const moe_stack_cfg
       if (int rc = combine(j - 1)) return rc;   // also forms x_j
       if (int rc = quantize_input(cur)) return rc;
     }
-    if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
-    if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
+    if (int rc = launch_route(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, c.k, c.gate, c.renormalize,
+                              w.logits[cur], w.idx[cur], w.w[cur], ss))
       return rc;
     // main: layer j's permutation
     if (two) {
@@ -465,8 +465,8 @@ int attn_stack_forward(const moe_layer_desc_t* layers, const moe_attn_desc_t* at
       if (int rc = attention(j, cur)) return rc;
       if (int rc = launch_residual_add(o_prev, w.A[cur], nullptr, c.dtype, c.T, c.d, oL, w.x[cur], ss)) return rc;
     }
-    if (int rc = launch_router_logits(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, w.logits[cur], ss)) return rc;
-    if (int rc = launch_topk(w.logits[cur], c.T, c.E, c.k, c.gate, c.renormalize, w.idx[cur], w.w[cur], ss))
+    if (int rc = launch_route(w.x[cur], l.W_R, l.bias, c.dtype, c.T, c.d, c.E, c.k, c.gate, c.renormalize,
+                              w.logits[cur], w.idx[cur], w.w[cur], ss))
       return rc;
     if (two) {
       if (int rc = record(E_route.ev[j], ss)) return rc;
@@ -536,8 +536,7 @@ int moe_route(const void* A, const void* W_R, const float* bias, int dtype, int6
   if (int rc = check_route(A, W_R, dtype, T, d, E, k, gate, logits, topk_idx, topk_w)) return rc;
   if (T == 0) return MOE_OK;
   const hipStream_t s = as_stream(stream);
-  if (A)
-    if (int rc = launch_router_logits(A, W_R, bias, dtype, T, d, E, logits, s)) return rc;
+  if (A) return launch_route(A, W_R, bias, dtype, T, d, E, k, gate, renormalize, logits, topk_idx, topk_w, s);
   return launch_topk(logits, T, E, k, gate, renormalize, topk_idx, topk_w, s);
 }
 

@@ -831,8 +831,8 @@ int launch_stack_backward(const moe_layer_desc_t* layers, int32_t L, const moe_s
   for (int j = 0; j < L; ++j) {
     const moe_layer_desc_t& l = layers[j];
     const bool last = j + 1 == L;
-    FSM_TRY(launch_router_logits(w.x[j], l.W_R, l.bias, MOE_BF16, T, d, c.E, w.logits[j], s));
-    FSM_TRY(launch_topk(w.logits[j], T, c.E, c.k, c.gate, c.renormalize, w.idx[j], w.w[j], s));
+    FSM_TRY(launch_route(w.x[j], l.W_R, l.bias, MOE_BF16, T, d, c.E, c.k, c.gate, c.renormalize, w.logits[j],
+                         w.idx[j], w.w[j], s));
     if (c.c_shared)
       FSM_TRY(launch_grouped_swiglu(w.x[j], w.shared_off, 1, l.Ws1, l.Ws2, l.Ws3, MOE_BF16, T, d, c.c_shared, w.S,
                                     w.shared_ws, s));

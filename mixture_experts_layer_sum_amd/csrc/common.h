@@ -88,6 +88,9 @@ int launch_router_logits(const void* A, const void* W_R, const float* bias, int 
                          int64_t d, int32_t E, float* logits, hipStream_t s);
 int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int gate, int renorm,
                 int32_t* topk_idx, float* topk_w, hipStream_t s);
+// logits, then top-k: one fused launch where one router tile holds all of a token's logits
+int launch_route(const void* A, const void* W_R, const float* bias, int dtype, int64_t T, int64_t d, int32_t E,
+                 int32_t k, int gate, int renorm, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
 size_t permute_ws_bytes(int64_t T, int32_t E, int32_t k);
 // moe_permute with its count arrays in the library's fixed device scratch (no workspace argument)
 int launch_permute_noalloc(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,

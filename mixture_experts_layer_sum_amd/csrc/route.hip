@@ -112,4 +112,14 @@ int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int gate, 
   return check_launch("top-k");
 }
 
+// The route step: router logits, then the top-k kernel on them.  (Selecting inside the router GEMM's
+// epilogue, where one 256 x 256 tile holds all of a token's logits, was measured slower for the
+// DeepSeek-V3-shaped batch: each CU's one tile then runs 256 rows of cross-lane selection steps
+// with eight waves, where this kernel spreads them over thousands of workgroups.)
+int launch_route(const void* A, const void* W_R, const float* bias, int dtype, int64_t T, int64_t d, int32_t E,
+                 int32_t k, int gate, int renorm, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  if (int rc = launch_router_logits(A, W_R, bias, dtype, T, d, E, logits, s)) return rc;
+  return launch_topk(logits, T, E, k, gate, renorm, topk_idx, topk_w, s);
+}
+
 }  // namespace fsm

@@ -142,6 +142,37 @@ def mx_random_codes(rows: int, cols: int, seed: int, device="cpu", scale_lo: int
     return codes, scales
 
 
+def mx_cancelling_codes(rows: int, cols: int, n_out: int, seed: int, device="cpu"):
+    """MXFP8 operands (H [rows, cols], W [n_out, cols]) of a product H W^T whose 128-wide K chunks
+    each hold one pair of large products that cancel exactly: in every chunk H is +v and -v at the
+    chunk's first two columns (E4M3 exponent field 9 or 10, so |v| in [4, 16)) and W has one value
+    there for both (field 6 to 8, positive); every other H element is small (field 1 or 2) with a
+    random sign and every other W element is random (field 6 to 8, random sign).  All block scales
+    are 2^0 (byte 127).  The exact result is then small beside the chunk's largest product, so a
+    product's accumulation error is not hidden by the rounding of its output.
+    Returns ((Hq, Hs), (Wq, Ws)) as uint8 tensors."""
+    g = _gen(seed, "cpu")
+
+    def field(lo, hi, shape):
+        return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32)
+
+    def code(sign, exp, man):
+        return (sign << 7) | (exp << 3) | man
+
+    Hq = code(field(0, 1, (rows, cols)), field(1, 2, (rows, cols)), field(0, 7, (rows, cols)))
+    Wq = code(field(0, 1, (n_out, cols)), field(6, 8, (n_out, cols)), field(0, 7, (n_out, cols)))
+    for k0 in range(0, cols, 128):
+        big = code(torch.zeros((rows,), dtype=torch.int32), field(9, 10, (rows,)), field(0, 7, (rows,)))
+        Hq[:, k0] = big
+        Hq[:, k0 + 1] = big | 0x80
+        w = code(torch.zeros((n_out,), dtype=torch.int32), field(6, 8, (n_out,)), field(0, 7, (n_out,)))
+        Wq[:, k0] = w
+        Wq[:, k0 + 1] = w
+    Hs = torch.full((rows, cols // 32), 127, dtype=torch.uint8)
+    Ws = torch.full((n_out, cols // 32), 127, dtype=torch.uint8)
+    return ((Hq.to(torch.uint8).to(device), Hs.to(device)), (Wq.to(torch.uint8).to(device), Ws.to(device)))
+
+
 def activations(cfg: MoEConfig, device="cpu", T: Optional[int] = None, layer: int = 0,
                 dtype=None) -> torch.Tensor:
     """Token activations A (or the stack input o_0) [T, d] ~ N(0,1), in the workload dtype."""

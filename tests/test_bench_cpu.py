@@ -86,6 +86,8 @@ def test_route_report_per_layer():
     assert r["frac_mfma_peak"] == pytest.approx(2.0 * c.T * c.d * c.E / (r["ms_per_layer"] * 1e-3) / 1e12
                                                 / bench.PEAK_BF16_TFLOPS, abs=1e-4)
     assert bench.route_report({"topk": {"ms_per_step": 1.0, "launches": 4}}, c) is None
+    fused = bench.route_report({"router_gemm": {"ms_per_step": 2.0, "launches": 4}}, c)   # top-k in the epilogue
+    assert fused["ms_per_layer"] == pytest.approx(2.0 / c.layers)
 
 
 def test_host_cpu_reports_cores():

@@ -18,8 +18,8 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.helpers import to_np
-from tests.mx_bound import check_down, check_end_to_end, check_hidden
+from tests.helpers import report, to_np
+from tests.mx_bound import E_INSTR, check_down, check_end_to_end, check_hidden, instr_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -364,3 +364,42 @@ def test_grouped_mxfp8_down_dsv3_full_size_sampled(ops):
         rows = np.array(list(range(a, min(a + 6, b))) + list(range(max(a, b - 6), b)))
         check_down(to_np(Y[rows]), (Hq[0][rows].cpu().numpy(), Hq[1][rows].cpu().numpy()),
                    (W3q[0][e].cpu().numpy(), W3q[1][e].cpu().numpy()), f"expert {e}")
+
+
+# =================================================================================================
+# the scaled fp8 instruction's accumulation error: the measurement behind E_INSTR (tests/mx_bound.py)
+# =================================================================================================
+@pytest.mark.parametrize("c", [128, 2048, 7168], ids=["one-instruction", "chain-16", "chain-56"])
+@pytest.mark.parametrize("kind", ["random-codes", "cancelling-pairs"])
+def test_mxfp8_instruction_error_measured(ops, c, kind):
+    """The second product with one group on operands drawn by the test (c = 128: each output is one
+    instruction's result; 2048 and 7168: chains of 16 and 56 into one fp32 accumulator).  Per
+    output, the error beyond Y's own bf16 rounding (2^-8 |ref|), over the sum across its 128-wide K
+    chunks of 2^floor(log2 max(largest |product|, |partial sum|)), is the instruction's error in the
+    unit the MXFP8 bars use; its maximum is reported and must not exceed E_INSTR.  Random codes
+    are what the bars meet in the products; the cancelling pairs leave small results beside large
+    products, so that the output's rounding does not hide the instruction's error."""
+    N, d = 256, 256
+    seed = mi.seed_for(93, c, 0 if kind == "random-codes" else 1)
+    if kind == "random-codes":
+        Hq = mi.mx_random_codes(N, c, seed + 1, DEV)
+        W3q = mi.mx_random_codes(d, c, seed + 2, DEV)
+    else:
+        Hq, W3q = mi.mx_cancelling_codes(N, c, d, seed, DEV)
+    Y = torch.full((N, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    off = torch.tensor([0, N], dtype=torch.int32, device=DEV)
+    ops.moe_grouped_mxfp8_down(Hq, off, (W3q[0].view(1, d, c), W3q[1].view(1, d, c // 32)), Y)
+    _sync()
+    Hh = (Hq[0].cpu().numpy(), Hq[1].cpu().numpy())
+    Wh = (W3q[0].cpu().numpy(), W3q[1].cpu().numpy())
+    ref = mx.mx_matmul(Hh, Wh)
+    unit = instr_bound(mx.mx_dequantize(*Hh), mx.mx_dequantize(*Wh)) / E_INSTR
+    err = np.abs(to_np(Y).astype(np.float64) - ref)
+    beyond = np.maximum(err - 2.0 ** -8 * np.abs(ref), 0.0)
+    e_meas = float((beyond / unit).max())
+    hidden = float((2.0 ** -8 * np.abs(ref) / unit).mean())
+    report(f"fp8 instruction error, {kind}, K = {c}", e_instr_measured=e_meas, e_instr_bar=E_INSTR,
+           bf16_rounding_over_unit_mean=hidden)
+    if kind == "cancelling-pairs":   # the construction makes the instruction's error visible
+        assert hidden < 0.25 * E_INSTR
+    assert e_meas <= E_INSTR, f"measured {e_meas:.3e} = 2^{np.log2(max(e_meas, 1e-300)):.2f} > E_INSTR"

@@ -128,6 +128,37 @@ def test_router_logits(ops, name):
     check_topk_property(to_np(logits), idx.cpu().numpy())
 
 
+@pytest.mark.parametrize("T,E,k,gate,renorm,bias", [(65536 + 77, 256, 8, "sigmoid", True, False),
+                                                    (66000, 128, 8, "softmax", True, True),
+                                                    (65600, 64, 6, "softmax", False, False),
+                                                    (65536, 200, 5, "softmax", True, True),
+                                                    (65536, 16, 1, "sigmoid", False, False)])
+def test_route_equals_topk_of_its_logits(ops, T, E, k, gate, renorm, bias):
+    """moe_route at batch sizes that run the 256-row router tiles: its ids and weights equal, bit for
+    bit, those of the logits-input call on the logits it wrote (so every bit-exact top-k test covers
+    this path); the logits match the oracle on sampled rows; the selection follows the oracle's rule
+    on them; a ragged last tile and E below the tile width are covered."""
+    d = 256
+    seed = mi.seed_for(92, T, E, k)
+    A = mi.normal((T, d), 1.0, seed, DEV, torch.bfloat16)
+    W_R = mi.normal((E, d), 0.1, seed + 1, DEV, torch.bfloat16)
+    b = mi.normal((E,), 1.0, seed + 2, DEV) if bias else None
+    logits = torch.full((T, E), float("nan"), dtype=torch.float32, device=DEV)
+    idx = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    ops.moe_route(A, W_R, k, gate, renorm, logits, idx, w, bias=b)
+    idx2 = torch.full_like(idx, -1)
+    w2 = torch.full_like(w, float("nan"))
+    ops.moe_route_from_logits(logits, k, gate, renorm, idx2, w2)
+    _sync()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    rows = mi.sample_rows(T, 512, seed + 3)
+    ref = oracle.router_logits(to_np(A[rows.to(DEV)]), to_np(W_R), None if b is None else to_np(b))
+    assert max_rel_err(to_np(logits[rows.to(DEV)]), ref) < 1e-5
+    np.testing.assert_array_equal(idx[rows.to(DEV)].cpu().numpy(), oracle.select_topk(to_np(logits[rows.to(DEV)]), k))
+
+
 def check_topk_property(L, idx):
     T, E = L.shape
     k = idx.shape[1]
