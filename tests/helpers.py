@@ -7,6 +7,8 @@ import os
 import numpy as np
 import torch
 
+import moe_inputs as mi
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # Tolerances of the parity bar: bf16 paths (fp32 accumulation) max|err| <= 2e-2 * max|ref|; fp32
@@ -23,6 +25,36 @@ NEAR_TIE = 1e-4  # tokens whose k-th and (k+1)-th logits differ by less are excl
 # A CPU emulation of the kernels' arithmetic (fp32 sums per 32-wide K step, bf16 H and Y) at the
 # DeepSeek-V3 and V2-Lite expert shapes uses at most 0.74 of it; a 1% error on a tile fails it.
 MIRROR_BETA = 2.0 ** -8
+
+# The backward pass's FarSkip stack test (tests/test_gpu_backward.py): its shapes, its modes and
+# masks, and the top-k margin its inputs keep at every layer.  Each side runs its own forward, so the
+# layer inputs drift apart by bf16 rounding flips; tests/test_tie_margin_cpu.py measures that drift
+# (kernel arithmetic emulated against the store-mirrored oracle, these shapes and cases): the logits
+# move by at most 1.1e-2 by the third layer, so two logits closer than 2.2e-2 may swap order; the
+# margin is 0.05, more than twice that.
+BWD_STACK = {"T": 256, "d": 128, "E": 8, "k": 2, "c": 128, "cs": 128, "L": 3, "gate": "softmax", "renorm": True}
+BWD_STACK_CASES = [("none", None), ("partial", None), ("outdated", None), ("partial", [1, 0, 1]),
+                   ("outdated", [0, 1, 1])]
+BWD_TIE_MARGIN = 0.05
+
+
+def make_layer(seed, T, d, E, c, cs, bias, empty=()):
+    """Seeded bf16 input A, weights W and output gradient dOut of one sublayer for the backward
+    tests (weights N(0, 1/fan_in); a router bias N(0, 0.5^2) when asked, -1e4 for `empty` experts)."""
+    g = lambda i, shape, std: mi.normal(shape, std, mi.seed_for(89, seed, i), "cpu", torch.bfloat16)
+    W = {"W_R": g(1, (E, d), d ** -0.5), "W1": g(2, (E, c, d), d ** -0.5), "W2": g(3, (E, c, d), d ** -0.5),
+         "W3": g(4, (E, d, c), c ** -0.5)}
+    W["bias"] = mi.normal((E,), 0.5, mi.seed_for(89, seed, 5)) if bias else None
+    if W["bias"] is not None:
+        for e in empty:
+            W["bias"][e] = -1e4
+    if cs:
+        W["Ws1"], W["Ws2"] = g(6, (cs, d), d ** -0.5), g(7, (cs, d), d ** -0.5)
+        W["Ws3"] = g(8, (d, cs), cs ** -0.5)
+    A = g(9, (T, d), 1.0)
+    dOut = mi.normal((T, d), 1.0, mi.seed_for(89, seed, 10))
+    return A, W, dOut
+
 
 # achieved errors of every float comparison, printed at the end of the session (conftest.py)
 RESULTS = []

@@ -13,7 +13,7 @@ import torch
 import moe_inputs as mi
 import oracle
 import oracle.moe_backward as ob
-from tests.helpers import assert_parity, to_np
+from tests.helpers import BWD_STACK, BWD_STACK_CASES, BWD_TIE_MARGIN, assert_parity, make_layer, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -25,22 +25,6 @@ BF = torch.bfloat16
 def ops():
     from mixture_experts_layer_sum_amd import ops as _ops
     return _ops
-
-
-def make_layer(seed, T, d, E, c, cs, bias, empty=()):
-    g = lambda i, shape, std: mi.normal(shape, std, mi.seed_for(89, seed, i), "cpu", BF)
-    W = {"W_R": g(1, (E, d), d ** -0.5), "W1": g(2, (E, c, d), d ** -0.5), "W2": g(3, (E, c, d), d ** -0.5),
-         "W3": g(4, (E, d, c), c ** -0.5)}
-    W["bias"] = mi.normal((E,), 0.5, mi.seed_for(89, seed, 5)) if bias else None
-    if W["bias"] is not None:
-        for e in empty:
-            W["bias"][e] = -1e4
-    if cs:
-        W["Ws1"], W["Ws2"] = g(6, (cs, d), d ** -0.5), g(7, (cs, d), d ** -0.5)
-        W["Ws3"] = g(8, (d, cs), cs ** -0.5)
-    A = g(9, (T, d), 1.0)
-    dOut = mi.normal((T, d), 1.0, mi.seed_for(89, seed, 10))
-    return A, W, dOut
 
 
 def run_backward(ops, A, W, dOut, k, gate, renorm, cs, with_dbias=True):
@@ -209,9 +193,11 @@ def test_layer_backward_dsv3_full_size_sampled(ops):
 # =================================================================================================
 # FarSkip stack backward
 # =================================================================================================
-def clean_stack_input(o0, layers64, k, gate, renorm, mode, mask, cs, delta=0.05, seed=0):
+def clean_stack_input(o0, layers64, k, gate, renorm, mode, mask, cs, delta=BWD_TIE_MARGIN, seed=0):
     """Redraw the token rows whose top-k choice is within delta of a tie at any layer of the
-    oracle's forward (tokens are independent through the stack), so that both sides choose alike."""
+    oracle's forward (tokens are independent through the stack), so that both sides choose alike:
+    every weight gradient sums over all tokens, so one token routed differently would move it.
+    delta is derived in tests/test_tie_margin_cpu.py."""
     o0 = o0.copy()
     rng = np.random.default_rng(seed)
     for _ in range(30):
@@ -229,11 +215,10 @@ def clean_stack_input(o0, layers64, k, gate, renorm, mode, mask, cs, delta=0.05,
     raise AssertionError("could not draw a stack input without near-ties")
 
 
-@pytest.mark.parametrize("mode,mask", [("none", None), ("partial", None), ("outdated", None),
-                                       ("partial", [1, 0, 1]), ("outdated", [0, 1, 1])])
+@pytest.mark.parametrize("mode,mask", BWD_STACK_CASES)
 def test_stack_backward_matches_oracle(ops, mode, mask):
-    T, d, E, k, c, cs, L = 256, 128, 8, 2, 128, 128, 3
-    gate, renorm = "softmax", True
+    T, d, E, k, c, cs, L = (BWD_STACK[key] for key in ("T", "d", "E", "k", "c", "cs", "L"))
+    gate, renorm = BWD_STACK["gate"], BWD_STACK["renorm"]
     layers = [make_layer(mi.seed_for(87, j, 1), T, d, E, c, cs, bias=(j == 1))[1] for j in range(L)]
     layers64 = [oracle_weights64(W) for W in layers]
     o0 = clean_stack_input(mi.normal((T, d), 1.0, mi.seed_for(87, 0, 9)).numpy().astype(np.float64), layers64, k, gate,

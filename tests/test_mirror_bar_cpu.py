@@ -12,28 +12,9 @@ import pytest
 
 import oracle
 from tests.helpers import assert_mirror, bf16_ulp, combine_bound, mirror_bound
+from tests.kernel_emulation import bf, emulated_mlp
 
 rnd = oracle.round_to_bf16
-
-
-def bf(x):
-    return rnd(np.asarray(x, np.float32)).astype(np.float32)
-
-
-def acc32(X, W, step=32):
-    """X [n, K] @ W[m, K]^T as an fp32 running sum of 32-wide K steps (each step's products are
-    exact in fp32 for bf16 operands)."""
-    out = np.zeros((X.shape[0], W.shape[0]), np.float32)
-    for k0 in range(0, X.shape[1], step):
-        part = X[:, k0:k0 + step].astype(np.float64) @ W[:, k0:k0 + step].astype(np.float64).T
-        out = (out + part.astype(np.float32)).astype(np.float32)
-    return out
-
-
-def emulated_mlp(X, W1, W2, W3):
-    U, G = acc32(X, W1), acc32(X, W2)
-    H = bf(U * (G / (np.float32(1) + np.exp(-G).astype(np.float32))))
-    return bf(acc32(H, W3)).astype(np.float64)
 
 
 def weights(rng, d, c, std=0.02):
