@@ -268,10 +268,19 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
         return e0.elapsed_time(e1) / it
 
     ms_copy = timed(lambda: b.copy_(a), 5)
+    ms_fill = timed(lambda: b.fill_(1.0), 5)
     ms_mm = timed(lambda: torch.matmul(m, n), 5)
+    # the library's register-only MFMA launch (1024 workgroups of 8 waves, no memory traffic)
+    probe, iters = torch.empty(1024 * 512, dtype=torch.float32, device=dev), 10000
+    mfma = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        ms = timed(lambda: ops.mfma_ceiling(shape, probe, iters), 3)
+        mfma[name] = round(1024 * 8 * iters * 262144 / (ms * 1e-3) / 1e12, 1)
     out["ceilings"] = {
         "device_copy_GBps": round(2 * a.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
+        "device_fill_GBps": round(a.numel() * 4 / (ms_fill * 1e-3) / 1e9, 1),
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
+        "mfma_register_only_bf16_TFLOPs": mfma,
     }
     # each kernel against the box's measured ceiling of its kind, beside its fraction of the peak
     for kind, v in out.items():
@@ -279,6 +288,7 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
             continue
         if "tflops" in v and kind != "ep8_share":
             v["frac_of_hipblaslt"] = round(v["tflops"] / out["ceilings"]["hipblaslt_bf16_8192cubed_TFLOPs"], 4)
+            v["frac_of_mfma_ceiling"] = round(v["tflops"] / mfma["16x16x32"], 4)
         if "gbs" in v:
             v["frac_of_device_copy"] = round(v["gbs"] / out["ceilings"]["device_copy_GBps"], 4)
     del a, b, m, n
@@ -898,6 +908,19 @@ def main():
                    "what": "median step times, profiling off, two-stream and one-stream steps alternated; "
                            "timing_events_cost_frac compares the timed (event-bracketed) steps with them"}
         log(f"interleaved: two streams {med['two_streams']:.2f} ms, one stream {med['one_stream']:.2f} ms")
+        # one profiled one-stream step: the share of its wall time in which a kernel runs (what is
+        # left idle is all a second stream could fill without sharing a CU with the first)
+        ops.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step(main_s)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        ops.profile_enable(False)
+        _, one = ops.profile_collect_intervals()
+        busy_ms = stream_overlap(one, main_s.cuda_stream)["main_busy_ms"]
+        compare["one_stream_kernel_busy_frac"] = round(busy_ms / wall_ms, 4)
+        compare["one_stream_idle_ms"] = round(wall_ms - busy_ms, 3)
 
     kernels = kernel_report(prof, c, args.steps, {"combine": fused_input_bytes(c, args.mode)})
     g = kernels.get("gemm_gate_up", {})

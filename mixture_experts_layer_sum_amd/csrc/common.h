@@ -93,6 +93,8 @@ int launch_route(const void* A, const void* W_R, const float* bias, int dtype, i
                  int32_t k, int gate, int renorm, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
 size_t permute_ws_bytes(int64_t T, int32_t E, int32_t k);
 // moe_permute with its count arrays in the library's fixed device scratch (no workspace argument)
+// register-only MFMA throughput launch (diag.hip): shape 0 = 16x16x32, 1 = 32x32x16 bf16
+int launch_mfma_ceiling(int shape, int iters, int blocks, float* out, hipStream_t s);
 int launch_permute_noalloc(const void* A, int dtype, int64_t T, int64_t d, int32_t E, int32_t k,
                            const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_src, int32_t* dest_row,
                            void* A_perm, hipStream_t s);

@@ -351,6 +351,12 @@ def farskip_stack_backward(layers: Sequence[dict], cfg: StackCfg, mode, o0, dOL,
                                      ws.numel(), _s(stream)))
 
 
+def mfma_ceiling(shape: int, out, iters: int, stream=None) -> None:
+    """Diagnostic: one register-only MFMA launch (shape 0 = 16x16x32, 1 = 32x32x16 bf16) of
+    out.numel() // 512 workgroups; FLOP = workgroups * 8 * iters * 262144."""
+    check("moe_mfma_ceiling", lib.moe_mfma_ceiling(int(shape), int(iters), out.numel() // 512, _p(out), _s(stream)))
+
+
 def profile_enable(on: bool = True) -> None:
     """Start/stop timing every library kernel launch with HIP events on its own stream."""
     check("moe_profile_enable", lib.moe_profile_enable(int(bool(on))))

@@ -395,3 +395,13 @@ def test_attn_stack_argument_errors():
     bad[4] = 96
     bad[9] = lib.farskip_attn_moe_stack_workspace_bytes(ctypes.byref(c_bf), 96)
     err(f(*bad), L.MOE_ERR_UNSUPPORTED, "c_attn")
+
+
+def test_mfma_ceiling_argument_errors():
+    """The register-only MFMA diagnostic checks its arguments on the host before any launch."""
+    f = lib.moe_mfma_ceiling
+    err(f(2, 10, 4, BAD, None), L.MOE_ERR_INVALID_ARG, "shape")
+    err(f(-1, 10, 4, BAD, None), L.MOE_ERR_INVALID_ARG, "shape")
+    err(f(0, 0, 4, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(1, 10, 0, BAD, None), L.MOE_ERR_INVALID_ARG)
+    err(f(0, 10, 4, None, None), L.MOE_ERR_INVALID_ARG, "out")
