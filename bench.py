@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--decode", type=int, default=1,
                    help="after the steps, time a 1024-token decode step through the same layers; 0 = skip")
     p.add_argument("--standalone", type=int, default=1,
-                   help="after the steps, time the layer-0 calls one at a time and two ceilings; 0 = skip")
+                   help="after the steps, time the layer-0 calls one at a time and the box's ceilings; 0 = skip")
     p.add_argument("--mxfp8", type=int, default=1,
                    help="after the steps, time the layer-0 routed experts with MXFP8 operands; 0 = skip")
     p.add_argument("--mxfp8-stack", type=int, default=1,
@@ -209,11 +209,11 @@ def ep_share(c, W, A_perm, off, Y, gws, reps: int, ep: int = 8) -> dict:
     return row
 
 
-def standalone(c, layers, o0, reps: int = 3) -> dict:
+def standalone(c, layers, o0, reps: int = 20) -> dict:
     """After the timed steps: the layer-0 calls one at a time on the whole GPU (the stack shares it
-    between two streams), including the explicit dispatch row copy that the stack folds into the
-    gate/up GEMM, and two measured ceilings of the box (a device copy and a large hipBLASLt
-    product through torch)."""
+    between two streams), `reps` times each, including the explicit dispatch row copy that the stack
+    folds into the gate/up GEMM; then the measured ceilings of the box (a device copy, a fill, a
+    large hipBLASLt product through torch, and the library's register-only MFMA launch)."""
     import torch
 
     from mixture_experts_layer_sum_amd import ops
@@ -295,7 +295,7 @@ def standalone(c, layers, o0, reps: int = 3) -> dict:
     return out
 
 
-def mxfp8(c, layers, o0, reps: int = 3) -> dict:
+def mxfp8(c, layers, o0, reps: int = 20) -> dict:
     """The layer-0 routed experts with MXFP8 operands: the weights quantised once (as at load
     time, untimed), then per repetition the token rows quantised and the gathered grouped product
     on them (fp8 MFMA against the 5 PFLOP/s dense fp8 peak)."""
