@@ -60,11 +60,13 @@ def test_topk_bitexact_config(ops, name):
     np.testing.assert_allclose(w, ref_w, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (3, 3), (8, 2), (64, 6), (65, 7), (128, 8), (200, 5), (256, 8),
-                                 (512, 16), (1024, 32)])
+@pytest.mark.parametrize("E,k", [(1, 1), (3, 3), (8, 2), (16, 16), (64, 6), (65, 7), (128, 8), (200, 5), (256, 8),
+                                 (256, 16), (257, 9), (64, 17), (512, 16), (1024, 32)])
 @pytest.mark.parametrize("gate,renorm", [("softmax", False), ("softmax", True), ("sigmoid", True)])
 def test_topk_ties_and_shapes(ops, E, k, gate, renorm):
-    # logits snapped to multiples of 0.5 so that exact ties are everywhere
+    # logits snapped to multiples of 0.5 so that exact ties are everywhere; the shapes straddle the
+    # two selection kernels (sixteen lanes per token up to E = 256 and k = 16, a wavefront beyond) and
+    # T = 777 leaves a partial block of tokens
     L = mi.logits(777, E, mi.seed_for(99, E, mi.T_LOGITS, k), quantum=0.5)
     idx, w = run_topk(ops, L, k, gate, renorm)
     ref_idx = oracle.select_topk(L.numpy(), k)
