@@ -239,7 +239,7 @@ def test_stack_dsv3_full_size_sampled(ops, name):
     The stack output equals the composed single calls bitwise.  Then, at every layer, 256 seeded
     tokens plus tokens added until every expert of that layer is reached are checked against the
     oracle on the GPU's own layer inputs (teacher-forced): routing, S + R and the next input, each
-    against the spec bar and against the store-mirrored oracle's element-wise bar."""
+    against the max|err| <= 2e-2 max|ref| bar and against the store-mirrored oracle's element-wise bar."""
     c = mi.BY_NAME[name]
     layers, o0 = make_stack(c)
     oL = run_stack(ops, c, layers, o0, "partial")
