@@ -112,9 +112,13 @@ def test_layer_backward_is_deterministic(ops):
 
 def test_layer_backward_dsv3_full_size_sampled(ops):
     """The DeepSeek-V3-shaped layer at full size (65536 tokens, 256 experts, top-8 sigmoid
-    renormalised, d = 7168, c = 2048, one 2048-wide shared expert): dA of 12 sampled tokens and the
-    weight gradients of two sampled experts against the oracle, composed from its per-token and
-    per-expert steps (the selection is checked for every token)."""
+    renormalised, d = 7168, c = 2048, one 2048-wide shared expert): dA of 256 sampled tokens (their
+    2048 slots reach nearly every expert) and the weight gradients of eight experts over all of their
+    rows (the first and the last, the largest and the smallest group, four seeded others) against
+    the oracle, composed from its per-token and per-expert steps.  The oracle runs expert-major: each
+    expert the samples need is fetched once, its contributions to every sampled token routed to it
+    are added, and its weight gradients are checked if it is one of the eight.  The selection is
+    checked for every token."""
     cfg = {c.name: c for c in mi.CONFIGS}["dsv3-stack"]
     T, d, E, k, c, cs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.c, cfg.shared_width
     W = mi.layer_weights(cfg, 0, DEV)
@@ -135,7 +139,6 @@ def test_layer_backward_dsv3_full_size_sampled(ops):
     ops.moe_permute(idx, E, off, src, dest)
     Y = torch.empty((T * k, d), dtype=BF, device=DEV)
     ops.moe_grouped_swiglu_gathered(A, src, k, off, W["W1"], W["W2"], W["W3"], Y)
-    sel = [0, 255]
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=DEV)
     grads = {"dA": f32(T, d), "dW_R": f32(E, d), "dW1": f32(E, c, d), "dW2": f32(E, c, d), "dW3": f32(E, d, c),
              "dWs1": f32(cs, d), "dWs2": f32(cs, d), "dWs3": f32(d, cs)}
@@ -148,44 +151,38 @@ def test_layer_backward_dsv3_full_size_sampled(ops):
     ref_w = oracle.gate_weights(L, ref_idx, cfg.gate, cfg.renormalize)
     dOut64 = dOut.cpu().numpy().astype(np.float64)
     st = oracle.round_to_bf16
-    keep = {}
 
-    def expert(key, e):   # the sampled experts' matrices are kept, the others fetched per use
-        if (key, e) in keep:
-            return keep[(key, e)]
-        m = to_np(W[key][e]).astype(np.float64)
-        if e in sel:
-            keep[(key, e)] = m
-        return m
-
+    counts = np.bincount(ref_idx.ravel(), minlength=E)
+    others = np.random.default_rng(mi.seed_for(cfg.cfg_id, 0, mi.T_SAMPLE, 1, 31)).permutation(E)
+    sel = {0, E - 1, int(np.argmax(counts)), int(np.argmin(counts))}
+    for e in others:
+        if len(sel) == 8:
+            break
+        sel.add(int(e))
+    rows_t = mi.sample_rows(T, 256, mi.seed_for(cfg.cfg_id, 0, mi.T_SAMPLE, 0, 31)).numpy()
+    n = len(rows_t)
+    x_s, dOut_s, idx_s = A64[rows_t], dOut64[rows_t], ref_idx[rows_t]
+    dX = np.zeros((n, d))          # the routed experts' input gradients of the sampled tokens
+    dw = np.zeros((n, k))          # dLoss / d(gate weight) per sampled slot
+    for e in sorted(set(idx_s.ravel().tolist()) | sel):
+        W1e, W2e, W3e = (to_np(W[key][e]).astype(np.float64) for key in ("W1", "W2", "W3"))
+        tt, ii = np.nonzero(idx_s == e)       # a token lists an expert at most once
+        if len(tt):
+            y = oracle.mlp(x_s[tt], W1e, W2e, W3e, store=st)
+            dw[tt, ii] = np.sum(dOut_s[tt] * y, axis=1)
+            dX[tt] += ob.mlp_backward(x_s[tt], W1e, W2e, W3e, ref_w[rows_t[tt], ii][:, None] * dOut_s[tt],
+                                      store=st)[0]
+        if e in sel:   # the weight gradients over all of the expert's rows
+            tok, slot = np.nonzero(ref_idx == e)
+            dY = ref_w[tok, slot][:, None] * dOut64[tok]
+            _, dW1, dW2, dW3 = ob.mlp_backward(A64[tok], W1e, W2e, W3e, dY, store=st)
+            for key, ref in (("dW1", dW1), ("dW2", dW2), ("dW3", dW3)):
+                assert_parity(grads[key][e].cpu().numpy(), ref, BF, f"{key} of expert {e} ({counts[e]} rows)")
     Ws = [to_np(W[key]).astype(np.float64) for key in ("Ws1", "Ws2", "Ws3")]
-    # sampled tokens: dA[t] = sum over slots of the expert's dX + the router's part + the shared part
-    rows_t = mi.sample_rows(T, 12, mi.seed_for(cfg.cfg_id, 0, mi.T_SAMPLE, 0, 31)).numpy()
+    dL = ob.gate_backward(L[rows_t], idx_s, dw, cfg.gate, cfg.renormalize)
+    ref_dA = dX + ob.router_backward(x_s, WR64, dL, store=st)[0] + ob.mlp_backward(x_s, *Ws, dOut_s, store=st)[0]
     got_dA = grads["dA"][torch.from_numpy(rows_t).to(DEV)].cpu().numpy()
-    ref_dA = np.zeros((len(rows_t), d))
-    for n, t in enumerate(rows_t):
-        x = A64[t:t + 1]
-        dw = np.zeros((1, k))
-        dX = np.zeros((1, d))
-        for i in range(k):
-            e = int(ref_idx[t, i])
-            W1e, W2e, W3e = expert("W1", e), expert("W2", e), expert("W3", e)
-            y = oracle.mlp(x, W1e, W2e, W3e, store=st)
-            dw[0, i] = np.sum(dOut64[t] * y[0])
-            dX += ob.mlp_backward(x, W1e, W2e, W3e, ref_w[t, i] * dOut64[t:t + 1], store=st)[0]
-        dL = ob.gate_backward(L[t:t + 1], ref_idx[t:t + 1], dw, cfg.gate, cfg.renormalize)
-        dA_r = ob.router_backward(x, WR64, dL, store=st)[0]
-        dA_s = ob.mlp_backward(x, Ws[0], Ws[1], Ws[2], dOut64[t:t + 1], store=st)[0]
-        ref_dA[n] = (dX + dA_r + dA_s)[0]
-    assert_parity(got_dA, ref_dA, BF, "dA of sampled tokens")
-    # sampled experts: the weight gradients over all of the expert's rows
-    for e in sel:
-        tok, slot = np.nonzero(ref_idx == e)
-        X = A64[tok]
-        dY = ref_w[tok, slot][:, None] * dOut64[tok]
-        _, dW1, dW2, dW3 = ob.mlp_backward(X, expert("W1", e), expert("W2", e), expert("W3", e), dY, store=st)
-        for key, ref in (("dW1", dW1), ("dW2", dW2), ("dW3", dW3)):
-            assert_parity(grads[key][e].cpu().numpy(), ref, BF, f"{key} of expert {e}")
+    assert_parity(got_dA, ref_dA, BF, f"dA of {n} sampled tokens ({len(set(idx_s.ravel().tolist()))} experts)")
     for key in ("dA", "dW_R", "dWs1", "dWs2", "dWs3"):
         assert torch.isfinite(grads[key]).all().item(), key
 
