@@ -308,9 +308,10 @@ DSV3 = {c.name: c for c in mi.CONFIGS}["dsv3-stack"]
 def test_grouped_mxfp8_dsv3_full_size_sampled(ops):
     """The DeepSeek-V3-shaped layer at full size in the bench's launch configuration: 65536 tokens
     x 8 slots over 256 experts (d = 7168, c = 2048), activations quantised and gathered through the
-    permutation.  Sampled token rows quantise bit-exactly; for rows of three experts H is checked
-    against the oracle (weights quantised by the oracle from the same bf16 values) and the whole
-    MLP's Y to its mean bar; the fused call equals the two calls bit for bit."""
+    permutation.  Sampled token rows quantise bit-exactly; for the first and last rows of eight
+    experts (the first and the last, the largest and the smallest group, four seeded others) H is
+    checked against the oracle (weights quantised by the oracle from the same bf16 values) and the
+    whole MLP's Y to its mean bar; the fused call equals the two calls bit for bit."""
     cfg = DSV3
     T, E, k, d, c = cfg.T, cfg.E, cfg.k, cfg.d, cfg.c
     W = mi.layer_weights(cfg, 0, DEV)
@@ -331,7 +332,13 @@ def test_grouped_mxfp8_dsv3_full_size_sampled(ops):
     ref = mx.mx_quantize(A_np[rows_t])
     np.testing.assert_array_equal(Aq[0][rows_t].cpu().numpy(), ref[0])
     np.testing.assert_array_equal(Aq[1][rows_t].cpu().numpy(), ref[1])
-    for e in (0, 131, 255):
+    sizes = np.diff(off_np)
+    sel = {0, E - 1, int(np.argmax(sizes)), int(np.argmin(sizes))}
+    for e in np.random.default_rng(mi.seed_for(cfg.cfg_id, 0, mi.T_SAMPLE, 2)).permutation(E):
+        if len(sel) == 8:
+            break
+        sel.add(int(e))
+    for e in sorted(sel):
         a, b = int(off_np[e]), int(off_np[e + 1])
         rows = np.array(list(range(a, min(a + 6, b))) + list(range(max(a, b - 6), b)))
         Wq = []
@@ -347,7 +354,9 @@ def test_grouped_mxfp8_dsv3_full_size_sampled(ops):
 
 def test_grouped_mxfp8_down_dsv3_full_size_sampled(ops):
     """The second product at the DeepSeek-V3 layer's full size (524288 grouped rows over 256
-    experts, c = 2048 -> d = 7168) on random MXFP8 operands; rows of three experts checked."""
+    experts, c = 2048 -> d = 7168) on random MXFP8 operands: the first and the last row of every
+    expert (its first and last M-tile) on 256 sampled output columns, one in each 28-column stripe
+    (so every 256-column N-tile is reached)."""
     cfg = DSV3
     N, E, d, c = cfg.T * cfg.k, cfg.E, cfg.d, cfg.c
     seed = mi.seed_for(cfg.cfg_id, 0, mi.T_MISC, 0, 77)
@@ -359,11 +368,19 @@ def test_grouped_mxfp8_down_dsv3_full_size_sampled(ops):
     Y = torch.empty((N, d), dtype=torch.bfloat16, device=DEV)
     ops.moe_grouped_mxfp8_down(Hq, torch.from_numpy(off).to(DEV), W3q, Y)
     _sync()
-    for e in (0, 77, 255):
+    stripe = d // 256
+    cols = np.arange(0, d, stripe) + np.random.default_rng(seed).integers(0, stripe, size=256)
+    cols_d = torch.from_numpy(cols).to(DEV)
+    checked = 0
+    for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
-        rows = np.array(list(range(a, min(a + 6, b))) + list(range(max(a, b - 6), b)))
-        check_down(to_np(Y[rows]), (Hq[0][rows].cpu().numpy(), Hq[1][rows].cpu().numpy()),
-                   (W3q[0][e].cpu().numpy(), W3q[1][e].cpu().numpy()), f"expert {e}")
+        if b == a:
+            continue
+        rows = np.array(sorted({a, b - 1}))
+        check_down(to_np(Y[rows][:, cols_d]), (Hq[0][rows].cpu().numpy(), Hq[1][rows].cpu().numpy()),
+                   (W3q[0][e][cols_d].cpu().numpy(), W3q[1][e][cols_d].cpu().numpy()), f"expert {e}")
+        checked += 1
+    assert checked == int(np.count_nonzero(np.diff(off)))
 
 
 # =================================================================================================
