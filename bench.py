@@ -89,6 +89,80 @@ def measured_traffic():
     return None
 
 
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "dsv3_stack_memory_pipeline_counters.txt")
+
+
+def measured_l2_hit():
+    """L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) of the routed gate/up and down products from the
+    committed counter summary of the stack, or {} when it was taken with other library sources."""
+    from mixture_experts_layer_sum_amd.profiling import gemm_args, is_routed_gate_up, source_digest
+    if not os.path.exists(COUNTER_PROFILE):
+        return {}
+    lines = open(COUNTER_PROFILE).read().splitlines()
+    digest = next((l.split()[5] for l in lines if l.startswith("# grouped GEMM source digest")), None)
+    if digest != source_digest():
+        return {}
+    out = {}
+    for l in lines:
+        if l.startswith("#") or "TCC_HIT_sum=" not in l or "TCC_MISS_sum=" not in l:
+            continue
+        name = l.split("  n=")[0]
+        a = gemm_args(name)
+        kind = ("gemm_gate_up" if is_routed_gate_up(name)
+                else "gemm_down" if a is not None and len(a) >= 6 and a[4] == 0 and a[5] == 0 else None)
+        if kind is None:
+            continue
+        hit = float(l.split("TCC_HIT_sum=")[1].split()[0])
+        miss = float(l.split("TCC_MISS_sum=")[1].split()[0])
+        out[kind] = hit / (hit + miss)
+    return out
+
+
+def delivery_ceilings(dev, hits: dict, tiles: dict) -> dict:
+    """The library's operand-delivery launch (256 workgroups, 64 KiB stages loaded into LDS as a
+    product's K step loads them, no arithmetic): all runs L2 hits; all from cold regions beyond the
+    memory-side cache (HBM); and, for each routed product, its measured L2 hit rate with the misses
+    from HBM, with one stage in flight (the products' two-stage ring) and with two, and with the
+    misses served by the memory-side cache (one stage in flight).  `tiles` gives
+    each product's 64 KiB operand stages per launch, so its K loop's operand rate can be read
+    against the probe's at its own hit rate."""
+    import torch
+
+    from mixture_experts_layer_sum_amd import ops
+    MB, blocks, cold = 1 << 20, 256, 7 << 20
+    buf = torch.ones(16 * MB + blocks * cold, dtype=torch.uint8, device=dev)
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+
+    def tbps(hot, infl, iters, cold_bytes=cold):
+        ops.delivery_probe(hot, cold_bytes, iters, infl, buf, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops.delivery_probe(hot, cold_bytes, iters, infl, buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        return round(blocks * iters * 65536 / (ms * 1e-3) / 1e12, 2), round(ms * 1e3 / iters, 3)
+
+    res = {"what": "TB/s into LDS over 256 CUs and us per 64 KiB stage per CU; misses from HBM unless "
+                   "named memside"}
+    for infl in (1, 2):
+        res[f"all_hit_in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(100, infl, 2000)))
+        res[f"all_hbm_in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(0, infl, 100)))
+    for kind, hit in hits.items():
+        hot = int(round(100 * hit))
+        row = {"l2_hit_pct": hot}
+        for infl in (1, 2):
+            row[f"in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(hot, infl, 400)))
+        # the same hit rate with every miss served by the memory-side cache (512 KiB cold regions)
+        row["memside_in_flight_1"] = dict(zip(("TBps", "us_per_stage"), tbps(hot, 1, 400, 512 << 10)))
+        if kind in tiles:
+            row["operand_stages_per_launch"] = tiles[kind]
+        res[kind] = row
+    del buf, out
+    return res
+
+
 def stream_overlap(launches, main_stream) -> dict:
     """Cross-stream overlap of the timed stack steps from the per-launch HIP-event intervals: M = the
     main stream's busy time (permutations, routed GEMMs), S = the side stream's (routers, top-k,
@@ -249,6 +323,10 @@ def standalone(c, layers, o0, reps: int = 20) -> dict:
     rep_ = kernel_report(prof, c, reps)
     out = {k_: rep_[k_] for k_ in ("permute_rows", "gemm_gate_up", "gemm_down", "combine") if k_ in rep_}
     out["ep8_share"] = ep_share(c, W, A_perm, off, Y, gws, reps)
+    # 64 KiB operand stages per launch of each routed product: its live 256 x 256 tiles times its K steps
+    rows_e = (off[1:] - off[:-1]).cpu()
+    mt = int(((rows_e + 255) // 256).sum().item())
+    stages = {"gemm_gate_up": mt * (2 * cc // 256) * (d // 64), "gemm_down": mt * (d // 256) * (cc // 64)}
     del A_perm, Y, gws, pws, logits
     # ceilings: plain device-to-device copy and a large bf16 product (hipBLASLt through torch)
     a = torch.empty(2**30 // 4 * 4, dtype=torch.float32, device=dev)
@@ -276,11 +354,16 @@ def standalone(c, layers, o0, reps: int = 20) -> dict:
     for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
         ms = timed(lambda: ops.mfma_ceiling(shape, probe, iters), 3)
         mfma[name] = round(1024 * 8 * iters * 262144 / (ms * 1e-3) / 1e12, 1)
+    nbytes = a.numel() * 4
+    del a, b, m, n
+    # the committed counter summary holds the DSV3 stack's products; other workloads get the bounds only
+    delivery = delivery_ceilings(dev, measured_l2_hit() if c.name == "dsv3-stack" else {}, stages)
     out["ceilings"] = {
-        "device_copy_GBps": round(2 * a.numel() * 4 / (ms_copy * 1e-3) / 1e9, 1),
-        "device_fill_GBps": round(a.numel() * 4 / (ms_fill * 1e-3) / 1e9, 1),
+        "device_copy_GBps": round(2 * nbytes / (ms_copy * 1e-3) / 1e9, 1),
+        "device_fill_GBps": round(nbytes / (ms_fill * 1e-3) / 1e9, 1),
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
         "mfma_register_only_bf16_TFLOPs": mfma,
+        "operand_delivery": delivery,
     }
     # each kernel against the box's measured ceiling of its kind, beside its fraction of the peak
     for kind, v in out.items():
@@ -291,7 +374,13 @@ def standalone(c, layers, o0, reps: int = 20) -> dict:
             v["frac_of_mfma_ceiling"] = round(v["tflops"] / mfma["16x16x32"], 4)
         if "gbs" in v:
             v["frac_of_device_copy"] = round(v["gbs"] / out["ceilings"]["device_copy_GBps"], 4)
-    del a, b, m, n
+    # each routed product's operand rate (its 64 KiB stages over the launch) against the probe's at
+    # the product's own L2 hit rate, one stage in flight as in its ring
+    for kind in ("gemm_gate_up", "gemm_down"):
+        if kind in out and kind in delivery and "avg_ms" in out[kind]:
+            rate = stages[kind] * 65536 / (out[kind]["avg_ms"] * 1e-3) / 1e12
+            out[kind]["operand_TBps"] = round(rate, 2)
+            out[kind]["frac_of_delivery_ceiling"] = round(rate / delivery[kind]["in_flight_1"]["TBps"], 4)
     return out
 
 

@@ -577,6 +577,29 @@ int moe_profile_collect_intervals(moe_kernel_time_t* out, moe_kernel_interval_t*
  */
 int moe_mfma_ceiling(int shape, int32_t iters, int32_t blocks, float* out, void* stream);
 
+/*
+ * Diagnostic, not part of the method: how fast a product's operand stream can reach LDS, the
+ * ceiling its K steps can be read against once the L2 hit rate is known.  Launches `blocks`
+ * workgroups of 512 threads on `stream` (each takes 128 KB of LDS, so one runs per CU); each runs
+ * `iters` stages of 64 KiB, loaded as a bf16 product's K step loads its two operand tiles: 64 runs
+ * of 1 KiB per stage, one 16-byte direct-to-LDS load per lane, then a wait and a barrier; no
+ * arithmetic.  Run r of stage i reads the hot window (the buffer's first MiB, which stays in
+ * every XCD's L2) when (7 r + 3 i) mod 100 < hot_pct, else the workgroup's own cold region
+ * (cold_bytes at offset 16 MiB + block * cold_bytes, swept in order: beyond the memory-side cache
+ * when blocks * cold_bytes is large, inside it when small).  Exactly hot_pct of every 100 stages'
+ * runs are hot.
+ *   in_flight  1: a stage is requested once the previous one has landed (the two-stage ring of the
+ *              products: one stage loads while the other is read); 2: two stages in flight
+ *   buf        device buffer of buf_bytes >= 16 MiB + blocks * cold_bytes (caller-owned; only read)
+ *   out        device buffer of blocks * 512 floats: each thread's sum of one byte of each LDS stage
+ * Bytes of one launch = blocks * iters * 65536; time it with events on `stream`.  Errors: hot_pct
+ * outside [0, 100], cold_bytes not a positive multiple of 128, iters < 1, blocks < 1, in_flight
+ * not 1/2, buf or out null, or buf_bytes too small -> MOE_ERR_INVALID_ARG; 16 MiB + blocks *
+ * cold_bytes >= 2 GiB -> MOE_ERR_UNSUPPORTED; launch -> MOE_ERR_HIP.
+ */
+int moe_delivery_probe(int32_t hot_pct, int64_t cold_bytes, int32_t iters, int32_t in_flight, int32_t blocks,
+                       const void* buf, int64_t buf_bytes, float* out, void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

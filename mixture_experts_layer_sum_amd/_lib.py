@@ -24,7 +24,7 @@ EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_permu
            "moe_combine", "farskip_stack_forward", "farskip_attn_moe_stack_forward",
            "farskip_attn_moe_stack_workspace_bytes", "farskip_stack_forward_mxfp8", "farskip_stack_mxfp8_workspace_bytes",
            "farskip_stack_workspace_bytes", "moe_profile_enable", "moe_profile_collect",
-           "moe_profile_collect_intervals", "moe_workspace_bytes", "moe_mfma_ceiling", "moe_last_error",
+           "moe_profile_collect_intervals", "moe_workspace_bytes", "moe_mfma_ceiling", "moe_delivery_probe", "moe_last_error",
            "moe_version")
 # moe_op_t: the operations moe_workspace_bytes knows
 MOE_OPS = {"permute": 0, "grouped_swiglu": 1, "grouped_swiglu_mxfp8": 2, "mxfp8_phase": 3, "stack": 4,
@@ -153,6 +153,8 @@ def _declare(lib):
     lib.moe_workspace_bytes.argtypes = [i, i64, i64, i32, i32, i64, i32, i64, i]
     lib.moe_mfma_ceiling.argtypes = [i, i32, i32, vp, vp]
     lib.moe_mfma_ceiling.restype = i
+    lib.moe_delivery_probe.argtypes = [i32, i64, i32, i32, i32, vp, i64, vp, vp]
+    lib.moe_delivery_probe.restype = i
     lib.moe_workspace_bytes.restype = sz
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p

@@ -405,3 +405,27 @@ def test_mfma_ceiling_argument_errors():
     err(f(0, 0, 4, BAD, None), L.MOE_ERR_INVALID_ARG)
     err(f(1, 10, 0, BAD, None), L.MOE_ERR_INVALID_ARG)
     err(f(0, 10, 4, None, None), L.MOE_ERR_INVALID_ARG, "out")
+
+
+def test_delivery_probe_argument_errors():
+    """The operand-delivery diagnostic checks its arguments on the host before any launch."""
+    f = lib.moe_delivery_probe
+    MB = 1 << 20
+    ok = dict(hot=50, cold=512 * 1024, iters=10, infl=1, blocks=4, buf=BAD, nbytes=16 * MB + 4 * 512 * 1024, out=BAD)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["hot"], a["cold"], a["iters"], a["infl"], a["blocks"], a["buf"], a["nbytes"], a["out"], None)
+
+    err(call(hot=-1), L.MOE_ERR_INVALID_ARG, "hot_pct")
+    err(call(hot=101), L.MOE_ERR_INVALID_ARG, "hot_pct")
+    err(call(cold=0), L.MOE_ERR_INVALID_ARG, "cold_bytes")
+    err(call(cold=1000), L.MOE_ERR_INVALID_ARG, "cold_bytes")
+    err(call(iters=0), L.MOE_ERR_INVALID_ARG)
+    err(call(blocks=0), L.MOE_ERR_INVALID_ARG)
+    err(call(infl=3), L.MOE_ERR_INVALID_ARG, "in_flight")
+    err(call(buf=None), L.MOE_ERR_INVALID_ARG, "null")
+    err(call(out=None), L.MOE_ERR_INVALID_ARG, "null")
+    err(call(nbytes=16 * MB), L.MOE_ERR_INVALID_ARG, "buf_bytes")
+    err(call(cold=8 * MB, blocks=256, nbytes=1 << 31), L.MOE_ERR_UNSUPPORTED, "2 GiB")
+

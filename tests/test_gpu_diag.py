@@ -1,5 +1,7 @@
-"""The register-only MFMA diagnostic (moe_mfma_ceiling) on the GPU: both shapes run, every thread
-writes its value, and the throughput is within the chip's dense bf16 figure."""
+"""The diagnostics on the GPU: the register-only MFMA launch (moe_mfma_ceiling) runs both shapes,
+every thread writes its value, and the throughput is within the chip's dense bf16 figure; the
+operand-delivery launch (moe_delivery_probe) lands every stage in LDS, and more L2 hits deliver
+faster."""
 import pytest
 import torch
 
@@ -22,3 +24,32 @@ def test_mfma_ceiling_runs(shape):
     tflops = blocks * 8 * iters * 262144 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     print(f"shape {shape}: {tflops:.0f} TFLOP/s")
     assert 100.0 < tflops < 2600.0
+
+
+def test_delivery_probe_lands_stages():
+    """Every workgroup's two LDS stages hold bytes of the buffer (all 0x01, so each thread's sum of
+    one byte per stage is exactly 2), for both ring depths; an all-hot stream is faster than one
+    whose runs all come from cold regions beyond the memory-side cache."""
+    from mixture_experts_layer_sum_amd import ops
+    MB = 1 << 20
+    blocks, cold = 256, 4 * MB
+    buf = torch.ones(16 * MB + blocks * cold, dtype=torch.uint8, device="cuda")
+    out = torch.full((blocks * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    rate = {}
+    for infl in (1, 2):
+        for hot, iters in ((100, 400), (0, 64)):
+            out.fill_(float("nan"))
+            ops.delivery_probe(hot, cold, iters, infl, buf, out)
+            torch.cuda.synchronize()
+            assert torch.equal(out, torch.full_like(out, 2.0)), (hot, infl)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ops.delivery_probe(hot, cold, iters, infl, buf, out)
+            e1.record()
+            torch.cuda.synchronize()
+            rate[(hot, infl)] = blocks * iters * 65536 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            print(f"hot {hot}% in flight {infl}: {rate[(hot, infl)]:.2f} TB/s")
+    for infl in (1, 2):
+        assert rate[(100, infl)] > rate[(0, infl)]
+        assert rate[(0, infl)] < 9.0   # cold runs come from HBM: below its 8 TB/s figure, with margin
+
