@@ -126,7 +126,10 @@ __device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? (r & 7) : ((r 
 
 // ROWS (ROWS_GROUPED / ROWS_SINGLE / ROWS_GATHER) also gives routed and shared launches their own
 // symbols, so profilers report them separately.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS, int BK_ = kBK, int S_ = kStages>
+// BNT: B (weight) rows are loaded with the nontemporal hint, for groups that fit in one M-tile, whose
+// weight lines no other workgroup reads.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int ROWS, int BK_ = kBK, int S_ = kStages,
+          bool BNT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p) {
   constexpr int NT = 64 * WAVES_M * WAVES_N, NW = NT / 64;
   constexpr int BK = BK_, S = S_;
@@ -273,8 +276,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_bf16(GemmArgs p
       _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
         FSM_LDS_DMA16(second ? rG : rU, &FSM_SM(BUF)[BM * BK + (wave * B_RUNS + i) * 512], dB[i] + kbb); \
     } else {                                                                                       \
-      _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                           \
-        FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);      \
+      _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i) {                                         \
+        if (BNT) FSM_LDS_DMA16_NT(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb); \
+        else FSM_LDS_DMA16(rBw, &FSM_SM(BUF)[BM * BK + (wb_row0 + i * RUN_ROWS) * BK], dB[i] + kb);    \
+      }                                                                                            \
     }                                                                                              \
   }
 #define FSM_BROW(J) \
@@ -588,9 +593,12 @@ void tile_rows(int64_t N, int32_t G, int64_t c, int dtype, int& bm1, int& bm2) {
 }
 
 // Both phases of the bf16 grouped product with tile configurations C1 (gate/up) and C2 (down).
+// stream_b: the routed launches load their weights with the nontemporal hint (64-row tiles only).
 template <const TileCfg& C1, const TileCfg& C2>
 int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t mt1, int64_t mt2, int64_t c,
-                     int64_t d, int32_t G, hipStream_t s, hipEvent_t mid, const int* kinds) {
+                     int64_t d, int32_t G, hipStream_t s, hipEvent_t mid, const int* kinds, bool stream_b) {
+  constexpr bool kSmall = C1.bm == kS1.bm && C2.bm == kS2.bm;
+  stream_b = stream_b && kSmall;
   a1.group_m = C1.gm;
   a1.n_tiles = int32_t(cdiv(c, C1.bn / 2));
   a1.quad_nb = quad_width(a1.n_tiles, a1.group_m);
@@ -598,8 +606,12 @@ int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t m
   constexpr int nt1 = 64 * C1.wm * C1.wn;
   {
     ProfScope prof(kinds ? kinds[0] : G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);
-    if (rows1 == ROWS_GATHER)
+    if (rows1 == ROWS_GATHER && stream_b)
+      k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GATHER, C1.bk, C1.st, kSmall><<<grid1, nt1, 0, s>>>(a1);
+    else if (rows1 == ROWS_GATHER)
       k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GATHER, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
+    else if (rows1 == ROWS_GROUPED && stream_b)
+      k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GROUPED, C1.bk, C1.st, kSmall><<<grid1, nt1, 0, s>>>(a1);
     else if (rows1 == ROWS_GROUPED)
       k_gemm_bf16<C1.bm, C1.bn, C1.wm, C1.wn, EPI_SWIGLU, ROWS_GROUPED, C1.bk, C1.st><<<grid1, nt1, 0, s>>>(a1);
     else
@@ -616,7 +628,9 @@ int launch_bf16_pair(GemmArgs& a1, GemmArgs& a2, int rows1, int rows2, int64_t m
   const dim3 grid2(unsigned(quad_grid(mt2, a2.n_tiles, a2.group_m, a2.quad_nb)));
   constexpr int nt2 = 64 * C2.wm * C2.wn;
   ProfScope prof(kinds ? kinds[1] : G > 1 ? MOE_K_GEMM_DOWN : MOE_K_DENSE_DOWN, s);
-  if (rows2 == ROWS_GROUPED)
+  if (rows2 == ROWS_GROUPED && stream_b)
+    k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_GROUPED, C2.bk, C2.st, kSmall><<<grid2, nt2, 0, s>>>(a2);
+  else if (rows2 == ROWS_GROUPED)
     k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_GROUPED, C2.bk, C2.st><<<grid2, nt2, 0, s>>>(a2);
   else
     k_gemm_bf16<C2.bm, C2.bn, C2.wm, C2.wn, EPI_PLAIN, ROWS_SINGLE, C2.bk, C2.st><<<grid2, nt2, 0, s>>>(a2);
@@ -700,9 +714,13 @@ int launch_grouped_swiglu(const void* X, const int32_t* offsets, int32_t G, cons
 
   const int rows1 = gather ? ROWS_GATHER : (G > 1 ? ROWS_GROUPED : ROWS_SINGLE);
   const int rows2 = G > 1 ? ROWS_GROUPED : ROWS_SINGLE;
+  // Routed groups that average at most one 64-row tile: each expert's weights are read by one M-tile
+  // per N-tile, so they stream past the caches (the shared expert's weights are reused by every
+  // M-tile and keep the default policy).
+  const bool stream_b = G > 1 && N <= int64_t(kS1.bm) * G;
   if (bf && small_tiles(N, G, c, dtype))
-    return launch_bf16_pair<kS1, kS2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds);
-  if (bf) return launch_bf16_pair<kP1, kP2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds);
+    return launch_bf16_pair<kS1, kS2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds, stream_b);
+  if (bf) return launch_bf16_pair<kP1, kP2>(a1, a2, rows1, rows2, mt1, mt2, c, d, G, s, mid, kinds, false);
   a1.n_tiles = int32_t(cdiv(c, F_BN));
   {
     ProfScope prof(kinds ? kinds[0] : G > 1 ? MOE_K_GEMM_GATE_UP : MOE_K_DENSE_GATE_UP, s);

@@ -116,7 +116,9 @@ struct MxArgs {
 // stages for the prefill-sized groups; 64 x 256 with 4 waves and three stages for groups of a few
 // dozen rows (a decode batch), where the product streams the weights and more bytes in flight per
 // CU matter more than the MFMA work.  Both sum every output over K in the same order.
-template <int EPI, int ROWS, int BM_ = 256, int WAVES_M_ = 2, int S_ = 2, bool SB = false>
+// BNT: the weight codes are loaded with the nontemporal hint (groups that fit in one M-tile, whose
+// weight lines no other workgroup reads).
+template <int EPI, int ROWS, int BM_ = 256, int WAVES_M_ = 2, int S_ = 2, bool SB = false, bool BNT = false>
 __global__ __launch_bounds__(256 * WAVES_M_) void k_gemm_mx(MxArgs p) {
   constexpr int BM = BM_, BN = 256, WAVES_M = WAVES_M_, WAVES_N = 4, NW = WAVES_M * WAVES_N, S = S_;
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
@@ -242,8 +244,10 @@ __global__ __launch_bounds__(256 * WAVES_M_) void k_gemm_mx(MxArgs p) {
     const uint32_t kb = uint32_t(KT) * RB + kb_zero;                                            \
     _Pragma("unroll") for (int i = 0; i < A_RUNS; ++i)                                          \
       FSM_LDS_DMA16(rA, &MX_SM(BUF)[(wave * A_RUNS + i) * RUN_ROWS * RB], dA[i] + kb); \
-    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i)                                          \
-      FSM_LDS_DMA16(rB, &MX_SM(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb);  \
+    _Pragma("unroll") for (int i = 0; i < B_RUNS; ++i) {                                        \
+      if (BNT) FSM_LDS_DMA16_NT(rB, &MX_SM(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb); \
+      else FSM_LDS_DMA16(rB, &MX_SM(BUF)[(BM + wb_row0 + i * RUN_ROWS) * RB], dB[i] + kb);      \
+    }                                                                                           \
     if (!SB) {                                                                                  \
       _Pragma("unroll") for (int i = 0; i < SL; ++i)                                            \
         FSM_LDS_DMA4(rS[i], &MX_SM(BUF)[DATA + (i * NW + wave) * 64 * 4], dS[i] + uint32_t(KT) * 4u + kb_zero); \
@@ -435,6 +439,8 @@ bool mx_small(int64_t N, int32_t G, int64_t c) {
   return N <= int64_t(MX_SMALL_ROWS) * G || (cdiv(N, MX_BM) + G) * cdiv(c, MX_BN / 2) < 256;
 }
 int mx_bm(int64_t N, int32_t G, int64_t c) { return mx_small(N, G, c) ? MX_SMALL_BM : MX_BM; }
+// routed groups that average at most one 64-row tile stream their weights (read once) past the caches
+bool mx_stream_b(int64_t N, int32_t G) { return G > 1 && N <= int64_t(MX_SMALL_BM) * G; }
 int64_t mx_max_tiles(int64_t N, int32_t G, int bm) { return cdiv(N, bm) + G; }
 
 // workspace: the M-tile table, then (fused call only) H's codes and scales
@@ -476,10 +482,15 @@ int mx_gate_up(const uint8_t* Xq, const uint8_t* Xs, const int32_t* offsets, int
   a.gather = gather; a.gather_k = gather_k; a.a_rows = x_rows;
   ProfScope prof(G > 1 ? MOE_K_MX_GATE_UP : MOE_K_MX_DENSE_GATE_UP, s);
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
-  if (bm == MX_SMALL_BM && gather)
+  const bool stream_b = mx_stream_b(N, G);
+  if (bm == MX_SMALL_BM && gather && stream_b)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER, MX_SMALL_BM, 1, 3, false, true><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM && gather)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GATHER, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
   else if (bm == MX_SMALL_BM && G == 1)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_SINGLE, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM && stream_b)
+    k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3, false, true><<<grid, 256, 0, s>>>(a);
   else if (bm == MX_SMALL_BM)
     k_gemm_mx<MX_SWIGLU, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
   else if (d % 512 == 0 && gather)
@@ -511,6 +522,8 @@ int mx_down(const uint8_t* Hq, const uint8_t* Hs, const int32_t* offsets, int32_
   const dim3 grid(unsigned(quad_grid(mx_max_tiles(N, G, bm), a.n_tiles, a.group_m, a.quad_nb)));
   if (bm == MX_SMALL_BM && G == 1)
     k_gemm_mx<MX_PLAIN, MX_ROWS_SINGLE, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
+  else if (bm == MX_SMALL_BM && mx_stream_b(N, G))
+    k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3, false, true><<<grid, 256, 0, s>>>(a);
   else if (bm == MX_SMALL_BM)
     k_gemm_mx<MX_PLAIN, MX_ROWS_GROUPED, MX_SMALL_BM, 1, 3><<<grid, 256, 0, s>>>(a);
   else if (c % 512 == 0 && G == 1)

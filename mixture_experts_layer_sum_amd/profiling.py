@@ -64,13 +64,15 @@ def _col(row, *names):
 
 def gemm_args(name: str):
     """Template arguments of a k_gemm_bf16 symbol as ints (BM, BN, waves_m, waves_n, epilogue, rows,
-    ...), or None for other kernels."""
+    ..., with true / false as 1 / 0), or None for other kernels."""
     i = name.find("k_gemm_bf16<")
     if i < 0:
         return None
     j = name.find(">", i)
+    flags = {"true": 1, "false": 0}
     try:
-        return tuple(int(a) for a in name[i + len("k_gemm_bf16<"):j].split(","))
+        return tuple(flags[a.strip()] if a.strip() in flags else int(a)
+                     for a in name[i + len("k_gemm_bf16<"):j].split(","))
     except ValueError:
         return None
 

@@ -73,6 +73,10 @@ def test_gemm_symbol_classification():
     shared = "void fsm::k_gemm_bf16<256, 256, 2, 4, 1, 1, 64, 2>(fsm::GemmArgs)"
     assert not profiling.is_routed_gate_up(shared) and not profiling.is_routed(shared)
     assert not profiling.is_routed(R) and profiling.gemm_args("fsm::k_combine(int)") is None
+    # the weight-streaming flag of the 64-row tiles prints as a bool
+    nt = "void fsm::k_gemm_bf16<64, 256, 1, 4, 1, 2, 64, 3, true>(fsm::GemmArgs)"
+    assert profiling.gemm_args(nt) == (64, 256, 1, 4, 1, 2, 64, 3, 1) and profiling.is_routed_gate_up(nt)
+    assert profiling.is_routed_gate_up("void fsm::k_gemm_bf16<256, 256, 2, 4, 1, 2, 64, 2, false>(fsm::GemmArgs)")
 
 
 def test_overlap_of_intervals():
