@@ -354,6 +354,8 @@ def standalone(c, layers, o0, reps: int = 20) -> dict:
     for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
         ms = timed(lambda: ops.mfma_ceiling(shape, probe, iters), 3)
         mfma[name] = round(1024 * 8 * iters * 262144 / (ms * 1e-3) / 1e12, 1)
+    ms = timed(lambda: ops.mfma_ceiling(2, probe, iters // 4), 3)   # scaled fp8, 4x the FLOP per MFMA
+    mfma_fp8 = round(1024 * 8 * (iters // 4) * 1048576 / (ms * 1e-3) / 1e12, 1)
     nbytes = a.numel() * 4
     del a, b, m, n
     # the committed counter summary holds the DSV3 stack's products; other workloads get the bounds only
@@ -363,6 +365,7 @@ def standalone(c, layers, o0, reps: int = 20) -> dict:
         "device_fill_GBps": round(nbytes / (ms_fill * 1e-3) / 1e9, 1),
         "hipblaslt_bf16_8192cubed_TFLOPs": round(2 * 8192**3 / (ms_mm * 1e-3) / 1e12, 1),
         "mfma_register_only_bf16_TFLOPs": mfma,
+        "mfma_register_only_fp8_scaled_16x16x128_TFLOPs": mfma_fp8,
         "operand_delivery": delivery,
     }
     # each kernel against the box's measured ceiling of its kind, beside its fraction of the peak
@@ -1088,6 +1091,13 @@ def main():
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
+        # the MXFP8 products against the chip's register-only scaled fp8 MFMA rate
+        fp8 = (result["standalone"] or {}).get("ceilings", {}).get("mfma_register_only_fp8_scaled_16x16x128_TFLOPs")
+        if fp8 and isinstance(result.get("mxfp8"), dict):
+            for kind in ("mx_gate_up", "mx_down"):
+                v = result["mxfp8"].get(kind)
+                if isinstance(v, dict) and "tflops" in v:
+                    v["frac_of_mfma_ceiling"] = round(v["tflops"] / fp8, 4)
     if args.configs and c.name == "dsv3-stack":
         log("timing one layer of each smaller workload")
         result["configs"] = leg("configs", lambda: per_config(cpu=bool(args.cpu_configs and args.cpu_sample)))

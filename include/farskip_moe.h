@@ -566,14 +566,17 @@ int moe_profile_collect_intervals(moe_kernel_time_t* out, moe_kernel_interval_t*
  * Diagnostic, not part of the method: the chip's register-only bf16 MFMA throughput, the ceiling
  * the products' MFMA fractions can be read against (the published dense peak assumes a clock the
  * chip does not hold under a full matrix load).  Launches `blocks` workgroups of 512 threads on
- * `stream`; each of their waves runs `iters` rounds of independent MFMAs on register operands with
- * no memory traffic, 262 144 FLOP per wave and round for either shape, and writes one float per
- * thread to out.
- *   shape   0: v_mfma_f32_16x16x32_bf16 (the instruction the bf16 products use);
- *           1: v_mfma_f32_32x32x16_bf16
+ * `stream`; each of their waves runs `iters` rounds of 16 independent MFMAs on register operands
+ * with no memory traffic, and writes one float per thread to out.
+ *   shape   0: v_mfma_f32_16x16x32_bf16 (the instruction the bf16 products use), 262 144 FLOP per
+ *              wave and round;
+ *           1: v_mfma_f32_32x32x16_bf16 (8 accumulators), 262 144 FLOP per wave and round;
+ *           2: v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3 codes (the MXFP8 products' instruction),
+ *              1 048 576 FLOP per wave and round
  *   out     device buffer of blocks * 512 floats (caller-owned; values meaningless)
- * FLOP of one launch = blocks * 8 * iters * 262144; time it with events on `stream`.  Errors:
- * shape not 0/1, iters < 1, blocks < 1 or out null -> MOE_ERR_INVALID_ARG; launch -> MOE_ERR_HIP.
+ * FLOP of one launch = blocks * 8 * iters * (FLOP per wave and round); time it with events on
+ * `stream`.  Errors: shape not 0/1/2, iters < 1, blocks < 1 or out null -> MOE_ERR_INVALID_ARG;
+ * launch -> MOE_ERR_HIP.
  */
 int moe_mfma_ceiling(int shape, int32_t iters, int32_t blocks, float* out, void* stream);
 

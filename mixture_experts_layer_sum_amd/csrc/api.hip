@@ -887,7 +887,7 @@ size_t moe_workspace_bytes(int op, int64_t T, int64_t d, int32_t E, int32_t k, i
 }
 
 int moe_mfma_ceiling(int shape, int32_t iters, int32_t blocks, float* out, void* stream) {
-  if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARG, "moe_mfma_ceiling: shape must be 0 or 1");
+  if (shape < 0 || shape > 2) return fail(MOE_ERR_INVALID_ARG, "moe_mfma_ceiling: shape must be 0, 1 or 2");
   if (iters < 1 || blocks < 1) return fail(MOE_ERR_INVALID_ARG, "moe_mfma_ceiling: iters and blocks must be >= 1");
   if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_mfma_ceiling: out is null");
   return fsm::launch_mfma_ceiling(shape, iters, blocks, out, static_cast<hipStream_t>(stream));

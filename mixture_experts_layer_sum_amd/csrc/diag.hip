@@ -6,8 +6,10 @@
 // memory traffic inside the loop, so the launch measures the matrix cores alone, at whatever clock
 // the chip holds under that load.  The two bf16 shapes a tile kernel can be built on are offered:
 // v_mfma_f32_16x16x32_bf16 (16 accumulators of 4 values per lane) and v_mfma_f32_32x32x16_bf16 (8
-// accumulators of 16 values per lane); both do 262 144 FLOP per wave and round.  The accumulators
-// are issued round-robin, so no MFMA waits for the one just before it in its wave.
+// accumulators of 16 values per lane), both 262 144 FLOP per wave and round, and the scaled fp8
+// instruction of the MXFP8 products, v_mfma_scale_f32_16x16x128_f8f6f4 (16 accumulators, 1 048 576
+// FLOP per wave and round).  The accumulators are issued round-robin, so no MFMA waits for the one
+// just before it in its wave.
 #include "common.h"
 #include "tile_kit.h"
 
@@ -32,6 +34,26 @@ __global__ __launch_bounds__(512) void k_mfma_ceiling(float* __restrict__ out, i
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  } else if (SHAPE == 2) {
+    // scaled fp8: 32 E4M3 codes per lane and operand, unit scales (E8M0 127); 65 536 FLOP per MFMA,
+    // so a round of 16 is 1 048 576 FLOP per wave
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    v8i fa, fb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fa[i] = int(0x38383838u + uint32_t(threadIdx.x & 7) + uint32_t(seed > 1.f));
+      fb[i] = int(0x30303030u + uint32_t(i));
+    }
+    f32x4 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, acc[j], 0, 0, 0, 127, 0, 127);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
@@ -109,7 +131,8 @@ int launch_delivery_probe(int hot_pct, int64_t cold_bytes, int iters, int in_fli
 
 int launch_mfma_ceiling(int shape, int iters, int blocks, float* out, hipStream_t s) {
   if (shape == 0) k_mfma_ceiling<0><<<blocks, 512, 0, s>>>(out, iters, 1e-3f);
-  else k_mfma_ceiling<1><<<blocks, 512, 0, s>>>(out, iters, 1e-3f);
+  else if (shape == 1) k_mfma_ceiling<1><<<blocks, 512, 0, s>>>(out, iters, 1e-3f);
+  else k_mfma_ceiling<2><<<blocks, 512, 0, s>>>(out, iters, 1e-3f);
   return check_launch("mfma ceiling");
 }
 

@@ -352,8 +352,9 @@ def farskip_stack_backward(layers: Sequence[dict], cfg: StackCfg, mode, o0, dOL,
 
 
 def mfma_ceiling(shape: int, out, iters: int, stream=None) -> None:
-    """Diagnostic: one register-only MFMA launch (shape 0 = 16x16x32, 1 = 32x32x16 bf16) of
-    out.numel() // 512 workgroups; FLOP = workgroups * 8 * iters * 262144."""
+    """Diagnostic: one register-only MFMA launch (shape 0 = 16x16x32, 1 = 32x32x16 bf16, 2 = scaled
+    fp8 16x16x128) of out.numel() // 512 workgroups; FLOP = workgroups * 8 * iters * 262144 for the
+    bf16 shapes, * 1048576 for the fp8 one."""
     check("moe_mfma_ceiling", lib.moe_mfma_ceiling(int(shape), int(iters), out.numel() // 512, _p(out), _s(stream)))
 
 

@@ -400,7 +400,7 @@ def test_attn_stack_argument_errors():
 def test_mfma_ceiling_argument_errors():
     """The register-only MFMA diagnostic checks its arguments on the host before any launch."""
     f = lib.moe_mfma_ceiling
-    err(f(2, 10, 4, BAD, None), L.MOE_ERR_INVALID_ARG, "shape")
+    err(f(3, 10, 4, BAD, None), L.MOE_ERR_INVALID_ARG, "shape")
     err(f(-1, 10, 4, BAD, None), L.MOE_ERR_INVALID_ARG, "shape")
     err(f(0, 0, 4, BAD, None), L.MOE_ERR_INVALID_ARG)
     err(f(1, 10, 0, BAD, None), L.MOE_ERR_INVALID_ARG)
