@@ -368,6 +368,14 @@ def test_grouped_swiglu_small_tiles_bitwise_equal_large(ops):
     _, Y_large = run_swiglu(ops, X, sizes, W1[:g].contiguous(), W2[:g].contiguous(), W3[:g].contiguous())
     off, Y_small = run_swiglu(ops, X, sizes + extra, W1, W2, W3)
     assert torch.equal(Y_large, Y_small)
+    # 30 more empty groups take the average to at most 64 rows (one 64-row tile per group on
+    # average), where the routed launches stream the weights with the nontemporal hint: the cache
+    # policy changes no value
+    more = [0] * 30
+    Gm = G + len(more)
+    W1m, W2m, W3m = (torch.cat([w, w[:len(more)]]) for w in (W1, W2, W3))
+    _, Y_stream = run_swiglu(ops, X, sizes + extra + more, W1m, W2m, W3m)
+    assert N <= 64 * Gm < 96 * Gm and torch.equal(Y_stream, Y_small)
     ref = oracle.grouped_mlp(to_np(X), off, ExpertSlices(W1), ExpertSlices(W2), ExpertSlices(W3))
     assert_parity(to_np(Y_small), ref, torch.bfloat16, "64-row tiles")
 
