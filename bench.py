@@ -1091,6 +1091,16 @@ def main():
     if args.standalone:
         log("timing the single calls alone and the ceilings")
         result["standalone"] = leg("standalone", lambda: standalone(c, layers, o0))
+        # the dominant kernel against its operand-delivery ceiling (both timed alone on the GPU)
+        sa = result["standalone"] if isinstance(result.get("standalone"), dict) else {}
+        gu = sa.get("gemm_gate_up", {})
+        dl = sa.get("ceilings", {}).get("operand_delivery", {}).get("gemm_gate_up", {})
+        if "frac_of_delivery_ceiling" in gu and dl:
+            result["roofline"]["operand_delivery"] = {
+                "l2_hit_pct": dl["l2_hit_pct"], "ceiling_TBps": dl["in_flight_1"]["TBps"],
+                "achieved_TBps": gu["operand_TBps"], "frac": gu["frac_of_delivery_ceiling"],
+                "what": "the kernel run alone: its 64 KiB operand stages per launch over its time, against the "
+                        "delivery probe at its L2 hit rate with one stage in flight (standalone.ceilings)"}
         # the MXFP8 products against the chip's register-only scaled fp8 MFMA rate
         fp8 = (result["standalone"] or {}).get("ceilings", {}).get("mfma_register_only_fp8_scaled_16x16x128_TFLOPs")
         if fp8 and isinstance(result.get("mxfp8"), dict):
