@@ -132,34 +132,37 @@ def delivery_ceilings(dev, hits: dict, tiles: dict) -> dict:
     MB, blocks, cold = 1 << 20, 256, 7 << 20
     buf = torch.ones(16 * MB + blocks * cold, dtype=torch.uint8, device=dev)
     out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
 
     def tbps(hot, infl, iters, cold_bytes=cold):
         ops.delivery_probe(hot, cold_bytes, iters, infl, buf, out)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        ops.delivery_probe(hot, cold_bytes, iters, infl, buf, out)
+        ops.delivery_probe(hot, cold_bytes, iters, infl, buf, out, clocks)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        return round(blocks * iters * 65536 / (ms * 1e-3) / 1e12, 2), round(ms * 1e3 / iters, 3)
+        cyc, ticks = clocks.tolist()
+        return {"TBps": round(blocks * iters * 65536 / (ms * 1e-3) / 1e12, 2), "us_per_stage": round(ms * 1e3 / iters, 3),
+                "clock_GHz": round(cyc / ticks * 0.1, 2) if ticks else None}
 
     res = {"what": "TB/s into LDS over 256 CUs and us per 64 KiB stage per CU; misses from HBM unless "
-                   "named memside"}
+                   "named memside; the shader clock workgroup 0 ran at"}
     for infl in (1, 2):
-        res[f"all_hit_in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(100, infl, 2000)))
-        res[f"all_hbm_in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(0, infl, 100)))
+        res[f"all_hit_in_flight_{infl}"] = tbps(100, infl, 2000)
+        res[f"all_hbm_in_flight_{infl}"] = tbps(0, infl, 100)
     for kind, hit in hits.items():
         hot = int(round(100 * hit))
         row = {"l2_hit_pct": hot}
         for infl in (1, 2):
-            row[f"in_flight_{infl}"] = dict(zip(("TBps", "us_per_stage"), tbps(hot, infl, 400)))
+            row[f"in_flight_{infl}"] = tbps(hot, infl, 400)
         # the same hit rate with every miss served by the memory-side cache (512 KiB cold regions)
-        row["memside_in_flight_1"] = dict(zip(("TBps", "us_per_stage"), tbps(hot, 1, 400, 512 << 10)))
+        row["memside_in_flight_1"] = tbps(hot, 1, 400, 512 << 10)
         if kind in tiles:
             row["operand_stages_per_launch"] = tiles[kind]
         res[kind] = row
-    del buf, out
+    del buf, out, clocks
     return res
 
 
@@ -1098,6 +1101,7 @@ def main():
         if "frac_of_delivery_ceiling" in gu and dl:
             result["roofline"]["operand_delivery"] = {
                 "l2_hit_pct": dl["l2_hit_pct"], "ceiling_TBps": dl["in_flight_1"]["TBps"],
+                "probe_clock_GHz": dl["in_flight_1"].get("clock_GHz"),
                 "achieved_TBps": gu["operand_TBps"], "frac": gu["frac_of_delivery_ceiling"],
                 "what": "the kernel run alone: its 64 KiB operand stages per launch over its time, against the "
                         "delivery probe at its L2 hit rate with one stage in flight (standalone.ceilings)"}

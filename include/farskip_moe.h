@@ -595,13 +595,16 @@ int moe_mfma_ceiling(int shape, int32_t iters, int32_t blocks, float* out, void*
  *              products: one stage loads while the other is read); 2: two stages in flight
  *   buf        device buffer of buf_bytes >= 16 MiB + blocks * cold_bytes (caller-owned; only read)
  *   out        device buffer of blocks * 512 floats: each thread's sum of one byte of each LDS stage
+ *   clocks     device buffer of 2 uint64 or NULL: workgroup 0's loop in shader-clock cycles
+ *              (s_memtime) and in ticks of the 100 MHz constant counter (s_memrealtime), so
+ *              clocks[0] / clocks[1] * 0.1 is the shader clock in GHz the probe ran at
  * Bytes of one launch = blocks * iters * 65536; time it with events on `stream`.  Errors: hot_pct
  * outside [0, 100], cold_bytes not a positive multiple of 128, iters < 1, blocks < 1, in_flight
  * not 1/2, buf or out null, or buf_bytes too small -> MOE_ERR_INVALID_ARG; 16 MiB + blocks *
  * cold_bytes >= 2 GiB -> MOE_ERR_UNSUPPORTED; launch -> MOE_ERR_HIP.
  */
 int moe_delivery_probe(int32_t hot_pct, int64_t cold_bytes, int32_t iters, int32_t in_flight, int32_t blocks,
-                       const void* buf, int64_t buf_bytes, float* out, void* stream);
+                       const void* buf, int64_t buf_bytes, float* out, uint64_t* clocks, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* moe_last_error(void);

@@ -153,7 +153,7 @@ def _declare(lib):
     lib.moe_workspace_bytes.argtypes = [i, i64, i64, i32, i32, i64, i32, i64, i]
     lib.moe_mfma_ceiling.argtypes = [i, i32, i32, vp, vp]
     lib.moe_mfma_ceiling.restype = i
-    lib.moe_delivery_probe.argtypes = [i32, i64, i32, i32, i32, vp, i64, vp, vp]
+    lib.moe_delivery_probe.argtypes = [i32, i64, i32, i32, i32, vp, i64, vp, vp, vp]
     lib.moe_delivery_probe.restype = i
     lib.moe_workspace_bytes.restype = sz
     lib.moe_last_error.argtypes = []

@@ -530,7 +530,7 @@ using namespace fsm;
 namespace fsm {
 // diag.hip: the operand-delivery launch behind moe_delivery_probe
 int launch_delivery_probe(int hot_pct, int64_t cold_bytes, int iters, int in_flight, int blocks,
-                          const void* buf, float* out, hipStream_t s);
+                          const void* buf, float* out, uint64_t* clocks, hipStream_t s);
 }  // namespace fsm
 
 extern "C" {
@@ -894,7 +894,7 @@ int moe_mfma_ceiling(int shape, int32_t iters, int32_t blocks, float* out, void*
 }
 
 int moe_delivery_probe(int32_t hot_pct, int64_t cold_bytes, int32_t iters, int32_t in_flight, int32_t blocks,
-                       const void* buf, int64_t buf_bytes, float* out, void* stream) {
+                       const void* buf, int64_t buf_bytes, float* out, uint64_t* clocks, void* stream) {
   if (hot_pct < 0 || hot_pct > 100) return fail(MOE_ERR_INVALID_ARG, "moe_delivery_probe: hot_pct must lie in [0, 100]");
   if (cold_bytes < 128 || cold_bytes % 128) return fail(MOE_ERR_INVALID_ARG, "moe_delivery_probe: cold_bytes must be a positive multiple of 128");
   if (iters < 1 || blocks < 1) return fail(MOE_ERR_INVALID_ARG, "moe_delivery_probe: iters and blocks must be >= 1");
@@ -903,7 +903,7 @@ int moe_delivery_probe(int32_t hot_pct, int64_t cold_bytes, int32_t iters, int32
   const int64_t need = (int64_t(16) << 20) + int64_t(blocks) * cold_bytes;
   if (need > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_delivery_probe: 16 MiB + blocks * cold_bytes must stay below 2 GiB");
   if (buf_bytes < need) return fail(MOE_ERR_INVALID_ARG, "moe_delivery_probe: buf_bytes < 16 MiB + blocks * cold_bytes");
-  return fsm::launch_delivery_probe(hot_pct, cold_bytes, iters, in_flight, blocks, buf, out,
+  return fsm::launch_delivery_probe(hot_pct, cold_bytes, iters, in_flight, blocks, buf, out, clocks,
                                     static_cast<hipStream_t>(stream));
 }
 

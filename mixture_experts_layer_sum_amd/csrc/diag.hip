@@ -88,13 +88,20 @@ __global__ __launch_bounds__(512) void k_mfma_ceiling(float* __restrict__ out, i
 template <int IN_FLIGHT>
 __global__ __launch_bounds__(512) void k_delivery_probe(const uint8_t* __restrict__ buf, uint32_t records,
                                                         uint32_t cold_bytes, int hot_pct, int iters,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, uint64_t* __restrict__ clocks) {
   constexpr int NW = 8, PER = 64 / NW, HOT_ROWS = (1 << 20) / 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][65536];
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(buf, records);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t cold_rows = cold_bytes / 128, cold_base = (16u << 20) + blockIdx.x * cold_bytes;
   uint32_t hrow = (blockIdx.x * 61u) % HOT_ROWS, crow = 0;
+  // block 0 times its own loop in shader-clock cycles and in ticks of the 100 MHz constant counter
+  const bool timer = clocks && blockIdx.x == 0 && threadIdx.x == 0;
+  uint64_t c0 = 0, r0 = 0;
+  if (timer) {
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   for (int it = 0; it < iters; ++it) {
     const int st = it & 1;
 #pragma unroll
@@ -113,19 +120,23 @@ __global__ __launch_bounds__(512) void k_delivery_probe(const uint8_t* __restric
     asm volatile("" ::: "memory");
   }
   __syncthreads();
+  if (timer) {
+    clocks[0] = __builtin_amdgcn_s_memtime() - c0;
+    clocks[1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
   out[int64_t(blockIdx.x) * 512 + threadIdx.x] = float(lds[0][threadIdx.x * 4]) + float(lds[1][threadIdx.x * 4]);
 }
 
 }  // namespace
 
 int launch_delivery_probe(int hot_pct, int64_t cold_bytes, int iters, int in_flight, int blocks,
-                          const void* buf, float* out, hipStream_t s) {
+                          const void* buf, float* out, uint64_t* clocks, hipStream_t s) {
   const uint32_t records = uint32_t((int64_t(16) << 20) + int64_t(blocks) * cold_bytes);
   const uint8_t* b = static_cast<const uint8_t*>(buf);
   if (in_flight == 1)
-    k_delivery_probe<1><<<blocks, 512, 0, s>>>(b, records, uint32_t(cold_bytes), hot_pct, iters, out);
+    k_delivery_probe<1><<<blocks, 512, 0, s>>>(b, records, uint32_t(cold_bytes), hot_pct, iters, out, clocks);
   else
-    k_delivery_probe<2><<<blocks, 512, 0, s>>>(b, records, uint32_t(cold_bytes), hot_pct, iters, out);
+    k_delivery_probe<2><<<blocks, 512, 0, s>>>(b, records, uint32_t(cold_bytes), hot_pct, iters, out, clocks);
   return check_launch("delivery probe");
 }
 

@@ -358,13 +358,16 @@ def mfma_ceiling(shape: int, out, iters: int, stream=None) -> None:
     check("moe_mfma_ceiling", lib.moe_mfma_ceiling(int(shape), int(iters), out.numel() // 512, _p(out), _s(stream)))
 
 
-def delivery_probe(hot_pct: int, cold_bytes: int, iters: int, in_flight: int, buf, out, stream=None) -> None:
+def delivery_probe(hot_pct: int, cold_bytes: int, iters: int, in_flight: int, buf, out, clocks=None,
+                   stream=None) -> None:
     """Diagnostic: one operand-delivery launch of out.numel() // 512 workgroups, each moving `iters`
     64 KiB stages into LDS with hot_pct percent of its 1 KiB runs from an L2-resident window and
-    the rest from its own cold region of cold_bytes in buf; bytes = workgroups * iters * 65536."""
+    the rest from its own cold region of cold_bytes in buf; bytes = workgroups * iters * 65536.
+    clocks (2 int64 on the device, or None): workgroup 0's loop in shader cycles and in 100 MHz ticks."""
     check("moe_delivery_probe", lib.moe_delivery_probe(int(hot_pct), int(cold_bytes), int(iters), int(in_flight),
                                                        out.numel() // 512, _p(buf), buf.numel() * buf.element_size(),
-                                                       _p(out), _s(stream)))
+                                                       _p(out), _p(clocks) if clocks is not None else None,
+                                                       _s(stream)))
 
 
 def profile_enable(on: bool = True) -> None:

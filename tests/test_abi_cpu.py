@@ -415,7 +415,7 @@ def test_delivery_probe_argument_errors():
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["hot"], a["cold"], a["iters"], a["infl"], a["blocks"], a["buf"], a["nbytes"], a["out"], None)
+        return f(a["hot"], a["cold"], a["iters"], a["infl"], a["blocks"], a["buf"], a["nbytes"], a["out"], None, None)
 
     err(call(hot=-1), L.MOE_ERR_INVALID_ARG, "hot_pct")
     err(call(hot=101), L.MOE_ERR_INVALID_ARG, "hot_pct")

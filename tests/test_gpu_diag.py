@@ -29,8 +29,9 @@ def test_mfma_ceiling_runs(shape):
 
 def test_delivery_probe_lands_stages():
     """Every workgroup's two LDS stages hold bytes of the buffer (all 0x01, so each thread's sum of
-    one byte per stage is exactly 2), for both ring depths; an all-hot stream is faster than one
-    whose runs all come from cold regions beyond the memory-side cache."""
+    one byte per stage is exactly 2), for both ring depths; workgroup 0's clock readout is a shader
+    clock; an all-hot stream is faster than one whose runs all come from cold regions beyond the
+    memory-side cache."""
     from mixture_experts_layer_sum_amd import ops
     MB = 1 << 20
     blocks, cold = 256, 4 * MB
@@ -40,9 +41,14 @@ def test_delivery_probe_lands_stages():
     for infl in (1, 2):
         for hot, iters in ((100, 400), (0, 64)):
             out.fill_(float("nan"))
-            ops.delivery_probe(hot, cold, iters, infl, buf, out)
+            clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+            ops.delivery_probe(hot, cold, iters, infl, buf, out, clocks)
             torch.cuda.synchronize()
             assert torch.equal(out, torch.full_like(out, 2.0)), (hot, infl)
+            cyc, ticks = clocks.tolist()
+            ghz = cyc / ticks * 0.1
+            print(f"hot {hot}% in flight {infl}: shader clock {ghz:.2f} GHz")
+            assert 0.3 < ghz < 3.5   # a shader clock, read against the 100 MHz counter
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             ops.delivery_probe(hot, cold, iters, infl, buf, out)
